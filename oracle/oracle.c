@@ -1,0 +1,188 @@
+/*
+ * oracle.c — plain, slow, obviously correct fp64 CPU reference for the
+ * half-precision GEMM and the lower-triangular transposed TRMM.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product library links, includes
+ * or calls this file; only the test suite, the smoke check and the CPU
+ * baseline leg of the benchmark load it.  It shares no code, header or table
+ * with the HIP path.
+ *
+ * Sources (web pages, cited by title and section):
+ *  - "Nvidia Tensor Core-MMA PTX编程入门", §4 (示例): the HGEMM problem
+ *    statement, C = A·B with A M×K row-major, B K×N column-major (element
+ *    (k, n) at B[k + n·K]) and C M×N row-major, all operands fp16.
+ *  - "GPU架构与CUDA", section 共享内存与分块 (tiled matmul): out-of-range
+ *    operands contribute nothing and only in-range outputs are written; and
+ *    section 混合精度核函数: fp16 products accumulated in a wider type.
+ *  - "异构计算中高性能TRMM与TRSM的递归算法实现", §2.1–§2.2: B <- α·Aᵀ·B for
+ *    lower-triangular A.
+ *
+ * The oracle computes each output straight from its definition, in fp64.
+ * fp16 inputs convert to fp64 exactly, every fp16×fp16 product is exact in
+ * fp64 (11+11 significand bits), so the only rounding is fp64 summation.
+ *
+ * Conventions: fp16 operands are passed as their IEEE-754 binary16 bit
+ * patterns (uint16_t).  HGEMM matrices use the layouts above with general
+ * leading dimensions.  TRMM matrices are column-major: element (r, c) of a
+ * column-major matrix X with leading dimension ldx sits at X[r + c·ldx].
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+
+/* ---- IEEE 754 binary16 decoding, from the format definition ----------------
+ * 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits.
+ *   exponent 0        : subnormal, value = fraction · 2^-24
+ *   exponent 1..30    : normal,    value = (1024 + fraction) · 2^(exponent-25)
+ *   exponent 31       : infinity (fraction 0) or NaN
+ */
+double oracle_half_to_double(uint16_t h)
+{
+    const int sign = (h >> 15) & 1;
+    const int expo = (h >> 10) & 0x1f;
+    const int frac = h & 0x3ff;
+    double v;
+    if (expo == 0)
+        v = ldexp((double)frac, -24);
+    else if (expo == 31)
+        v = frac ? NAN : INFINITY;
+    else
+        v = ldexp((double)(1024 + frac), expo - 25);
+    return sign ? -v : v;
+}
+
+/* Decoding every pattern once keeps the triple loops below affordable; each
+ * entry is exactly oracle_half_to_double of its index. */
+static double g_h2d[65536];
+static int g_h2d_ready = 0;
+
+static void h2d_init(void)
+{
+    if (g_h2d_ready)
+        return;
+    for (int i = 0; i < 65536; ++i)
+        g_h2d[i] = oracle_half_to_double((uint16_t)i);
+    g_h2d_ready = 1;
+}
+
+static double cin_value(const void *Cin, int cin_dtype, int64_t idx)
+{
+    if (cin_dtype == 0)
+        return g_h2d[((const uint16_t *)Cin)[idx]];
+    return (double)((const float *)Cin)[idx];
+}
+
+/* ---- HGEMM: ref = α·A·B + β·C_in ------------------------------------------
+ * A   : M×K row-major fp16, element (i,k) at A[i*lda + k]
+ * B   : K×N column-major fp16, element (k,j) at B[j*ldb + k]
+ * Cin : M×N row-major, fp16 (cin_dtype 0) or fp32 (cin_dtype 1); read only
+ *       when beta != 0 (BLAS convention, so a NaN-filled C_in with β = 0
+ *       does not leak into the result)
+ * ref : M×N row-major fp64, element (i,j) at ref[i*ldr + j]
+ * When alpha == 0 the product is not formed (A and B are not read).
+ */
+void oracle_hgemm(int64_t M, int64_t N, int64_t K, double alpha,
+                  const uint16_t *A, int64_t lda,
+                  const uint16_t *B, int64_t ldb,
+                  double beta, const void *Cin, int64_t ldc, int cin_dtype,
+                  double *ref, int64_t ldr)
+{
+    h2d_init();
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < M; ++i) {
+        for (int64_t j = 0; j < N; ++j) {
+            double acc = 0.0;
+            if (alpha != 0.0) {
+                for (int64_t k = 0; k < K; ++k)
+                    acc += g_h2d[A[i * lda + k]] * g_h2d[B[j * ldb + k]];
+            }
+            double r = alpha * acc;
+            if (beta != 0.0)
+                r += beta * cin_value(Cin, cin_dtype, i * ldc + j);
+            ref[i * ldr + j] = r;
+        }
+    }
+}
+
+/* Same definition, evaluated only at the listed (rows[s], cols[s]). */
+void oracle_hgemm_sampled(int64_t K, double alpha,
+                          const uint16_t *A, int64_t lda,
+                          const uint16_t *B, int64_t ldb,
+                          double beta, const void *Cin, int64_t ldc,
+                          int cin_dtype, int64_t nsamp, const int64_t *rows,
+                          const int64_t *cols, double *ref)
+{
+    h2d_init();
+#pragma omp parallel for schedule(dynamic, 8)
+    for (int64_t s = 0; s < nsamp; ++s) {
+        const int64_t i = rows[s], j = cols[s];
+        double acc = 0.0;
+        if (alpha != 0.0) {
+            for (int64_t k = 0; k < K; ++k)
+                acc += g_h2d[A[i * lda + k]] * g_h2d[B[j * ldb + k]];
+        }
+        double r = alpha * acc;
+        if (beta != 0.0)
+            r += beta * cin_value(Cin, cin_dtype, i * ldc + j);
+        ref[s] = r;
+    }
+}
+
+/* ---- TRMM, left side, A lower triangular, transposed ----------------------
+ * ref(i,j) = α · Σ_{k=i}^{n-1} A(k,i) · B(k,j)   for 0 <= i < n, 0 <= j < m
+ * This is (α·Aᵀ·B)(i,j) with the strictly upper triangle of A taken as zero:
+ * A(k,i) for k < i is never read.
+ * A : n×n column-major fp16 (lda >= n); B : n×m column-major fp16 (ldb >= n)
+ * ref : n×m column-major fp64, element (i,j) at ref[i + j*ldr]
+ */
+void oracle_trmm_lower_trans(int64_t n, int64_t m, double alpha,
+                             const uint16_t *A, int64_t lda,
+                             const uint16_t *B, int64_t ldb,
+                             double *ref, int64_t ldr)
+{
+    h2d_init();
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t j = 0; j < m; ++j) {
+        for (int64_t i = 0; i < n; ++i) {
+            double acc = 0.0;
+            for (int64_t k = i; k < n; ++k)
+                acc += g_h2d[A[k + i * lda]] * g_h2d[B[k + j * ldb]];
+            ref[i + j * ldr] = alpha * acc;
+        }
+    }
+}
+
+/* Same definition at the listed (rows[s], cols[s]) = (i, j) pairs. */
+void oracle_trmm_lower_trans_sampled(int64_t n, double alpha,
+                                     const uint16_t *A, int64_t lda,
+                                     const uint16_t *B, int64_t ldb,
+                                     int64_t nsamp, const int64_t *rows,
+                                     const int64_t *cols, double *ref)
+{
+    h2d_init();
+#pragma omp parallel for schedule(dynamic, 8)
+    for (int64_t s = 0; s < nsamp; ++s) {
+        const int64_t i = rows[s], j = cols[s];
+        double acc = 0.0;
+        for (int64_t k = i; k < n; ++k)
+            acc += g_h2d[A[k + i * lda]] * g_h2d[B[k + j * ldb]];
+        ref[s] = alpha * acc;
+    }
+}
+
+/* Number of OpenMP threads a parallel region here would use. */
+int oracle_num_threads(void)
+{
+    int t = 1;
+#pragma omp parallel
+    {
+#pragma omp single
+        {
+#ifdef _OPENMP
+            extern int omp_get_num_threads(void);
+            t = omp_get_num_threads();
+#endif
+        }
+    }
+    return t;
+}

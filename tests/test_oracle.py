@@ -1,0 +1,245 @@
+"""Pins for the fp64 oracle: checks against facts that do not come from the
+oracle itself (closed forms, a library routine, brute force, the block
+identity of the triangular multiply).  CPU only.
+
+Pages: "Nvidia Tensor Core-MMA PTX编程入门" §4 (HGEMM layouts),
+"GPU架构与CUDA" 共享内存与分块 / 混合精度核函数, "异构计算中高性能TRMM与TRSM的
+递归算法实现" §2.1–§2.2 (TRMM definition and block recursion).
+"""
+import itertools
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+
+
+def _np_gemm(A, Bt, alpha=1.0, beta=0.0, C=None):
+    """numpy fp64 matmul as an independent special case of the definition."""
+    r = alpha * (A.astype(np.float64) @ Bt.astype(np.float64).T)
+    if beta != 0.0:
+        r = r + beta * C.astype(np.float64)
+    return r
+
+
+# ---------------------------------------------------------------- decoding
+def test_half_decode_matches_numpy_for_every_pattern():
+    bits = np.arange(65536, dtype=np.uint16)
+    ref = bits.view(np.float16).astype(np.float64)
+    got = np.array([oracle.half_to_double(int(b)) for b in bits])
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    # sign of zero is kept
+    assert np.signbit(got[0x8000]) and not np.signbit(got[0])
+
+
+# ---------------------------------------------------------------- HGEMM pins
+@pytest.mark.parametrize("M,N,K", [(1, 1, 1), (3, 5, 7), (17, 9, 33), (32, 32, 16), (5, 64, 100)])
+def test_hgemm_matches_numpy_matmul(M, N, K):
+    rng = np.random.default_rng(M * 1000 + N * 10 + K)
+    A = workloads.uniform_f16(rng, (M, K))
+    Bt = workloads.uniform_f16(rng, (N, K))
+    C = workloads.uniform_f16(rng, (M, N))
+    for alpha, beta in [(1.0, 0.0), (1.5, 0.5), (-2.0, 1.0)]:
+        got = oracle.hgemm(A, Bt, alpha, beta, C)
+        ref = _np_gemm(A, Bt, alpha, beta, C)
+        np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_hgemm_brute_force_python_loops():
+    rng = np.random.default_rng(7)
+    M, N, K = 4, 3, 6
+    A = workloads.uniform_f16(rng, (M, K))
+    Bt = workloads.uniform_f16(rng, (N, K))
+    C = workloads.uniform_f16(rng, (M, N)).astype(np.float32)
+    got = oracle.hgemm(A, Bt, 0.75, -1.25, C)
+    for i in range(M):
+        for j in range(N):
+            s = 0.0
+            for k in range(K):
+                s += float(A[i, k]) * float(Bt[j, k])
+            assert got[i, j] == pytest.approx(0.75 * s - 1.25 * float(C[i, j]), abs=1e-13)
+
+
+def test_hgemm_strided_operands():
+    """General leading dimensions: a view into a wider buffer gives the same result."""
+    rng = np.random.default_rng(11)
+    Abig = workloads.uniform_f16(rng, (9, 40))
+    Bbig = workloads.uniform_f16(rng, (7, 48))
+    Cbig = workloads.uniform_f16(rng, (9, 20))
+    A, Bt, C = Abig[:, :33], Bbig[:, :33], Cbig[:, :7]
+    got = oracle.hgemm(A, Bt, 1.0, 2.0, C)
+    ref = oracle.hgemm(A.copy(), Bt.copy(), 1.0, 2.0, C.copy())
+    assert np.array_equal(got, ref)
+    np.testing.assert_allclose(got, _np_gemm(A, Bt, 1.0, 2.0, C), rtol=1e-12, atol=1e-12)
+
+
+def test_identity_gives_A_exactly():
+    rng = np.random.default_rng(3)
+    A = workloads.uniform_f16(rng, (37, 29))
+    I = np.eye(29, dtype=np.float16)        # B = I; its column-major storage is I too
+    got = oracle.hgemm(A, I)
+    assert np.array_equal(got, A.astype(np.float64))
+
+
+@pytest.mark.parametrize("K", [1, 256, 1000])
+def test_all_ones_give_K(K):
+    A = np.ones((6, K), np.float16)
+    Bt = np.ones((5, K), np.float16)
+    assert np.all(oracle.hgemm(A, Bt) == K)
+    C = np.ones((6, 5), np.float16)
+    assert np.all(oracle.hgemm(A, Bt, 1.5, 0.5, C) == 1.5 * K + 0.5)
+
+
+def test_rank_one_outer_product():
+    vals = np.array([-2, -1, -0.5, 0.5, 1, 2], np.float16)
+    u, v = vals, vals[::-1].copy()
+    K = 77
+    A = np.repeat(u[:, None], K, axis=1)
+    Bt = np.repeat(v[:, None], K, axis=1)
+    got = oracle.hgemm(A, Bt)
+    assert np.array_equal(got, K * np.outer(u.astype(np.float64), v.astype(np.float64)))
+
+
+def test_beta_zero_does_not_read_C():
+    rng = np.random.default_rng(5)
+    A = workloads.uniform_f16(rng, (8, 16))
+    Bt = workloads.uniform_f16(rng, (8, 16))
+    C = np.full((8, 8), np.nan, np.float16)
+    got = oracle.hgemm(A, Bt, 1.0, 0.0, C)
+    assert np.isfinite(got).all()
+    assert np.array_equal(got, oracle.hgemm(A, Bt))
+
+
+def test_alpha_zero_does_not_read_A_B():
+    A = np.full((4, 9), np.nan, np.float16)
+    Bt = np.full((3, 9), np.inf, np.float16)
+    C = np.arange(12, dtype=np.float32).reshape(4, 3)
+    got = oracle.hgemm(A, Bt, 0.0, 2.0, C)
+    assert np.array_equal(got, 2.0 * C.astype(np.float64))
+
+
+def test_integer_inputs_exact():
+    rng = np.random.default_rng(9)
+    A = workloads.integer_f16(rng, (20, 300))
+    Bt = workloads.integer_f16(rng, (30, 300))
+    got = oracle.hgemm(A, Bt)
+    exact = A.astype(np.int64) @ Bt.astype(np.int64).T
+    assert np.array_equal(got, exact.astype(np.float64))
+
+
+def test_hgemm_sampled_equals_full():
+    rng = np.random.default_rng(12)
+    A = workloads.uniform_f16(rng, (50, 70))
+    Bt = workloads.uniform_f16(rng, (40, 70))
+    C = workloads.uniform_f16(rng, (50, 40))
+    full = oracle.hgemm(A, Bt, 1.5, 0.5, C)
+    ri, cj = workloads.sample_indices(1, 50, 40, 64)
+    got = oracle.hgemm_sampled(A, Bt, ri, cj, 1.5, 0.5, C)
+    assert np.array_equal(got, full[ri, cj])
+
+
+def test_swap_symmetry():
+    """(A·B)ᵀ = Bᵀ·Aᵀ: swapping operand roles transposes the result."""
+    rng = np.random.default_rng(13)
+    A = workloads.uniform_f16(rng, (11, 23))
+    Bt = workloads.uniform_f16(rng, (7, 23))
+    assert np.array_equal(oracle.hgemm(Bt, A), oracle.hgemm(A, Bt).T)
+
+
+# ---------------------------------------------------------------- TRMM pins
+def _trmm_inputs(n, m, seed, upper_fill=0.0):
+    rng = np.random.default_rng(seed)
+    S = workloads.uniform_f16(rng, (n, n))
+    D = workloads.uniform_f16(rng, (n,), 0.5, 1.5)
+    B = workloads.uniform_f16(rng, (n, m))
+    A = np.tril(S, -1)
+    A[np.arange(n), np.arange(n)] = D
+    A[np.triu_indices(n, 1)] = upper_fill
+    return A, B     # logical [row, col]
+
+
+@pytest.mark.parametrize("n,m", [(1, 1), (5, 3), (33, 17), (64, 8)])
+def test_trmm_matches_dense_zeroed_upper(n, m):
+    A, B = _trmm_inputs(n, m, n + m)
+    got = oracle.trmm_lower_trans(np.ascontiguousarray(A.T), np.ascontiguousarray(B.T), 1.25)
+    ref = 1.25 * (np.tril(A).astype(np.float64).T @ B.astype(np.float64))
+    np.testing.assert_allclose(got.T, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_trmm_brute_force_python_loops():
+    A, B = _trmm_inputs(6, 4, 1)
+    got = oracle.trmm_lower_trans(np.ascontiguousarray(A.T), np.ascontiguousarray(B.T), -0.5)
+    for i in range(6):
+        for j in range(4):
+            s = sum(float(A[k, i]) * float(B[k, j]) for k in range(i, 6))
+            assert got[j, i] == pytest.approx(-0.5 * s, abs=1e-13)
+
+
+def test_trmm_upper_triangle_not_referenced():
+    A0, B = _trmm_inputs(40, 9, 2, 0.0)
+    An, _ = _trmm_inputs(40, 9, 2, np.nan)
+    Ab, _ = _trmm_inputs(40, 9, 2, 1e4)
+    ref = oracle.trmm_lower_trans(np.ascontiguousarray(A0.T), np.ascontiguousarray(B.T))
+    for Ax in (An, Ab):
+        got = oracle.trmm_lower_trans(np.ascontiguousarray(Ax.T), np.ascontiguousarray(B.T))
+        assert np.array_equal(got, ref)
+
+
+def test_trmm_identity():
+    rng = np.random.default_rng(4)
+    B = workloads.uniform_f16(rng, (30, 6))
+    I = np.eye(30, dtype=np.float16)
+    got = oracle.trmm_lower_trans(I, np.ascontiguousarray(B.T), 2.0)
+    assert np.array_equal(got, 2.0 * B.T.astype(np.float64))
+
+
+def test_trmm_tril_ones_closed_form():
+    n, m = 50, 5
+    A = np.tril(np.ones((n, n), np.float16))
+    B = np.ones((n, m), np.float16)
+    got = oracle.trmm_lower_trans(np.ascontiguousarray(A.T), np.ascontiguousarray(B.T), 3.0)
+    expect = 3.0 * (n - np.arange(n, dtype=np.float64))
+    assert np.array_equal(got, np.tile(expect, (m, 1)))
+
+
+def test_trmm_block_recursion_identity():
+    """With A = [[A11,0],[A21,A22]]: Aᵀ·B = [A11ᵀB1 + A21ᵀB2 ; A22ᵀB2]."""
+    n, m, h = 24, 5, 10
+    A, B = _trmm_inputs(n, m, 8)
+    full = oracle.trmm_lower_trans(np.ascontiguousarray(A.T), np.ascontiguousarray(B.T))
+    top = oracle.trmm_lower_trans(np.ascontiguousarray(A[:h, :h].T), np.ascontiguousarray(B[:h].T))
+    upd = oracle.hgemm(np.ascontiguousarray(B[h:].T), np.ascontiguousarray(A[h:, :h].T))  # (A21ᵀB2)ᵀ
+    bot = oracle.trmm_lower_trans(np.ascontiguousarray(A[h:, h:].T), np.ascontiguousarray(B[h:].T))
+    np.testing.assert_allclose(full[:, :h], top + upd, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(full[:, h:], bot, rtol=1e-12, atol=1e-12)
+
+
+def test_trmm_integer_exact():
+    rng = np.random.default_rng(21)
+    n, m = 70, 11
+    A = np.tril(workloads.integer_f16(rng, (n, n)))
+    B = workloads.integer_f16(rng, (n, m))
+    got = oracle.trmm_lower_trans(np.ascontiguousarray(A.T), np.ascontiguousarray(B.T))
+    exact = A.astype(np.int64).T @ B.astype(np.int64)
+    assert np.array_equal(got, exact.T.astype(np.float64))
+
+
+def test_trmm_sampled_equals_full():
+    A, B = _trmm_inputs(45, 13, 6)
+    Acm, Bcm = np.ascontiguousarray(A.T), np.ascontiguousarray(B.T)
+    full = oracle.trmm_lower_trans(Acm, Bcm, 0.5)
+    ri, cj = workloads.sample_indices(4, 45, 13, 100)
+    got = oracle.trmm_lower_trans_sampled(Acm, Bcm, ri, cj, 0.5)
+    assert np.array_equal(got, full[cj, ri])
+
+
+def test_empty_shapes():
+    A = np.zeros((0, 5), np.float16)
+    Bt = np.zeros((3, 5), np.float16)
+    assert oracle.hgemm(A, Bt).shape == (0, 3)
+    A = np.ones((4, 0), np.float16)
+    Bt = np.ones((3, 0), np.float16)
+    assert np.array_equal(oracle.hgemm(A, Bt), np.zeros((4, 3)))
