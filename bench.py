@@ -1,0 +1,187 @@
+"""Benchmark of the hot path on one MI355X.
+
+One step = one pass over the whole path on resident synthetic inputs:
+  * HGEMM M = N = K = 8192, fp16 A (row-major) and B (column-major), fp32
+    accumulation, fp32 C, alpha = 1, beta = 0;
+  * TRMM Out = Aᵀ·B, n = m = 8192, A lower triangular fp16, B fp16, Out fp32,
+    recursion split at n/2 down to 256-leaves.
+
+Prints one JSON line.  `value` is the HGEMM throughput in TFLOP/s (2·M·N·K per
+call over the average HGEMM kernel time, measured with HIP events on the
+stream the kernels run on); the TRMM time per call is reported next to it.
+`roofline` prices the HGEMM kernel against the dense fp16 MFMA peak;
+`cpu_baseline` times the fp64 oracle on a bounded row block of the same
+HGEMM on this host's cores.
+
+    python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--no-cpu-baseline]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_FP16_TFLOPS = 2516.6   # 256 CU × 4096 flop/clk/CU × 2.4 GHz, dense fp16 MFMA
+PEAK_HBM_GBS = 8000.0
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in ("hg_kernels.hip", "hg_api.cpp", "hg_internal.h"):
+        with open(os.path.join(ROOT, "half_precision_gemm_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(src_hash):
+    """HBM bytes per HGEMM launch from the committed rocprofv3 counter runs,
+    if they were taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "hgemm_8192_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("kernel_source_sha256_16") != src_hash:
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(A, Bt, target_s=12.0):
+    """The oracle as it stands on a row block of the 8192³ HGEMM, sized for
+    about target_s seconds; reported as TFLOP/s of that block."""
+    import numpy as np
+    import oracle
+    K = A.shape[1]
+    r = 8
+    t0 = time.perf_counter()
+    oracle.hgemm(np.ascontiguousarray(A[:r]), Bt)
+    dt = time.perf_counter() - t0
+    rows = int(max(8, min(A.shape[0], r * target_s / max(dt, 1e-6))))
+    t0 = time.perf_counter()
+    oracle.hgemm(np.ascontiguousarray(A[:rows]), Bt)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * rows * Bt.shape[0] * K
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"fp64 oracle on rows 0..{rows - 1} of the 8192^3 HGEMM "
+                      f"({rows}x{Bt.shape[0]} outputs, K={K}), {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-trmm", action="store_true", help="time the HGEMM alone")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the path is a single-GPU kernel; multi-GPU sharding is a design note only)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import half_precision_gemm_amd as hg
+    import workloads
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wg = workloads.WORKLOADS["hgemm_8192"]
+    wt = workloads.WORKLOADS["trmm_8192"]
+    A, Bt, _ = workloads.gemm_inputs(wg)
+    Ad = torch.from_numpy(A).to(dev)
+    Btd = torch.from_numpy(Bt).to(dev)
+    Cd = torch.empty((wg.M, wg.N), dtype=torch.float32, device=dev)
+    do_trmm = not args.no_trmm
+    if do_trmm:
+        TA, TB = workloads.trmm_inputs(wt)
+        TAd = torch.from_numpy(TA).to(dev)
+        TBd = torch.from_numpy(TB).to(dev)
+        del TA, TB
+        TOut = torch.empty((wt.m, wt.n), dtype=torch.float32, device=dev)
+
+    stream = torch.cuda.current_stream(dev)
+
+    def step(evs=None):
+        if evs is not None:
+            evs[0].record(stream)
+        hg.hgemm(Ad, Btd, Cd, wg.alpha, wg.beta)
+        if evs is not None:
+            evs[1].record(stream)
+        if do_trmm:
+            hg.trmm_lower_trans(TAd, TBd, TOut, wt.alpha, wt.leaf)
+            if evs is not None:
+                evs[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for k in range(args.steps):
+        step(evs[k])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    gemm_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    trmm_ms = [e[1].elapsed_time(e[2]) for e in evs] if do_trmm else []
+    gemm_avg = sum(gemm_ms) / len(gemm_ms)
+    tflops = wg.flops / (gemm_avg * 1e-3) / 1e12
+    print(f"[bench] timed {args.steps} steps: hgemm avg {gemm_avg:.4f} ms "
+          f"(min {min(gemm_ms):.4f}), {tflops:.1f} TFLOP/s", file=sys.stderr, flush=True)
+
+    src_hash = kernel_source_hash()
+    out = {
+        "metric": "HGEMM TFLOP/s + % of MI355X FP16 MFMA peak at 8192^3; TRMM ms at n=8192",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(total_ms / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16 in, f32 accumulate",
+        "data": "synthetic: numpy PCG64 uniform[-1,1] rounded to fp16, seeds 3 (HGEMM) and 4 (TRMM)",
+        "config": {"workload": "hgemm_8192 + trmm_8192",
+                   "hgemm": {"M": wg.M, "N": wg.N, "K": wg.K, "A": "row-major fp16",
+                             "B": "col-major fp16", "C": "fp32", "alpha": 1.0, "beta": 0.0},
+                   "trmm": ({"n": wt.n, "m": wt.m, "leaf": wt.leaf, "out": "fp32",
+                             "A": "lower, col-major fp16", "B": "col-major fp16"}
+                            if do_trmm else None)},
+        "pct_of_fp16_mfma_peak": round(100.0 * tflops / PEAK_FP16_TFLOPS, 2),
+        "hgemm_ms": {"avg": round(gemm_avg, 4), "min": round(min(gemm_ms), 4),
+                     "max": round(max(gemm_ms), 4)},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_FP16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_FP16_TFLOPS, 4),
+                     "traffic": traffic_from_profiles(src_hash),
+                     "kernel": "hgemm_kernel<256x256x64> at M=N=K=8192, fp32 out",
+                     "algorithmic_flops_per_launch": wg.flops},
+        "kernel_source_sha256_16": src_hash,
+    }
+    if do_trmm:
+        tavg = sum(trmm_ms) / len(trmm_ms)
+        out["trmm_ms"] = {"avg": round(tavg, 4), "min": round(min(trmm_ms), 4),
+                          "max": round(max(trmm_ms), 4)}
+        out["trmm_effective_tflops"] = round(wt.flops / (tavg * 1e-3) / 1e12, 2)
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle) ...", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(A, Bt)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

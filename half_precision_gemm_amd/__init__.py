@@ -1,0 +1,133 @@
+"""Python binding of libhgemm.so, the MI355X (gfx950) half-precision GEMM and
+recursive TRMM library whose C ABI is declared in include/hgemm.h.
+
+Argument marshalling only: every step of the computation runs in the
+library's HIP kernels.  PyTorch supplies device memory and the current
+stream.  There is no fallback: if the library is missing or fails to load,
+importing this package raises.
+
+    hgemm(A, Bt, C, alpha=1.0, beta=0.0)
+        C = alpha·A·B + beta·C.  A: (M, K) float16, row-major.  Bt: (N, K)
+        float16, which is B (K×N) stored column-major.  C: (M, N) float16 or
+        float32, row-major.  Each needs unit stride along its last axis; row
+        strides become lda / ldb / ldc.
+
+    trmm_lower_trans(A, B, Out, alpha=1.0, leaf=256)
+        Out = alpha·Aᵀ·B with A lower triangular (strict upper never read).
+        Column-major matrices are passed as their row-major transposes:
+        A is an (n, n) float16 tensor whose row c is column c of A; B is
+        (m, n) float16 whose row j is column j of B; Out is (m, n) float32
+        in the same convention.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libhgemm.so")
+
+HG_F16 = 0
+HG_F32 = 1
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
+                      "or python -m half_precision_gemm_amd.build")
+
+lib = ctypes.CDLL(LIB_PATH)
+_i64, _f32, _vp, _int = ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_int
+lib.hgemm.argtypes = [_i64, _i64, _i64, _f32, _vp, _i64, _vp, _i64, _f32, _vp, _i64, _int, _vp]
+lib.hgemm.restype = _int
+lib.trmm_lower_trans.argtypes = [_i64, _i64, _f32, _vp, _i64, _vp, _i64, _vp, _i64, _int, _i64,
+                                 _vp]
+lib.trmm_lower_trans.restype = _int
+lib.hg_strerror.argtypes = [_int]
+lib.hg_strerror.restype = ctypes.c_char_p
+lib.hg_trmm_plan.argtypes = [_i64, _i64, ctypes.POINTER(_i64), _i64]
+lib.hg_trmm_plan.restype = _i64
+
+EXPORTS = ("hgemm", "trmm_lower_trans", "hg_strerror", "hg_trmm_plan")
+
+
+class HgError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed with status {status}: "
+                         f"{lib.hg_strerror(status).decode()}")
+
+
+def strerror(status: int) -> str:
+    return lib.hg_strerror(status).decode()
+
+
+def _stream_handle(t):
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _check_matrix(t, name, dtypes):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be 2-D")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.numel() and t.shape[1] > 1 and t.stride(1) != 1:
+        raise ValueError(f"{name} needs unit stride along its last axis")
+
+
+def _ld(t) -> int:
+    return max(1, t.stride(0)) if t.shape[0] > 1 else max(1, t.shape[1])
+
+
+def hgemm(A, Bt, C, alpha: float = 1.0, beta: float = 0.0):
+    """C = alpha·A·B + beta·C on the current stream; returns C."""
+    import torch
+    _check_matrix(A, "A", (torch.float16,))
+    _check_matrix(Bt, "Bt", (torch.float16,))
+    _check_matrix(C, "C", (torch.float16, torch.float32))
+    M, K = A.shape
+    N = Bt.shape[0]
+    if Bt.shape[1] != K or tuple(C.shape) != (M, N):
+        raise ValueError(f"shape mismatch: A {tuple(A.shape)}, Bt {tuple(Bt.shape)}, "
+                         f"C {tuple(C.shape)}")
+    out_dtype = HG_F16 if C.dtype == torch.float16 else HG_F32
+    st = lib.hgemm(M, N, K, float(alpha), A.data_ptr() or None, _ld(A), Bt.data_ptr() or None,
+                   _ld(Bt), float(beta), C.data_ptr() or None, _ld(C), out_dtype,
+                   _stream_handle(C))
+    if st != 0:
+        raise HgError("hgemm", st)
+    return C
+
+
+def trmm_lower_trans(A, B, Out, alpha: float = 1.0, leaf: int = 256):
+    """Out = alpha·Aᵀ·B (A lower triangular) on the current stream; returns Out."""
+    import torch
+    _check_matrix(A, "A", (torch.float16,))
+    _check_matrix(B, "B", (torch.float16,))
+    _check_matrix(Out, "Out", (torch.float32,))
+    n = A.shape[0]
+    m = B.shape[0]
+    if tuple(A.shape) != (n, n) or B.shape[1] != n or tuple(Out.shape) != (m, n):
+        raise ValueError(f"shape mismatch: A {tuple(A.shape)}, B {tuple(B.shape)}, "
+                         f"Out {tuple(Out.shape)}")
+    st = lib.trmm_lower_trans(n, m, float(alpha), A.data_ptr() or None, _ld(A),
+                              B.data_ptr() or None, _ld(B), Out.data_ptr() or None, _ld(Out),
+                              HG_F32, int(leaf), _stream_handle(Out))
+    if st != 0:
+        raise HgError("trmm_lower_trans", st)
+    return Out
+
+
+def trmm_plan(n: int, leaf: int = 256):
+    """The recursion trmm_lower_trans runs: list of (kind, offset, size, depth),
+    kind 0 = leaf, 1 = update (see hg_trmm_plan in include/hgemm.h)."""
+    cnt = lib.hg_trmm_plan(n, leaf, None, 0)
+    if cnt < 0:
+        raise HgError("hg_trmm_plan", int(cnt))
+    buf = (_i64 * (4 * cnt))()
+    lib.hg_trmm_plan(n, leaf, buf, cnt)
+    return [tuple(buf[4 * i:4 * i + 4]) for i in range(cnt)]

@@ -1,0 +1,281 @@
+// hg_api.cpp — host side of the C ABI declared in include/hgemm.h: argument
+// validation (BLAS xerbla-style status codes), quick returns, kernel
+// selection, and the recursive TRMM driver of
+// "异构计算中高性能TRMM与TRSM的递归算法实现" §2.1–§2.2.
+#include "hgemm.h"
+
+#include <stdint.h>
+
+#include <algorithm>
+#include <vector>
+
+#include "hg_internal.h"
+
+namespace {
+
+constexpr int64_t kI32Max = 0x7fffffff;
+
+struct Extent {
+    uintptr_t lo, hi;  // [lo, hi) in bytes; empty when lo == hi
+};
+
+Extent extent(const void *p, int64_t rows, int64_t ld, int64_t cols, int64_t esize)
+{
+    if (rows <= 0 || cols <= 0 || p == nullptr)
+        return {0, 0};
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+    return {lo, lo + (uintptr_t)(((rows - 1) * ld + cols) * esize)};
+}
+
+bool overlap(const Extent &a, const Extent &b)
+{
+    return a.lo < a.hi && b.lo < b.hi && a.lo < b.hi && b.lo < a.hi;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? HG_OK : HG_ERR_HIP_BASE + (int)e; }
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+// Recursion of the TRMM driver, depth first: for a diagonal block (o, s),
+// s <= leaf is a leaf; otherwise with h = floor(s/2): recurse on (o, h),
+// update rows o..o+h-1 from the block below the diagonal, recurse on
+// (o+h, s-h).
+struct Node {
+    int64_t kind, o, s, depth;
+};
+
+void plan_rec(int64_t o, int64_t s, int64_t leaf, int64_t depth, std::vector<Node> &out)
+{
+    if (s <= leaf) {
+        out.push_back({0, o, s, depth});
+        return;
+    }
+    const int64_t h = s / 2;
+    plan_rec(o, h, leaf, depth + 1, out);
+    out.push_back({1, o, s, depth});
+    plan_rec(o + h, s - h, leaf, depth + 1, out);
+}
+
+hg::Tile choose_batched_tile(int64_t M, int64_t maxN, int64_t nbatch)
+{
+    const int64_t big = ((M + 255) / 256) * ((maxN + 255) / 256) * nbatch;
+    if (big >= 256)
+        return hg::Tile::Big;
+    const int64_t mid = ((M + 127) / 128) * ((maxN + 127) / 128) * nbatch;
+    if (mid >= 128)
+        return hg::Tile::Mid;
+    return hg::Tile::Small;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *hg_strerror(int status)
+{
+    if (status == HG_OK)
+        return "success";
+    if (status >= HG_ERR_HIP_BASE)
+        return hipGetErrorString(static_cast<hipError_t>(status - HG_ERR_HIP_BASE));
+    switch (status) {
+    case -1: return "invalid argument 1";
+    case -2: return "invalid argument 2";
+    case -3: return "invalid argument 3";
+    case -4: return "invalid argument 4";
+    case -5: return "invalid argument 5";
+    case -6: return "invalid argument 6";
+    case -7: return "invalid argument 7";
+    case -8: return "invalid argument 8";
+    case -9: return "invalid argument 9";
+    case -10: return "invalid argument 10";
+    case -11: return "invalid argument 11";
+    case -12: return "invalid argument 12";
+    case -13: return "invalid argument 13";
+    default: return "unknown status";
+    }
+}
+
+int hgemm(int64_t M, int64_t N, int64_t K, float alpha, const void *A, int64_t lda, const void *B,
+          int64_t ldb, float beta, void *C, int64_t ldc, int out_dtype, void *stream)
+{
+    if (M < 0 || M > kI32Max)
+        return -1;
+    if (N < 0 || N > kI32Max)
+        return -2;
+    if (K < 0 || K > kI32Max)
+        return -3;
+    if (lda < std::max<int64_t>(1, K))
+        return -6;
+    if (ldb < std::max<int64_t>(1, K))
+        return -8;
+    if (ldc < std::max<int64_t>(1, N))
+        return -11;
+    if (out_dtype != HG_F16 && out_dtype != HG_F32)
+        return -12;
+    if (M == 0 || N == 0)
+        return HG_OK;
+    if (C == nullptr)
+        return -10;
+    const bool out_f16 = out_dtype == HG_F16;
+    const int64_t esize = out_f16 ? 2 : 4;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (alpha == 0.0f || K == 0)
+        return hip_status(hg::launch_scale(C, ldc, M, N, beta, out_f16, s));
+    if (A == nullptr)
+        return -5;
+    if (B == nullptr)
+        return -7;
+    const Extent ec = extent(C, M, ldc, N, esize);
+    if (overlap(ec, extent(A, M, lda, K, 2)) || overlap(ec, extent(B, N, ldb, K, 2)))
+        return -10;
+
+    hg::GemmParams p{};
+    p.A = static_cast<const _Float16 *>(A);
+    p.B = static_cast<const _Float16 *>(B);
+    p.C = C;
+    p.lda = lda;
+    p.ldb = ldb;
+    p.ldc = ldc;
+    p.M = (int32_t)M;
+    p.nbatch = 1;
+    p.alpha = alpha;
+    p.beta = beta;
+    p.e[0] = {0, 0, 0, (int32_t)N, (int32_t)K};
+    hg::LaunchOpts o{};
+    o.out_f16 = out_f16;
+    o.beta_read = beta != 0.0f;
+    o.tri = false;
+    o.vec = aligned16(A) && aligned16(B) && lda % 8 == 0 && ldb % 8 == 0;
+    o.tile = hg::choose_tile(M, N, K);
+    return hip_status(hg::launch_gemm(p, o, s));
+}
+
+int64_t hg_trmm_plan(int64_t n, int64_t leaf, int64_t *nodes, int64_t cap)
+{
+    if (n < 0)
+        return -1;
+    if (nodes == nullptr && cap > 0)
+        return -2;
+    if (leaf <= 0)
+        leaf = 256;
+    std::vector<Node> v;
+    if (n > 0)
+        plan_rec(0, n, leaf, 0, v);
+    for (int64_t i = 0; i < (int64_t)v.size() && i < cap; ++i) {
+        nodes[4 * i + 0] = v[i].kind;
+        nodes[4 * i + 1] = v[i].o;
+        nodes[4 * i + 2] = v[i].s;
+        nodes[4 * i + 3] = v[i].depth;
+    }
+    return (int64_t)v.size();
+}
+
+int trmm_lower_trans(int64_t n, int64_t m, float alpha, const void *A, int64_t lda, const void *B,
+                     int64_t ldb, void *Out, int64_t ldo, int out_dtype, int64_t leaf,
+                     void *stream)
+{
+    if (n < 0 || n > kI32Max)
+        return -1;
+    if (m < 0 || m > kI32Max)
+        return -2;
+    if (lda < std::max<int64_t>(1, n))
+        return -5;
+    if (ldb < std::max<int64_t>(1, n))
+        return -7;
+    if (ldo < std::max<int64_t>(1, n))
+        return -9;
+    if (out_dtype != HG_F32)
+        return -10;
+    if (n == 0 || m == 0)
+        return HG_OK;
+    if (Out == nullptr)
+        return -8;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (leaf <= 0)
+        leaf = 256;
+    // Out (column-major n×m) seen as row-major m×n with leading dimension ldo.
+    if (alpha == 0.0f)
+        return hip_status(hg::launch_scale(Out, ldo, m, n, 0.0f, false, s));
+    if (A == nullptr)
+        return -4;
+    if (B == nullptr)
+        return -6;
+    const Extent eo = extent(Out, m, ldo, n, 4);
+    if (overlap(eo, extent(A, n, lda, n, 2)) || overlap(eo, extent(B, m, ldb, n, 2)))
+        return -8;
+
+    std::vector<Node> plan;
+    plan_rec(0, n, leaf, 0, plan);
+    int64_t max_depth = 0;
+    for (const Node &x : plan)
+        max_depth = std::max(max_depth, x.depth);
+
+    // Every GEMM here is in the row-major view of the column-major operands:
+    //   C'(j, i) = Out(o+i, j)             C' = Out + o,        ldc = ldo
+    //   A'(j, k) = B(o+h+k, j)  (M'=m)     A' = B + o+h,        lda' = ldb
+    //   B'(i, k) = A(o+h+k, o+i) (N'×K')   B' = A + o·lda+o+h,  ldb' = lda
+    // i.e. Out1ᵀ += alpha·B2ᵀ·A21, the transpose of Out1 += alpha·A21ᵀ·B2.
+    hg::GemmParams base{};
+    base.A = static_cast<const _Float16 *>(B);
+    base.B = static_cast<const _Float16 *>(A);
+    base.C = Out;
+    base.lda = ldb;
+    base.ldb = lda;
+    base.ldc = ldo;
+    base.M = (int32_t)m;
+    base.alpha = alpha;
+    const bool base_vec = aligned16(A) && aligned16(B) && lda % 8 == 0 && ldb % 8 == 0;
+
+    auto run_batch = [&](const std::vector<hg::BatchEntry> &ents, bool tri, float beta) -> int {
+        for (size_t first = 0; first < ents.size(); first += hg::kMaxBatch) {
+            hg::GemmParams p = base;
+            p.beta = beta;
+            const size_t cnt = std::min<size_t>(hg::kMaxBatch, ents.size() - first);
+            p.nbatch = (int32_t)cnt;
+            bool vec = base_vec;
+            int64_t maxN = 0;
+            for (size_t i = 0; i < cnt; ++i) {
+                p.e[i] = ents[first + i];
+                vec = vec && p.e[i].a_off % 8 == 0 && p.e[i].b_off % 8 == 0;
+                maxN = std::max<int64_t>(maxN, p.e[i].N);
+            }
+            hg::LaunchOpts o{};
+            o.out_f16 = false;
+            o.beta_read = beta != 0.0f;
+            o.tri = tri;
+            o.vec = vec;
+            o.tile = choose_batched_tile(m, maxN, (int64_t)cnt);
+            const hipError_t e = hg::launch_gemm(p, o, s);
+            if (e != hipSuccess)
+                return hip_status(e);
+        }
+        return HG_OK;
+    };
+
+    // Leaves: Out(o+i, j) = alpha·Σ_{k>=i} A(o+k, o+i)·B(o+k, j), written once.
+    std::vector<hg::BatchEntry> ents;
+    for (const Node &x : plan)
+        if (x.kind == 0)
+            ents.push_back({x.o, x.o * lda + x.o, x.o, (int32_t)x.s, (int32_t)x.s});
+    int st = run_batch(ents, true, 0.0f);
+    if (st != HG_OK)
+        return st;
+    // Updates, deepest level first; within a level they write disjoint rows.
+    for (int64_t d = max_depth; d >= 0; --d) {
+        ents.clear();
+        for (const Node &x : plan) {
+            if (x.kind != 1 || x.depth != d)
+                continue;
+            const int64_t h = x.s / 2;
+            ents.push_back({x.o + h, x.o * lda + x.o + h, x.o, (int32_t)h, (int32_t)(x.s - h)});
+        }
+        if (ents.empty())
+            continue;
+        st = run_batch(ents, false, 1.0f);
+        if (st != HG_OK)
+            return st;
+    }
+    return HG_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,57 @@
+// Internal interface between the host API (hg_api.cpp) and the gfx950
+// kernels (hg_kernels.hip).  Not part of the public ABI.
+#pragma once
+
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+namespace hg {
+
+// One GEMM of a batched launch.  All GEMMs of a launch share M, lda, ldb,
+// ldc, alpha, beta and the base pointers; each has its own element offsets
+// and its own N and K.  The TRMM driver uses this to run every leaf, or every
+// update of one recursion level, in a single launch.
+struct BatchEntry {
+    int64_t a_off;   // element offset into A (row-major M×K operand)
+    int64_t b_off;   // element offset into B (N×K operand, K contiguous)
+    int64_t c_off;   // element offset into C (row-major M×N)
+    int32_t N;
+    int32_t K;
+};
+
+constexpr int kMaxBatch = 32;
+
+struct GemmParams {
+    const _Float16 *A;
+    const _Float16 *B;
+    void *C;
+    int64_t lda, ldb, ldc;
+    int32_t M;
+    int32_t nbatch;
+    float alpha, beta;
+    BatchEntry e[kMaxBatch];
+};
+
+// Kernel families the launcher can pick.
+enum class Tile { Big, Mid, Small };
+
+struct LaunchOpts {
+    bool out_f16;     // C element type
+    bool beta_read;   // beta != 0: read C
+    bool tri;         // TRMM leaf: B operand element (j, k) is zero for k < j
+    bool vec;         // 16-byte aligned operands: vector loads
+    Tile tile;
+};
+
+// Validated arguments in, kernels launched on `stream`; returns hipError_t.
+hipError_t launch_gemm(const GemmParams &p, const LaunchOpts &o, hipStream_t stream);
+
+// C = beta·C over an M×N window (beta == 0 writes zeros without reading).
+hipError_t launch_scale(void *C, int64_t ldc, int64_t M, int64_t N, float beta,
+                        bool out_f16, hipStream_t stream);
+
+// Tile family the launcher would choose for a single M×N GEMM.
+Tile choose_tile(int64_t M, int64_t N, int64_t K);
+
+}  // namespace hg

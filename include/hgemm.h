@@ -1,0 +1,134 @@
+/*
+ * hgemm.h — C ABI of the MI355X (gfx950) half-precision GEMM library.
+ *
+ * Two operations:
+ *
+ *   hgemm             C = alpha·A·B + beta·C, fp16 A and B, fp32 accumulation,
+ *                     fp16 or fp32 C.  Problem statement and layouts from
+ *                     "Nvidia Tensor Core-MMA PTX编程入门" §4 (A M×K row-major,
+ *                     B K×N column-major, C M×N row-major); ragged edges are
+ *                     masked as in the tiled matmul of "GPU架构与CUDA"
+ *                     (section 共享内存与分块); fp16 inputs with fp32
+ *                     accumulation as in its section 混合精度核函数.
+ *
+ *   trmm_lower_trans  Out = alpha·Aᵀ·B with A lower triangular, computed by
+ *                     the recursive 2×2 blocking of
+ *                     "异构计算中高性能TRMM与TRSM的递归算法实现" §2.1–§2.2:
+ *                     split at n/2 until a block is at most `leaf`, leaf blocks
+ *                     by a triangle-masked kernel, and every A21ᵀ·B2 update by
+ *                     the GEMM kernel of hgemm with beta = 1.
+ *
+ * All matrix pointers are DEVICE pointers on the current HIP device.  Calls
+ * are asynchronous on `stream` (a hipStream_t; NULL = the default stream);
+ * results are valid once the stream has been synchronised.  The library
+ * allocates nothing, never copies between host and device, keeps no state
+ * and is thread-safe.  The caller owns every buffer.
+ *
+ * Return value: 0 on success.  A negative value -i means argument i (1-based,
+ * in the order of the prototype) is invalid, following the BLAS xerbla
+ * convention; nothing is launched in that case.  A value 1000 + e means the
+ * HIP runtime reported hipError_t e at launch.  hg_strerror() names a status.
+ */
+#ifndef HGEMM_H
+#define HGEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of C (hgemm) and Out (trmm_lower_trans). */
+#define HG_F16 0
+#define HG_F32 1
+
+#define HG_OK 0
+#define HG_ERR_HIP_BASE 1000
+
+/*
+ * hgemm — C = alpha·A·B + beta·C.
+ *
+ *  1 M, 2 N, 3 K : problem sizes, each >= 0.
+ *  4 alpha       : scale of the product (fp32).
+ *  5 A, 6 lda    : fp16, M×K row-major, element (i,k) at A[i*lda + k];
+ *                  lda >= max(1, K).
+ *  7 B, 8 ldb    : fp16, K×N column-major, element (k,j) at B[j*ldb + k]
+ *                  (equivalently Bᵀ stored N×K row-major); ldb >= max(1, K).
+ *  9 beta        : scale of the incoming C (fp32).  When beta == 0, C is
+ *                  write-only (NaN or garbage in C does not propagate).
+ * 10 C, 11 ldc   : M×N row-major, element (i,j) at C[i*ldc + j], of type
+ *                  out_dtype for both the read (beta != 0) and the write;
+ *                  ldc >= max(1, N).  Elements outside the M×N window
+ *                  (the ldc padding) are never read or written.
+ * 12 out_dtype   : HG_F16 (rounded to nearest even) or HG_F32.
+ * 13 stream      : hipStream_t to launch on.
+ *
+ * Arithmetic: each product fp16×fp16 is exact in fp32 and is summed in fp32
+ * in an unspecified order; the result is alpha·acc + beta·C_in in fp32, then
+ * converted to out_dtype.
+ * Quick returns: M == 0 or N == 0 touches nothing.  alpha == 0 or K == 0
+ * does not read A or B and sets C = beta·C (C = 0 when beta == 0).
+ * A and B may be NULL only when they are not read.  C must not overlap A or B
+ * (checked on the host; error -10).  Fast path: A and B 16-byte aligned with
+ * lda and ldb multiples of 8; anything else takes a slower, element-wise
+ * load path with identical results.
+ */
+int hgemm(int64_t M, int64_t N, int64_t K, float alpha,
+          const void *A, int64_t lda,
+          const void *B, int64_t ldb,
+          float beta, void *C, int64_t ldc,
+          int out_dtype, void *stream);
+
+/*
+ * trmm_lower_trans — Out = alpha·Aᵀ·B, A lower triangular.
+ *
+ *  1 n, 2 m      : A is n×n, B and Out are n×m; each >= 0.
+ *  3 alpha       : scale (fp32), applied once to every output.
+ *  4 A, 5 lda    : fp16, n×n column-major, element (r,c) at A[r + c*lda];
+ *                  lda >= max(1, n).  Only the lower triangle (r >= c) is
+ *                  read; the strictly upper triangle is never referenced.
+ *  6 B, 7 ldb    : fp16, n×m column-major input; ldb >= max(1, n).
+ *  8 Out, 9 ldo  : n×m column-major output, element (r,c) at Out[r + c*ldo];
+ *                  ldo >= max(1, n); write-only (its previous contents are
+ *                  ignored).  Must not overlap A or B (error -8).
+ * 10 out_dtype   : HG_F32 (the updates accumulate into Out in fp32; HG_F16
+ *                  is rejected with -10).
+ * 11 leaf        : recursion cut-off; a diagonal block of size <= leaf is
+ *                  handled by the triangle-masked leaf kernel.  leaf <= 0
+ *                  selects 256.
+ * 12 stream      : hipStream_t to launch on.
+ *
+ * Order of work: all leaves first (independent, one batched launch), then the
+ * A21ᵀ·B2 updates level by level from the deepest to the outermost (one
+ * batched launch per level).  For every output element this is the same
+ * order of accumulation as the depth-first recursion.
+ */
+int trmm_lower_trans(int64_t n, int64_t m, float alpha,
+                     const void *A, int64_t lda,
+                     const void *B, int64_t ldb,
+                     void *Out, int64_t ldo, int out_dtype,
+                     int64_t leaf, void *stream);
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *hg_strerror(int status);
+
+/*
+ * hg_trmm_plan — the recursion trmm_lower_trans runs for (n, leaf), for
+ * inspection; host only, launches nothing.
+ *
+ * Writes up to `cap` nodes into `nodes`, 4 int64 per node:
+ *   {kind, offset, size, depth}
+ *   kind 0 = leaf:   Out[o:o+s] = alpha·tril(A[o:o+s, o:o+s])ᵀ·B[o:o+s]
+ *   kind 1 = update: Out[o:o+h] += alpha·A[o+h:o+s, o:o+h]ᵀ·B[o+h:o+s]
+ *                    with s = size and h = floor(s/2)
+ * in depth-first recursion order, and returns the total node count (which
+ * may exceed cap; then only the first cap are written).  Returns -1 for
+ * n < 0, -2 when nodes is NULL with cap > 0.
+ */
+int64_t hg_trmm_plan(int64_t n, int64_t leaf, int64_t *nodes, int64_t cap);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HGEMM_H */

@@ -1,0 +1,180 @@
+"""Host-side checks of the C ABI (CPU only, no kernel launches).
+
+Every call here returns before the library touches the HIP runtime:
+argument validation (BLAS xerbla-style negative status = position of the
+first bad argument), quick returns, status strings and the TRMM recursion
+plan of "异构计算中高性能TRMM与TRSM的递归算法实现" §2.1–§2.2.  Pointer
+arguments are fake addresses that are never dereferenced.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hgemm.h")
+
+
+@pytest.fixture(scope="module")
+def lib(hg):
+    return hg.lib
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?(?:int|int64_t|char|void)\s*\*?\s*(\w+)\s*\(",
+                                 text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == ["hg_strerror", "hg_trmm_plan", "hgemm", "trmm_lower_trans"]
+
+
+def test_library_exports_every_declared_symbol(hg):
+    lib = ctypes.CDLL(hg.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), f"libhgemm.so does not export {name}"
+    assert set(hg.EXPORTS) == set(declared_functions())
+
+
+P = 0x10000      # fake device addresses, never dereferenced on these paths
+Q = 0x20000000
+R = 0x40000000
+
+
+def gemm(lib, M=4, N=4, K=4, alpha=1.0, A=P, lda=None, B=Q, ldb=None, beta=0.0, C=R, ldc=None,
+         dt=0):
+    lda = max(1, K) if lda is None else lda
+    ldb = max(1, K) if ldb is None else ldb
+    ldc = max(1, N) if ldc is None else ldc
+    return lib.hgemm(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, dt, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(M=-1), -1), (dict(N=-1), -2), (dict(K=-1), -3),
+    (dict(M=2 ** 31), -1), (dict(N=2 ** 31), -2), (dict(K=2 ** 31), -3),
+    (dict(K=8, lda=7), -6), (dict(K=0, lda=0), -6),
+    (dict(K=8, ldb=7), -8), (dict(N=8, ldc=7), -11),
+    (dict(dt=2), -12), (dict(dt=-1), -12),
+    (dict(C=None), -10), (dict(A=None), -5), (dict(B=None), -7),
+])
+def test_hgemm_argument_errors(lib, kw, code):
+    assert gemm(lib, **kw) == code
+
+
+def test_hgemm_first_bad_argument_wins(lib):
+    assert gemm(lib, M=-1, N=-1, dt=7) == -1
+    assert gemm(lib, K=8, lda=1, ldb=1) == -6
+
+
+def test_hgemm_quick_return_touches_nothing(lib):
+    # M == 0 or N == 0: success without looking at any pointer
+    assert gemm(lib, M=0, A=None, B=None, C=None) == 0
+    assert gemm(lib, N=0, A=None, B=None, C=None, ldc=1) == 0
+
+
+def test_hgemm_overlap_rejected(lib):
+    # C (fp16 4×4, ld 4) starting inside A's extent
+    assert gemm(lib, A=P, C=P + 8) == -10
+    assert gemm(lib, B=Q, C=Q + 30) == -10
+    # alpha == 0 does not read A, so no overlap with A is checked there;
+    # that path launches, so it is covered by the GPU tests instead
+
+
+@pytest.mark.parametrize("args,code", [
+    ((-1, 4, 1.0, P, 4, Q, 4, R, 4, 1, 256), -1),
+    ((4, -1, 1.0, P, 4, Q, 4, R, 4, 1, 256), -2),
+    ((8, 4, 1.0, P, 7, Q, 8, R, 8, 1, 256), -5),
+    ((8, 4, 1.0, P, 8, Q, 7, R, 8, 1, 256), -7),
+    ((8, 4, 1.0, P, 8, Q, 8, R, 7, 1, 256), -9),
+    ((8, 4, 1.0, P, 8, Q, 8, R, 8, 0, 256), -10),     # fp16 Out is not supported
+    ((8, 4, 1.0, P, 8, Q, 8, None, 8, 1, 256), -8),
+    ((8, 4, 1.0, None, 8, Q, 8, R, 8, 1, 256), -4),
+    ((8, 4, 1.0, P, 8, None, 8, R, 8, 1, 256), -6),
+    ((8, 4, 1.0, P, 8, Q, 8, Q + 16, 8, 1, 256), -8),  # Out overlaps B
+    ((0, 4, 1.0, None, 1, None, 1, None, 1, 1, 256), 0),
+    ((8, 0, 1.0, None, 8, None, 8, None, 8, 1, 256), 0),
+])
+def test_trmm_argument_errors(lib, args, code):
+    assert lib.trmm_lower_trans(*args, None) == code
+
+
+def test_strerror(hg):
+    assert hg.strerror(0) == "success"
+    assert "argument 6" in hg.strerror(-6)
+    assert hg.strerror(-99) == "unknown status"
+    assert isinstance(hg.strerror(1000 + 1), str)
+
+
+# ------------------------------------------------------------ recursion plan
+def test_plan_n8192_leaf256(hg):
+    plan = hg.trmm_plan(8192, 256)
+    leaves = [p for p in plan if p[0] == 0]
+    upd = [p for p in plan if p[0] == 1]
+    assert len(leaves) == 32 and len(upd) == 31
+    assert all(p[2] == 256 for p in leaves)
+    assert sorted({p[3] for p in upd}) == [0, 1, 2, 3, 4]          # five levels
+    # flop share of the GEMM updates: each update is h·(s-h)·m multiply-adds
+    # against n(n+1)m/2 for the whole triangle -> 96.9 % at n=8192, leaf 256
+    # (the page claims "more than 90 %" in §2.2 and ">= 70 %" in §2.1)
+    n = 8192
+    gemm_macs = sum((p[2] // 2) * (p[2] - p[2] // 2) for p in upd)
+    share = gemm_macs / (n * (n + 1) / 2)
+    assert share == pytest.approx(0.969, abs=5e-4)
+    assert share > 0.9
+
+
+@pytest.mark.parametrize("n,leaf", [(1, 256), (255, 256), (257, 256), (1000, 256), (1000, 64),
+                                    (4097, 128), (13, 1), (8192, 8192)])
+def test_plan_structure(hg, n, leaf):
+    plan = hg.trmm_plan(n, leaf)
+    # leaves tile [0, n) in order, each of size <= leaf
+    leaves = [(p[1], p[2]) for p in plan if p[0] == 0]
+    pos = 0
+    for o, s in leaves:
+        assert o == pos and 1 <= s <= max(leaf, 1)
+        pos += s
+    assert pos == n
+    # every update block has s > leaf, splits at floor(s/2), and covers the
+    # strictly-lower part below its top half exactly once overall
+    covered = 0
+    for kind, o, s, d in plan:
+        if kind == 1:
+            assert s > leaf and 0 <= o and o + s <= n
+            h = s // 2
+            covered += h * (s - h)
+    covered += sum(s * (s + 1) // 2 for _, s in leaves)
+    assert covered == n * (n + 1) // 2      # every (k >= i) pair exactly once
+
+
+@pytest.mark.parametrize("n,leaf", [(8192, 256), (1000, 64), (777, 16)])
+def test_plan_batched_order_matches_recursion(hg, n, leaf):
+    """Running all leaves, then updates deepest level first, gives every row
+    the same sequence of contributions as the depth-first recursion: along the
+    recursion order, the updates touching any one row have strictly
+    decreasing depth, and updates of one depth touch disjoint rows."""
+    plan = hg.trmm_plan(n, leaf)
+    seen = {}
+    by_depth = {}
+    for kind, o, s, d in plan:
+        if kind != 1:
+            continue
+        h = s // 2
+        for r in range(o, o + h):           # every row of Out1
+            if r in seen:
+                assert d < seen[r][-1]
+            seen.setdefault(r, []).append(d)
+        by_depth.setdefault(d, []).append((o, o + h))
+    for d, iv in by_depth.items():
+        iv.sort()
+        for (a0, a1), (b0, b1) in zip(iv, iv[1:]):
+            assert a1 <= b0
+
+
+def test_plan_errors(hg):
+    assert hg.lib.hg_trmm_plan(-1, 256, None, 0) == -1
+    assert hg.lib.hg_trmm_plan(10, 256, None, 5) == -2
+    assert hg.trmm_plan(0) == []
+    assert hg.trmm_plan(10, 0) == [(0, 0, 10, 0)]     # leaf <= 0 means 256

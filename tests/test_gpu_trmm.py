@@ -1,0 +1,150 @@
+"""TRMM parity on the GPU: Out = alpha·Aᵀ·B with A lower triangular, by the
+recursive blocking of "异构计算中高性能TRMM与TRSM的递归算法实现" §2.1–§2.2
+(split at n/2, triangle-masked leaf, A21ᵀ·B2 updates through the GEMM with
+beta = 1), against the fp64 oracle to |err| <= 1e-3·sqrt(n) + 2^-10·|ref|,
+plus exact pins.
+
+Column-major convention: an n×m column-major matrix is a torch (m, n) tensor
+whose row j is column j.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from tolerance import check_close
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def dev(x):
+    return torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
+
+
+def trmm_inputs(n, m, seed, upper_fill=0.0):
+    rng = np.random.default_rng(seed)
+    S = workloads.uniform_f16(rng, (n, n))
+    D = workloads.uniform_f16(rng, (n,), 0.5, 1.5)
+    B = workloads.uniform_f16(rng, (n, m))
+    A = np.tril(S, -1)
+    A[np.arange(n), np.arange(n)] = D
+    A[np.triu_indices(n, 1)] = upper_fill
+    return np.ascontiguousarray(A.T), np.ascontiguousarray(B.T)
+
+
+def run(hg, A_cm, B_cm, alpha=1.0, leaf=256):
+    m, n = B_cm.shape
+    Out = torch.full((m, n), float("nan"), dtype=torch.float32, device=DEV)
+    hg.trmm_lower_trans(dev(A_cm), dev(B_cm), Out, alpha, leaf)
+    torch.cuda.synchronize()
+    return Out.cpu().numpy()
+
+
+def test_workload_8192(hg):
+    """n = m = 8192, leaf 256, in the benchmark's launch configuration:
+    1024 sampled entries against the oracle, and the full result against the
+    GPU GEMM on the densified (explicitly zero-upper) A — a different kernel
+    path (plain tiles, no triangle mask, one K loop per output)."""
+    w = workloads.WORKLOADS["trmm_8192"]
+    print("[case] trmm_8192", flush=True)
+    A_cm, B_cm = workloads.trmm_inputs(w)
+    Ad, Bd = dev(A_cm), dev(B_cm)
+    Out = torch.full((w.m, w.n), float("nan"), dtype=torch.float32, device=DEV)
+    hg.trmm_lower_trans(Ad, Bd, Out, w.alpha, w.leaf)
+    dense = torch.zeros((w.m, w.n), dtype=torch.float32, device=DEV)
+    hg.hgemm(Bd, Ad, dense, w.alpha, 0.0)      # (Aᵀ·B)ᵀ = Bᵀ·A in the row-major view
+    torch.cuda.synchronize()
+    out = Out.cpu().numpy()
+    ri, cj = workloads.sample_indices(w.seed, w.n, w.m)
+    ref = oracle.trmm_lower_trans_sampled(A_cm, B_cm, ri, cj, w.alpha)
+    check_close(out[cj, ri], ref, w.n, "trmm_8192 sampled")
+    dn = dense.cpu().numpy()
+    check_close(out, dn.astype(np.float64), w.n, "trmm_8192 vs dense GEMM")
+
+
+@pytest.mark.parametrize("n,m", [(1, 1), (1, 7), (255, 1), (255, 256), (257, 7), (257, 256),
+                                 (1000, 7), (1000, 256), (513, 100), (2048, 300)])
+def test_odd_and_small_shapes_full(hg, n, m):
+    print(f"[case] trmm n={n} m={m}", flush=True)
+    A_cm, B_cm = trmm_inputs(n, m, n * 7 + m)
+    out = run(hg, A_cm, B_cm, 0.75)
+    ref = oracle.trmm_lower_trans(A_cm, B_cm, 0.75)
+    check_close(out, ref, n, f"n={n} m={m}")
+
+
+@pytest.mark.parametrize("leaf", [256, 128, 64, 1000, 3])
+def test_leaf_invariance(hg, leaf):
+    n, m = 1000, 130
+    A_cm, B_cm = trmm_inputs(n, m, 77)
+    out = run(hg, A_cm, B_cm, 1.0, leaf)
+    ref = oracle.trmm_lower_trans(A_cm, B_cm)
+    check_close(out, ref, n, f"leaf={leaf}")
+
+
+def test_identity_exact(hg):
+    n, m = 700, 90
+    B_cm = workloads.uniform_f16(np.random.default_rng(3), (m, n))
+    out = run(hg, np.eye(n, dtype=np.float16), B_cm, 2.0)
+    assert np.array_equal(out, 2.0 * B_cm.astype(np.float32))
+
+
+def test_tril_ones_closed_form(hg):
+    n, m = 1100, 40
+    A = np.tril(np.ones((n, n), np.float16))
+    out = run(hg, np.ascontiguousarray(A.T), np.ones((m, n), np.float16), 0.5)
+    expect = 0.5 * (n - np.arange(n, dtype=np.float32))
+    assert np.array_equal(out, np.tile(expect, (m, 1)))
+
+
+@pytest.mark.parametrize("fill", [np.nan, 1e4, -np.inf])
+def test_upper_triangle_never_read(hg, fill):
+    n, m = 777, 64
+    A0, B_cm = trmm_inputs(n, m, 5, 0.0)
+    Ax, _ = trmm_inputs(n, m, 5, fill)
+    base = run(hg, A0, B_cm)
+    got = run(hg, Ax, B_cm)
+    assert np.array_equal(base.view(np.uint32), got.view(np.uint32))
+
+
+def test_integer_bit_exact(hg):
+    rng = np.random.default_rng(17)
+    n, m = 1500, 120
+    A = np.tril(workloads.integer_f16(rng, (n, n)))
+    B = workloads.integer_f16(rng, (n, m))
+    out = run(hg, np.ascontiguousarray(A.T), np.ascontiguousarray(B.T))
+    exact = A.astype(np.int64).T @ B.astype(np.int64)
+    assert np.array_equal(out, exact.T.astype(np.float32))
+
+
+def test_alpha_zero_gives_zeros_without_reading(hg):
+    n, m = 300, 20
+    A = np.full((n, n), np.nan, np.float16)
+    B = np.full((m, n), np.nan, np.float16)
+    out = run(hg, A, B, 0.0)
+    assert np.array_equal(out, np.zeros((m, n), np.float32))
+
+
+def test_strided_operands(hg):
+    """Leading dimensions larger than n; Out's padding stays untouched."""
+    n, m, pad = 600, 50, 24
+    A_cm, B_cm = trmm_inputs(n, m, 9)
+    Ab = np.zeros((n, n + pad), np.float16)
+    Ab[:, :n] = A_cm
+    Bb = np.zeros((m, n + pad), np.float16)
+    Bb[:, :n] = B_cm
+    Ob = torch.full((m, n + pad), -7.0, dtype=torch.float32, device=DEV)
+    hg.trmm_lower_trans(dev(Ab)[:, :n], dev(Bb)[:, :n], Ob[:, :n], 1.0, 128)
+    torch.cuda.synchronize()
+    got = Ob.cpu().numpy()
+    assert np.all(got[:, n:] == -7.0)
+    check_close(got[:, :n], oracle.trmm_lower_trans(A_cm, B_cm), n, "strided")
+
+
+def test_deterministic(hg):
+    A_cm, B_cm = trmm_inputs(1030, 200, 2)
+    a = run(hg, A_cm, B_cm)
+    b = run(hg, A_cm, B_cm)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
