@@ -13,7 +13,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libhgemm.so")
-SOURCES = [os.path.join(CSRC, "hg_api.cpp"), os.path.join(CSRC, "hg_kernels.hip")]
+SOURCES = [os.path.join(CSRC, "hg_api.cpp"), os.path.join(CSRC, "hg_kernels.hip"),
+           os.path.join(CSRC, "hg_fast.hip")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

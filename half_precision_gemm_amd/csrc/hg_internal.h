@@ -47,6 +47,11 @@ struct LaunchOpts {
 // Validated arguments in, kernels launched on `stream`; returns hipError_t.
 hipError_t launch_gemm(const GemmParams &p, const LaunchOpts &o, hipStream_t stream);
 
+// 256×256 direct-to-LDS pipelined kernel (hg_fast.hip): usable when the
+// operands allow 16-byte buffer loads and K % 8 == 0, and not for TRI.
+bool fast_path_ok(const GemmParams &p, const LaunchOpts &o);
+hipError_t launch_gemm_fast(const GemmParams &p, const LaunchOpts &o, hipStream_t stream);
+
 // C = beta·C over an M×N window (beta == 0 writes zeros without reading).
 hipError_t launch_scale(void *C, int64_t ldc, int64_t M, int64_t N, float beta,
                         bool out_f16, hipStream_t stream);

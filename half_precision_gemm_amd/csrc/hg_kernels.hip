@@ -412,6 +412,8 @@ hipError_t launch_gemm(const GemmParams &p, const LaunchOpts &o, hipStream_t str
 {
     switch (o.tile) {
     case Tile::Big:
+        if (fast_path_ok(p, o))
+            return launch_gemm_fast(p, o, stream);
         return launch_tile<CfgBig>(p, o, stream);
     case Tile::Mid:
         return launch_tile<CfgMid>(p, o, stream);

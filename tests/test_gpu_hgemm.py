@@ -111,6 +111,31 @@ def test_tile_families_ragged(hg, M, N, K):
     check_close(out[rows], ref_edge, K, "last rows")
 
 
+@pytest.mark.parametrize("K", [8, 40, 96, 256, 1000])
+def test_big_tiles_short_k(hg, K):
+    """Large M, N (256×256 tiles, the pipelined path) with short K: the
+    prefetch ring runs past the end of K on most iterations; repeated so
+    that back-to-back workgroups on a CU reuse the same LDS."""
+    print(f"[case] big tiles short K={K}", flush=True)
+    M, N = 4096, 3840
+    A = rnd(K, (M, K))
+    Bt = rnd(K + 1, (N, K))
+    ri, cj = workloads.sample_indices(K, M, N, 4096)
+    ref = oracle.hgemm_sampled(A, Bt, ri, cj)
+    Ad, Btd = dev(A), dev(Bt)
+    first = None
+    for rep in range(3):
+        Cd = torch.full((M, N), float("nan"), dtype=torch.float32, device=DEV)
+        hg.hgemm(Ad, Btd, Cd)
+        torch.cuda.synchronize()
+        out = Cd.cpu().numpy()
+        check_close(out[ri, cj], ref, K, f"K={K} rep {rep}")
+        if first is None:
+            first = out
+        else:
+            assert np.array_equal(first.view(np.uint32), out.view(np.uint32))
+
+
 def test_unaligned_operands(hg):
     """Odd leading dimensions and 2-byte-offset bases take the element-wise
     load path; results still match the oracle."""
