@@ -31,7 +31,7 @@ PEAK_HBM_GBS = 8000.0
 
 def kernel_source_hash():
     h = hashlib.sha256()
-    for f in ("hg_kernels.hip", "hg_api.cpp", "hg_internal.h"):
+    for f in ("hg_fast.hip", "hg_kernels.hip", "hg_api.cpp", "hg_internal.h"):
         with open(os.path.join(ROOT, "half_precision_gemm_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -78,6 +78,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-trmm", action="store_true", help="time the HGEMM alone")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="also run one plain device-to-device copy of BYTES bytes, the "
+                         "reference kernel that scales the FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -119,6 +122,14 @@ def main():
             hg.trmm_lower_trans(TAd, TBd, TOut, wt.alpha, wt.leaf)
             if evs is not None:
                 evs[2].record(stream)
+
+    if args.copy_calibration:
+        src = torch.empty(args.copy_calibration // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     for _ in range(args.warmup):
         step()
@@ -168,7 +179,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_FP16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_FP16_TFLOPS, 4),
                      "traffic": traffic_from_profiles(src_hash),
-                     "kernel": "hgemm_kernel<256x256x64> at M=N=K=8192, fp32 out",
+                     "kernel": "hgemm_fast_kernel (256x256 tile, 32-wide K slices) at M=N=K=8192, fp32 out",
                      "algorithmic_flops_per_launch": wg.flops},
         "kernel_source_sha256_16": src_hash,
     }

@@ -4,25 +4,34 @@
 // (C = alpha·A·B + beta·C, A M×K row-major, B K×N column-major, fp16 in,
 // fp32 accumulate; "Nvidia Tensor Core-MMA PTX编程入门" §4 and the masked
 // tiled matmul of "GPU架构与CUDA" 共享内存与分块), for operands whose rows
-// are 16-byte aligned and K a multiple of 8.  What differs:
+// are 16-byte aligned and K a multiple of 8; with TRI it is also the
+// triangle-masked leaf of the recursive TRMM ("异构计算中高性能TRMM与TRSM的
+// 递归算法实现" §2.2).  Design:
 //
-//  * Global→LDS staging uses the gfx950 direct buffer→LDS path
-//    (buffer_load_dwordx4 … lds): no staging registers and no ds_write.
-//    Each wave instruction moves 8 rows × 128 bytes; lane l fetches the
-//    logical 16-byte chunk (l mod 8) XOR (row mod 8) of its row, so the
-//    contiguous LDS image is already XOR-swizzled for the fragment reads.
+//  * One workgroup = 4 waves (2×2) per 256×256 tile; each wave owns a
+//    128×128 sub-tile = 4×4 blocks of v_mfma_f32_32x32x16_f16, 256 fp32
+//    accumulators per lane (the AGPR file).
+//  * K is walked in BK = 32 slices held in a ring of NST = 4 LDS slots
+//    (32 KiB each), filled by the gfx950 direct buffer→LDS path
+//    (buffer_load_dwordx4 … lds): no staging registers, no ds_write.  Each
+//    wave instruction moves 16 rows × 64 bytes; lane l fetches the logical
+//    16-byte chunk that the XOR swizzle places at position l, so the LDS
+//    image is already swizzled for the fragment reads.
 //  * Ragged M/N edges and the K tail are zero-filled by the buffer unit's
-//    range check: out-of-range rows and chunks get an offset past the
-//    resource's size, which loads as zero.  No branches in the main loop.
-//  * The K loop is software pipelined: the buffer→LDS loads of slice t+1
-//    are issued at the top of slice t, MFMA operand fragments of k-step s+1
-//    are read from LDS while the 16 MFMAs of k-step s run, and the barrier
-//    that hands over the next slice sits in the middle of the last k-step so
-//    that its first fragments are already in flight when the slice starts.
+//    range check (out-of-range rows and chunks get an offset past the
+//    resource size, which loads as zero): no branches in the main loop.
+//  * Software pipeline: slices are prefetched NST-1 ahead; within a slice,
+//    every MFMA is followed by at most one LDS fragment read (for the next
+//    k-step) or one ring load, in a fixed program order; one workgroup
+//    barrier per slice, in front of its last k-step.
+//  * Persistent workgroups: one per CU walks a strided list of tiles; the
+//    next tile's first slices are requested before the current tile's
+//    epilogue, so loads overlap the stores.
 //
-// One workgroup = 4 waves (2×2) computes a 256×256 tile; each wave owns a
-// 128×128 sub-tile = 4×4 blocks of v_mfma_f32_32x32x16_f16, 256 fp32
-// accumulators per lane (the AGPR file).  Two LDS stages of 64 KiB each.
+// Workgroup→tile order: tile ids are regrouped per XCD (consecutive
+// workgroup ids run on different XCDs, each with its own L2), then each
+// XCD's range is walked in bands of 4 tile rows, column by column, so the
+// tiles resident on one XCD share A row panels and B column panels.
 #include "hg_internal.h"
 
 typedef int32_t hg_int32x4 __attribute__((ext_vector_type(4)));
@@ -40,47 +49,71 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef _Float16 halfx4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// Slice depth and ring depth.  BK = 32 with 4 stages keeps three slices in
-// flight (about 3000 MFMA cycles of cover for the global latency) in 128 KiB
-// of LDS; BK = 64 with 2 stages is the shallow alternative.
+// Tunables (compile-time).  BK = 32 with 4 slots keeps three slices in
+// flight in 128 KiB of LDS; the wave layout is WM × WN.
 #ifndef HG_FAST_BK
 #define HG_FAST_BK 32
 #endif
 #ifndef HG_FAST_NST
 #define HG_FAST_NST 4
 #endif
-
 #ifndef HG_FAST_WM
 #define HG_FAST_WM 2
 #endif
 #ifndef HG_FAST_WN
 #define HG_FAST_WN 2
 #endif
+#ifndef HG_FAST_RPL
+#define HG_FAST_RPL (256 / (HG_FAST_BK * 2))
+#endif
+#ifndef HG_FAST_XCD
+#define HG_FAST_XCD 1
+#endif
+#ifndef HG_FAST_PERSIST_MAXK
+#define HG_FAST_PERSIST_MAXK 4096
+#endif
+#ifndef HG_FAST_GROUP
+#define HG_FAST_GROUP 4
+#endif
 
 constexpr int BM = 256, BN = 256, BK = HG_FAST_BK, NST = HG_FAST_NST;
-constexpr int D = NST - 1;                  // prefetch distance in slices
-static_assert(D >= 2, "slice kt+1 must be fully issued before iteration kt");
 constexpr int WM = HG_FAST_WM, WN = HG_FAST_WN, NW = WM * WN;   // waves per workgroup
 constexpr int THREADS = NW * 64;
 constexpr int WTM = BM / WM, WTN = BN / WN;                     // wave sub-tile
 constexpr int TM = WTM / 32, TN = WTN / 32;                     // 32×32 blocks per wave
 constexpr int RB = BK * 2;                  // bytes per LDS row
 constexpr int KC = BK / 8;                  // 16-byte chunks per row
-#ifndef HG_FAST_RPL
-#define HG_FAST_RPL (256 / (HG_FAST_BK * 2))
-#endif
-constexpr int RPL = HG_FAST_RPL;             // rows per 256-byte bank line (64 banks)
+constexpr int RPL = HG_FAST_RPL;            // rows per 256-byte bank line (64 banks)
 constexpr int RPI = 1024 / RB;              // rows per buffer→LDS wave instruction
 constexpr int RPW = BM / NW;                // tile rows each wave loads, per operand
 constexpr int LPS = RPW / RPI;              // load instructions per wave per operand
 constexpr int SPS = BK / 16;                // MFMA k-steps per slice
 constexpr int LDS_A = BM * RB;
 constexpr int LDS_STAGE = LDS_A + BN * RB;
+constexpr int D = NST - 1;                  // prefetch distance in slices
 constexpr uint32_t OOB = 0x80000000u;       // offset that the range check rejects
+// k-steps of an iteration that carry its loads: all of them when slices are
+// prefetched two or more ahead; with a single slice ahead (D = 1), the loads
+// of slice kt+1 must all be issued before the barrier in front of the last
+// k-step.
+#ifndef HG_FAST_LSTEPS
+#define HG_FAST_LSTEPS (HG_FAST_NST > 2 ? HG_FAST_BK / 16 : 2)
+#endif
+constexpr int LSTEPS = HG_FAST_LSTEPS;
+constexpr int P = TM * TN;                  // MFMAs per k-step
+constexpr int R = TM + TN;                  // fragment reads per k-step
+constexpr int V = 2 * LPS / LSTEPS;         // ring loads per load-carrying k-step
+// Loads still allowed in flight at a slice's barrier: those issued after
+// slice kt+1's, i.e. slices kt+2 .. kt+D-1 and slice kt+D's share so far.
+constexpr int VM_AT_BARRIER =
+    D == 1 ? 0 : 2 * LPS * (D - 2) + V * (LSTEPS < SPS - 1 ? LSTEPS : SPS - 1);
 static_assert(BK == 32 || BK == 64, "");
 static_assert(LPS * RPI == RPW && TM >= 2 && TN >= 1, "");
 static_assert(NST >= 2 && NST * LDS_STAGE <= 160 * 1024, "LDS budget");
+static_assert(V * LSTEPS == 2 * LPS, "loads must split evenly over the k-steps");
+static_assert(LSTEPS <= SPS && (D >= 2 || LSTEPS < SPS), "");
 
 // Physical 16-byte chunk of logical chunk kc in LDS row r.  The LDS serves a
 // 16-byte read for 16 lanes per cycle over 64 four-byte banks (256 bytes);
@@ -88,19 +121,17 @@ static_assert(NST >= 2 && NST * LDS_STAGE <= 160 * 1024, "LDS budget");
 // XOR spreads over 16 distinct bank groups.
 __device__ __forceinline__ int swz(int r, int kc) { return kc ^ ((r / RPL) & (KC - 1)); }
 
-// s_waitcnt vmcnt(n) only (expcnt and lgkmcnt left at their maxima).
+// s_waitcnt on one counter only (the others left at their maxima).
 template <int n>
 __device__ __forceinline__ void wait_vmcnt()
 {
     __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
 }
-// s_waitcnt lgkmcnt(n) only.
 template <int n>
 __device__ __forceinline__ void wait_lgkmcnt()
 {
     __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | ((n & 15) << 8));
 }
-
 
 // Raw buffer resource: base address, no stride, `bytes` in range.
 __device__ __forceinline__ hg_int32x4 make_rsrc(const void *base, uint32_t bytes)
@@ -114,19 +145,13 @@ __device__ __forceinline__ hg_int32x4 make_rsrc(const void *base, uint32_t bytes
     return r;
 }
 
-#ifndef HG_FAST_XCD
-#define HG_FAST_XCD 1
-#endif
-#ifndef HG_FAST_GROUP
-#define HG_FAST_GROUP 4
-#endif
-
-__device__ __forceinline__ void map_tile(int wg, int total, int tiles_m, int tiles_n, int &batch,
+// Tile id → (batch, tile row, tile column); see the header comment.
+__device__ __forceinline__ void map_tile(int id, int total, int tiles_m, int tiles_n, int &batch,
                                          int &tm, int &tn)
 {
     const int per = total >> 3, rem = total & 7;
-    const int x = wg & 7;
-    const int q = HG_FAST_XCD ? x * per + min(x, rem) + (wg >> 3) : wg;
+    const int x = id & 7;
+    const int q = HG_FAST_XCD ? x * per + min(x, rem) + (id >> 3) : id;
     const int per_batch = tiles_m * tiles_n;
     batch = q / per_batch;
     const int l = q - batch * per_batch;
@@ -139,38 +164,62 @@ __device__ __forceinline__ void map_tile(int wg, int total, int tiles_m, int til
     tn = r / gsz;
 }
 
-template <bool OUT_F16, bool BETA>
+// Everything a workgroup needs to know about one tile.
+struct TileInfo {
+    int batch, m0, n0, N, K, rows_a, rows_b, kt0, nk;
+    hg_int32x4 ra, rb;
+};
+
+// First tile with id >= *id (stepping by `stride`) that has work; false if
+// none is left.  Entries of a batched launch narrower than the grid leave
+// empty tiles, which are skipped here (uniformly for the workgroup).
+template <bool TRI>
+__device__ __forceinline__ bool find_tile(const GemmParams &p, int &id, int stride, int total,
+                                          int tiles_m, int tiles_n, TileInfo &T)
+{
+    for (; id < total; id += stride) {
+        int batch, tm, tn;
+        map_tile(id, total, tiles_m, tiles_n, batch, tm, tn);
+        const int N = p.e[batch].N;
+        const int m0 = tm * BM, n0 = tn * BN;
+        if (m0 >= p.M || n0 >= N)
+            continue;
+        T.batch = batch;
+        T.m0 = m0;
+        T.n0 = n0;
+        T.N = N;
+        T.K = p.e[batch].K;
+        T.rows_a = min(p.M - m0, BM);
+        T.rows_b = min(N - n0, BN);
+        // TRI: B element (j, k) counts only for k >= j, so slices wholly
+        // left of the tile's first column are skipped.
+        T.kt0 = TRI ? n0 / BK : 0;
+        T.nk = (T.K + BK - 1) / BK - T.kt0;
+        const _Float16 *Ab = p.A + p.e[batch].a_off + (int64_t)m0 * p.lda;
+        const _Float16 *Bb = p.B + p.e[batch].b_off + (int64_t)n0 * p.ldb;
+        T.ra = make_rsrc(Ab, (uint32_t)(((int64_t)(T.rows_a - 1) * p.lda + T.K) * 2));
+        T.rb = make_rsrc(Bb, (uint32_t)(((int64_t)(T.rows_b - 1) * p.ldb + T.K) * 2));
+        return true;
+    }
+    return false;
+}
+
+template <bool OUT_F16, bool BETA, bool TRI>
 __global__ void __launch_bounds__(THREADS, 1)
 hgemm_fast_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int cvec)
 {
     __shared__ __attribute__((aligned(1024))) unsigned char smem[NST * LDS_STAGE];
 
-    int batch, tm, tn;
-    map_tile(blockIdx.x, total, tiles_m, tiles_n, batch, tm, tn);
-    const int M = p.M;
-    const int N = p.e[batch].N;
-    const int K = p.e[batch].K;
-    const int m0 = tm * BM;
-    const int n0 = tn * BN;
-    if (m0 >= M || n0 >= N)
-        return;
-    const int64_t lda = p.lda, ldb = p.ldb;
-    const int rows_a = min(M - m0, BM);
-    const int rows_b = min(N - n0, BN);
-    const _Float16 *Ab = p.A + p.e[batch].a_off + (int64_t)m0 * lda;
-    const _Float16 *Bb = p.B + p.e[batch].b_off + (int64_t)n0 * ldb;
-    const hg_int32x4 ra = make_rsrc(Ab, (uint32_t)(((int64_t)(rows_a - 1) * lda + K) * 2));
-    const hg_int32x4 rb = make_rsrc(Bb, (uint32_t)(((int64_t)(rows_b - 1) * ldb + K) * 2));
-
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = wave / WN, wn = wave % WN;
+    const uint32_t lds_base = (uint32_t)reinterpret_cast<uintptr_t>(smem);
+    const int stride = gridDim.x;
 
-    // Load geometry: wave w fills tile rows 64w .. 64w+63 of A and of B,
-    // RPI rows per instruction; lane l covers row RPI·i + (l div KC) of its
-    // group, physical chunk l mod KC, so it fetches the logical chunk that
-    // swz() puts there.
-    uint32_t aoff[LPS], boff[LPS];
+    // Load geometry: wave w fills tile rows RPW·w .. RPW·w+RPW-1 of A and of
+    // B, RPI rows per instruction; lane l covers row RPI·i + (l div KC) of its
+    // group, physical chunk l mod KC, so it fetches the logical chunk lkc[i]
+    // that swz() puts there.
     int lkc[LPS];
 #pragma unroll
     for (int i = 0; i < LPS; ++i) {
@@ -180,25 +229,31 @@ hgemm_fast_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int c
         for (int c = 0; c < KC; ++c)
             kc = swz(row, c) == lane % KC ? c : kc;
         lkc[i] = kc;
-        aoff[i] = row < rows_a ? (uint32_t)(row * (int)lda * 2 + kc * 16) : OOB;
-        boff[i] = row < rows_b ? (uint32_t)(row * (int)ldb * 2 + kc * 16) : OOB;
     }
-    const uint32_t lds_base = (uint32_t)reinterpret_cast<uintptr_t>(smem);
-
+    // Per-tile byte offsets of this lane's chunks (OOB for rows past the edge).
+    uint32_t aoff[LPS], boff[LPS];
+    auto set_offsets = [&](const TileInfo &T) {
+#pragma unroll
+        for (int i = 0; i < LPS; ++i) {
+            const int row = wave * RPW + i * RPI + lane / KC;
+            aoff[i] = row < T.rows_a ? (uint32_t)(row * (int)p.lda * 2 + lkc[i] * 16) : OOB;
+            boff[i] = row < T.rows_b ? (uint32_t)(row * (int)p.ldb * 2 + lkc[i] * 16) : OOB;
+        }
+    };
     // Loads q = first .. first+count-1 of slice kt into ring slot `slot`
     // (q < LPS: A rows, else B rows).  A slice past the end of K has
     // kval <= 0, so every lane gets the out-of-range offset and the slot is
     // zero-filled: the ring never needs a branch.
-    auto issue = [&](int kt, int slot, int first, int count) {
-        const uint32_t kb = (uint32_t)kt * RB;
-        const int kval = K - kt * BK;              // K % 8 == 0: chunks are all in or all out
+    auto issue = [&](const TileInfo &T, int kt, int slot, int first, int count) {
+        const uint32_t kb = (uint32_t)(T.kt0 + kt) * RB;
+        const int kval = T.K - (T.kt0 + kt) * BK;  // K % 8 == 0: chunks are all in or all out
         const uint32_t sbase = lds_base + slot * LDS_STAGE + wave * RPW * RB;
 #pragma unroll
         for (int q = first; q < first + count; ++q) {
             const bool isb = q >= LPS;
             const int i = isb ? q - LPS : q;
             const uint32_t off = lkc[i] * 8 < kval ? (isb ? boff[i] : aoff[i]) + kb : OOB;
-            hg_raw_buffer_load_lds(isb ? rb : ra,
+            hg_raw_buffer_load_lds(isb ? T.rb : T.ra,
                                    reinterpret_cast<hg_lds_u32 *>(
                                        (uintptr_t)(sbase + (isb ? LDS_A : 0) + i * 1024)),
                                    16, (int)off, 0, 0, 0);
@@ -206,7 +261,8 @@ hgemm_fast_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int c
     };
 
     // Fragment reads: row (lane mod 32) of each 32-row block, logical chunk
-    // 2s + (lane div 32) of k-step s.
+    // 2s + (lane div 32) of k-step s.  The same (lane, element) → k map is
+    // used for both operands, so the MFMA contracts matching k.
     const int frow = lane & 31;
     const int fhi = lane >> 5;
     auto frag_addr = [&](int slot, int s, bool isb) -> const unsigned char * {
@@ -214,14 +270,7 @@ hgemm_fast_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int c
         return smem + slot * LDS_STAGE + (isb ? LDS_A : 0) + (row0 + frow) * RB +
                swz(frow, 2 * s + fhi) * 16;
     };
-
     floatx16 acc[TM][TN];
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-            acc[i][j] = floatx16{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
-
     half8 fa[2][TM], fb[2][TN];
     // Fragment f of k-step s: f < TM is A block f, else B block f - TM.
     auto read_frag = [&](int fs, int slot, int s, int f) {
@@ -231,141 +280,230 @@ hgemm_fast_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int c
             fb[fs][f - TM] =
                 *reinterpret_cast<const half8 *>(frag_addr(slot, s, true) + (f - TM) * 32 * RB);
     };
-    auto read_frags = [&](int fs, int slot, int s) {
+    // TRI: zero the B fragment elements (j, k) with k < j.  Fragment j of
+    // k-step s holds row jrow = n0 + wn·WTN + 32j + (lane mod 32) and the 8
+    // k from kfirst = (kt0+kt)·BK + 16s + 8·(lane div 32); the first
+    // clamp(jrow - kfirst, 0, 8) of them are zeroed by a select (so NaN or
+    // Inf stored above the diagonal cannot reach the MFMA).
+    auto mask_tri = [&](const TileInfo &T, int fs, int kt, int s) {
+        const int kfirst = (T.kt0 + kt) * BK + 16 * s + 8 * fhi;
 #pragma unroll
-        for (int f = 0; f < TM + TN; ++f)
-            read_frag(fs, slot, s, f);
-    };
-    auto mfma = [&](int fs, int i, int j) {
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[fs][j], fa[fs][i], acc[i][j], 0, 0, 0);
-    };
-
-    // Ring of NST slices: slice t lives in slot t mod NST.  Slices
-    // t+1 .. t+NST-1 are in flight while slice t is multiplied; the slot of
-    // slice t-1 is refilled at the top of iteration t, after the barrier of
-    // iteration t-1 has seen every wave finish reading it.
-    // Ring schedule.  Slice t lives in slot t mod NST and is prefetched
-    // D = NST-1 slices ahead: the loads issued while slice kt is multiplied
-    // refill the slot of slice kt-1, which every wave finished reading before
-    // the barrier of iteration kt-1.
-    const int nk = (K + BK - 1) / BK;
-    for (int t = 0; t < D; ++t)
-        issue(t, t, 0, 2 * LPS);
-    wait_vmcnt<2 * LPS * (D - 1)>();             // slice 0 has landed
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-    read_frags(0, 0, 0);
-    int slot = 0;                                 // slot of slice kt
-    int lslot = D;                                // slot of slice kt + D
-    // Each k-step reads the fragments of the next k-step (TM+TN reads) and
-    // issues V loads of slice kt+D, spread over its TM·TN MFMAs in a fixed
-    // program order (a scheduling fence after every MFMA keeps it).  Before
-    // the last k-step the wave waits for slice kt+1 and crosses the barrier,
-    // so the last k-step reads slice kt+1's first fragments under its MFMAs.
-    // A slice index past the end of K multiplies a zero-filled slot.
-    constexpr int P = TM * TN, R = TM + TN, V = 2 * LPS / SPS;
-    static_assert(V * SPS == 2 * LPS, "loads must split evenly over the k-steps");
-    static_assert(P >= R + 2 * V, "interleave pattern needs enough MFMAs");
-    for (int kt = 0; kt < nk; ++kt) {
-        const int nxt = slot + 1 == NST ? 0 : slot + 1;
+        for (int j = 0; j < TN; ++j) {
+            const int t = T.n0 + wn * WTN + j * 32 + frow - kfirst;   // elements to zero
+            u32x4 w = __builtin_bit_cast(u32x4, fb[fs][j]);
 #pragma unroll
-        for (int s = 0; s < SPS; ++s) {
-            const bool last = s == SPS - 1;
-            if (last) {
-                // Before the barrier: this wave's loads of slice kt+1 have
-                // landed, and its reads of slice kt are complete (after the
-                // barrier other waves may start refilling slice kt's slot).
-                // Issued after slice kt+1 so far: slices kt+2 .. kt+D-1 and
-                // the first SPS-1 k-steps' share of slice kt+D.
-                wait_vmcnt<2 * LPS * (D - 2) + V * (SPS - 1)>();
-                wait_lgkmcnt<0>();
-                __builtin_amdgcn_s_barrier();
-                __builtin_amdgcn_sched_barrier(0);
+            for (int d = 0; d < 4; ++d) {
+                const uint32_t m = (2 * d >= t ? 0x0000ffffu : 0u) | (2 * d + 1 >= t ? 0xffff0000u : 0u);
+                w[d] &= m;
             }
-            const int rslot = last ? nxt : slot;   // where the next fragments come from
-            const int rstep = last ? 0 : s + 1;
-            const int fs = s & 1;
-#pragma unroll
-            for (int k = 0; k < P; ++k) {
-                mfma(fs, k / TN, k % TN);
-                if (k < R)                                   // reads early: they gate the next k-step
-                    read_frag(fs ^ 1, rslot, rstep, k);
-                else if ((k - R) % 2 == 1 && (k - R) / 2 < V)  // loads after them, every other MFMA
-                    issue(kt + D, lslot, s * V + (k - R) / 2, 1);
-                __builtin_amdgcn_sched_barrier(0);
-            }
+            fb[fs][j] = __builtin_bit_cast(half8, w);
         }
-        slot = nxt;
-        lslot = lslot + 1 == NST ? 0 : lslot + 1;
-    }
-    // The ring's last loads (zero fills past the end of K) must land before
-    // the workgroup can release its LDS.
-    wait_vmcnt<0>();
+    };
 
-    // Epilogue: block (i, j) holds Cᵀ; lane covers row m0 + wm·128 + 32i +
-    // (lane mod 32) and columns n0 + wn·128 + 32j + 8g + 4·(lane div 32) + 0..3.
+    int id = blockIdx.x;
+    TileInfo T;
+    if (!find_tile<TRI>(p, id, stride, total, tiles_m, tiles_n, T))
+        return;
+    set_offsets(T);
+    for (int t = 0; t < D; ++t)
+        issue(T, t, t, 0, 2 * LPS);
+
     const float alpha = p.alpha;
     const float beta = p.beta;
     const int64_t ldc = p.ldc;
-    const bool full = rows_a == BM && rows_b == BN && cvec;
+    for (;;) {
+        // ---- K loop of tile T.  Ring: slice t in slot t mod NST, prefetched
+        // D = NST-1 ahead; the loads issued during slice kt refill the slot of
+        // slice kt-1, which every wave finished reading before slice kt-1's
+        // barrier.
+        // The tile's first D slices have landed (own loads; the previous
+        // tile's epilogue stores are covered too, as loads and stores share
+        // the counter), then everyone else's.
+        wait_vmcnt<0>();
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-        const int row = m0 + wm * WTM + i * 32 + frow;
+        for (int f = 0; f < R; ++f)
+            read_frag(0, 0, 0, f);
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
+        for (int i = 0; i < TM; ++i)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int col = n0 + wn * WTN + j * 32 + 8 * g + 4 * fhi;
-                const floatx4 v = {acc[i][j][4 * g + 0], acc[i][j][4 * g + 1],
-                                   acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
-                const int64_t off = p.e[batch].c_off + (int64_t)row * ldc + col;
-                if (full) {
-                    if (OUT_F16) {
-                        halfx4 *cp = reinterpret_cast<halfx4 *>(static_cast<_Float16 *>(p.C) + off);
-                        halfx4 c = {};
-                        if (BETA)
-                            c = *cp;
-                        halfx4 h;
+            for (int j = 0; j < TN; ++j)
+                acc[i][j] = floatx16{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+        int slot = 0;                             // slot of slice kt
+        int lslot = D;                            // slot of slice kt + D
+        for (int kt = 0; kt < T.nk; ++kt) {
+            const int nxt = slot + 1 == NST ? 0 : slot + 1;
 #pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            h[e] = (_Float16)(BETA ? __builtin_fmaf(alpha, v[e], beta * (float)c[e])
-                                                   : alpha * v[e]);
-                        *cp = h;
-                    } else {
-                        floatx4 *cp = reinterpret_cast<floatx4 *>(static_cast<float *>(p.C) + off);
-                        floatx4 c = {};
-                        if (BETA)
-                            c = *cp;
-                        floatx4 r;
+            for (int s = 0; s < SPS; ++s) {
+                const bool last = s == SPS - 1;
+                if (last) {
+                    // This wave's loads of slice kt+1 have landed and its reads
+                    // of slice kt are complete: after the barrier other waves
+                    // may read slice kt+1 and refill slice kt's slot.
+                    wait_vmcnt<VM_AT_BARRIER>();
+                    wait_lgkmcnt<0>();
+                    __builtin_amdgcn_s_barrier();
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                const int rslot = last ? nxt : slot;   // where the next fragments come from
+                const int rstep = last ? 0 : s + 1;
+                const int fs = s & 1;
+                if (TRI)
+                    mask_tri(T, fs, kt, s);
 #pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            r[e] = BETA ? __builtin_fmaf(alpha, v[e], beta * c[e]) : alpha * v[e];
-                        *cp = r;
+                for (int k = 0; k < P; ++k) {
+                    acc[k / TN][k % TN] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                        fb[fs][k % TN], fa[fs][k / TN], acc[k / TN][k % TN], 0, 0, 0);
+                    // After MFMA k: the ops o (reads first: they gate the next
+                    // k-step; then loads) with o·P / (R+V) == k.
+#pragma unroll
+                    for (int o = 0; o < R + V; ++o) {
+                        if ((o * P) / (R + V) != k)
+                            continue;
+                        if (o < R)
+                            read_frag(fs ^ 1, rslot, rstep, o);
+                        else if (s < LSTEPS)
+                            issue(T, kt + D, lslot, s * V + (o - R), 1);
                     }
-                } else if (row < M) {
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+            slot = nxt;
+            lslot = lslot + 1 == NST ? 0 : lslot + 1;
+        }
+        // Ring drained (its last loads are zero fills past the end of K) and
+        // every wave done with LDS: the slots are free for the next tile.
+        wait_vmcnt<0>();
+        wait_lgkmcnt<0>();
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+
+        // ---- Next tile's first slices, in flight during this epilogue.
+        int nid = id + stride;
+        TileInfo Tn;
+        const bool more = find_tile<TRI>(p, nid, stride, total, tiles_m, tiles_n, Tn);
+        if (more) {
+            set_offsets(Tn);
+            for (int t = 0; t < D; ++t)
+                issue(Tn, t, t, 0, 2 * LPS);
+        }
+
+        // ---- Epilogue of tile T.  Block (i, j) of the accumulators is Cᵀ
+        // (the B fragment is the MFMA's first operand): lane covers row
+        // m0 + wm·WTM + 32i + (lane mod 32) and, for register group g,
+        // columns n0 + wn·WTN + 32j + 8g + 4·(lane div 32) + 0..3.
+        if (T.rows_a == BM && T.rows_b == BN && cvec) {
+            // Interior tile: one row block at a time, all of its C_in loads
+            // (beta != 0) issued before any of its stores.
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        if (col + e < N) {
+            for (int i = 0; i < TM; ++i) {
+                const int row = T.m0 + wm * WTM + i * 32 + frow;
+                const int64_t roff =
+                    p.e[T.batch].c_off + (int64_t)row * ldc + T.n0 + wn * WTN + 4 * fhi;
+                if (OUT_F16) {
+                    _Float16 *cr = static_cast<_Float16 *>(p.C) + roff;
+                    halfx4 cin[TN][4];
+                    if (BETA) {
+#pragma unroll
+                        for (int j = 0; j < TN; ++j)
+#pragma unroll
+                            for (int g = 0; g < 4; ++g)
+                                cin[j][g] = *reinterpret_cast<const halfx4 *>(cr + j * 32 + 8 * g);
+                    }
+#pragma unroll
+                    for (int j = 0; j < TN; ++j)
+#pragma unroll
+                        for (int g = 0; g < 4; ++g) {
+                            halfx4 h;
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                const float v = acc[i][j][4 * g + e];
+                                h[e] = (_Float16)(BETA ? __builtin_fmaf(alpha, v, beta * (float)cin[j][g][e])
+                                                       : alpha * v);
+                            }
+                            *reinterpret_cast<halfx4 *>(cr + j * 32 + 8 * g) = h;
+                        }
+                } else {
+                    float *cr = static_cast<float *>(p.C) + roff;
+                    floatx4 cin[TN][4];
+                    if (BETA) {
+#pragma unroll
+                        for (int j = 0; j < TN; ++j)
+#pragma unroll
+                            for (int g = 0; g < 4; ++g)
+                                cin[j][g] = *reinterpret_cast<const floatx4 *>(cr + j * 32 + 8 * g);
+                    }
+#pragma unroll
+                    for (int j = 0; j < TN; ++j)
+#pragma unroll
+                        for (int g = 0; g < 4; ++g) {
+                            floatx4 r;
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                const float v = acc[i][j][4 * g + e];
+                                r[e] = BETA ? __builtin_fmaf(alpha, v, beta * cin[j][g][e]) : alpha * v;
+                            }
+                            *reinterpret_cast<floatx4 *>(cr + j * 32 + 8 * g) = r;
+                        }
+                }
+            }
+        } else {
+            // Edge tile: element-wise guarded stores.
+#pragma unroll
+            for (int i = 0; i < TM; ++i) {
+                const int row = T.m0 + wm * WTM + i * 32 + frow;
+                if (row >= p.M)
+                    continue;
+#pragma unroll
+                for (int j = 0; j < TN; ++j) {
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const int col = T.n0 + wn * WTN + j * 32 + 8 * g + 4 * fhi;
+                        const int64_t off = p.e[T.batch].c_off + (int64_t)row * ldc + col;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            if (col + e >= T.N)
+                                continue;
+                            const float v = acc[i][j][4 * g + e];
                             if (OUT_F16) {
                                 _Float16 *cp = static_cast<_Float16 *>(p.C) + off + e;
-                                const float r = BETA ? __builtin_fmaf(alpha, v[e], beta * (float)*cp)
-                                                     : alpha * v[e];
-                                *cp = (_Float16)r;
+                                *cp = (_Float16)(BETA ? __builtin_fmaf(alpha, v, beta * (float)*cp)
+                                                      : alpha * v);
                             } else {
                                 float *cp = static_cast<float *>(p.C) + off + e;
-                                const float r = BETA ? __builtin_fmaf(alpha, v[e], beta * *cp)
-                                                     : alpha * v[e];
-                                *cp = r;
+                                *cp = BETA ? __builtin_fmaf(alpha, v, beta * *cp) : alpha * v;
                             }
                         }
                     }
                 }
             }
         }
+        if (!more)
+            break;
+        T = Tn;
+        id = nid;
     }
 }
 
-template <bool OUT_F16, bool BETA>
+// Persistent grid size: one workgroup per CU (the 128 KiB ring allows one).
+int cu_count()
+{
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return 256;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            n <= 0)
+            n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
+template <bool OUT_F16, bool BETA, bool TRI>
 hipError_t launch(const GemmParams &p, hipStream_t stream)
 {
     int maxN = 0;
@@ -382,7 +520,21 @@ hipError_t launch(const GemmParams &p, hipStream_t stream)
     int cvec = (reinterpret_cast<uintptr_t>(p.C) % align == 0) && (p.ldc % 4 == 0);
     for (int b = 0; b < p.nbatch; ++b)
         cvec = cvec && (p.e[b].c_off % 4 == 0);
-    hipLaunchKernelGGL((hgemm_fast_kernel<OUT_F16, BETA>), dim3((unsigned)total64), dim3(THREADS),
+    // Persistent grid (one workgroup per CU, a multiple of 8 so that every
+    // workgroup's strided tile ids stay on its own XCD) for short K, where
+    // the per-tile prologue and epilogue are a large share of a tile; long-K
+    // tiles run one workgroup per tile.
+    int maxK = 0;
+    for (int b = 0; b < p.nbatch; ++b)
+        maxK = p.e[b].K > maxK ? p.e[b].K : maxK;
+    int64_t grid = total64;
+    if (maxK < HG_FAST_PERSIST_MAXK) {
+        grid = cu_count();
+        grid = grid / 8 * 8 > 0 ? grid / 8 * 8 : grid;
+        if (grid > total64)
+            grid = total64;
+    }
+    hipLaunchKernelGGL((hgemm_fast_kernel<OUT_F16, BETA, TRI>), dim3((unsigned)grid), dim3(THREADS),
                        0, stream, p, tiles_m, tiles_n, (int)total64, cvec);
     return hipGetLastError();
 }
@@ -391,7 +543,7 @@ hipError_t launch(const GemmParams &p, hipStream_t stream)
 
 bool fast_path_ok(const GemmParams &p, const LaunchOpts &o)
 {
-    if (o.tri || !o.vec)
+    if (!o.vec || (o.tri && (o.out_f16 || o.beta_read)))
         return false;
     // 32-bit buffer offsets: every tile's byte range must stay below 2^31.
     if (p.lda > (1 << 21) || p.ldb > (1 << 21))
@@ -404,9 +556,13 @@ bool fast_path_ok(const GemmParams &p, const LaunchOpts &o)
 
 hipError_t launch_gemm_fast(const GemmParams &p, const LaunchOpts &o, hipStream_t stream)
 {
+    if (o.tri)
+        return launch<false, false, true>(p, stream);     // TRMM leaves: fp32, written once
     if (o.out_f16)
-        return o.beta_read ? launch<true, true>(p, stream) : launch<true, false>(p, stream);
-    return o.beta_read ? launch<false, true>(p, stream) : launch<false, false>(p, stream);
+        return o.beta_read ? launch<true, true, false>(p, stream)
+                           : launch<true, false, false>(p, stream);
+    return o.beta_read ? launch<false, true, false>(p, stream)
+                       : launch<false, false, false>(p, stream);
 }
 
 }  // namespace hg

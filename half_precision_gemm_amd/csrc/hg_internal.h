@@ -48,7 +48,8 @@ struct LaunchOpts {
 hipError_t launch_gemm(const GemmParams &p, const LaunchOpts &o, hipStream_t stream);
 
 // 256×256 direct-to-LDS pipelined kernel (hg_fast.hip): usable when the
-// operands allow 16-byte buffer loads and K % 8 == 0, and not for TRI.
+// operands allow 16-byte buffer loads and K % 8 == 0 (TRI: fp32 output
+// written once).
 bool fast_path_ok(const GemmParams &p, const LaunchOpts &o);
 hipError_t launch_gemm_fast(const GemmParams &p, const LaunchOpts &o, hipStream_t stream);
 
