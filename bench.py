@@ -50,13 +50,29 @@ def traffic_from_profiles(src_hash):
     return d.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(A, Bt, target_s=12.0):
+def mfma_ceiling():
+    """Run the MFMA-only ceiling probe (register-resident fp16 operands drawn
+    like the benchmark's); None if it is not built or fails."""
+    import subprocess
+    exe = os.path.join(ROOT, "half_precision_gemm_amd", "mfma_ceiling")
+    if not os.path.exists(exe):
+        return None
+    try:
+        r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+        d = json.loads(r.stdout.strip().splitlines()[-1])
+        d["frac_of_published_peak"] = round(d["mfma_ceiling_tflops"] / PEAK_FP16_TFLOPS, 4)
+        return d
+    except Exception as e:  # reported, never fatal for the benchmark
+        return {"error": str(e)[:200]}
+
+
+def cpu_baseline(A, Bt, target_s=15.0):
     """The oracle as it stands on a row block of the 8192³ HGEMM, sized for
     about target_s seconds; reported as TFLOP/s of that block."""
     import numpy as np
     import oracle
     K = A.shape[1]
-    r = 8
+    r = 96
     t0 = time.perf_counter()
     oracle.hgemm(np.ascontiguousarray(A[:r]), Bt)
     dt = time.perf_counter() - t0
@@ -78,6 +94,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-trmm", action="store_true", help="time the HGEMM alone")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the MFMA-only throughput ceiling probe")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="also run one plain device-to-device copy of BYTES bytes, the "
                          "reference kernel that scales the FETCH_SIZE / WRITE_SIZE counters")
@@ -188,6 +206,8 @@ def main():
         out["trmm_ms"] = {"avg": round(tavg, 4), "min": round(min(trmm_ms), 4),
                           "max": round(max(trmm_ms), 4)}
         out["trmm_effective_tflops"] = round(wt.flops / (tavg * 1e-3) / 1e12, 2)
+    if not args.no_ceiling:
+        out["mfma_ceiling"] = mfma_ceiling()
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle) ...", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(A, Bt)
