@@ -114,6 +114,7 @@ static_assert(LPS * RPI == RPW && TM >= 2 && TN >= 1, "");
 static_assert(NST >= 2 && NST * LDS_STAGE <= 160 * 1024, "LDS budget");
 static_assert(V * LSTEPS == 2 * LPS, "loads must split evenly over the k-steps");
 static_assert(LSTEPS <= SPS && (D >= 2 || LSTEPS < SPS), "");
+static_assert(TN >= 2, "B fragment reads need TN >= 2 MFMA slots");
 
 // Physical 16-byte chunk of logical chunk kc in LDS row r.  The LDS serves a
 // 16-byte read for 16 lanes per cycle over 64 four-byte banks (256 bytes);
@@ -210,7 +211,8 @@ hgemm_fast_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int c
 {
     __shared__ __attribute__((aligned(1024))) unsigned char smem[NST * LDS_STAGE];
 
-    const int lane = threadIdx.x & 63;
+    // Lane index, re-materialised at every tile (see the top of the tile loop).
+    int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = wave / WN, wn = wave % WN;
     const uint32_t lds_base = (uint32_t)reinterpret_cast<uintptr_t>(smem);
@@ -221,18 +223,18 @@ hgemm_fast_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int c
     // group, physical chunk l mod KC, so it fetches the logical chunk lkc[i]
     // that swz() puts there.
     int lkc[LPS];
-#pragma unroll
-    for (int i = 0; i < LPS; ++i) {
-        const int row = wave * RPW + i * RPI + lane / KC;
-        int kc = 0;
-#pragma unroll
-        for (int c = 0; c < KC; ++c)
-            kc = swz(row, c) == lane % KC ? c : kc;
-        lkc[i] = kc;
-    }
     // Per-tile byte offsets of this lane's chunks (OOB for rows past the edge).
     uint32_t aoff[LPS], boff[LPS];
     auto set_offsets = [&](const TileInfo &T) {
+#pragma unroll
+        for (int i = 0; i < LPS; ++i) {
+            const int row = wave * RPW + i * RPI + lane / KC;
+            int kc = 0;
+#pragma unroll
+            for (int c = 0; c < KC; ++c)
+                kc = swz(row, c) == lane % KC ? c : kc;
+            lkc[i] = kc;
+        }
 #pragma unroll
         for (int i = 0; i < LPS; ++i) {
             const int row = wave * RPW + i * RPI + lane / KC;
@@ -263,19 +265,22 @@ hgemm_fast_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int c
     // Fragment reads: row (lane mod 32) of each 32-row block, logical chunk
     // 2s + (lane div 32) of k-step s.  The same (lane, element) → k map is
     // used for both operands, so the MFMA contracts matching k.
-    const int frow = lane & 31;
-    const int fhi = lane >> 5;
     auto frag_addr = [&](int slot, int s, bool isb) -> const unsigned char * {
+        const int frow = lane & 31;
+        const int fhi = lane >> 5;
         const int row0 = isb ? wn * WTN : wm * WTM;
         return smem + slot * LDS_STAGE + (isb ? LDS_A : 0) + (row0 + frow) * RB +
                swz(frow, 2 * s + fhi) * 16;
     };
     floatx16 acc[TM][TN];
-    half8 fa[2][TM], fb[2][TN];
+    // A fragments are single-buffered: block i's next fragment is read right
+    // after the MFMAs that use the current one (i outer, j inner); B
+    // fragments, used through the whole k-step, are double-buffered.
+    half8 fa[TM], fb[2][TN];
     // Fragment f of k-step s: f < TM is A block f, else B block f - TM.
     auto read_frag = [&](int fs, int slot, int s, int f) {
         if (f < TM)
-            fa[fs][f] = *reinterpret_cast<const half8 *>(frag_addr(slot, s, false) + f * 32 * RB);
+            fa[f] = *reinterpret_cast<const half8 *>(frag_addr(slot, s, false) + f * 32 * RB);
         else
             fb[fs][f - TM] =
                 *reinterpret_cast<const half8 *>(frag_addr(slot, s, true) + (f - TM) * 32 * RB);
@@ -286,6 +291,8 @@ hgemm_fast_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int c
     // clamp(jrow - kfirst, 0, 8) of them are zeroed by a select (so NaN or
     // Inf stored above the diagonal cannot reach the MFMA).
     auto mask_tri = [&](const TileInfo &T, int fs, int kt, int s) {
+        const int frow = lane & 31;
+        const int fhi = lane >> 5;
         const int kfirst = (T.kt0 + kt) * BK + 16 * s + 8 * fhi;
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
@@ -311,15 +318,32 @@ hgemm_fast_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int c
     const float alpha = p.alpha;
     const float beta = p.beta;
     const int64_t ldc = p.ldc;
+    // Vector-memory operations an interior epilogue issues after the next
+    // tile's first slices (its C_in loads and its stores; all lanes active).
+    // The counter retires in issue order, so waiting until at most
+    // (first-slice loads) + EPI_OPS remain means slice 0 has landed while
+    // the epilogue's stores are still draining.
+    constexpr int EPI_OPS = TM * TN * 4 * (BETA ? 2 : 1);
+    constexpr int VM_TILE0 = 2 * LPS * (D - 1);
+    constexpr int VM_AFTER_EPI = VM_TILE0 + EPI_OPS < 63 ? VM_TILE0 + EPI_OPS : 63;
+    int prev = 0;                      // 0: first tile, 1: after an interior epilogue, 2: after an edge one
     for (;;) {
+        // Values derived from the lane index are recomputed per tile rather
+        // than kept live across the epilogue (where the accumulators need
+        // the register file).
+        __asm__ volatile("" : "+v"(lane));
         // ---- K loop of tile T.  Ring: slice t in slot t mod NST, prefetched
         // D = NST-1 ahead; the loads issued during slice kt refill the slot of
         // slice kt-1, which every wave finished reading before slice kt-1's
-        // barrier.
-        // The tile's first D slices have landed (own loads; the previous
-        // tile's epilogue stores are covered too, as loads and stores share
-        // the counter), then everyone else's.
-        wait_vmcnt<0>();
+        // barrier.  First: this wave's loads of slice 0 have landed (an edge
+        // epilogue's stores vary per lane, so after one everything is
+        // waited for), then everyone else's.
+        if (prev == 0)
+            wait_vmcnt<VM_TILE0>();
+        else if (prev == 1)
+            wait_vmcnt<VM_AFTER_EPI>();
+        else
+            wait_vmcnt<0>();
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -354,17 +378,22 @@ hgemm_fast_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int c
 #pragma unroll
                 for (int k = 0; k < P; ++k) {
                     acc[k / TN][k % TN] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                        fb[fs][k % TN], fa[fs][k / TN], acc[k / TN][k % TN], 0, 0, 0);
-                    // After MFMA k: the ops o (reads first: they gate the next
-                    // k-step; then loads) with o·P / (R+V) == k.
+                        fb[fs][k % TN], fa[k / TN], acc[k / TN][k % TN], 0, 0, 0);
+                    // After MFMA k: the next k-step's B fragment k (k < TN),
+                    // its A fragment i once block row i's last MFMA is issued,
+                    // and ring loads spread over the remaining MFMAs.
+                    if (k < TN)
+                        read_frag(fs ^ 1, rslot, rstep, TM + k);
+                    if (k % TN == TN - 1)
+                        read_frag(fs ^ 1, rslot, rstep, k / TN);
+                    else if (k >= TN && s < LSTEPS) {
+                        constexpr int SLOTS = (P - TN) - (P - TN) / TN;   // MFMAs with no A read
+                        const int idx = (k - TN) - (k - TN) / TN;         // rank among them
+                        // loads v = 0..V-1 at slots spread evenly over SLOTS
 #pragma unroll
-                    for (int o = 0; o < R + V; ++o) {
-                        if ((o * P) / (R + V) != k)
-                            continue;
-                        if (o < R)
-                            read_frag(fs ^ 1, rslot, rstep, o);
-                        else if (s < LSTEPS)
-                            issue(T, kt + D, lslot, s * V + (o - R), 1);
+                        for (int v = 0; v < V; ++v)
+                            if ((v * SLOTS) / V == idx)
+                                issue(T, kt + D, lslot, s * V + v, 1);
                     }
                     __builtin_amdgcn_sched_barrier(0);
                 }
@@ -388,12 +417,16 @@ hgemm_fast_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int c
             for (int t = 0; t < D; ++t)
                 issue(Tn, t, t, 0, 2 * LPS);
         }
+        __builtin_amdgcn_sched_barrier(0);   // those loads precede every epilogue access
 
+        const int frow = lane & 31;
+        const int fhi = lane >> 5;
         // ---- Epilogue of tile T.  Block (i, j) of the accumulators is Cᵀ
         // (the B fragment is the MFMA's first operand): lane covers row
         // m0 + wm·WTM + 32i + (lane mod 32) and, for register group g,
         // columns n0 + wn·WTN + 32j + 8g + 4·(lane div 32) + 0..3.
-        if (T.rows_a == BM && T.rows_b == BN && cvec) {
+        prev = T.rows_a == BM && T.rows_b == BN && cvec ? 1 : 2;
+        if (prev == 1) {
             // Interior tile: one row block at a time, all of its C_in loads
             // (beta != 0) issued before any of its stores.
 #pragma unroll
