@@ -197,7 +197,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_FP16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_FP16_TFLOPS, 4),
                      "traffic": traffic_from_profiles(src_hash),
-                     "kernel": "hgemm_fast_kernel (256x256 tile, 32-wide K slices) at M=N=K=8192, fp32 out",
+                     "kernel": "hgemm_fast_kernel (256x256 tile, 64-wide K stages) at M=N=K=8192, fp32 out",
                      "algorithmic_flops_per_launch": wg.flops},
         "kernel_source_sha256_16": src_hash,
     }

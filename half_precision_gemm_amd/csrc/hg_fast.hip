@@ -11,22 +11,28 @@
 //  * One workgroup = 4 waves (2×2) per 256×256 tile; each wave owns a
 //    128×128 sub-tile = 4×4 blocks of v_mfma_f32_32x32x16_f16, 256 fp32
 //    accumulators per lane (the AGPR file).
-//  * K is walked in BK = 32 slices held in a ring of NST = 4 LDS slots
-//    (32 KiB each), filled by the gfx950 direct buffer→LDS path
-//    (buffer_load_dwordx4 … lds): no staging registers, no ds_write.  Each
-//    wave instruction moves 16 rows × 64 bytes; lane l fetches the logical
+//  * K is walked in BK = 64 stages: one 128-byte cache line per operand row,
+//    so every L1→L2 request is a whole line (32-wide stages split each line
+//    over two requests, which doubled the request rate and the TA stalls).
+//    Operands reach LDS through the gfx950 direct buffer→LDS path
+//    (buffer_load_dwordx4 … lds; each wave instruction moves 8 rows × 128
+//    bytes): no staging registers, no ds_write.  Lane l fetches the logical
 //    16-byte chunk that the XOR swizzle places at position l, so the LDS
 //    image is already swizzled for the fragment reads.
+//  * The 160 KiB of LDS hold a 3-slot ring of A stages and a 2-slot ring of
+//    B stages (32 KiB each).  The extra A slot lets A loads run two stages
+//    ahead, so each k-step carries the same number of ring loads (4 per
+//    wave, evenly spaced) while every load still has at least three k-steps
+//    to land; one barrier per stage, in front of its last k-step.
 //  * Ragged M/N edges and the K tail are zero-filled by the buffer unit's
 //    range check (out-of-range rows and chunks get an offset past the
 //    resource size, which loads as zero): no branches in the main loop.
-//  * Software pipeline: slices are prefetched NST-1 ahead; within a slice,
-//    every MFMA is followed by at most one LDS fragment read (for the next
-//    k-step) or one ring load, in a fixed program order; one workgroup
-//    barrier per slice, in front of its last k-step.
-//  * Persistent workgroups: one per CU walks a strided list of tiles; the
-//    next tile's first slices are requested before the current tile's
-//    epilogue, so loads overlap the stores.
+//  * Fragments are double-buffered in registers; within a k-step each MFMA
+//    is followed by at most one LDS fragment read (for the next k-step) or
+//    one ring load, in a fixed program order.
+//  * Persistent workgroups (short K): one per CU walks a strided list of
+//    tiles; the next tile's first stages are requested before the current
+//    tile's epilogue, so loads overlap the stores.
 //
 // Workgroup→tile order: tile ids are regrouped per XCD (consecutive
 // workgroup ids run on different XCDs, each with its own L2), then each
@@ -51,22 +57,14 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef _Float16 halfx4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// Tunables (compile-time).  BK = 32 with 4 slots keeps three slices in
-// flight in 128 KiB of LDS; the wave layout is WM × WN.
-#ifndef HG_FAST_BK
-#define HG_FAST_BK 32
-#endif
-#ifndef HG_FAST_NST
-#define HG_FAST_NST 4
-#endif
+// Tunables (compile-time).  K is walked in BK = 64 stages (one 128-byte
+// cache line per operand row), two LDS stages of 64 KiB; the wave layout is
+// WM × WN.
 #ifndef HG_FAST_WM
 #define HG_FAST_WM 2
 #endif
 #ifndef HG_FAST_WN
 #define HG_FAST_WN 2
-#endif
-#ifndef HG_FAST_RPL
-#define HG_FAST_RPL (256 / (HG_FAST_BK * 2))
 #endif
 #ifndef HG_FAST_XCD
 #define HG_FAST_XCD 1
@@ -77,50 +75,44 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 #ifndef HG_FAST_GROUP
 #define HG_FAST_GROUP 4
 #endif
-
-constexpr int BM = 256, BN = 256, BK = HG_FAST_BK, NST = HG_FAST_NST;
+constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int NSA = 3, NSB = 2;             // LDS slots of the A and B rings
 constexpr int WM = HG_FAST_WM, WN = HG_FAST_WN, NW = WM * WN;   // waves per workgroup
 constexpr int THREADS = NW * 64;
 constexpr int WTM = BM / WM, WTN = BN / WN;                     // wave sub-tile
 constexpr int TM = WTM / 32, TN = WTN / 32;                     // 32×32 blocks per wave
-constexpr int RB = BK * 2;                  // bytes per LDS row
-constexpr int KC = BK / 8;                  // 16-byte chunks per row
-constexpr int RPL = HG_FAST_RPL;            // rows per 256-byte bank line (64 banks)
-constexpr int RPI = 1024 / RB;              // rows per buffer→LDS wave instruction
+constexpr int RB = BK * 2;                  // bytes per LDS row (128: one cache line)
+constexpr int KC = BK / 8;                  // 16-byte chunks per row (8)
+constexpr int RPL = 256 / RB;               // rows per 256-byte bank line (64 banks)
+constexpr int RPI = 1024 / RB;              // rows per buffer→LDS wave instruction (8)
 constexpr int RPW = BM / NW;                // tile rows each wave loads, per operand
-constexpr int LPS = RPW / RPI;              // load instructions per wave per operand
-constexpr int SPS = BK / 16;                // MFMA k-steps per slice
-constexpr int LDS_A = BM * RB;
-constexpr int LDS_STAGE = LDS_A + BN * RB;
-constexpr int D = NST - 1;                  // prefetch distance in slices
+constexpr int LPS = RPW / RPI;              // load instructions per wave per operand per stage
+constexpr int SPS = BK / 16;                // MFMA k-steps per stage (4)
+constexpr int SLOT = BM * RB;               // bytes of one operand's stage (32 KiB)
+constexpr int LDS_B = NSA * SLOT;           // B ring after the A ring
+constexpr int LDS_BYTES = (NSA + NSB) * SLOT;
 constexpr uint32_t OOB = 0x80000000u;       // offset that the range check rejects
-// k-steps of an iteration that carry its loads: all of them when slices are
-// prefetched two or more ahead; with a single slice ahead (D = 1), the loads
-// of slice kt+1 must all be issued before the barrier in front of the last
-// k-step.
-#ifndef HG_FAST_LSTEPS
-#define HG_FAST_LSTEPS (HG_FAST_NST > 2 ? HG_FAST_BK / 16 : 2)
-#endif
-constexpr int LSTEPS = HG_FAST_LSTEPS;
 constexpr int P = TM * TN;                  // MFMAs per k-step
 constexpr int R = TM + TN;                  // fragment reads per k-step
-constexpr int V = 2 * LPS / LSTEPS;         // ring loads per load-carrying k-step
-// Loads still allowed in flight at a slice's barrier: those issued after
-// slice kt+1's, i.e. slices kt+2 .. kt+D-1 and slice kt+D's share so far.
-constexpr int VM_AT_BARRIER =
-    D == 1 ? 0 : 2 * LPS * (D - 2) + V * (LSTEPS < SPS - 1 ? LSTEPS : SPS - 1);
-static_assert(BK == 32 || BK == 64, "");
-static_assert(LPS * RPI == RPW && TM >= 2 && TN >= 1, "");
-static_assert(NST >= 2 && NST * LDS_STAGE <= 160 * 1024, "LDS budget");
-static_assert(V * LSTEPS == 2 * LPS, "loads must split evenly over the k-steps");
-static_assert(LSTEPS <= SPS && (D >= 2 || LSTEPS < SPS), "");
-static_assert(TN >= 2, "B fragment reads need TN >= 2 MFMA slots");
+constexpr int LH = LPS / 2;                 // loads per k-step
+static_assert(SPS == 4 && BM == BN, "");
+static_assert(LPS * RPI == RPW && LPS % 2 == 0 && TM >= 2 && TN >= 1, "");
+static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+static_assert(P >= R + LH, "one fragment read or ring load per MFMA");
 
 // Physical 16-byte chunk of logical chunk kc in LDS row r.  The LDS serves a
 // 16-byte read for 16 lanes per cycle over 64 four-byte banks (256 bytes);
 // a fragment read has 16 consecutive rows at one logical chunk, which this
 // XOR spreads over 16 distinct bank groups.
 __device__ __forceinline__ int swz(int r, int kc) { return kc ^ ((r / RPL) & (KC - 1)); }
+
+// Fragment read order within a k-step: A block 0, then every B block, then
+// A blocks 1..TM-1 -- the order in which the MFMAs (block row i outer, block
+// column j inner) first use them.  f < TM is A block f, else B block f - TM.
+__device__ __forceinline__ constexpr int read_order(int o)
+{
+    return o == 0 ? 0 : (o <= TN ? TM + o - 1 : o - TN);
+}
 
 // s_waitcnt on one counter only (the others left at their maxima).
 template <int n>
@@ -209,7 +201,7 @@ template <bool OUT_F16, bool BETA, bool TRI>
 __global__ void __launch_bounds__(THREADS, 1)
 hgemm_fast_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int cvec)
 {
-    __shared__ __attribute__((aligned(1024))) unsigned char smem[NST * LDS_STAGE];
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[LDS_BYTES];
 
     // Lane index, re-materialised at every tile (see the top of the tile loop).
     int lane = threadIdx.x & 63;
@@ -242,24 +234,29 @@ hgemm_fast_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int c
             boff[i] = row < T.rows_b ? (uint32_t)(row * (int)p.ldb * 2 + lkc[i] * 16) : OOB;
         }
     };
-    // Loads q = first .. first+count-1 of slice kt into ring slot `slot`
-    // (q < LPS: A rows, else B rows).  A slice past the end of K has
-    // kval <= 0, so every lane gets the out-of-range offset and the slot is
-    // zero-filled: the ring never needs a branch.
-    auto issue = [&](const TileInfo &T, int kt, int slot, int first, int count) {
+    // Loads q = first .. first+count-1 of operand `isb` (A or B) of stage
+    // kt into that operand's ring slot `slot`.  A stage past the end of K
+    // has kval <= 0, so every lane gets the out-of-range offset and the slot
+    // is zero-filled: the ring never needs a branch.
+    auto issue = [&](const TileInfo &T, bool isb, int kt, int slot, int first, int count) {
         const uint32_t kb = (uint32_t)(T.kt0 + kt) * RB;
         const int kval = T.K - (T.kt0 + kt) * BK;  // K % 8 == 0: chunks are all in or all out
-        const uint32_t sbase = lds_base + slot * LDS_STAGE + wave * RPW * RB;
+        const uint32_t sbase = lds_base + (isb ? LDS_B : 0) + slot * SLOT + wave * RPW * RB;
 #pragma unroll
-        for (int q = first; q < first + count; ++q) {
-            const bool isb = q >= LPS;
-            const int i = isb ? q - LPS : q;
+        for (int i = first; i < first + count; ++i) {
             const uint32_t off = lkc[i] * 8 < kval ? (isb ? boff[i] : aoff[i]) + kb : OOB;
             hg_raw_buffer_load_lds(isb ? T.rb : T.ra,
-                                   reinterpret_cast<hg_lds_u32 *>(
-                                       (uintptr_t)(sbase + (isb ? LDS_A : 0) + i * 1024)),
+                                   reinterpret_cast<hg_lds_u32 *>((uintptr_t)(sbase + i * 1024)),
                                    16, (int)off, 0, 0, 0);
         }
+    };
+    // Every load of the first stages of tile T: A and B of stage 0, A of
+    // stage 1 and the first half of B of stage 1 (the K loop issues the rest).
+    auto prologue = [&](const TileInfo &T) {
+        issue(T, false, 0, 0, 0, LPS);
+        issue(T, true, 0, 0, 0, LPS);
+        issue(T, false, 1, 1, 0, LPS);
+        issue(T, true, 1, 1, 0, LH);
     };
 
     // Fragment reads: row (lane mod 32) of each 32-row block, logical chunk
@@ -269,21 +266,20 @@ hgemm_fast_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int c
         const int frow = lane & 31;
         const int fhi = lane >> 5;
         const int row0 = isb ? wn * WTN : wm * WTM;
-        return smem + slot * LDS_STAGE + (isb ? LDS_A : 0) + (row0 + frow) * RB +
+        return smem + (isb ? LDS_B : 0) + slot * SLOT + (row0 + frow) * RB +
                swz(frow, 2 * s + fhi) * 16;
     };
     floatx16 acc[TM][TN];
-    // A fragments are single-buffered: block i's next fragment is read right
-    // after the MFMAs that use the current one (i outer, j inner); B
-    // fragments, used through the whole k-step, are double-buffered.
-    half8 fa[TM], fb[2][TN];
+    // Fragments are double-buffered: the next k-step's are read into the
+    // other set while this k-step's MFMAs run.
+    half8 fa[2][TM], fb[2][TN];
     // Fragment f of k-step s: f < TM is A block f, else B block f - TM.
-    auto read_frag = [&](int fs, int slot, int s, int f) {
+    auto read_frag = [&](int fs, int aslot, int bslot, int s, int f) {
         if (f < TM)
-            fa[f] = *reinterpret_cast<const half8 *>(frag_addr(slot, s, false) + f * 32 * RB);
+            fa[fs][f] = *reinterpret_cast<const half8 *>(frag_addr(aslot, s, false) + f * 32 * RB);
         else
             fb[fs][f - TM] =
-                *reinterpret_cast<const half8 *>(frag_addr(slot, s, true) + (f - TM) * 32 * RB);
+                *reinterpret_cast<const half8 *>(frag_addr(bslot, s, true) + (f - TM) * 32 * RB);
     };
     // TRI: zero the B fragment elements (j, k) with k < j.  Fragment j of
     // k-step s holds row jrow = n0 + wn·WTN + 32j + (lane mod 32) and the 8
@@ -312,8 +308,7 @@ hgemm_fast_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int c
     if (!find_tile<TRI>(p, id, stride, total, tiles_m, tiles_n, T))
         return;
     set_offsets(T);
-    for (int t = 0; t < D; ++t)
-        issue(T, t, t, 0, 2 * LPS);
+    prologue(T);
 
     const float alpha = p.alpha;
     const float beta = p.beta;
@@ -324,7 +319,7 @@ hgemm_fast_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int c
     // (first-slice loads) + EPI_OPS remain means slice 0 has landed while
     // the epilogue's stores are still draining.
     constexpr int EPI_OPS = TM * TN * 4 * (BETA ? 2 : 1);
-    constexpr int VM_TILE0 = 2 * LPS * (D - 1);
+    constexpr int VM_TILE0 = LPS + LH;  // stage 1's loads, issued after stage 0's
     constexpr int VM_AFTER_EPI = VM_TILE0 + EPI_OPS < 63 ? VM_TILE0 + EPI_OPS : 63;
     int prev = 0;                      // 0: first tile, 1: after an interior epilogue, 2: after an edge one
     for (;;) {
@@ -332,12 +327,18 @@ hgemm_fast_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int c
         // than kept live across the epilogue (where the accumulators need
         // the register file).
         __asm__ volatile("" : "+v"(lane));
-        // ---- K loop of tile T.  Ring: slice t in slot t mod NST, prefetched
-        // D = NST-1 ahead; the loads issued during slice kt refill the slot of
-        // slice kt-1, which every wave finished reading before slice kt-1's
-        // barrier.  First: this wave's loads of slice 0 have landed (an edge
-        // epilogue's stores vary per lane, so after one everything is
-        // waited for), then everyone else's.
+        // ---- K loop of tile T.  Stage t's A lives in A slot t mod 3, its B
+        // in B slot t mod 2.  A slot t mod 3 is free after the barrier in
+        // stage t-3 (in front of its last k-step, when every wave has
+        // finished reading stage t-3), B slot t mod 2 after the one in stage
+        // t-2.  Each k-step of stage kt carries LH ring loads: k-step 3 (after
+        // the barrier) the first half of B of stage kt+2, k-step 0 the second
+        // half of B of stage kt+1, k-steps 1 and 2 the A of stage kt+2.  The
+        // barrier of stage kt publishes stage kt+1 (whose last loads were
+        // issued in k-step 0), so every load has at least three k-steps to
+        // land.  First: this wave's loads of stage 0 have landed (an edge
+        // epilogue's stores vary per lane, so after one everything is waited
+        // for), then everyone else's.
         if (prev == 0)
             wait_vmcnt<VM_TILE0>();
         else if (prev == 1)
@@ -348,58 +349,61 @@ hgemm_fast_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int c
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int f = 0; f < R; ++f)
-            read_frag(0, 0, 0, f);
+            read_frag(0, 0, 0, 0, f);
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
             for (int j = 0; j < TN; ++j)
                 acc[i][j] = floatx16{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
-        int slot = 0;                             // slot of slice kt
-        int lslot = D;                            // slot of slice kt + D
+        int as = 0, bs = 0;                       // A and B slots of stage kt
         for (int kt = 0; kt < T.nk; ++kt) {
-            const int nxt = slot + 1 == NST ? 0 : slot + 1;
+            const int an = as == NSA - 1 ? 0 : as + 1;   // stage kt+1
+            const int a2 = an == NSA - 1 ? 0 : an + 1;   // stage kt+2
+            const int bn = bs ^ 1;
 #pragma unroll
             for (int s = 0; s < SPS; ++s) {
                 const bool last = s == SPS - 1;
                 if (last) {
-                    // This wave's loads of slice kt+1 have landed and its reads
-                    // of slice kt are complete: after the barrier other waves
-                    // may read slice kt+1 and refill slice kt's slot.
-                    wait_vmcnt<VM_AT_BARRIER>();
+                    // This wave's loads of stage kt+1 have landed (only the A
+                    // loads of stage kt+2 may be in flight) and its reads of
+                    // stage kt are complete: after the barrier every wave may
+                    // read stage kt+1 and refill stage kt's slots.
+                    wait_vmcnt<LPS>();
                     wait_lgkmcnt<0>();
                     __builtin_amdgcn_s_barrier();
                     __builtin_amdgcn_sched_barrier(0);
                 }
-                const int rslot = last ? nxt : slot;   // where the next fragments come from
+                const int ra = last ? an : as;     // where the next fragments come from
+                const int rb = last ? bn : bs;
                 const int rstep = last ? 0 : s + 1;
                 const int fs = s & 1;
                 if (TRI)
                     mask_tri(T, fs, kt, s);
+                // Ring loads of this k-step: operand, stage, slot, first index.
+                const bool lb = s == 0 || s == 3;
+                const int lkt = s == 0 ? kt + 1 : kt + 2;
+                const int lsl = s == 0 ? bn : s == 3 ? bs : a2;
+                const int lfirst = s == 0 || s == 2 ? LH : 0;
 #pragma unroll
                 for (int k = 0; k < P; ++k) {
                     acc[k / TN][k % TN] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                        fb[fs][k % TN], fa[k / TN], acc[k / TN][k % TN], 0, 0, 0);
-                    // After MFMA k: the next k-step's B fragment k (k < TN),
-                    // its A fragment i once block row i's last MFMA is issued,
-                    // and ring loads spread over the remaining MFMAs.
-                    if (k < TN)
-                        read_frag(fs ^ 1, rslot, rstep, TM + k);
-                    if (k % TN == TN - 1)
-                        read_frag(fs ^ 1, rslot, rstep, k / TN);
-                    else if (k >= TN && s < LSTEPS) {
-                        constexpr int SLOTS = (P - TN) - (P - TN) / TN;   // MFMAs with no A read
-                        const int idx = (k - TN) - (k - TN) / TN;         // rank among them
-                        // loads v = 0..V-1 at slots spread evenly over SLOTS
-#pragma unroll
-                        for (int v = 0; v < V; ++v)
-                            if ((v * SLOTS) / V == idx)
-                                issue(T, kt + D, lslot, s * V + v, 1);
+                        fb[fs][k % TN], fa[fs][k / TN], acc[k / TN][k % TN], 0, 0, 0);
+                    // After MFMA k: one ring load every P/LH MFMAs (from the
+                    // second on), the next k-step's fragments after the
+                    // others, in the order the next k-step consumes them.
+                    constexpr int GAP = P / LH;
+                    if (k % GAP == GAP / 2 && k / GAP < LH)
+                        issue(T, lb, lkt, lsl, lfirst + k / GAP, 1);
+                    else {
+                        const int o = k - (k >= GAP / 2 ? 1 + (k - GAP / 2) / GAP : 0);
+                        if (o < R)
+                            read_frag(fs ^ 1, ra, rb, rstep, read_order(o));
                     }
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
-            slot = nxt;
-            lslot = lslot + 1 == NST ? 0 : lslot + 1;
+            as = an;
+            bs = bn;
         }
         // Ring drained (its last loads are zero fills past the end of K) and
         // every wave done with LDS: the slots are free for the next tile.
@@ -414,8 +418,7 @@ hgemm_fast_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int c
         const bool more = find_tile<TRI>(p, nid, stride, total, tiles_m, tiles_n, Tn);
         if (more) {
             set_offsets(Tn);
-            for (int t = 0; t < D; ++t)
-                issue(Tn, t, t, 0, 2 * LPS);
+            prologue(Tn);
         }
         __builtin_amdgcn_sched_barrier(0);   // those loads precede every epilogue access
 
