@@ -32,7 +32,7 @@ HG_F32 = 1
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
-                      "or python -m half_precision_gemm_amd.build")
+                      "or python half_precision_gemm_amd/build.py")
 
 lib = ctypes.CDLL(LIB_PATH)
 _i64, _f32, _vp, _int = ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_int

@@ -1,6 +1,6 @@
 """Build libhgemm.so (the C-ABI library with its gfx950 kernels) in-tree.
 
-    python -m half_precision_gemm_amd.build          # or __graft_entry__.build()
+    python half_precision_gemm_amd/build.py          # or __graft_entry__.build()
 
 hipcc cross-compiles for gfx950 without a GPU.  Packed-fp32 VALU ops are
 disabled for all device code (-packed-fp32-ops feature off).
