@@ -8,28 +8,27 @@
 // triangle-masked leaf of the recursive TRMM ("异构计算中高性能TRMM与TRSM的
 // 递归算法实现" §2.2).  Design:
 //
-//  * One workgroup = 4 waves (2×2) per 256×256 tile; each wave owns a
-//    128×128 sub-tile = 4×4 blocks of v_mfma_f32_32x32x16_f16, 256 fp32
-//    accumulators per lane (the AGPR file).
-//  * K is walked in BK = 64 stages: one 128-byte cache line per operand row,
-//    so every L1→L2 request is a whole line (32-wide stages split each line
-//    over two requests, which doubled the request rate and the TA stalls).
+//  * One workgroup = 8 waves (2 per SIMD) per 256×256 tile, laid out 2×4;
+//    each wave owns a 128×64 sub-tile = 8×4 blocks of
+//    v_mfma_f32_16x16x32_f16, 128 fp32 accumulators per lane.  The 16×16×32
+//    shape draws less power per flop than 32×32×16 on these data, so the
+//    chip holds a higher clock; two waves per SIMD keep the matrix core fed
+//    while the other waits on LDS, whose per-wave throughput (about 27
+//    bytes per clock for reads and direct loads together) would otherwise
+//    bound a single wave.
+//  * K is walked in BK = 64 stages: one 128-byte cache line per operand row.
 //    Operands reach LDS through the gfx950 direct buffer→LDS path
 //    (buffer_load_dwordx4 … lds; each wave instruction moves 8 rows × 128
 //    bytes): no staging registers, no ds_write.  Lane l fetches the logical
 //    16-byte chunk that the XOR swizzle places at position l, so the LDS
 //    image is already swizzled for the fragment reads.
 //  * The 160 KiB of LDS hold a 3-slot ring of A stages and a 2-slot ring of
-//    B stages (32 KiB each).  The extra A slot lets A loads run two stages
-//    ahead, so each k-step carries the same number of ring loads (4 per
-//    wave, evenly spaced) while every load still has at least three k-steps
-//    to land; one barrier per stage, in front of its last k-step.
+//    B stages (32 KiB each); one barrier per stage.
 //  * Ragged M/N edges and the K tail are zero-filled by the buffer unit's
 //    range check (out-of-range rows and chunks get an offset past the
 //    resource size, which loads as zero): no branches in the main loop.
-//  * Fragments are double-buffered in registers; within a k-step each MFMA
-//    is followed by at most one LDS fragment read (for the next k-step) or
-//    one ring load, in a fixed program order.
+//  * Each stage is four quarters of 16 MFMAs; fragment reads and ring loads
+//    are spread evenly over the MFMAs at compile-time positions.
 //  * Persistent workgroups (short K): one per CU walks a strided list of
 //    tiles; the next tile's first stages are requested before the current
 //    tile's epilogue, so loads overlap the stores.
@@ -39,6 +38,8 @@
 // XCD's range is walked in bands of 4 tile rows, column by column, so the
 // tiles resident on one XCD share A row panels and B column panels.
 #include "hg_internal.h"
+
+#include <utility>
 
 typedef int32_t hg_int32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) uint32_t hg_lds_u32;
@@ -52,20 +53,10 @@ namespace hg {
 namespace {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
-typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef _Float16 halfx4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// Tunables (compile-time).  K is walked in BK = 64 stages (one 128-byte
-// cache line per operand row), two LDS stages of 64 KiB; the wave layout is
-// WM × WN.
-#ifndef HG_FAST_WM
-#define HG_FAST_WM 2
-#endif
-#ifndef HG_FAST_WN
-#define HG_FAST_WN 2
-#endif
 #ifndef HG_FAST_XCD
 #define HG_FAST_XCD 1
 #endif
@@ -75,30 +66,35 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 #ifndef HG_FAST_GROUP
 #define HG_FAST_GROUP 4
 #endif
+#ifndef HG_FAST_NW
+#define HG_FAST_NW 4
+#endif
 constexpr int BM = 256, BN = 256, BK = 64;
 constexpr int NSA = 3, NSB = 2;             // LDS slots of the A and B rings
-constexpr int WM = HG_FAST_WM, WN = HG_FAST_WN, NW = WM * WN;   // waves per workgroup
+constexpr int NW = HG_FAST_NW;              // waves per workgroup (4: 2×2, 8: 2×4)
+constexpr int WM = 2, WN = NW / 2;
 constexpr int THREADS = NW * 64;
-constexpr int WTM = BM / WM, WTN = BN / WN;                     // wave sub-tile
-constexpr int TM = WTM / 32, TN = WTN / 32;                     // 32×32 blocks per wave
+constexpr int WTM = BM / WM, WTN = BN / WN; // wave sub-tile (128×128 or 128×64)
+constexpr int FB = 16;                      // MFMA output block edge (16×16)
+constexpr int KS = 32;                      // k per MFMA
+constexpr int TM = WTM / FB, TN = WTN / FB; // 16×16 blocks per wave
 constexpr int RB = BK * 2;                  // bytes per LDS row (128: one cache line)
 constexpr int KC = BK / 8;                  // 16-byte chunks per row (8)
 constexpr int RPL = 256 / RB;               // rows per 256-byte bank line (64 banks)
 constexpr int RPI = 1024 / RB;              // rows per buffer→LDS wave instruction (8)
 constexpr int RPW = BM / NW;                // tile rows each wave loads, per operand
 constexpr int LPS = RPW / RPI;              // load instructions per wave per operand per stage
-constexpr int SPS = BK / 16;                // MFMA k-steps per stage (4)
+constexpr int SPS = BK / KS;                // MFMA k-steps per stage (2)
+constexpr int NQ = 4;                       // quarters per stage (k-step × half of the A blocks)
+constexpr int TMQ = TM / 2;                 // A blocks per quarter
+constexpr int PQ = TMQ * TN;                // MFMAs per quarter
 constexpr int SLOT = BM * RB;               // bytes of one operand's stage (32 KiB)
 constexpr int LDS_B = NSA * SLOT;           // B ring after the A ring
 constexpr int LDS_BYTES = (NSA + NSB) * SLOT;
 constexpr uint32_t OOB = 0x80000000u;       // offset that the range check rejects
-constexpr int P = TM * TN;                  // MFMAs per k-step
-constexpr int R = TM + TN;                  // fragment reads per k-step
-constexpr int LH = LPS / 2;                 // loads per k-step
-static_assert(SPS == 4 && BM == BN, "");
-static_assert(LPS * RPI == RPW && LPS % 2 == 0 && TM >= 2 && TN >= 1, "");
+static_assert((NW == 4 || NW == 8) && SPS == 2 && BM == BN && TM == 8, "");
+static_assert(LPS * RPI == RPW, "");
 static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
-static_assert(P >= R + LH, "one fragment read or ring load per MFMA");
 
 // Physical 16-byte chunk of logical chunk kc in LDS row r.  The LDS serves a
 // 16-byte read for 16 lanes per cycle over 64 four-byte banks (256 bytes);
@@ -106,12 +102,86 @@ static_assert(P >= R + LH, "one fragment read or ring load per MFMA");
 // XOR spreads over 16 distinct bank groups.
 __device__ __forceinline__ int swz(int r, int kc) { return kc ^ ((r / RPL) & (KC - 1)); }
 
-// Fragment read order within a k-step: A block 0, then every B block, then
-// A blocks 1..TM-1 -- the order in which the MFMAs (block row i outer, block
-// column j inner) first use them.  f < TM is A block f, else B block f - TM.
-__device__ __forceinline__ constexpr int read_order(int o)
+// ---- Schedule of one stage.  Quarter q runs k-step q/2 on A blocks
+// (q%2)·TMQ .. +TMQ-1 and all TN B blocks, B block outer (the quarter's A
+// blocks are all used by its first TMQ MFMAs, B block j first by MFMA
+// TMQ·j).  A fragments are read one quarter ahead (two sets,
+// one per quarter parity), B fragments one k-step ahead (two sets, one per
+// k-step), half of them in each quarter of the k-step before:
+//   q0: A of q1 (stage kt, k-step 0)      + B blocks 0,1 of k-step 1
+//   q1: A of q2 (stage kt, k-step 1)      + B blocks 2,3 of k-step 1
+//   q2: A of q3 (stage kt, k-step 1) | barrier | B blocks 0,1 of stage kt+1, k-step 0
+//   q3: A of q0 (stage kt+1, k-step 0)    + B blocks 2,3 of stage kt+1, k-step 0
+// The barrier (in front of MFMA BAR_K of quarter 2) follows every read of
+// stage kt and precedes every read of stage kt+1.  Ring loads, LPS/2 per
+// quarter: quarters 0 and 1 the A of stage kt+2 (its slot was freed by the
+// previous stage's barrier), quarters 2 (after the barrier) and 3 the B of
+// stage kt+2 (its slot is the one this barrier frees).
+// Op after MFMA k of quarter q: kRA + i reads A block i of the quarter's
+// range, kRB + i the quarter's i-th B block, kLD + i ring load i.  Reads and
+// loads are spread evenly over the quarter: a wave's LDS traffic stays
+// steady instead of arriving in bursts that block its instruction stream
+// (with one wave per SIMD, every such stall idles the matrix core).
+constexpr int kNone = 0, kRA = 1, kRB = 8, kLD = 16;
+constexpr int BAR_K = NW == 8 ? 10 : 13;
+__device__ __forceinline__ constexpr int sched8(int q, int k)
 {
-    return o == 0 ? 0 : (o <= TN ? TM + o - 1 : o - TN);
+    if (q == 2) {
+        switch (k) {
+        case 0: return kRA + 0;
+        case 2: return kRA + 1;
+        case 4: return kRA + 2;
+        case 6: return kRA + 3;
+        case 10: return kLD + 0;
+        case 11: return kRB + 0;
+        case 13: return kRB + 1;
+        case 14: return kLD + 1;
+        default: return kNone;
+        }
+    }
+    switch (k) {
+    case 0: return kRA + 0;
+    case 1: return kLD + 0;
+    case 2: return kRA + 1;
+    case 4: return kRA + 2;
+    case 5: return kLD + 1;
+    case 6: return kRA + 3;
+    case 8: return kRB + 0;
+    case 10: return kRB + 1;
+    default: return kNone;
+    }
+}
+// Four waves: 32 MFMAs, 4 A + 4 B reads and 4 loads per quarter.
+__device__ __forceinline__ constexpr int sched4(int q, int k)
+{
+    if (q == 2) {
+        if (k <= 9 && k % 3 == 0)
+            return kRA + k / 3;
+        if (k >= 16 && k % 4 == 0)
+            return kRB + (k - 16) / 4;
+        if (k >= 14 && k <= 26 && k % 4 == 2)
+            return kLD + (k - 14) / 4;
+        return kNone;
+    }
+    if (k % 4 == 0)
+        return k < 16 ? kRA + k / 4 : kRB + (k - 16) / 4;
+    if (k % 8 == 2)
+        return kLD + k / 8;
+    return kNone;
+}
+__device__ __forceinline__ constexpr int sched(int q, int k) { return NW == 8 ? sched8(q, k) : sched4(q, k); }
+
+// f(integral_constant<int, i>) for i = 0 .. N-1, so that schedule lookups
+// inside f are constant expressions.
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, I...>)
+{
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F &&f)
+{
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
 // s_waitcnt on one counter only (the others left at their maxima).
@@ -197,7 +267,7 @@ __device__ __forceinline__ bool find_tile(const GemmParams &p, int &id, int stri
     return false;
 }
 
-template <bool OUT_F16, bool BETA, bool TRI>
+template <bool OUT_F16, bool BETA, bool TRI, bool KCHK>
 __global__ void __launch_bounds__(THREADS, 1)
 hgemm_fast_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int cvec)
 {
@@ -234,72 +304,79 @@ hgemm_fast_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int c
             boff[i] = row < T.rows_b ? (uint32_t)(row * (int)p.ldb * 2 + lkc[i] * 16) : OOB;
         }
     };
-    // Loads q = first .. first+count-1 of operand `isb` (A or B) of stage
-    // kt into that operand's ring slot `slot`.  A stage past the end of K
-    // has kval <= 0, so every lane gets the out-of-range offset and the slot
-    // is zero-filled: the ring never needs a branch.
-    auto issue = [&](const TileInfo &T, bool isb, int kt, int slot, int first, int count) {
+    // Load i of operand `isb` (A or B) of stage kt into that operand's ring
+    // slot `slot`.  The stage's K offset is folded into the buffer resource
+    // (base advanced, range shortened, both scalar), so the per-lane offset
+    // stays the tile's constant and no vector instruction sits in front of
+    // the load; a stage past the end of K gets an empty range and is
+    // zero-filled, so the ring never needs a branch.  With KCHK (K not a
+    // multiple of BK) the last stage is partial: each lane's chunk is checked
+    // against K and chunks past it get the out-of-range offset.
+    auto issue = [&](const TileInfo &T, bool isb, int kt, int slot, int i) {
         const uint32_t kb = (uint32_t)(T.kt0 + kt) * RB;
-        const int kval = T.K - (T.kt0 + kt) * BK;  // K % 8 == 0: chunks are all in or all out
         const uint32_t sbase = lds_base + (isb ? LDS_B : 0) + slot * SLOT + wave * RPW * RB;
+        hg_int32x4 r = isb ? T.rb : T.ra;
+        uint32_t off = isb ? boff[i] : aoff[i];
+        if constexpr (KCHK) {
+            const int kval = T.K - (T.kt0 + kt) * BK;  // K % 8 == 0: chunks are all in or all out
+            off = lkc[i] * 8 < kval ? off + kb : OOB;
+        } else {
+            const uint64_t base = ((uint64_t)(uint32_t)r[1] << 32 | (uint32_t)r[0]) + kb;
+            r[0] = (int)(uint32_t)base;
+            r[1] = (int)(uint32_t)(base >> 32);
+            r[2] = kt < T.nk ? (int)((uint32_t)r[2] - kb) : 0;
+        }
+        hg_raw_buffer_load_lds(r, reinterpret_cast<hg_lds_u32 *>((uintptr_t)(sbase + i * 1024)), 16,
+                               (int)off, 0, 0, 0);
+    };
+    // Every load of the first stages of tile T: A and B of stages 0 and 1
+    // (the K loop issues the rest).
+    auto prologue = [&](const TileInfo &T) {
 #pragma unroll
-        for (int i = first; i < first + count; ++i) {
-            const uint32_t off = lkc[i] * 8 < kval ? (isb ? boff[i] : aoff[i]) + kb : OOB;
-            hg_raw_buffer_load_lds(isb ? T.rb : T.ra,
-                                   reinterpret_cast<hg_lds_u32 *>((uintptr_t)(sbase + i * 1024)),
-                                   16, (int)off, 0, 0, 0);
+        for (int st = 0; st < 2; ++st) {
+#pragma unroll
+            for (int i = 0; i < LPS; ++i)
+                issue(T, false, st, st, i);
+#pragma unroll
+            for (int i = 0; i < LPS; ++i)
+                issue(T, true, st, st, i);
         }
     };
-    // Every load of the first stages of tile T: A and B of stage 0, A of
-    // stage 1 and the first half of B of stage 1 (the K loop issues the rest).
-    auto prologue = [&](const TileInfo &T) {
-        issue(T, false, 0, 0, 0, LPS);
-        issue(T, true, 0, 0, 0, LPS);
-        issue(T, false, 1, 1, 0, LPS);
-        issue(T, true, 1, 1, 0, LH);
-    };
 
-    // Fragment reads: row (lane mod 32) of each 32-row block, logical chunk
-    // 2s + (lane div 32) of k-step s.  The same (lane, element) → k map is
-    // used for both operands, so the MFMA contracts matching k.
-    auto frag_addr = [&](int slot, int s, bool isb) -> const unsigned char * {
-        const int frow = lane & 31;
-        const int fhi = lane >> 5;
-        const int row0 = isb ? wn * WTN : wm * WTM;
-        return smem + (isb ? LDS_B : 0) + slot * SLOT + (row0 + frow) * RB +
-               swz(frow, 2 * s + fhi) * 16;
+    // Fragment of a 16×16×32 MFMA operand: row (lane mod 16) of a 16-row
+    // block, logical chunk 4s + (lane div 16) of k-step s (8 consecutive k).
+    // The same (lane, element) → k map is used for both operands, so the
+    // MFMA contracts matching k.
+    auto frag_ptr = [&](bool isb, int slot, int s, int blk) -> const half8 * {
+        const int frow = lane & 15;
+        const int fhi = lane >> 4;
+        const int row = (isb ? wn * WTN : wm * WTM) + blk * FB + frow;
+        return reinterpret_cast<const half8 *>(smem + (isb ? LDS_B : 0) + slot * SLOT + row * RB +
+                                               swz(frow, KS / 8 * s + fhi) * 16);
     };
-    floatx16 acc[TM][TN];
-    // Fragments are double-buffered: the next k-step's are read into the
-    // other set while this k-step's MFMAs run.
-    half8 fa[2][TM], fb[2][TN];
-    // Fragment f of k-step s: f < TM is A block f, else B block f - TM.
-    auto read_frag = [&](int fs, int aslot, int bslot, int s, int f) {
-        if (f < TM)
-            fa[fs][f] = *reinterpret_cast<const half8 *>(frag_addr(aslot, s, false) + f * 32 * RB);
-        else
-            fb[fs][f - TM] =
-                *reinterpret_cast<const half8 *>(frag_addr(bslot, s, true) + (f - TM) * 32 * RB);
-    };
-    // TRI: zero the B fragment elements (j, k) with k < j.  Fragment j of
-    // k-step s holds row jrow = n0 + wn·WTN + 32j + (lane mod 32) and the 8
-    // k from kfirst = (kt0+kt)·BK + 16s + 8·(lane div 32); the first
+    floatx4 acc[TM][TN];
+    // A fragments: one set per quarter parity (TMQ blocks each); B
+    // fragments: one set per k-step of the stage (all TN blocks).
+    half8 fa[2][TMQ], fb[SPS][TN];
+    // TRI: zero the B fragment elements (j, k) with k < j.  Block j of k-step
+    // s holds row jrow = n0 + wn·WTN + 16j + (lane mod 16) and the 8 k from
+    // kfirst = (kt0+kt)·BK + 32s + 8·(lane div 16); the first
     // clamp(jrow - kfirst, 0, 8) of them are zeroed by a select (so NaN or
     // Inf stored above the diagonal cannot reach the MFMA).
-    auto mask_tri = [&](const TileInfo &T, int fs, int kt, int s) {
-        const int frow = lane & 31;
-        const int fhi = lane >> 5;
-        const int kfirst = (T.kt0 + kt) * BK + 16 * s + 8 * fhi;
+    auto mask_tri = [&](const TileInfo &T, int kt, int s) {
+        const int frow = lane & 15;
+        const int fhi = lane >> 4;
+        const int kfirst = (T.kt0 + kt) * BK + KS * s + 8 * fhi;
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
-            const int t = T.n0 + wn * WTN + j * 32 + frow - kfirst;   // elements to zero
-            u32x4 w = __builtin_bit_cast(u32x4, fb[fs][j]);
+            const int t = T.n0 + wn * WTN + j * FB + frow - kfirst;   // elements to zero
+            u32x4 w = __builtin_bit_cast(u32x4, fb[s][j]);
 #pragma unroll
             for (int d = 0; d < 4; ++d) {
                 const uint32_t m = (2 * d >= t ? 0x0000ffffu : 0u) | (2 * d + 1 >= t ? 0xffff0000u : 0u);
                 w[d] &= m;
             }
-            fb[fs][j] = __builtin_bit_cast(half8, w);
+            fb[s][j] = __builtin_bit_cast(half8, w);
         }
     };
 
@@ -314,12 +391,12 @@ hgemm_fast_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int c
     const float beta = p.beta;
     const int64_t ldc = p.ldc;
     // Vector-memory operations an interior epilogue issues after the next
-    // tile's first slices (its C_in loads and its stores; all lanes active).
+    // tile's prologue (its C_in loads and its stores; all lanes active).
     // The counter retires in issue order, so waiting until at most
-    // (first-slice loads) + EPI_OPS remain means slice 0 has landed while
+    // (loads after stage 0) + EPI_OPS remain means stage 0 has landed while
     // the epilogue's stores are still draining.
-    constexpr int EPI_OPS = TM * TN * 4 * (BETA ? 2 : 1);
-    constexpr int VM_TILE0 = LPS + LH;  // stage 1's loads, issued after stage 0's
+    constexpr int EPI_OPS = TM * TN * (BETA ? 2 : 1);
+    constexpr int VM_TILE0 = 2 * LPS;       // stage 1's loads, issued after stage 0's
     constexpr int VM_AFTER_EPI = VM_TILE0 + EPI_OPS < 63 ? VM_TILE0 + EPI_OPS : 63;
     int prev = 0;                      // 0: first tile, 1: after an interior epilogue, 2: after an edge one
     for (;;) {
@@ -328,17 +405,9 @@ hgemm_fast_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int c
         // the register file).
         __asm__ volatile("" : "+v"(lane));
         // ---- K loop of tile T.  Stage t's A lives in A slot t mod 3, its B
-        // in B slot t mod 2.  A slot t mod 3 is free after the barrier in
-        // stage t-3 (in front of its last k-step, when every wave has
-        // finished reading stage t-3), B slot t mod 2 after the one in stage
-        // t-2.  Each k-step of stage kt carries LH ring loads: k-step 3 (after
-        // the barrier) the first half of B of stage kt+2, k-step 0 the second
-        // half of B of stage kt+1, k-steps 1 and 2 the A of stage kt+2.  The
-        // barrier of stage kt publishes stage kt+1 (whose last loads were
-        // issued in k-step 0), so every load has at least three k-steps to
-        // land.  First: this wave's loads of stage 0 have landed (an edge
-        // epilogue's stores vary per lane, so after one everything is waited
-        // for), then everyone else's.
+        // in B slot t mod 2.  First: this wave's loads of stage 0 have
+        // landed (an edge epilogue's stores vary per lane, so after one
+        // everything is waited for), then everyone else's.
         if (prev == 0)
             wait_vmcnt<VM_TILE0>();
         else if (prev == 1)
@@ -347,61 +416,71 @@ hgemm_fast_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int c
             wait_vmcnt<0>();
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
+        // Fragments of quarter 0: A blocks 0..TMQ-1 and every B block of
+        // k-step 0.  Drained before the loop, so that the compiler's
+        // counter waits inside the loop see only the loop's own reads.
 #pragma unroll
-        for (int f = 0; f < R; ++f)
-            read_frag(0, 0, 0, 0, f);
+        for (int f = 0; f < TMQ; ++f)
+            fa[0][f] = *frag_ptr(false, 0, 0, f);
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+            fb[0][j] = *frag_ptr(true, 0, 0, j);
+        wait_lgkmcnt<0>();
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
             for (int j = 0; j < TN; ++j)
-                acc[i][j] = floatx16{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+                acc[i][j] = floatx4{0, 0, 0, 0};
         int as = 0, bs = 0;                       // A and B slots of stage kt
         for (int kt = 0; kt < T.nk; ++kt) {
             const int an = as == NSA - 1 ? 0 : as + 1;   // stage kt+1
             const int a2 = an == NSA - 1 ? 0 : an + 1;   // stage kt+2
             const int bn = bs ^ 1;
-#pragma unroll
-            for (int s = 0; s < SPS; ++s) {
-                const bool last = s == SPS - 1;
-                if (last) {
-                    // This wave's loads of stage kt+1 have landed (only the A
-                    // loads of stage kt+2 may be in flight) and its reads of
-                    // stage kt are complete: after the barrier every wave may
-                    // read stage kt+1 and refill stage kt's slots.
-                    wait_vmcnt<LPS>();
-                    wait_lgkmcnt<0>();
-                    __builtin_amdgcn_s_barrier();
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-                const int ra = last ? an : as;     // where the next fragments come from
-                const int rb = last ? bn : bs;
-                const int rstep = last ? 0 : s + 1;
-                const int fs = s & 1;
-                if (TRI)
-                    mask_tri(T, fs, kt, s);
-                // Ring loads of this k-step: operand, stage, slot, first index.
-                const bool lb = s == 0 || s == 3;
-                const int lkt = s == 0 ? kt + 1 : kt + 2;
-                const int lsl = s == 0 ? bn : s == 3 ? bs : a2;
-                const int lfirst = s == 0 || s == 2 ? LH : 0;
-#pragma unroll
-                for (int k = 0; k < P; ++k) {
-                    acc[k / TN][k % TN] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                        fb[fs][k % TN], fa[fs][k / TN], acc[k / TN][k % TN], 0, 0, 0);
-                    // After MFMA k: one ring load every P/LH MFMAs (from the
-                    // second on), the next k-step's fragments after the
-                    // others, in the order the next k-step consumes them.
-                    constexpr int GAP = P / LH;
-                    if (k % GAP == GAP / 2 && k / GAP < LH)
-                        issue(T, lb, lkt, lsl, lfirst + k / GAP, 1);
-                    else {
-                        const int o = k - (k >= GAP / 2 ? 1 + (k - GAP / 2) / GAP : 0);
-                        if (o < R)
-                            read_frag(fs ^ 1, ra, rb, rstep, read_order(o));
+            static_for<NQ>([&](auto qc) __attribute__((always_inline)) {
+                constexpr int q = decltype(qc)::value;
+                constexpr int s = q >> 1, h = q & 1;
+                if constexpr (TRI && h == 0)
+                    mask_tri(T, kt, s);
+                // Ring loads of this quarter: operand, stage, slot, first index.
+                constexpr bool lb = q >= 2;
+                constexpr int lfirst = (q & 1) * (LPS / 2);
+                const int lsl = lb ? bs : a2;
+                // Reads of this quarter: A of quarter q+1 (set (q+1)%2, its
+                // blocks, its k-step, the next stage's slot for q = 3); B
+                // blocks (q%2)·TN/2 .. of the next k-step.
+                constexpr int tq = (q + 1) & 3;
+                constexpr int ra_set = tq & 1, ra_step = tq >> 1;
+                constexpr int rb_step = q < 2 ? 1 : 0;
+                const int ra_slot = q == 3 ? an : as;
+                const int rb_slot = q < 2 ? bs : bn;
+                static_for<PQ>([&](auto kc) __attribute__((always_inline)) {
+                    constexpr int k = decltype(kc)::value;
+                    if constexpr (q == 2 && k == BAR_K) {
+                        // This wave's loads of stage kt+1 have landed (only the
+                        // A loads of stage kt+2 may be in flight) and its reads
+                        // of stage kt are complete: after the barrier every
+                        // wave may read stage kt+1 and refill stage kt's B slot.
+                        wait_vmcnt<LPS>();
+                        wait_lgkmcnt<0>();
+                        __builtin_amdgcn_s_barrier();
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                    constexpr int a = k % TMQ, j = k / TMQ;
+                    acc[h * TMQ + a][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                        fb[s][j], fa[h][a], acc[h * TMQ + a][j], 0, 0, 0);
+                    constexpr int op = sched(q, k);
+                    if constexpr (op >= kLD) {
+                        issue(T, lb, kt + 2, lsl, lfirst + op - kLD);
+                    } else if constexpr (op >= kRB) {
+                        constexpr int jb = (q & 1) * (TN / 2) + op - kRB;
+                        fb[rb_step][jb] = *frag_ptr(true, rb_slot, rb_step, jb);
+                    } else if constexpr (op >= kRA) {
+                        constexpr int f = op - kRA;
+                        fa[ra_set][f] = *frag_ptr(false, ra_slot, ra_step, ra_set * TMQ + f);
                     }
                     __builtin_amdgcn_sched_barrier(0);
-                }
-            }
+                });
+            });
             as = an;
             bs = bn;
         }
@@ -412,7 +491,7 @@ hgemm_fast_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int c
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
 
-        // ---- Next tile's first slices, in flight during this epilogue.
+        // ---- Next tile's first stages, in flight during this epilogue.
         int nid = id + stride;
         TileInfo Tn;
         const bool more = find_tile<TRI>(p, nid, stride, total, tiles_m, tiles_n, Tn);
@@ -422,94 +501,83 @@ hgemm_fast_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int c
         }
         __builtin_amdgcn_sched_barrier(0);   // those loads precede every epilogue access
 
-        const int frow = lane & 31;
-        const int fhi = lane >> 5;
+        const int frow = lane & 15;
+        const int fhi = lane >> 4;
         // ---- Epilogue of tile T.  Block (i, j) of the accumulators is Cᵀ
         // (the B fragment is the MFMA's first operand): lane covers row
-        // m0 + wm·WTM + 32i + (lane mod 32) and, for register group g,
-        // columns n0 + wn·WTN + 32j + 8g + 4·(lane div 32) + 0..3.
+        // m0 + wm·WTM + 16i + (lane mod 16) and columns
+        // n0 + wn·WTN + 16j + 4·(lane div 16) + 0..3.
         prev = T.rows_a == BM && T.rows_b == BN && cvec ? 1 : 2;
         if (prev == 1) {
             // Interior tile: one row block at a time, all of its C_in loads
             // (beta != 0) issued before any of its stores.
 #pragma unroll
             for (int i = 0; i < TM; ++i) {
-                const int row = T.m0 + wm * WTM + i * 32 + frow;
+                const int row = T.m0 + wm * WTM + i * FB + frow;
                 const int64_t roff =
                     p.e[T.batch].c_off + (int64_t)row * ldc + T.n0 + wn * WTN + 4 * fhi;
                 if (OUT_F16) {
                     _Float16 *cr = static_cast<_Float16 *>(p.C) + roff;
-                    halfx4 cin[TN][4];
+                    halfx4 cin[TN];
                     if (BETA) {
 #pragma unroll
                         for (int j = 0; j < TN; ++j)
-#pragma unroll
-                            for (int g = 0; g < 4; ++g)
-                                cin[j][g] = *reinterpret_cast<const halfx4 *>(cr + j * 32 + 8 * g);
+                            cin[j] = *reinterpret_cast<const halfx4 *>(cr + j * FB);
                     }
 #pragma unroll
-                    for (int j = 0; j < TN; ++j)
+                    for (int j = 0; j < TN; ++j) {
+                        halfx4 hv;
 #pragma unroll
-                        for (int g = 0; g < 4; ++g) {
-                            halfx4 h;
-#pragma unroll
-                            for (int e = 0; e < 4; ++e) {
-                                const float v = acc[i][j][4 * g + e];
-                                h[e] = (_Float16)(BETA ? __builtin_fmaf(alpha, v, beta * (float)cin[j][g][e])
-                                                       : alpha * v);
-                            }
-                            *reinterpret_cast<halfx4 *>(cr + j * 32 + 8 * g) = h;
+                        for (int e = 0; e < 4; ++e) {
+                            const float v = acc[i][j][e];
+                            hv[e] = (_Float16)(BETA ? __builtin_fmaf(alpha, v, beta * (float)cin[j][e])
+                                                    : alpha * v);
                         }
+                        *reinterpret_cast<halfx4 *>(cr + j * FB) = hv;
+                    }
                 } else {
                     float *cr = static_cast<float *>(p.C) + roff;
-                    floatx4 cin[TN][4];
+                    floatx4 cin[TN];
                     if (BETA) {
 #pragma unroll
                         for (int j = 0; j < TN; ++j)
-#pragma unroll
-                            for (int g = 0; g < 4; ++g)
-                                cin[j][g] = *reinterpret_cast<const floatx4 *>(cr + j * 32 + 8 * g);
+                            cin[j] = *reinterpret_cast<const floatx4 *>(cr + j * FB);
                     }
 #pragma unroll
-                    for (int j = 0; j < TN; ++j)
+                    for (int j = 0; j < TN; ++j) {
+                        floatx4 r;
 #pragma unroll
-                        for (int g = 0; g < 4; ++g) {
-                            floatx4 r;
-#pragma unroll
-                            for (int e = 0; e < 4; ++e) {
-                                const float v = acc[i][j][4 * g + e];
-                                r[e] = BETA ? __builtin_fmaf(alpha, v, beta * cin[j][g][e]) : alpha * v;
-                            }
-                            *reinterpret_cast<floatx4 *>(cr + j * 32 + 8 * g) = r;
+                        for (int e = 0; e < 4; ++e) {
+                            const float v = acc[i][j][e];
+                            r[e] = BETA ? __builtin_fmaf(alpha, v, beta * cin[j][e]) : alpha * v;
                         }
+                        *reinterpret_cast<floatx4 *>(cr + j * FB) = r;
+                    }
                 }
             }
         } else {
             // Edge tile: element-wise guarded stores.
 #pragma unroll
             for (int i = 0; i < TM; ++i) {
-                const int row = T.m0 + wm * WTM + i * 32 + frow;
+                const int row = T.m0 + wm * WTM + i * FB + frow;
                 if (row >= p.M)
                     continue;
 #pragma unroll
                 for (int j = 0; j < TN; ++j) {
+                    const int col = T.n0 + wn * WTN + j * FB + 4 * fhi;
+                    const int64_t off = p.e[T.batch].c_off + (int64_t)row * ldc + col;
 #pragma unroll
-                    for (int g = 0; g < 4; ++g) {
-                        const int col = T.n0 + wn * WTN + j * 32 + 8 * g + 4 * fhi;
-                        const int64_t off = p.e[T.batch].c_off + (int64_t)row * ldc + col;
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            if (col + e >= T.N)
-                                continue;
-                            const float v = acc[i][j][4 * g + e];
-                            if (OUT_F16) {
-                                _Float16 *cp = static_cast<_Float16 *>(p.C) + off + e;
-                                *cp = (_Float16)(BETA ? __builtin_fmaf(alpha, v, beta * (float)*cp)
-                                                      : alpha * v);
-                            } else {
-                                float *cp = static_cast<float *>(p.C) + off + e;
-                                *cp = BETA ? __builtin_fmaf(alpha, v, beta * *cp) : alpha * v;
-                            }
+                    for (int e = 0; e < 4; ++e) {
+                        if (col + e >= T.N)
+                            continue;
+                        const float v = acc[i][j][e];
+                        if (OUT_F16) {
+                            _Float16 *cp = static_cast<_Float16 *>(p.C) + off + e;
+                            *cp = (_Float16)(BETA ? __builtin_fmaf(alpha, v, beta * (float)*cp)
+                                                  : alpha * v);
+                        } else {
+                            float *cp = static_cast<float *>(p.C) + off + e;
+                            *cp = BETA ? __builtin_fmaf(alpha, v, beta * *cp) : alpha * v;
                         }
                     }
                 }
@@ -570,8 +638,15 @@ hipError_t launch(const GemmParams &p, hipStream_t stream)
         if (grid > total64)
             grid = total64;
     }
-    hipLaunchKernelGGL((hgemm_fast_kernel<OUT_F16, BETA, TRI>), dim3((unsigned)grid), dim3(THREADS),
-                       0, stream, p, tiles_m, tiles_n, (int)total64, cvec);
+    bool kchk = false;
+    for (int b = 0; b < p.nbatch; ++b)
+        kchk = kchk || p.e[b].K % BK != 0;
+    if (kchk)
+        hipLaunchKernelGGL((hgemm_fast_kernel<OUT_F16, BETA, TRI, true>), dim3((unsigned)grid),
+                           dim3(THREADS), 0, stream, p, tiles_m, tiles_n, (int)total64, cvec);
+    else
+        hipLaunchKernelGGL((hgemm_fast_kernel<OUT_F16, BETA, TRI, false>), dim3((unsigned)grid),
+                           dim3(THREADS), 0, stream, p, tiles_m, tiles_n, (int)total64, cvec);
     return hipGetLastError();
 }
 
