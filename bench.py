@@ -13,7 +13,12 @@ stream the kernels run on); the TRMM time per call is reported next to it.
 `cpu_baseline` times the fp64 oracle on a bounded row block of the same
 HGEMM on this host's cores.
 
-    python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps 50] [--warmup 100] [--no-cpu-baseline]
+
+The default warm-up (about 0.15 s of back-to-back steps) lets the shader
+clock settle: under the board power cap it takes a few tens of milliseconds
+of sustained MFMA load to reach its steady level, and the first calls after
+an idle period run slower.
 """
 import argparse
 import hashlib
@@ -90,8 +95,8 @@ def cpu_baseline(A, Bt, target_s=15.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-trmm", action="store_true", help="time the HGEMM alone")
     ap.add_argument("--no-ceiling", action="store_true",
@@ -197,7 +202,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_FP16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_FP16_TFLOPS, 4),
                      "traffic": traffic_from_profiles(src_hash),
-                     "kernel": "hgemm_fast_kernel (256x256 tile, 64-wide K stages) at M=N=K=8192, fp32 out",
+                     "kernel": "hgemm_fast_kernel (256x256 tile, 4 waves, v_mfma_f32_16x16x32_f16, 64-wide K stages) at M=N=K=8192, fp32 out",
                      "algorithmic_flops_per_launch": wg.flops},
         "kernel_source_sha256_16": src_hash,
     }

@@ -1,12 +1,14 @@
-// mfma_ceiling — measures the MFMA-only throughput ceiling of the GPU for
-// v_mfma_f32_32x32x16_f16 on operands like the benchmark's (fp16 values drawn
-// uniformly from [-1, 1)), and the shader clock it runs at.
+// mfma_ceiling — measures the MFMA-only throughput ceiling of the GPU on
+// operands like the benchmark's (fp16 values drawn uniformly from [-1, 1)),
+// and the shader clock it runs at.
 //
-// Every wave keeps 16 independent 32×32 fp32 accumulators and issues MFMAs
-// back to back on register-resident operands: no memory traffic, no LDS, no
-// barriers.  What remains is the matrix core rate at the clock the power
-// limit allows for this data, i.e. the highest rate any fp16 GEMM kernel can
-// reach on these inputs.  Prints one JSON line.
+// Every wave keeps independent fp32 accumulators and issues MFMAs back to
+// back on register-resident operands: no memory traffic, no LDS, no
+// barriers.  What remains is the matrix core rate at the clock the board
+// power limit allows for this data, i.e. the highest rate any fp16 GEMM
+// kernel can reach on these inputs.  Measured for v_mfma_f32_16x16x32_f16
+// (the GEMM kernel's instruction) with one and two waves per SIMD, and for
+// v_mfma_f32_32x32x16_f16 with one.  Prints one JSON line.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -15,34 +17,57 @@
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
 
-constexpr int kWGs = 1024, kThreads = 256, kIters = 4000, kChains = 16;
+constexpr int kIters = 4000;
+constexpr int kWaves = 4096;   // 256 CUs × 4 SIMDs × 4 rounds at one wave per SIMD
 
-__global__ void __launch_bounds__(256, 1)
+// SHAPE 16: 32 chains of 16×16×32 per wave (128 accumulators per lane);
+// SHAPE 32: 8 chains of 32×32×16 (128 accumulators).  WPS waves per SIMD.
+// The first MFMA operand stays the same for four consecutive instructions,
+// as in the GEMM kernel's inner loop (B block outer).
+template <int SHAPE, int WPS>
+__global__ void __launch_bounds__(256 * WPS, 1)
 mfma_loop(const half8 *__restrict__ src, float *__restrict__ out, long long *__restrict__ stamps)
 {
-    const int t = blockIdx.x * kThreads + threadIdx.x;
-    const half8 a0 = src[4 * t + 0], b0 = src[4 * t + 1];
-    const half8 a1 = src[4 * t + 2], b1 = src[4 * t + 3];
-    floatx16 acc[kChains];
-    for (int i = 0; i < kChains; ++i)
-        acc[i] = floatx16{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+    const int t = blockIdx.x * 256 * WPS + threadIdx.x;
+    half8 a[4], b[4];
+    for (int i = 0; i < 4; ++i) {
+        a[i] = src[8 * t + i];
+        b[i] = src[8 * t + 4 + i];
+    }
+    float s = 0.f;
     const long long c0 = clock64(), w0 = wall_clock64();
-    for (int it = 0; it < kIters; ++it) {
+    if constexpr (SHAPE == 16) {
+        floatx4 acc[32];
+        for (int i = 0; i < 32; ++i)
+            acc[i] = floatx4{0, 0, 0, 0};
+        for (int it = 0; it < kIters; ++it) {
 #pragma unroll
-        for (int i = 0; i < kChains; ++i)
-            acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16((i & 1) ? a1 : a0, (i & 2) ? b1 : b0,
-                                                            acc[i], 0, 0, 0);
+            for (int i = 0; i < 32; ++i)
+                acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(b[(i >> 2) & 3], a[i & 3], acc[i], 0, 0, 0);
+        }
+        for (int i = 0; i < 32; ++i)
+            for (int j = 0; j < 4; ++j)
+                s += acc[i][j];
+    } else {
+        floatx16 acc[8];
+        for (int i = 0; i < 8; ++i)
+            acc[i] = floatx16{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+        for (int it = 0; it < kIters; ++it) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b[(i >> 2) & 1], a[i & 3], acc[i], 0, 0, 0);
+        }
+        for (int i = 0; i < 8; ++i)
+            for (int j = 0; j < 16; ++j)
+                s += acc[i][j];
     }
     const long long c1 = clock64(), w1 = wall_clock64();
-    float s = 0.f;
-    for (int i = 0; i < kChains; ++i)
-        for (int j = 0; j < 16; ++j)
-            s += acc[i][j];
     out[t] = s;                                  // keeps the loop live
     if (threadIdx.x == 0) {
-        stamps[4 * blockIdx.x + 0] = c1 - c0;    // shader clock cycles
-        stamps[4 * blockIdx.x + 1] = w1 - w0;    // 100 MHz wall-clock ticks
+        stamps[2 * blockIdx.x + 0] = c1 - c0;    // shader clock cycles
+        stamps[2 * blockIdx.x + 1] = w1 - w0;    // 100 MHz wall-clock ticks
     }
 }
 
@@ -51,14 +76,53 @@ mfma_loop(const half8 *__restrict__ src, float *__restrict__ out, long long *__r
         hipError_t e_ = (x);                                                                 \
         if (e_ != hipSuccess) {                                                              \
             fprintf(stderr, "mfma_ceiling: %s failed: %s\n", #x, hipGetErrorString(e_));     \
-            return 1;                                                                        \
+            return false;                                                                    \
         }                                                                                    \
     } while (0)
+
+// Best of 5 runs: TFLOP/s and the mean shader clock (GHz) of that run.
+template <int SHAPE, int WPS>
+bool measure(const half8 *src, float *out, long long *stamps, double &tflops, double &ghz)
+{
+    const int wgs = kWaves / (4 * WPS);
+    // flop per wave per iteration: 32 × (2·16·16·32) or 8 × (2·32·32·16)
+    const double per_wave = SHAPE == 16 ? 32.0 * 16384.0 : 8.0 * 32768.0;
+    const double flops = (double)kWaves * kIters * per_wave;
+    hipEvent_t e0, e1;
+    CHECK(hipEventCreate(&e0));
+    CHECK(hipEventCreate(&e1));
+    std::vector<long long> st((size_t)wgs * 2);
+    tflops = 0;
+    ghz = 0;
+    for (int rep = 0; rep < 5; ++rep) {
+        CHECK(hipEventRecord(e0, 0));
+        hipLaunchKernelGGL((mfma_loop<SHAPE, WPS>), dim3(wgs), dim3(256 * WPS), 0, 0, src, out, stamps);
+        CHECK(hipGetLastError());
+        CHECK(hipEventRecord(e1, 0));
+        CHECK(hipEventSynchronize(e1));
+        float ms = 0;
+        CHECK(hipEventElapsedTime(&ms, e0, e1));
+        CHECK(hipMemcpy(st.data(), stamps, st.size() * sizeof(long long), hipMemcpyDeviceToHost));
+        double cyc = 0, ticks = 0;
+        for (int i = 0; i < wgs; ++i) {
+            cyc += (double)st[2 * i];
+            ticks += (double)st[2 * i + 1];
+        }
+        const double tf = flops / (ms * 1e-3) / 1e12;
+        if (tf > tflops) {
+            tflops = tf;
+            ghz = cyc / (ticks / 100e6) / 1e9;
+        }
+    }
+    CHECK(hipEventDestroy(e0));
+    CHECK(hipEventDestroy(e1));
+    return true;
+}
 
 int main()
 {
     // Operands: fp16 values uniform in [-1, 1) from a fixed 32-bit LCG.
-    std::vector<_Float16> h((size_t)kWGs * kThreads * 4 * 8);
+    std::vector<_Float16> h((size_t)kWaves * 64 * 8 * 8);
     uint32_t x = 12345u;
     for (auto &v : h) {
         x = x * 1664525u + 1013904223u;
@@ -67,40 +131,24 @@ int main()
     half8 *src = nullptr;
     float *out = nullptr;
     long long *stamps = nullptr;
-    CHECK(hipMalloc(&src, h.size() * sizeof(_Float16)));
-    CHECK(hipMalloc(&out, (size_t)kWGs * kThreads * sizeof(float)));
-    CHECK(hipMalloc(&stamps, (size_t)kWGs * 4 * sizeof(long long)));
-    CHECK(hipMemcpy(src, h.data(), h.size() * sizeof(_Float16), hipMemcpyHostToDevice));
-    hipEvent_t e0, e1;
-    CHECK(hipEventCreate(&e0));
-    CHECK(hipEventCreate(&e1));
-    const double flops = (double)kWGs * (kThreads / 64) * kIters * kChains * 2.0 * 32 * 32 * 16;
-    double best = 0, best_ghz = 0;
-    std::vector<long long> st((size_t)kWGs * 4);
-    for (int rep = 0; rep < 5; ++rep) {
-        CHECK(hipEventRecord(e0, 0));
-        hipLaunchKernelGGL(mfma_loop, dim3(kWGs), dim3(kThreads), 0, 0, src, out, stamps);
-        CHECK(hipGetLastError());
-        CHECK(hipEventRecord(e1, 0));
-        CHECK(hipEventSynchronize(e1));
-        float ms = 0;
-        CHECK(hipEventElapsedTime(&ms, e0, e1));
-        CHECK(hipMemcpy(st.data(), stamps, st.size() * sizeof(long long), hipMemcpyDeviceToHost));
-        double cyc = 0, ticks = 0;
-        for (int i = 0; i < kWGs; ++i) {
-            cyc += (double)st[4 * i];
-            ticks += (double)st[4 * i + 1];
-        }
-        const double tf = flops / (ms * 1e-3) / 1e12;
-        const double ghz = cyc / (ticks / 100e6) / 1e9;
-        if (tf > best) {
-            best = tf;
-            best_ghz = ghz;
-        }
+    if (hipMalloc(&src, h.size() * sizeof(_Float16)) != hipSuccess ||
+        hipMalloc(&out, (size_t)kWaves * 64 * sizeof(float)) != hipSuccess ||
+        hipMalloc(&stamps, (size_t)kWaves * 2 * sizeof(long long)) != hipSuccess ||
+        hipMemcpy(src, h.data(), h.size() * sizeof(_Float16), hipMemcpyHostToDevice) != hipSuccess) {
+        fprintf(stderr, "mfma_ceiling: allocation or copy failed\n");
+        return 1;
     }
+    double t16a, g16a, t16b, g16b, t32, g32;
+    if (!measure<16, 1>(src, out, stamps, t16a, g16a) || !measure<16, 2>(src, out, stamps, t16b, g16b) ||
+        !measure<32, 1>(src, out, stamps, t32, g32))
+        return 1;
+    const bool two = t16b > t16a;
     printf("{\"mfma_ceiling_tflops\": %.1f, \"clock_ghz\": %.3f, \"instruction\": "
-           "\"v_mfma_f32_32x32x16_f16\", \"operands\": \"fp16 uniform [-1,1)\", \"repeats\": 5}\n",
-           best, best_ghz);
+           "\"v_mfma_f32_16x16x32_f16\", \"waves_per_simd\": %d, "
+           "\"one_wave_per_simd\": {\"tflops\": %.1f, \"clock_ghz\": %.3f}, "
+           "\"v_mfma_f32_32x32x16_f16\": {\"tflops\": %.1f, \"clock_ghz\": %.3f}, "
+           "\"operands\": \"fp16 uniform [-1,1)\", \"repeats\": 5}\n",
+           two ? t16b : t16a, two ? g16b : g16a, two ? 2 : 1, t16a, g16a, t32, g32);
     hipFree(src);
     hipFree(out);
     hipFree(stamps);
