@@ -92,6 +92,99 @@ def cpu_baseline(A, Bt, target_s=15.0):
                       f"({rows}x{Bt.shape[0]} outputs, K={K}), {dt:.1f} s"}
 
 
+def _time_calls(fn, warmup, reps, stream):
+    """Per-call HIP-event times (ms) of `reps` calls after `warmup` untimed
+    ones, plus the mean over the same number of back-to-back calls (which
+    includes launch cost)."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    for a, b in evs:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    ts = sorted(a.elapsed_time(b) for a, b in evs)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(reps):
+        fn()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return ts[len(ts) // 2], ts[0], a.elapsed_time(b) / reps
+
+
+def config_sweep(hg, stream, main_gemm_ms=None, main_trmm_ms=None):
+    """Every configuration of the workload list: GPU median / min per call
+    (HIP events on the kernels' stream), TFLOP/s, % of the fp16 MFMA peak and
+    GB/s of compulsory traffic, next to the fp64 oracle on this host (in full
+    for the three smaller HGEMMs, on the 1024 sampled entries for 8192³ and
+    for the TRMM, with the time per entry).  The 8192³ HGEMM and the TRMM
+    reuse the GPU times of the benchmark's timed steps."""
+    import numpy as np
+    import torch
+    import oracle
+    import workloads
+    dev = torch.device("cuda:0")
+    res = {}
+    reps = {"hgemm_256": 200, "hgemm_1000_ragged": 200, "hgemm_4096": 50}
+    for name, w in workloads.WORKLOADS.items():
+        print(f"[bench] config {name} ...", file=sys.stderr, flush=True)
+        r = {}
+        if isinstance(w, workloads.GemmWorkload):
+            A, Bt, C = workloads.gemm_inputs(w)
+            esz = 2 if w.out_dtype == "f16" else 4
+            cbytes = w.M * w.N * esz * (2 if w.beta != 0.0 else 1)
+            nbytes = 2 * (w.M * w.K + w.N * w.K) + cbytes
+            if name in reps:
+                Ad, Btd = torch.from_numpy(A).to(dev), torch.from_numpy(Bt).to(dev)
+                Cd = torch.from_numpy(C).to(dev)
+                fn = lambda: hg.hgemm(Ad, Btd, Cd, w.alpha, w.beta)
+                med, mn, b2b = _time_calls(fn, 20, reps[name], stream)
+                r.update({"gpu_ms_median": round(med, 5), "gpu_ms_min": round(mn, 5),
+                          "gpu_ms_back_to_back_mean": round(b2b, 5), "reps": reps[name]})
+                del Ad, Btd, Cd
+            elif main_gemm_ms is not None:
+                med = main_gemm_ms
+                r.update({"gpu_ms_avg": round(med, 5), "from": "the benchmark's timed steps"})
+            else:
+                med = None
+            if med:
+                tf = w.flops / (med * 1e-3) / 1e12
+                r.update({"tflops": round(tf, 2), "pct_of_fp16_mfma_peak": round(100 * tf / PEAK_FP16_TFLOPS, 3),
+                          "compulsory_bytes": nbytes, "gbs": round(nbytes / (med * 1e-3) / 1e9, 1)})
+            t0 = time.perf_counter()
+            if w.M * w.N <= 4096 * 4096:
+                oracle.hgemm(A, Bt, w.alpha, w.beta, C)
+                dt = time.perf_counter() - t0
+                r["oracle"] = {"seconds": round(dt, 4), "entries": w.M * w.N, "mode": "full",
+                               "cores": oracle.num_threads()}
+            else:
+                ri, cj = workloads.sample_indices(w.seed, w.M, w.N)
+                oracle.hgemm_sampled(A, Bt, ri, cj, w.alpha, w.beta, C)
+                dt = time.perf_counter() - t0
+                r["oracle"] = {"seconds": round(dt, 4), "entries": int(ri.size), "mode": "sampled",
+                               "us_per_entry": round(dt / ri.size * 1e6, 2), "cores": oracle.num_threads()}
+        else:
+            if main_trmm_ms is not None:
+                r.update({"gpu_ms_avg": round(main_trmm_ms, 5), "from": "the benchmark's timed steps",
+                          "effective_tflops": round(w.flops / (main_trmm_ms * 1e-3) / 1e12, 2),
+                          "pct_of_342us_phase_bound": round(100 * 0.342 / main_trmm_ms, 1)})
+            TA, TB = workloads.trmm_inputs(w)
+            ri, cj = workloads.sample_indices(w.seed, w.n, w.m)
+            t0 = time.perf_counter()
+            oracle.trmm_lower_trans_sampled(TA, TB, ri, cj, w.alpha)
+            dt = time.perf_counter() - t0
+            r["oracle"] = {"seconds": round(dt, 4), "entries": int(ri.size), "mode": "sampled",
+                           "us_per_entry": round(dt / ri.size * 1e6, 2), "cores": oracle.num_threads()}
+            del TA, TB
+        res[name] = r
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -99,6 +192,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-trmm", action="store_true", help="time the HGEMM alone")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-configuration sweep (GPU and oracle times of every workload)")
     ap.add_argument("--no-ceiling", action="store_true",
                     help="skip the MFMA-only throughput ceiling probe")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -211,6 +306,9 @@ def main():
         out["trmm_ms"] = {"avg": round(tavg, 4), "min": round(min(trmm_ms), 4),
                           "max": round(max(trmm_ms), 4)}
         out["trmm_effective_tflops"] = round(wt.flops / (tavg * 1e-3) / 1e12, 2)
+    if not args.no_configs:
+        out["configs"] = config_sweep(hg, stream, gemm_avg,
+                                      (sum(trmm_ms) / len(trmm_ms)) if do_trmm else None)
     if not args.no_ceiling:
         out["mfma_ceiling"] = mfma_ceiling()
     if not args.no_cpu_baseline:
