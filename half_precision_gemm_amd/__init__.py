@@ -13,7 +13,9 @@ importing this package raises.
         strides become lda / ldb / ldc.
 
     trmm_lower_trans(A, B, Out, alpha=1.0, leaf=256)
-        Out = alpha·Aᵀ·B with A lower triangular (strict upper never read).
+    trmm_lower_trans_by_level(A, B, Out, alpha=1.0, leaf=256)
+        Out = alpha·Aᵀ·B with A lower triangular (strict upper never read);
+        the second schedules it one launch per recursion level.
         Column-major matrices are passed as their row-major transposes:
         A is an (n, n) float16 tensor whose row c is column c of A; B is
         (m, n) float16 whose row j is column j of B; Out is (m, n) float32
@@ -41,12 +43,15 @@ lib.hgemm.restype = _int
 lib.trmm_lower_trans.argtypes = [_i64, _i64, _f32, _vp, _i64, _vp, _i64, _vp, _i64, _int, _i64,
                                  _vp]
 lib.trmm_lower_trans.restype = _int
+lib.hg_trmm_lower_trans_by_level.argtypes = lib.trmm_lower_trans.argtypes
+lib.hg_trmm_lower_trans_by_level.restype = _int
 lib.hg_strerror.argtypes = [_int]
 lib.hg_strerror.restype = ctypes.c_char_p
 lib.hg_trmm_plan.argtypes = [_i64, _i64, ctypes.POINTER(_i64), _i64]
 lib.hg_trmm_plan.restype = _i64
 
-EXPORTS = ("hgemm", "trmm_lower_trans", "hg_strerror", "hg_trmm_plan")
+EXPORTS = ("hgemm", "trmm_lower_trans", "hg_trmm_lower_trans_by_level", "hg_strerror",
+           "hg_trmm_plan")
 
 
 class HgError(RuntimeError):
@@ -105,6 +110,17 @@ def hgemm(A, Bt, C, alpha: float = 1.0, beta: float = 0.0):
 
 def trmm_lower_trans(A, B, Out, alpha: float = 1.0, leaf: int = 256):
     """Out = alpha·Aᵀ·B (A lower triangular) on the current stream; returns Out."""
+    return _trmm(lib.trmm_lower_trans, "trmm_lower_trans", A, B, Out, alpha, leaf)
+
+
+def trmm_lower_trans_by_level(A, B, Out, alpha: float = 1.0, leaf: int = 256):
+    """trmm_lower_trans scheduled as one batched launch per recursion level
+    (same result, bit for bit); see hg_trmm_lower_trans_by_level."""
+    return _trmm(lib.hg_trmm_lower_trans_by_level, "hg_trmm_lower_trans_by_level", A, B, Out,
+                 alpha, leaf)
+
+
+def _trmm(fn, fname, A, B, Out, alpha, leaf):
     import torch
     _check_matrix(A, "A", (torch.float16,))
     _check_matrix(B, "B", (torch.float16,))
@@ -114,11 +130,10 @@ def trmm_lower_trans(A, B, Out, alpha: float = 1.0, leaf: int = 256):
     if tuple(A.shape) != (n, n) or B.shape[1] != n or tuple(Out.shape) != (m, n):
         raise ValueError(f"shape mismatch: A {tuple(A.shape)}, B {tuple(B.shape)}, "
                          f"Out {tuple(Out.shape)}")
-    st = lib.trmm_lower_trans(n, m, float(alpha), A.data_ptr() or None, _ld(A),
-                              B.data_ptr() or None, _ld(B), Out.data_ptr() or None, _ld(Out),
-                              HG_F32, int(leaf), _stream_handle(Out))
+    st = fn(n, m, float(alpha), A.data_ptr() or None, _ld(A), B.data_ptr() or None, _ld(B),
+            Out.data_ptr() or None, _ld(Out), HG_F32, int(leaf), _stream_handle(Out))
     if st != 0:
-        raise HgError("trmm_lower_trans", st)
+        raise HgError(fname, st)
     return Out
 
 

@@ -170,9 +170,17 @@ int64_t hg_trmm_plan(int64_t n, int64_t leaf, int64_t *nodes, int64_t cap)
     return (int64_t)v.size();
 }
 
-int trmm_lower_trans(int64_t n, int64_t m, float alpha, const void *A, int64_t lda, const void *B,
-                     int64_t ldb, void *Out, int64_t ldo, int out_dtype, int64_t leaf,
-                     void *stream)
+}  // extern "C"
+
+namespace {
+
+// Both TRMM entry points: `fused` allows the one-launch schedule (each
+// output tile walks its own leaf and updates in recursion order); without
+// it, or when the recursion's boundaries do not fall on tile edges, one
+// batched launch per recursion level.
+int trmm_impl(int64_t n, int64_t m, float alpha, const void *A, int64_t lda, const void *B,
+              int64_t ldb, void *Out, int64_t ldo, int out_dtype, int64_t leaf, void *stream,
+              bool fused)
 {
     if (n < 0 || n > kI32Max)
         return -1;
@@ -226,6 +234,16 @@ int trmm_lower_trans(int64_t n, int64_t m, float alpha, const void *A, int64_t l
     base.alpha = alpha;
     const bool base_vec = aligned16(A) && aligned16(B) && lda % 8 == 0 && ldb % 8 == 0;
 
+    if (fused) {
+        hg::GemmParams p = base;
+        p.beta = 1.0f;
+        p.leaf = (int32_t)std::min<int64_t>(leaf, kI32Max);
+        p.nbatch = 1;
+        p.e[0] = {0, 0, 0, (int32_t)n, (int32_t)n};
+        if (hg::trmm_fused_ok(p))
+            return hip_status(hg::launch_trmm_fused(p, s));
+    }
+
     auto run_batch = [&](const std::vector<hg::BatchEntry> &ents, bool tri, float beta) -> int {
         for (size_t first = 0; first < ents.size(); first += hg::kMaxBatch) {
             hg::GemmParams p = base;
@@ -276,6 +294,24 @@ int trmm_lower_trans(int64_t n, int64_t m, float alpha, const void *A, int64_t l
             return st;
     }
     return HG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int trmm_lower_trans(int64_t n, int64_t m, float alpha, const void *A, int64_t lda, const void *B,
+                     int64_t ldb, void *Out, int64_t ldo, int out_dtype, int64_t leaf,
+                     void *stream)
+{
+    return trmm_impl(n, m, alpha, A, lda, B, ldb, Out, ldo, out_dtype, leaf, stream, true);
+}
+
+int hg_trmm_lower_trans_by_level(int64_t n, int64_t m, float alpha, const void *A, int64_t lda,
+                                 const void *B, int64_t ldb, void *Out, int64_t ldo, int out_dtype,
+                                 int64_t leaf, void *stream)
+{
+    return trmm_impl(n, m, alpha, A, lda, B, ldb, Out, ldo, out_dtype, leaf, stream, false);
 }
 
 }  // extern "C"

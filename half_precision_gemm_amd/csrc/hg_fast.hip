@@ -39,6 +39,7 @@
 // tiles resident on one XCD share A row panels and B column panels.
 #include "hg_internal.h"
 
+#include <type_traits>
 #include <utility>
 
 typedef int32_t hg_int32x4 __attribute__((ext_vector_type(4)));
@@ -65,6 +66,9 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 #endif
 #ifndef HG_FAST_GROUP
 #define HG_FAST_GROUP 4
+#endif
+#ifndef HG_FAST_EPI_PREFETCH
+#define HG_FAST_EPI_PREFETCH 1              // row blocks of C read ahead in the epilogue
 #endif
 #ifndef HG_FAST_NW
 #define HG_FAST_NW 4
@@ -230,6 +234,9 @@ __device__ __forceinline__ void map_tile(int id, int total, int tiles_m, int til
 // Everything a workgroup needs to know about one tile.
 struct TileInfo {
     int batch, m0, n0, N, K, rows_a, rows_b, kt0, nk;
+    int kend;      // FUSED: end of this K segment (stage kt0 + nk, in elements)
+    int first;     // FUSED: the tile's first segment (C written, not read)
+    int tri;       // FUSED: the leaf segment (triangle mask applies)
     hg_int32x4 ra, rb;
 };
 
@@ -267,7 +274,78 @@ __device__ __forceinline__ bool find_tile(const GemmParams &p, int &id, int stri
     return false;
 }
 
-template <bool OUT_F16, bool BETA, bool TRI, bool KCHK>
+// ---- Recursive TRMM in one launch ("异构计算中高性能TRMM与TRSM的递归算法实现"
+// §2.1–§2.2).  In the GEMM view used here (C = Outᵀ, M = m, N = K = n), the
+// recursion splits a diagonal block (o, s) at h = ⌊s/2⌋: the tiles of output
+// columns [o, o+h) receive the update over K = [o+h, o+s) after everything
+// below that node; a block of at most `leaf` columns is a leaf, whose tiles
+// take K from their own first column to the leaf's end under the triangle
+// mask.  For one output tile the leaf and the updates that touch it cover
+// contiguous K ranges in increasing order, ending at the leaf's end and at
+// the ends of the ancestors whose upper half holds the tile, deepest first:
+// exactly the order in which the depth-first recursion accumulates into
+// that tile.  So one workgroup can walk a tile's segments in that order,
+// writing C = α·acc after the first and C = fma(α, acc, C) after each later
+// one -- the same arithmetic, per element, as the level-by-level launches.
+
+// End of the K segment that starts at kpos for the tile whose first column
+// is n0.
+__device__ __forceinline__ int trmm_seg_end(int n0, int kpos, int n, int leaf)
+{
+    int o = 0, s = n, best = n;
+    while (s > leaf) {
+        const int h = s / 2;
+        if (n0 < o + h) {
+            if (o + s > kpos && o + s < best)
+                best = o + s;
+            s = h;
+        } else {
+            o += h;
+            s -= h;
+        }
+    }
+    if (o + s > kpos && o + s < best)
+        best = o + s;
+    return best;
+}
+
+// Work item of workgroup w in round r: output tile q = r·G + w (r even) or
+// r·G + G-1-w (r odd) of the tiles ordered by column, so that the columns
+// with the most K work run first and the rounds of every workgroup add up
+// to about the same work (a tile's work falls linearly with its column).
+// kpos < 0 starts the tile's first segment.  False once q is past the end.
+__device__ __forceinline__ bool fused_item(const GemmParams &p, int w, int G, int round, int kpos,
+                                           int total, int tiles_m, TileInfo &T)
+{
+    const int q = round * G + ((round & 1) ? G - 1 - w : w);
+    if (q >= total)
+        return false;
+    const int tm = q % tiles_m, tn = q / tiles_m;
+    const int N = p.e[0].N, K = p.e[0].K;
+    const int m0 = tm * BM, n0 = tn * BN;
+    if (kpos < 0)
+        kpos = n0;
+    const int kend = trmm_seg_end(n0, kpos, K, p.leaf);
+    T.batch = 0;
+    T.m0 = m0;
+    T.n0 = n0;
+    T.N = N;
+    T.K = K;
+    T.rows_a = min(p.M - m0, BM);
+    T.rows_b = min(N - n0, BN);
+    T.kt0 = kpos / BK;
+    T.nk = (kend - kpos) / BK;
+    T.kend = kend;
+    T.first = kpos == n0;
+    T.tri = kpos == n0;
+    const _Float16 *Ab = p.A + (int64_t)m0 * p.lda;
+    const _Float16 *Bb = p.B + (int64_t)n0 * p.ldb;
+    T.ra = make_rsrc(Ab, (uint32_t)(((int64_t)(T.rows_a - 1) * p.lda + K) * 2));
+    T.rb = make_rsrc(Bb, (uint32_t)(((int64_t)(T.rows_b - 1) * p.ldb + K) * 2));
+    return true;
+}
+
+template <bool OUT_F16, bool BETA, bool TRI, bool KCHK, bool FUSED>
 __global__ void __launch_bounds__(THREADS, 1)
 hgemm_fast_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int cvec)
 {
@@ -380,10 +458,13 @@ hgemm_fast_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int c
         }
     };
 
-    int id = blockIdx.x;
+    int id = blockIdx.x;              // FUSED: the round
     TileInfo T;
-    if (!find_tile<TRI>(p, id, stride, total, tiles_m, tiles_n, T))
+    if (FUSED ? !fused_item(p, blockIdx.x, stride, 0, -1, total, tiles_m, T)
+              : !find_tile<TRI>(p, id, stride, total, tiles_m, tiles_n, T))
         return;
+    if (FUSED)
+        id = 0;
     set_offsets(T);
     prologue(T);
 
@@ -395,7 +476,7 @@ hgemm_fast_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int c
     // The counter retires in issue order, so waiting until at most
     // (loads after stage 0) + EPI_OPS remain means stage 0 has landed while
     // the epilogue's stores are still draining.
-    constexpr int EPI_OPS = TM * TN * (BETA ? 2 : 1);
+    constexpr int EPI_OPS = TM * TN * (BETA && !FUSED ? 2 : 1);   // FUSED: the smaller count
     constexpr int VM_TILE0 = 2 * LPS;       // stage 1's loads, issued after stage 0's
     constexpr int VM_AFTER_EPI = VM_TILE0 + EPI_OPS < 63 ? VM_TILE0 + EPI_OPS : 63;
     int prev = 0;                      // 0: first tile, 1: after an interior epilogue, 2: after an edge one
@@ -439,8 +520,10 @@ hgemm_fast_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int c
             static_for<NQ>([&](auto qc) __attribute__((always_inline)) {
                 constexpr int q = decltype(qc)::value;
                 constexpr int s = q >> 1, h = q & 1;
-                if constexpr (TRI && h == 0)
-                    mask_tri(T, kt, s);
+                if constexpr (TRI && h == 0) {
+                    if (!FUSED || T.tri)
+                        mask_tri(T, kt, s);
+                }
                 // Ring loads of this quarter: operand, stage, slot, first index.
                 constexpr bool lb = q >= 2;
                 constexpr int lfirst = (q & 1) * (LPS / 2);
@@ -494,7 +577,15 @@ hgemm_fast_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int c
         // ---- Next tile's first stages, in flight during this epilogue.
         int nid = id + stride;
         TileInfo Tn;
-        const bool more = find_tile<TRI>(p, nid, stride, total, tiles_m, tiles_n, Tn);
+        bool more;
+        if constexpr (FUSED) {
+            // The tile's next segment, or the next round's tile.
+            nid = T.kend < T.K ? id : id + 1;
+            more = fused_item(p, blockIdx.x, stride, nid, T.kend < T.K ? T.kend : -1, total, tiles_m,
+                              Tn);
+        } else {
+            more = find_tile<TRI>(p, nid, stride, total, tiles_m, tiles_n, Tn);
+        }
         if (more) {
             set_offsets(Tn);
             prologue(Tn);
@@ -507,81 +598,87 @@ hgemm_fast_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int c
         // (the B fragment is the MFMA's first operand): lane covers row
         // m0 + wm·WTM + 16i + (lane mod 16) and columns
         // n0 + wn·WTN + 16j + 4·(lane div 16) + 0..3.
-        prev = T.rows_a == BM && T.rows_b == BN && cvec ? 1 : 2;
-        if (prev == 1) {
-            // Interior tile: one row block at a time, all of its C_in loads
-            // (beta != 0) issued before any of its stores.
+        // RD: the epilogue reads C (beta != 0; FUSED: every segment after the
+        // tile's first).
+        auto epilogue = [&](auto rdc) __attribute__((always_inline)) {
+            constexpr bool RD = decltype(rdc)::value;
+            prev = T.rows_a == BM && T.rows_b == BN && cvec ? 1 : 2;
+            if (prev == 1) {
+                // Interior tile.  When C is read, its loads run CP row blocks
+                // ahead of the stores (the fragment registers are free here),
+                // so the epilogue waits on memory about TM/CP times, not TM.
+                typedef typename std::conditional<OUT_F16, halfx4, floatx4>::type cvec;
+                typedef typename std::conditional<OUT_F16, _Float16, float>::type celt;
+                constexpr int CP = RD ? HG_FAST_EPI_PREFETCH : 1;
+                cvec cin[CP][TN];
+                auto crow = [&](int i) -> celt * {
+                    const int row = T.m0 + wm * WTM + i * FB + frow;
+                    return static_cast<celt *>(p.C) + p.e[T.batch].c_off + (int64_t)row * ldc +
+                           T.n0 + wn * WTN + 4 * fhi;
+                };
+                if (RD) {
 #pragma unroll
-            for (int i = 0; i < TM; ++i) {
-                const int row = T.m0 + wm * WTM + i * FB + frow;
-                const int64_t roff =
-                    p.e[T.batch].c_off + (int64_t)row * ldc + T.n0 + wn * WTN + 4 * fhi;
-                if (OUT_F16) {
-                    _Float16 *cr = static_cast<_Float16 *>(p.C) + roff;
-                    halfx4 cin[TN];
-                    if (BETA) {
+                    for (int i = 0; i < CP; ++i)
 #pragma unroll
                         for (int j = 0; j < TN; ++j)
-                            cin[j] = *reinterpret_cast<const halfx4 *>(cr + j * FB);
-                    }
+                            cin[i][j] = *reinterpret_cast<const cvec *>(crow(i) + j * FB);
+                }
+#pragma unroll
+                for (int i = 0; i < TM; ++i) {
+                    celt *cr = crow(i);
 #pragma unroll
                     for (int j = 0; j < TN; ++j) {
-                        halfx4 hv;
+                        cvec r;
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
                             const float v = acc[i][j][e];
-                            hv[e] = (_Float16)(BETA ? __builtin_fmaf(alpha, v, beta * (float)cin[j][e])
-                                                    : alpha * v);
+                            r[e] = (celt)(RD ? __builtin_fmaf(alpha, v, beta * (float)cin[i % CP][j][e])
+                                             : alpha * v);
                         }
-                        *reinterpret_cast<halfx4 *>(cr + j * FB) = hv;
+                        *reinterpret_cast<cvec *>(cr + j * FB) = r;
                     }
-                } else {
-                    float *cr = static_cast<float *>(p.C) + roff;
-                    floatx4 cin[TN];
-                    if (BETA) {
+                    if (RD && i + CP < TM) {
 #pragma unroll
                         for (int j = 0; j < TN; ++j)
-                            cin[j] = *reinterpret_cast<const floatx4 *>(cr + j * FB);
+                            cin[i % CP][j] = *reinterpret_cast<const cvec *>(crow(i + CP) + j * FB);
                     }
+                }
+            } else {
+                // Edge tile: element-wise guarded stores.
+#pragma unroll
+                for (int i = 0; i < TM; ++i) {
+                    const int row = T.m0 + wm * WTM + i * FB + frow;
+                    if (row >= p.M)
+                        continue;
 #pragma unroll
                     for (int j = 0; j < TN; ++j) {
-                        floatx4 r;
+                        const int col = T.n0 + wn * WTN + j * FB + 4 * fhi;
+                        const int64_t off = p.e[T.batch].c_off + (int64_t)row * ldc + col;
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
+                            if (col + e >= T.N)
+                                continue;
                             const float v = acc[i][j][e];
-                            r[e] = BETA ? __builtin_fmaf(alpha, v, beta * cin[j][e]) : alpha * v;
+                            if (OUT_F16) {
+                                _Float16 *cp = static_cast<_Float16 *>(p.C) + off + e;
+                                *cp = (_Float16)(RD ? __builtin_fmaf(alpha, v, beta * (float)*cp)
+                                                      : alpha * v);
+                            } else {
+                                float *cp = static_cast<float *>(p.C) + off + e;
+                                *cp = RD ? __builtin_fmaf(alpha, v, beta * *cp) : alpha * v;
+                            }
                         }
-                        *reinterpret_cast<floatx4 *>(cr + j * FB) = r;
                     }
                 }
             }
+        };
+        if constexpr (FUSED) {
+            if (T.first)
+                epilogue(std::false_type{});
+            else
+                epilogue(std::true_type{});
         } else {
-            // Edge tile: element-wise guarded stores.
-#pragma unroll
-            for (int i = 0; i < TM; ++i) {
-                const int row = T.m0 + wm * WTM + i * FB + frow;
-                if (row >= p.M)
-                    continue;
-#pragma unroll
-                for (int j = 0; j < TN; ++j) {
-                    const int col = T.n0 + wn * WTN + j * FB + 4 * fhi;
-                    const int64_t off = p.e[T.batch].c_off + (int64_t)row * ldc + col;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        if (col + e >= T.N)
-                            continue;
-                        const float v = acc[i][j][e];
-                        if (OUT_F16) {
-                            _Float16 *cp = static_cast<_Float16 *>(p.C) + off + e;
-                            *cp = (_Float16)(BETA ? __builtin_fmaf(alpha, v, beta * (float)*cp)
-                                                  : alpha * v);
-                        } else {
-                            float *cp = static_cast<float *>(p.C) + off + e;
-                            *cp = BETA ? __builtin_fmaf(alpha, v, beta * *cp) : alpha * v;
-                        }
-                    }
-                }
-            }
+            epilogue(std::integral_constant<bool, BETA>{});
         }
         if (!more)
             break;
@@ -642,15 +739,66 @@ hipError_t launch(const GemmParams &p, hipStream_t stream)
     for (int b = 0; b < p.nbatch; ++b)
         kchk = kchk || p.e[b].K % BK != 0;
     if (kchk)
-        hipLaunchKernelGGL((hgemm_fast_kernel<OUT_F16, BETA, TRI, true>), dim3((unsigned)grid),
+        hipLaunchKernelGGL((hgemm_fast_kernel<OUT_F16, BETA, TRI, true, false>), dim3((unsigned)grid),
                            dim3(THREADS), 0, stream, p, tiles_m, tiles_n, (int)total64, cvec);
     else
-        hipLaunchKernelGGL((hgemm_fast_kernel<OUT_F16, BETA, TRI, false>), dim3((unsigned)grid),
+        hipLaunchKernelGGL((hgemm_fast_kernel<OUT_F16, BETA, TRI, false, false>), dim3((unsigned)grid),
                            dim3(THREADS), 0, stream, p, tiles_m, tiles_n, (int)total64, cvec);
     return hipGetLastError();
 }
 
 }  // namespace
+
+hipError_t launch_trmm_fused(const GemmParams &p, hipStream_t stream)
+{
+    const int tiles_m = (p.M + BM - 1) / BM;
+    const int tiles_n = p.e[0].N / BN;
+    const int64_t total64 = (int64_t)tiles_m * tiles_n;
+    if (total64 <= 0)
+        return hipSuccess;
+    if (total64 > 0x7fffffff)
+        return hipErrorInvalidConfiguration;
+    const int cvec = reinterpret_cast<uintptr_t>(p.C) % 16 == 0 && p.ldc % 4 == 0;
+    int64_t grid = cu_count();
+    grid = grid / 8 * 8 > 0 ? grid / 8 * 8 : grid;
+    if (grid > total64)
+        grid = total64;
+    hipLaunchKernelGGL((hgemm_fast_kernel<false, true, true, false, true>), dim3((unsigned)grid),
+                       dim3(THREADS), 0, stream, p, tiles_m, tiles_n, (int)total64, cvec);
+    return hipGetLastError();
+}
+
+bool trmm_fused_ok(const GemmParams &p)
+{
+    if (p.lda > (1 << 21) || p.ldb > (1 << 21) || p.leaf < BN)
+        return false;
+    if (reinterpret_cast<uintptr_t>(p.A) % 16 != 0 || reinterpret_cast<uintptr_t>(p.B) % 16 != 0 ||
+        p.lda % 8 != 0 || p.ldb % 8 != 0)
+        return false;
+    // Every recursion boundary on a tile edge (and a multiple of BK).
+    const int n = p.e[0].N;
+    if (n % BN != 0)
+        return false;
+    struct Frame {
+        int o, s;
+    };
+    Frame st[64];
+    int top = 0;
+    st[top++] = {0, n};
+    while (top > 0) {
+        const Frame f = st[--top];
+        if (f.o % BN != 0 || f.s % BN != 0)
+            return false;
+        if (f.s <= p.leaf)
+            continue;
+        const int h = f.s / 2;
+        if (top + 2 > 64)
+            return false;
+        st[top++] = {f.o, h};
+        st[top++] = {f.o + h, f.s - h};
+    }
+    return true;
+}
 
 bool fast_path_ok(const GemmParams &p, const LaunchOpts &o)
 {

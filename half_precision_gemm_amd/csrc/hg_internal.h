@@ -30,6 +30,7 @@ struct GemmParams {
     int32_t M;
     int32_t nbatch;
     float alpha, beta;
+    int32_t leaf;    // recursive TRMM in one launch: the recursion's leaf size
     BatchEntry e[kMaxBatch];
 };
 
@@ -52,6 +53,15 @@ hipError_t launch_gemm(const GemmParams &p, const LaunchOpts &o, hipStream_t str
 // written once).
 bool fast_path_ok(const GemmParams &p, const LaunchOpts &o);
 hipError_t launch_gemm_fast(const GemmParams &p, const LaunchOpts &o, hipStream_t stream);
+
+// Recursive TRMM (Out = alpha·Aᵀ·B, A lower) in one launch, in the GEMM view
+// C = Outᵀ (M = m, N = K = n; p.A = B, p.B = A, p.C = Out, p.e[0] = {0, 0,
+// 0, n, n}, p.leaf): every output tile walks its leaf and then the recursion's
+// updates that touch it, deepest first, in one persistent workgroup.
+// trmm_fused_ok: the operands suit the fast path and every recursion
+// boundary falls on a 256-column tile edge.
+bool trmm_fused_ok(const GemmParams &p);
+hipError_t launch_trmm_fused(const GemmParams &p, hipStream_t stream);
 
 // C = beta·C over an M×N window (beta == 0 writes zeros without reading).
 hipError_t launch_scale(void *C, int64_t ldc, int64_t M, int64_t N, float beta,

@@ -98,16 +98,37 @@ int hgemm(int64_t M, int64_t N, int64_t K, float alpha,
  *                  selects 256.
  * 12 stream      : hipStream_t to launch on.
  *
- * Order of work: all leaves first (independent, one batched launch), then the
- * A21ᵀ·B2 updates level by level from the deepest to the outermost (one
- * batched launch per level).  For every output element this is the same
- * order of accumulation as the depth-first recursion.
+ * Order of work: every element of Out receives its leaf term first, then
+ * the A21ᵀ·B2 update terms of the recursion nodes above it from the deepest
+ * to the outermost -- the order of accumulation of the depth-first
+ * recursion.  Each term is a GEMM computed in fp32 and added as
+ * Out = alpha·acc (leaf) or Out = fma(alpha, acc, Out) (update, beta = 1).
+ * When every recursion boundary falls on a multiple of 256 (n a multiple of
+ * 256 split down to leaves of at least 256) and the operands are 16-byte
+ * aligned with lda, ldb multiples of 8, all terms run in one launch in which
+ * each 256×256 output tile walks its own terms in that order; otherwise one
+ * batched launch runs all leaves and one each update level.  Both schedules
+ * give the same bits (see hg_trmm_lower_trans_by_level).
  */
 int trmm_lower_trans(int64_t n, int64_t m, float alpha,
                      const void *A, int64_t lda,
                      const void *B, int64_t ldb,
                      void *Out, int64_t ldo, int out_dtype,
                      int64_t leaf, void *stream);
+
+/*
+ * hg_trmm_lower_trans_by_level — trmm_lower_trans (same arguments, same
+ * status codes, same result bit for bit) scheduled as in the recursion's
+ * description, "异构计算中高性能TRMM与TRSM的递归算法实现" §2.2: one batched
+ * launch for all leaves, then one batched GEMM launch (beta = 1) per
+ * recursion level, deepest first.  For verification and comparison of the
+ * two schedules.
+ */
+int hg_trmm_lower_trans_by_level(int64_t n, int64_t m, float alpha,
+                                 const void *A, int64_t lda,
+                                 const void *B, int64_t ldb,
+                                 void *Out, int64_t ldo, int out_dtype,
+                                 int64_t leaf, void *stream);
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char *hg_strerror(int status);

@@ -29,7 +29,8 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["hg_strerror", "hg_trmm_plan", "hgemm", "trmm_lower_trans"]
+    assert declared_functions() == ["hg_strerror", "hg_trmm_lower_trans_by_level", "hg_trmm_plan",
+                                    "hgemm", "trmm_lower_trans"]
 
 
 def test_library_exports_every_declared_symbol(hg):

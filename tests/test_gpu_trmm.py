@@ -35,10 +35,11 @@ def trmm_inputs(n, m, seed, upper_fill=0.0):
     return np.ascontiguousarray(A.T), np.ascontiguousarray(B.T)
 
 
-def run(hg, A_cm, B_cm, alpha=1.0, leaf=256):
+def run(hg, A_cm, B_cm, alpha=1.0, leaf=256, by_level=False):
     m, n = B_cm.shape
     Out = torch.full((m, n), float("nan"), dtype=torch.float32, device=DEV)
-    hg.trmm_lower_trans(dev(A_cm), dev(B_cm), Out, alpha, leaf)
+    fn = hg.trmm_lower_trans_by_level if by_level else hg.trmm_lower_trans
+    fn(dev(A_cm), dev(B_cm), Out, alpha, leaf)
     torch.cuda.synchronize()
     return Out.cpu().numpy()
 
@@ -148,3 +149,48 @@ def test_deterministic(hg):
     a = run(hg, A_cm, B_cm)
     b = run(hg, A_cm, B_cm)
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+# ---- the one-launch schedule (every recursion boundary on a 256-column tile
+# edge) against the level-by-level schedule: same terms, same order, same
+# bits; and against the oracle.
+@pytest.mark.parametrize("n,m,leaf", [(2048, 300, 256), (4096, 512, 256), (1024, 1000, 512),
+                                      (1280, 256, 1280), (1536, 70, 256), (512, 33, 256),
+                                      (256, 1, 256), (3072, 64, 256), (2560, 100, 256)])
+def test_schedules_bit_identical(hg, n, m, leaf):
+    """n = 3072 and 2560 have recursion boundaries off the 256 grid (both calls
+    then run level by level); the others run the one-launch schedule."""
+    print(f"[case] trmm schedules n={n} m={m} leaf={leaf}", flush=True)
+    A_cm, B_cm = trmm_inputs(n, m, n + 3 * m + leaf)
+    one = run(hg, A_cm, B_cm, 1.25, leaf)
+    lev = run(hg, A_cm, B_cm, 1.25, leaf, by_level=True)
+    assert np.array_equal(one.view(np.uint32), lev.view(np.uint32))
+    check_close(one, oracle.trmm_lower_trans(A_cm, B_cm, 1.25), n, f"n={n} m={m} leaf={leaf}")
+
+
+def test_one_launch_integer_bit_exact(hg):
+    rng = np.random.default_rng(23)
+    n, m = 2048, 200
+    A = np.tril(workloads.integer_f16(rng, (n, n)))
+    B = workloads.integer_f16(rng, (n, m))
+    out = run(hg, np.ascontiguousarray(A.T), np.ascontiguousarray(B.T))
+    exact = A.astype(np.int64).T @ B.astype(np.int64)
+    assert np.array_equal(out, exact.T.astype(np.float32))
+
+
+@pytest.mark.parametrize("fill", [np.nan, -np.inf])
+def test_one_launch_upper_triangle_never_read(hg, fill):
+    n, m = 1024, 96
+    A0, B_cm = trmm_inputs(n, m, 8, 0.0)
+    Ax, _ = trmm_inputs(n, m, 8, fill)
+    base = run(hg, A0, B_cm)
+    got = run(hg, Ax, B_cm)
+    assert np.array_equal(base.view(np.uint32), got.view(np.uint32))
+
+
+def test_one_launch_tril_ones_closed_form(hg):
+    n, m = 2048, 40
+    A = np.tril(np.ones((n, n), np.float16))
+    out = run(hg, np.ascontiguousarray(A.T), np.ones((m, n), np.float16), 0.5)
+    expect = 0.5 * (n - np.arange(n, dtype=np.float32))
+    assert np.array_equal(out, np.tile(expect, (m, 1)))
