@@ -36,7 +36,7 @@ PEAK_HBM_GBS = 8000.0
 
 def kernel_source_hash():
     h = hashlib.sha256()
-    for f in ("hg_fast.hip", "hg_kernels.hip", "hg_api.cpp", "hg_internal.h"):
+    for f in ("hg_fast.hip", "hg_ring.hip", "hg_kernels.hip", "hg_api.cpp", "hg_internal.h"):
         with open(os.path.join(ROOT, "half_precision_gemm_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]

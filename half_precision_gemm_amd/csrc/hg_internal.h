@@ -54,6 +54,12 @@ hipError_t launch_gemm(const GemmParams &p, const LaunchOpts &o, hipStream_t str
 bool fast_path_ok(const GemmParams &p, const LaunchOpts &o);
 hipError_t launch_gemm_fast(const GemmParams &p, const LaunchOpts &o, hipStream_t stream);
 
+// 64×64 / 128×128 tiles with a deep ring of direct buffer→LDS stages
+// (hg_ring.hip), for the Small and Mid tile families when the operands
+// allow 16-byte buffer loads, K % 8 == 0 and no triangle mask is needed.
+bool ring_path_ok(const GemmParams &p, const LaunchOpts &o);
+hipError_t launch_gemm_ring(const GemmParams &p, const LaunchOpts &o, hipStream_t stream);
+
 // Recursive TRMM (Out = alpha·Aᵀ·B, A lower) in one launch, in the GEMM view
 // C = Outᵀ (M = m, N = K = n; p.A = B, p.B = A, p.C = Out, p.e[0] = {0, 0,
 // 0, n, n}, p.leaf): every output tile walks its leaf and then the recursion's

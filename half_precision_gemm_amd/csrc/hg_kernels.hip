@@ -416,8 +416,12 @@ hipError_t launch_gemm(const GemmParams &p, const LaunchOpts &o, hipStream_t str
             return launch_gemm_fast(p, o, stream);
         return launch_tile<CfgBig>(p, o, stream);
     case Tile::Mid:
+        if (ring_path_ok(p, o))
+            return launch_gemm_ring(p, o, stream);
         return launch_tile<CfgMid>(p, o, stream);
     default:
+        if (ring_path_ok(p, o))
+            return launch_gemm_ring(p, o, stream);
         return launch_tile<CfgSmall>(p, o, stream);
     }
 }

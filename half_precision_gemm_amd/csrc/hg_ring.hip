@@ -1,0 +1,305 @@
+// hg_ring.hip — the small- and mid-tile path of the half-precision GEMM on
+// gfx950: C = alpha·A·B + beta·C, A M×K row-major, B K×N column-major, fp16 in,
+// fp32 accumulate ("Nvidia Tensor Core-MMA PTX编程入门" §4; masked tiles as in
+// the tiled matmul of "GPU架构与CUDA" 共享内存与分块), for operands whose rows
+// are 16-byte aligned and K a multiple of 8.
+//
+// Problems too small to give every CU a 256×256 tile run 64×64 or 128×128
+// tiles, where one 64-wide K stage is only 8 or 32 MFMAs per wave: a tile is
+// bound by memory latency, not by the matrix cores.  So the K walk is a deep
+// ring of LDS stages filled by direct buffer→LDS loads (no staging
+// registers): NS stages, NS-1 of them in flight, one barrier per stage.
+//
+//  * 4 waves (2×2) per tile, 16×16×32 MFMA blocks (B fragment first, so each
+//    16×16 result block is Cᵀ and a lane holds 4 consecutive columns of one
+//    row); 128-byte LDS rows with the chunk index XOR-swizzled by (row/2) mod
+//    8, which the loads realise by having each lane fetch the logical chunk
+//    placed at its position; conflict-free 16-byte fragment reads.
+//  * Rows past M or N get an offset beyond the buffer range (zero fill); with
+//    KCHK (K not a multiple of 64) each lane's chunk is checked against K;
+//    stages past the end of K get an empty buffer range.
+#include "hg_internal.h"
+
+#include <type_traits>
+
+typedef int32_t hg_r_int32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) uint32_t hg_r_lds_u32;
+
+extern "C" __device__ void hg_ring_buffer_load_lds(hg_r_int32x4 rsrc, hg_r_lds_u32 *lds, int size,
+                                                   int voffset, int soffset, int offset,
+                                                   int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
+
+namespace hg {
+namespace {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef _Float16 halfx4 __attribute__((ext_vector_type(4)));
+
+constexpr int BK = 64, RB = 128, KC = 8, THREADS = 256, NWAVES = 4;
+constexpr uint32_t OOB = 0x80000000u;
+
+__device__ __forceinline__ int swz(int r, int kc) { return kc ^ ((r >> 1) & 7); }
+
+template <int n>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+__device__ __forceinline__ hg_r_int32x4 rsrc_of(const void *base, uint32_t bytes)
+{
+    const uint64_t b = reinterpret_cast<uint64_t>(base);
+    hg_r_int32x4 r;
+    r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+    r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
+    r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+    r[3] = 0x00020000;
+    return r;
+}
+
+// Workgroup id → (batch, tile row, tile column): ids regrouped per XCD, then
+// bands of 4 tile rows walked column by column (tiles on one XCD share
+// panels in its L2).
+__device__ __forceinline__ void ring_map(int wg, int total, int tiles_m, int tiles_n, int &batch,
+                                         int &tm, int &tn)
+{
+    const int per = total >> 3, rem = total & 7;
+    const int x = wg & 7;
+    const int q = x * per + min(x, rem) + (wg >> 3);
+    const int per_batch = tiles_m * tiles_n;
+    batch = q / per_batch;
+    const int l = q - batch * per_batch;
+    const int band = l / (4 * tiles_n);
+    const int first = band * 4;
+    const int gsz = min(tiles_m - first, 4);
+    const int r = l - band * 4 * tiles_n;
+    tm = first + r % gsz;
+    tn = r / gsz;
+}
+
+template <int BM, int BN, bool OUT_F16, bool BETA, bool KCHK>
+__global__ void __launch_bounds__(THREADS, 1)
+hgemm_ring_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int cvec)
+{
+    constexpr int SLOT = (BM + BN) * RB;                   // one stage: A rows then B rows
+    constexpr int NS = (128 * 1024) / SLOT < 8 ? (128 * 1024) / SLOT : 8;   // ring depth
+    constexpr int WTM = BM / 2, WTN = BN / 2;              // wave sub-tile
+    constexpr int TM = WTM / 16, TN = WTN / 16;            // 16×16 blocks per wave
+    constexpr int LA = BM / (NWAVES * 8), LB = BN / (NWAVES * 8);   // load instructions per wave
+    constexpr int L = LA + LB;                             // ... per stage
+    static_assert(NS >= 3 && LA >= 1 && LB >= 1 && (NS - 2) * L <= 63, "");
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[NS * SLOT];
+
+    int batch, tm, tn;
+    ring_map(blockIdx.x, total, tiles_m, tiles_n, batch, tm, tn);
+    const int M = p.M, N = p.e[batch].N, K = p.e[batch].K;
+    const int m0 = tm * BM, n0 = tn * BN;
+    if (m0 >= M || n0 >= N)
+        return;                                            // whole workgroup
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    const int rows_a = min(M - m0, BM), rows_b = min(N - n0, BN);
+    const hg_r_int32x4 ra = rsrc_of(p.A + p.e[batch].a_off + (int64_t)m0 * p.lda,
+                                    (uint32_t)(((int64_t)(rows_a - 1) * p.lda + K) * 2));
+    const hg_r_int32x4 rb = rsrc_of(p.B + p.e[batch].b_off + (int64_t)n0 * p.ldb,
+                                    (uint32_t)(((int64_t)(rows_b - 1) * p.ldb + K) * 2));
+    const uint32_t lds_base = (uint32_t)reinterpret_cast<uintptr_t>(smem);
+    const int nk = (K + BK - 1) / BK;
+
+    // Load i of a wave covers tile rows (wave·(LA or LB) + i)·8 .. +7; lane l
+    // takes row +(l div 8) and the logical chunk that swz() puts at l mod 8.
+    uint32_t off[L];
+    int lkc[L];
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+        const bool isb = i >= LA;
+        const int row = ((isb ? LB : LA) * wave + (isb ? i - LA : i)) * 8 + (lane >> 3);
+        int kc = 0;
+#pragma unroll
+        for (int c = 0; c < KC; ++c)
+            kc = swz(row, c) == (lane & 7) ? c : kc;
+        lkc[i] = kc;
+        const int rows = isb ? rows_b : rows_a;
+        const int64_t ld = isb ? p.ldb : p.lda;
+        off[i] = row < rows ? (uint32_t)(row * (int)ld * 2 + kc * 16) : OOB;
+    }
+    // Every load of stage kt into its ring slot.
+    auto issue = [&](int kt) {
+        const int slot = kt % NS;
+        const uint32_t kb = (uint32_t)kt * RB;
+#pragma unroll
+        for (int i = 0; i < L; ++i) {
+            const bool isb = i >= LA;
+            hg_r_int32x4 r = isb ? rb : ra;
+            uint32_t o = off[i];
+            if constexpr (KCHK) {
+                o = lkc[i] * 8 < K - kt * BK ? o + kb : OOB;
+            } else {
+                const uint64_t base = ((uint64_t)(uint32_t)r[1] << 32 | (uint32_t)r[0]) + kb;
+                r[0] = (int)(uint32_t)base;
+                r[1] = (int)(uint32_t)(base >> 32);
+                r[2] = kt < nk ? (int)((uint32_t)r[2] - kb) : 0;
+            }
+            const int row0 = ((isb ? LB : LA) * wave + (isb ? i - LA : i)) * 8;
+            const uint32_t dst = lds_base + slot * SLOT + (isb ? BM * RB : 0) + row0 * RB;
+            hg_ring_buffer_load_lds(r, reinterpret_cast<hg_r_lds_u32 *>((uintptr_t)dst), 16, (int)o,
+                                    0, 0, 0);
+        }
+    };
+
+    floatx4 acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+            acc[i][j] = floatx4{0, 0, 0, 0};
+
+#pragma unroll
+    for (int s = 0; s < NS - 1; ++s)
+        issue(s);
+    const int frow = lane & 15, fhi = lane >> 4;
+    for (int kt = 0; kt < nk; ++kt) {
+        // This wave's loads of stage kt have landed (stages kt+1 .. kt+NS-2
+        // may be in flight); after the barrier everyone's have, and every
+        // wave is done with stage kt-1, whose slot takes stage kt+NS-1.
+        wait_vmcnt<(NS - 2) * L>();
+        __builtin_amdgcn_s_barrier();
+        issue(kt + NS - 1);
+        const unsigned char *As = smem + (kt % NS) * SLOT;
+        const unsigned char *Bs = As + BM * RB;
+#pragma unroll
+        for (int s = 0; s < BK / 32; ++s) {
+            half8 fa[TM], fb[TN];
+#pragma unroll
+            for (int i = 0; i < TM; ++i) {
+                const int row = wm * WTM + i * 16 + frow;
+                fa[i] = *reinterpret_cast<const half8 *>(As + row * RB + swz(row, 4 * s + fhi) * 16);
+            }
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const int row = wn * WTN + j * 16 + frow;
+                fb[j] = *reinterpret_cast<const half8 *>(Bs + row * RB + swz(row, 4 * s + fhi) * 16);
+            }
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+        }
+    }
+    wait_vmcnt<0>();   // the ring's last zero-fill loads (none reach memory) drain before exit
+
+    // Epilogue: lane covers row m0 + wm·WTM + 16i + (lane mod 16) and columns
+    // n0 + wn·WTN + 16j + 4·(lane div 16) + 0..3.
+    const float alpha = p.alpha, beta = p.beta;
+    const int64_t ldc = p.ldc;
+    typedef typename std::conditional<OUT_F16, halfx4, floatx4>::type cvec_t;
+    typedef typename std::conditional<OUT_F16, _Float16, float>::type celt;
+    celt *Cb = static_cast<celt *>(p.C) + p.e[batch].c_off;
+    if (rows_a == BM && rows_b == BN && cvec) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            const int row = m0 + wm * WTM + i * 16 + frow;
+            celt *cr = Cb + (int64_t)row * ldc + n0 + wn * WTN + 4 * fhi;
+            cvec_t cin[TN];
+            if (BETA) {
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+                    cin[j] = *reinterpret_cast<const cvec_t *>(cr + j * 16);
+            }
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                cvec_t r;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float v = acc[i][j][e];
+                    r[e] = (celt)(BETA ? __builtin_fmaf(alpha, v, beta * (float)cin[j][e]) : alpha * v);
+                }
+                *reinterpret_cast<cvec_t *>(cr + j * 16) = r;
+            }
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            const int row = m0 + wm * WTM + i * 16 + frow;
+            if (row >= M)
+                continue;
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const int col = n0 + wn * WTN + j * 16 + 4 * fhi;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    if (col + e >= N)
+                        continue;
+                    celt *cp = Cb + (int64_t)row * ldc + col + e;
+                    const float v = acc[i][j][e];
+                    *cp = (celt)(BETA ? __builtin_fmaf(alpha, v, beta * (float)*cp) : alpha * v);
+                }
+            }
+        }
+    }
+}
+
+template <int BM, int BN, bool OUT_F16, bool BETA>
+hipError_t launch_ring_cfg(const GemmParams &p, hipStream_t stream)
+{
+    int maxN = 0;
+    bool kchk = false;
+    for (int b = 0; b < p.nbatch; ++b) {
+        maxN = p.e[b].N > maxN ? p.e[b].N : maxN;
+        kchk = kchk || p.e[b].K % BK != 0;
+    }
+    const int tiles_m = (p.M + BM - 1) / BM;
+    const int tiles_n = (maxN + BN - 1) / BN;
+    const int64_t total64 = (int64_t)tiles_m * tiles_n * p.nbatch;
+    if (total64 <= 0)
+        return hipSuccess;
+    if (total64 > 0x7fffffff)
+        return hipErrorInvalidConfiguration;
+    const uintptr_t align = OUT_F16 ? 8 : 16;
+    int cvec = (reinterpret_cast<uintptr_t>(p.C) % align == 0) && (p.ldc % 4 == 0);
+    for (int b = 0; b < p.nbatch; ++b)
+        cvec = cvec && (p.e[b].c_off % 4 == 0);
+    if (kchk)
+        hipLaunchKernelGGL((hgemm_ring_kernel<BM, BN, OUT_F16, BETA, true>), dim3((unsigned)total64),
+                           dim3(THREADS), 0, stream, p, tiles_m, tiles_n, (int)total64, cvec);
+    else
+        hipLaunchKernelGGL((hgemm_ring_kernel<BM, BN, OUT_F16, BETA, false>), dim3((unsigned)total64),
+                           dim3(THREADS), 0, stream, p, tiles_m, tiles_n, (int)total64, cvec);
+    return hipGetLastError();
+}
+
+template <int BM, int BN>
+hipError_t launch_ring_tile(const GemmParams &p, const LaunchOpts &o, hipStream_t s)
+{
+    if (o.out_f16)
+        return o.beta_read ? launch_ring_cfg<BM, BN, true, true>(p, s)
+                           : launch_ring_cfg<BM, BN, true, false>(p, s);
+    return o.beta_read ? launch_ring_cfg<BM, BN, false, true>(p, s)
+                       : launch_ring_cfg<BM, BN, false, false>(p, s);
+}
+
+}  // namespace
+
+bool ring_path_ok(const GemmParams &p, const LaunchOpts &o)
+{
+    if (!o.vec || o.tri)
+        return false;
+    if (p.lda > (1 << 21) || p.ldb > (1 << 21))
+        return false;
+    for (int b = 0; b < p.nbatch; ++b)
+        if (p.e[b].K % 8 != 0)
+            return false;
+    return true;
+}
+
+hipError_t launch_gemm_ring(const GemmParams &p, const LaunchOpts &o, hipStream_t stream)
+{
+    if (o.tile == Tile::Mid)
+        return launch_ring_tile<128, 128>(p, o, stream);
+    return launch_ring_tile<64, 64>(p, o, stream);
+}
+
+}  // namespace hg
