@@ -14,7 +14,7 @@ Pages followed (cited by title and section):
   * "GPU架构与CUDA", 共享内存与分块 (masked tiled matmul) and 混合精度核函数
     (fp16 inputs, wider accumulation).
   * "异构计算中高性能TRMM与TRSM的递归算法实现" §2.1–§2.2: B <- α·Aᵀ·B with A
-    lower triangular.
+    lower triangular; §2.3: the triangular solve, here X = α·A⁻ᵀ·B.
 
 Every function here is pinned by ``tests/test_oracle.py`` against closed forms,
 brute force and library routines (see that file's docstrings).
@@ -75,6 +75,12 @@ def _load():
                                                             vp, i64, i64, vp,
                                                             vp, vp]
             lib.oracle_trmm_lower_trans_sampled.restype = None
+            lib.oracle_trsm_lower_trans.argtypes = [i64, i64, f64, vp, i64, vp,
+                                                    i64, vp, i64]
+            lib.oracle_trsm_lower_trans.restype = None
+            lib.oracle_trsm_lower_trans_cols.argtypes = [i64, f64, vp, i64, vp, i64,
+                                                         i64, vp, vp, i64]
+            lib.oracle_trsm_lower_trans_cols.restype = None
             lib.oracle_num_threads.argtypes = []
             lib.oracle_num_threads.restype = ctypes.c_int
             _lib = lib
@@ -204,4 +210,47 @@ def trmm_lower_trans_sampled(A_cm: np.ndarray, B_cm: np.ndarray, rows: np.ndarra
     lib.oracle_trmm_lower_trans_sampled(n, float(alpha), _ptr(A_cm), _ld(A_cm),
                                         _ptr(B_cm), _ld(B_cm), rows.size,
                                         _ptr(rows), _ptr(cols), _ptr(ref))
+    return ref
+
+
+def trsm_lower_trans(A_cm: np.ndarray, B_cm: np.ndarray, alpha: float = 1.0) -> np.ndarray:
+    """fp64 reference of X = α·A⁻ᵀ·B (the X with Aᵀ·X = α·B), A lower
+    triangular (strict upper unread), by back substitution per column.
+
+    Same convention as ``trmm_lower_trans``: ``A_cm`` (n, n) fp16 whose row c
+    is column c of A, ``B_cm`` (m, n) fp16 whose row j is column j of B.
+    Returns X as an (m, n) fp64 array whose row j is column j of X.
+    """
+    lib = _load()
+    _f16_2d(A_cm, "A_cm")
+    _f16_2d(B_cm, "B_cm")
+    n = A_cm.shape[0]
+    if A_cm.shape != (n, n) or B_cm.shape[1] != n:
+        raise ValueError("shape mismatch")
+    m = B_cm.shape[0]
+    ref = np.empty((m, n), dtype=np.float64)
+    if n and m:
+        lib.oracle_trsm_lower_trans(n, m, float(alpha), _ptr(A_cm), _ld(A_cm),
+                                    _ptr(B_cm), _ld(B_cm), _ptr(ref), n)
+    return ref
+
+
+def trsm_lower_trans_cols(A_cm: np.ndarray, B_cm: np.ndarray, cols: np.ndarray,
+                          alpha: float = 1.0) -> np.ndarray:
+    """``trsm_lower_trans`` for the listed columns of B only: row s of the
+    (len(cols), n) result is column cols[s] of X."""
+    lib = _load()
+    _f16_2d(A_cm, "A_cm")
+    _f16_2d(B_cm, "B_cm")
+    n = A_cm.shape[0]
+    if A_cm.shape != (n, n) or B_cm.shape[1] != n:
+        raise ValueError("shape mismatch")
+    cols = np.ascontiguousarray(cols, dtype=np.int64)
+    if cols.size and (cols.min() < 0 or cols.max() >= B_cm.shape[0]):
+        raise IndexError("column index out of range")
+    ref = np.empty((cols.size, n), dtype=np.float64)
+    if n and cols.size:
+        lib.oracle_trsm_lower_trans_cols(n, float(alpha), _ptr(A_cm), _ld(A_cm),
+                                         _ptr(B_cm), _ld(B_cm), cols.size, _ptr(cols),
+                                         _ptr(ref), n)
     return ref

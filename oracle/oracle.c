@@ -15,9 +15,10 @@
  *    operands contribute nothing and only in-range outputs are written; and
  *    section 混合精度核函数: fp16 products accumulated in a wider type.
  *  - "异构计算中高性能TRMM与TRSM的递归算法实现", §2.1–§2.2: B <- α·Aᵀ·B for
- *    lower-triangular A.
+ *    lower-triangular A; §2.3: the triangular solve, here X = α·A⁻ᵀ·B.
  *
- * The oracle computes each output straight from its definition, in fp64.
+ * The oracle computes each output straight from its definition, in fp64
+ * (the solve by plain back substitution).
  * fp16 inputs convert to fp64 exactly, every fp16×fp16 product is exact in
  * fp64 (11+11 significand bits), so the only rounding is fp64 summation.
  *
@@ -167,6 +168,58 @@ void oracle_trmm_lower_trans_sampled(int64_t n, double alpha,
         for (int64_t k = i; k < n; ++k)
             acc += g_h2d[A[k + i * lda]] * g_h2d[B[k + j * ldb]];
         ref[s] = alpha * acc;
+    }
+}
+
+/* ---- TRSM, left side, A lower triangular, transposed ----------------------
+ * "异构计算中高性能TRMM与TRSM的递归算法实现" §2.3 solves X = A\B column by
+ * column; this is the transposed lower case, X = α·A⁻ᵀ·B, i.e. the X with
+ * Aᵀ·X = α·B.  Aᵀ is upper triangular, so each column j is found by back
+ * substitution from the last row:
+ *   x(i,j) = (α·B(i,j) − Σ_{k=i+1}^{n-1} A(k,i)·x(k,j)) / A(i,i),
+ *   for i = n-1, n-2, …, 0.
+ * Only the lower triangle of A is read (A(k,i) with k >= i).  A singular
+ * diagonal gives ±inf/NaN as the arithmetic does.
+ * A : n×n column-major fp16; B : n×m column-major fp16;
+ * ref : n×m column-major fp64, element (i,j) at ref[i + j*ldr]
+ */
+void oracle_trsm_lower_trans(int64_t n, int64_t m, double alpha,
+                             const uint16_t *A, int64_t lda,
+                             const uint16_t *B, int64_t ldb,
+                             double *ref, int64_t ldr)
+{
+    h2d_init();
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t j = 0; j < m; ++j) {
+        double *x = ref + j * ldr;
+        for (int64_t i = n - 1; i >= 0; --i) {
+            double acc = alpha * g_h2d[B[i + j * ldb]];
+            for (int64_t k = i + 1; k < n; ++k)
+                acc -= g_h2d[A[k + i * lda]] * x[k];
+            x[i] = acc / g_h2d[A[i + i * lda]];
+        }
+    }
+}
+
+/* Same solve for the listed columns only: column cols[s] of X goes to
+ * ref[0..n-1 + s*ldr]. */
+void oracle_trsm_lower_trans_cols(int64_t n, double alpha,
+                                  const uint16_t *A, int64_t lda,
+                                  const uint16_t *B, int64_t ldb,
+                                  int64_t ncols, const int64_t *cols,
+                                  double *ref, int64_t ldr)
+{
+    h2d_init();
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t s = 0; s < ncols; ++s) {
+        const int64_t j = cols[s];
+        double *x = ref + s * ldr;
+        for (int64_t i = n - 1; i >= 0; --i) {
+            double acc = alpha * g_h2d[B[i + j * ldb]];
+            for (int64_t k = i + 1; k < n; ++k)
+                acc -= g_h2d[A[k + i * lda]] * x[k];
+            x[i] = acc / g_h2d[A[i + i * lda]];
+        }
     }
 }
 

@@ -25,6 +25,9 @@ def hashes():
             out[name] = {"A_cm": workloads.sha256(A), "B_cm": workloads.sha256(B)}
         ri, cj = workloads.sample_indices(w.seed, 8192, 8192)
         out[name]["samples_8192"] = workloads.sha256(ri) + workloads.sha256(cj)[:16]
+    for name, w in workloads.TRSM_WORKLOADS.items():
+        A, B = workloads.trsm_inputs(w)
+        out[name] = {"A_cm": workloads.sha256(A), "B_cm": workloads.sha256(B)}
     return out
 
 

@@ -243,3 +243,112 @@ def test_empty_shapes():
     A = np.ones((4, 0), np.float16)
     Bt = np.ones((3, 0), np.float16)
     assert np.array_equal(oracle.hgemm(A, Bt), np.zeros((4, 3)))
+
+
+# ---- TRSM: X = α·A⁻ᵀ·B, A lower ("异构计算中高性能TRMM与TRSM的递归算法实现" §2.3) ----
+
+def _trsm_inputs(n, m, seed, upper_fill=0.0):
+    """Well-conditioned lower A (the TRSM workload recipe) and B, as logical
+    [row, col] fp16 arrays; the strict upper triangle holds `upper_fill`."""
+    A_cm, B_cm = workloads.trsm_inputs(workloads.TrsmWorkload("t", n, m, 1.0, 256, seed))
+    A = A_cm.T.copy()
+    if upper_fill != 0.0:
+        A[np.triu_indices(n, 1)] = upper_fill
+    return A, np.ascontiguousarray(B_cm.T)
+
+
+def _trsm(A, B, alpha=1.0):
+    """oracle.trsm_lower_trans on logical [row, col] arrays; returns X [row, col]."""
+    return oracle.trsm_lower_trans(np.ascontiguousarray(A.T), np.ascontiguousarray(B.T), alpha).T
+
+
+def test_trsm_identity_returns_alpha_B():
+    rng = np.random.default_rng(40)
+    B = workloads.uniform_f16(rng, (37, 6))
+    I = np.eye(37, dtype=np.float16)
+    assert np.array_equal(_trsm(I, B, 1.5), 1.5 * B.astype(np.float64))
+
+
+def test_trsm_diagonal_powers_of_two():
+    rng = np.random.default_rng(41)
+    n, m = 29, 5
+    e = rng.integers(-3, 4, n)
+    A = np.diag(np.ldexp(1.0, e)).astype(np.float16)
+    B = workloads.uniform_f16(rng, (n, m))
+    expect = -0.75 * B.astype(np.float64) / np.ldexp(1.0, e)[:, None]
+    assert np.array_equal(_trsm(A, B, -0.75), expect)
+
+
+@pytest.mark.parametrize("n,m", [(1, 1), (7, 3), (64, 5), (300, 4)])
+def test_trsm_matches_scipy_solve_triangular(n, m):
+    import scipy.linalg
+    A, B = _trsm_inputs(n, m, 42 + n)
+    got = _trsm(A, B, 1.25)
+    ref = scipy.linalg.solve_triangular(A.astype(np.float64), 1.25 * B.astype(np.float64),
+                                        trans="T", lower=True)
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12 * max(1.0, np.abs(ref).max()))
+
+
+def test_trsm_brute_force_inverse():
+    A, B = _trsm_inputs(6, 4, 43)
+    ref = np.linalg.inv(A.astype(np.float64).T) @ (0.5 * B.astype(np.float64))
+    np.testing.assert_allclose(_trsm(A, B, 0.5), ref, rtol=0, atol=1e-13)
+
+
+def test_trsm_residual_is_zero():
+    """The defining equation Aᵀ·X = α·B, evaluated by a matrix product."""
+    A, B = _trsm_inputs(500, 9, 44)
+    X = _trsm(A, B, 2.0)
+    r = A.astype(np.float64).T @ X - 2.0 * B.astype(np.float64)
+    assert np.abs(r).max() < 1e-12
+
+
+def test_trsm_upper_triangle_not_referenced():
+    A0, B = _trsm_inputs(40, 7, 45)
+    ref = _trsm(A0, B)
+    for fill in (np.nan, 1e4):
+        Ax, _ = _trsm_inputs(40, 7, 45, fill)
+        assert np.array_equal(_trsm(Ax, B), ref)
+
+
+def test_trsm_undoes_trmm_exactly():
+    """Integer unit lower A and integer B: C = Aᵀ·B is exact (oracle TRMM, an
+    independent routine), fits fp16 exactly, and the solve returns B."""
+    rng = np.random.default_rng(46)
+    n, m = 120, 8
+    A = np.eye(n)
+    low = np.tril_indices(n, -1)
+    pick = rng.random(low[0].size) < 0.02
+    A[low[0][pick], low[1][pick]] = rng.choice([-1.0, 1.0], pick.sum())
+    A = A.astype(np.float16)
+    B = workloads.integer_f16(rng, (n, m), -3, 3)
+    C = oracle.trmm_lower_trans(np.ascontiguousarray(A.T), np.ascontiguousarray(B.T)).T
+    assert np.abs(C).max() <= 2048 and np.array_equal(C, np.round(C))
+    X = _trsm(A, C.astype(np.float16))
+    assert np.array_equal(X, B.astype(np.float64))
+
+
+def test_trsm_bidiagonal_closed_form():
+    """A = I + subdiagonal a (entries in {-1, 0, 1}): A⁻¹(r, c) is the product
+    of -a_k over c <= k < r, so X = α·(A⁻¹)ᵀ·B exactly (integers)."""
+    rng = np.random.default_rng(47)
+    n, m = 60, 4
+    a = rng.integers(-1, 2, n - 1).astype(np.float64)
+    A = np.eye(n)
+    A[np.arange(1, n), np.arange(n - 1)] = a
+    inv = np.zeros((n, n))
+    for c in range(n):
+        inv[c, c] = 1.0
+        for r in range(c + 1, n):
+            inv[r, c] = inv[r - 1, c] * -a[r - 1]
+    B = workloads.integer_f16(rng, (n, m), -2, 2)
+    expect = 3.0 * (inv.T @ B.astype(np.float64))
+    assert np.array_equal(_trsm(A.astype(np.float16), B, 3.0), expect)
+
+
+def test_trsm_cols_equals_full():
+    A, B = _trsm_inputs(77, 12, 48)
+    Acm, Bcm = np.ascontiguousarray(A.T), np.ascontiguousarray(B.T)
+    full = oracle.trsm_lower_trans(Acm, Bcm, -1.5)
+    cols = np.array([11, 0, 5, 5, 3])
+    assert np.array_equal(oracle.trsm_lower_trans_cols(Acm, Bcm, cols, -1.5), full[cols])

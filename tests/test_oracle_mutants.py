@@ -36,6 +36,17 @@ MUTANTS = {
     # TRMM: A used untransposed
     "trmm_A_not_transposed": ("acc += g_h2d[A[k + i * lda]] * g_h2d[B[k + j * ldb]];\n            ref[i + j * ldr]",
                               "acc += g_h2d[A[i + k * lda]] * g_h2d[B[k + j * ldb]];\n            ref[i + j * ldr]"),
+    # TRSM: substitution term added instead of subtracted
+    "trsm_sign": ("acc -= g_h2d[A[k + i * lda]] * x[k];", "acc += g_h2d[A[k + i * lda]] * x[k];"),
+    # TRSM: division by the diagonal dropped
+    "trsm_no_divide": ("x[i] = acc / g_h2d[A[i + i * lda]];", "x[i] = acc;"),
+    # TRSM: A used untransposed (reads the strict upper triangle)
+    "trsm_untransposed": ("acc -= g_h2d[A[k + i * lda]] * x[k];", "acc -= g_h2d[A[i + k * lda]] * x[k];"),
+    # TRSM: alpha not applied
+    "trsm_alpha_dropped": ("double acc = alpha * g_h2d[B[i + j * ldb]];", "double acc = g_h2d[B[i + j * ldb]];"),
+    # TRSM: last row's term dropped from every sum
+    "trsm_last_term_dropped": ("for (int64_t k = i + 1; k < n; ++k)\n                acc -= ",
+                               "for (int64_t k = i + 1; k + 1 < n; ++k)\n                acc -= "),
     # fp16 decoding: subnormal scale off by one binade
     "decode_subnormal_scale": ("v = ldexp((double)frac, -24);", "v = ldexp((double)frac, -25);"),
     # fp16 decoding: exponent bias off by one

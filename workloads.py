@@ -69,6 +69,33 @@ WORKLOADS = {
 }
 
 
+@dataclass(frozen=True)
+class TrsmWorkload:
+    name: str
+    n: int
+    m: int
+    alpha: float
+    leaf: int
+    seed: int
+    note: str = ""
+
+    @property
+    def flops(self) -> float:
+        # back substitution: Σ_i 2·(n-1-i)·m multiply-adds plus n·m divisions ≈ n²·m
+        return float(self.n) * self.n * self.m
+
+
+# The triangular solve X = α·A⁻ᵀ·B ("异构计算中高性能TRMM与TRSM的递归算法实现"
+# §2.3, timed there at 8192×8192).  A lower triangular matrix with O(1) random
+# off-diagonal entries has a condition number that grows exponentially with n,
+# so the strict lower part is scaled by 1/sqrt(n) and the diagonal drawn from
+# [1, 2]: the 2-norm condition number stays near 3 at every n.
+TRSM_WORKLOADS = {
+    "trsm_8192": TrsmWorkload("trsm_8192", 8192, 8192, 1.0, 256, 5,
+                              "A lower: strict lower U[-1,1]/sqrt(n), diagonal U[1,2], upper 0; B U[-1,1]"),
+}
+
+
 def uniform_f16(rng: np.random.Generator, shape, lo: float = -1.0, hi: float = 1.0) -> np.ndarray:
     return rng.uniform(lo, hi, shape).astype(np.float16)
 
@@ -113,6 +140,27 @@ def trmm_inputs(w: TrmmWorkload):
     A_cm = np.ascontiguousarray(A.T)   # row c of A_cm = column c of A
     del A
     B_cm = np.ascontiguousarray(B.T)   # row j of B_cm = column j of B
+    return A_cm, B_cm
+
+
+def trsm_inputs(w: TrsmWorkload):
+    """Return (A_cm (n,n) f16, B_cm (m,n) f16) in the column-major convention.
+
+    Draw order: S (n,n) U[-1,1], D (n,) U[1,2], B (n,m) U[-1,1], all indexed
+    logically [row, column].  A = strict-lower part of S·(1/sqrt(n)), rounded
+    to fp16, plus diag(D); its upper triangle is exactly zero.
+    """
+    rng = np.random.default_rng(w.seed)
+    n, m = w.n, w.m
+    S = (rng.uniform(-1.0, 1.0, (n, n)) * (1.0 / np.sqrt(n))).astype(np.float16)
+    D = uniform_f16(rng, (n,), 1.0, 2.0)
+    B = uniform_f16(rng, (n, m))
+    A = np.tril(S, -1)
+    A[np.arange(n), np.arange(n)] = D
+    del S
+    A_cm = np.ascontiguousarray(A.T)
+    del A
+    B_cm = np.ascontiguousarray(B.T)
     return A_cm, B_cm
 
 
