@@ -20,6 +20,12 @@ importing this package raises.
         A is an (n, n) float16 tensor whose row c is column c of A; B is
         (m, n) float16 whose row j is column j of B; Out is (m, n) float32
         in the same convention.
+
+    trsm_lower_trans(A, B, Out, alpha=1.0, leaf=256, work=None)
+        Out = alpha·A⁻ᵀ·B (the X with Aᵀ·X = alpha·B), A lower triangular,
+        same conventions as trmm_lower_trans.  `work` is a device uint8
+        tensor of at least trsm_workspace_size(n, m, leaf) bytes; when None
+        one is allocated with torch for the call.
 """
 from __future__ import annotations
 
@@ -36,6 +42,14 @@ if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
                       "or python half_precision_gemm_amd/build.py")
 
+# PyTorch ships its own HIP runtime and loads it under a name the dynamic
+# loader does not match against the system copy the library was linked with.
+# Loading the library first would put two HIP runtimes in the process, and
+# the library's launches would then go through one that does not own the
+# tensors' memory or streams.  Importing torch first makes the library bind
+# to torch's runtime (same soname), so there is exactly one.
+import torch  # noqa: E402,F401
+
 lib = ctypes.CDLL(LIB_PATH)
 _i64, _f32, _vp, _int = ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_int
 lib.hgemm.argtypes = [_i64, _i64, _i64, _f32, _vp, _i64, _vp, _i64, _f32, _vp, _i64, _int, _vp]
@@ -45,13 +59,18 @@ lib.trmm_lower_trans.argtypes = [_i64, _i64, _f32, _vp, _i64, _vp, _i64, _vp, _i
 lib.trmm_lower_trans.restype = _int
 lib.hg_trmm_lower_trans_by_level.argtypes = lib.trmm_lower_trans.argtypes
 lib.hg_trmm_lower_trans_by_level.restype = _int
+lib.trsm_lower_trans.argtypes = [_i64, _i64, _f32, _vp, _i64, _vp, _i64, _vp, _i64, _int, _i64,
+                                 _vp, _i64, _vp]
+lib.trsm_lower_trans.restype = _int
+lib.hg_trsm_workspace_size.argtypes = [_i64, _i64, _i64]
+lib.hg_trsm_workspace_size.restype = _i64
 lib.hg_strerror.argtypes = [_int]
 lib.hg_strerror.restype = ctypes.c_char_p
 lib.hg_trmm_plan.argtypes = [_i64, _i64, ctypes.POINTER(_i64), _i64]
 lib.hg_trmm_plan.restype = _i64
 
 EXPORTS = ("hgemm", "trmm_lower_trans", "hg_trmm_lower_trans_by_level", "hg_strerror",
-           "hg_trmm_plan")
+           "hg_trmm_plan", "trsm_lower_trans", "hg_trsm_workspace_size")
 
 
 class HgError(RuntimeError):
@@ -134,6 +153,39 @@ def _trmm(fn, fname, A, B, Out, alpha, leaf):
             Out.data_ptr() or None, _ld(Out), HG_F32, int(leaf), _stream_handle(Out))
     if st != 0:
         raise HgError(fname, st)
+    return Out
+
+
+def trsm_workspace_size(n: int, m: int, leaf: int = 256) -> int:
+    """Bytes of device workspace trsm_lower_trans needs (hg_trsm_workspace_size)."""
+    sz = lib.hg_trsm_workspace_size(n, m, leaf)
+    if sz < 0:
+        raise HgError("hg_trsm_workspace_size", int(sz))
+    return int(sz)
+
+
+def trsm_lower_trans(A, B, Out, alpha: float = 1.0, leaf: int = 256, work=None):
+    """Out = alpha·A⁻ᵀ·B (A lower triangular) on the current stream; returns Out."""
+    import torch
+    _check_matrix(A, "A", (torch.float16,))
+    _check_matrix(B, "B", (torch.float16,))
+    _check_matrix(Out, "Out", (torch.float32,))
+    n = A.shape[0]
+    m = B.shape[0]
+    if tuple(A.shape) != (n, n) or B.shape[1] != n or tuple(Out.shape) != (m, n):
+        raise ValueError(f"shape mismatch: A {tuple(A.shape)}, B {tuple(B.shape)}, "
+                         f"Out {tuple(Out.shape)}")
+    need = trsm_workspace_size(n, m, leaf) if int(leaf) <= 256 else 0
+    if work is None:
+        work = torch.empty(max(need, 1), dtype=torch.uint8, device=Out.device)
+    elif not (isinstance(work, torch.Tensor) and work.is_cuda and work.is_contiguous()):
+        raise ValueError("work must be a contiguous device tensor")
+    st = lib.trsm_lower_trans(n, m, float(alpha), A.data_ptr() or None, _ld(A),
+                              B.data_ptr() or None, _ld(B), Out.data_ptr() or None, _ld(Out),
+                              HG_F32, int(leaf), work.data_ptr() or None,
+                              work.numel() * work.element_size(), _stream_handle(Out))
+    if st != 0:
+        raise HgError("trsm_lower_trans", st)
     return Out
 
 

@@ -14,7 +14,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libhgemm.so")
 SOURCES = [os.path.join(CSRC, "hg_api.cpp"), os.path.join(CSRC, "hg_kernels.hip"),
-           os.path.join(CSRC, "hg_fast.hip"), os.path.join(CSRC, "hg_ring.hip")]
+           os.path.join(CSRC, "hg_fast.hip"), os.path.join(CSRC, "hg_ring.hip"),
+           os.path.join(CSRC, "hg_trsm.hip")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

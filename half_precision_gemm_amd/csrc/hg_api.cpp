@@ -1,12 +1,13 @@
 // hg_api.cpp — host side of the C ABI declared in include/hgemm.h: argument
 // validation (BLAS xerbla-style status codes), quick returns, kernel
-// selection, and the recursive TRMM driver of
-// "异构计算中高性能TRMM与TRSM的递归算法实现" §2.1–§2.2.
+// selection, and the recursive TRMM and TRSM drivers of
+// "异构计算中高性能TRMM与TRSM的递归算法实现" §2.1–§2.3.
 #include "hgemm.h"
 
 #include <stdint.h>
 
 #include <algorithm>
+#include <utility>
 #include <vector>
 
 #include "hg_internal.h"
@@ -91,6 +92,7 @@ const char *hg_strerror(int status)
     case -11: return "invalid argument 11";
     case -12: return "invalid argument 12";
     case -13: return "invalid argument 13";
+    case -14: return "invalid argument 14";
     default: return "unknown status";
     }
 }
@@ -312,6 +314,233 @@ int hg_trmm_lower_trans_by_level(int64_t n, int64_t m, float alpha, const void *
                                  int64_t leaf, void *stream)
 {
     return trmm_impl(n, m, alpha, A, lda, B, ldb, Out, ldo, out_dtype, leaf, stream, false);
+}
+
+}  // extern "C"
+
+namespace {
+
+// ---- Recursive TRSM, X = alpha·A⁻ᵀ·B ("异构计算中高性能TRMM与TRSM的递归算法实现"
+// §2.1, §2.3).  With A = [[A11, 0], [A21, A22]] split at h = floor(s/2),
+// Aᵀ·X = alpha·B reads
+//   A22ᵀ·X2 = alpha·B2                        (solve the lower half first)
+//   A11ᵀ·X1 = alpha·B1 − A21ᵀ·X2               (GEMM update, then solve)
+// down to leaves of at most `leaf` rows.
+
+void trsm_leaves(int64_t o, int64_t s, int64_t leaf, std::vector<std::pair<int64_t, int64_t>> &out)
+{
+    if (s <= leaf) {
+        out.push_back({o, s});
+        return;
+    }
+    const int64_t h = s / 2;
+    trsm_leaves(o, h, leaf, out);
+    trsm_leaves(o + h, s - h, leaf, out);
+}
+
+// Workspace: the leaf inverses (fp16 ld×ld blocks, in ascending leaf
+// order), then W, the fp16 copy of X (n×m column-major, ldw = n rounded up
+// to 8), each part 256-byte aligned.
+struct TrsmLayout {
+    std::vector<std::pair<int64_t, int64_t>> leaves;
+    int32_t ld = 0;
+    int64_t v_bytes = 0;
+    int64_t ldw = 0;
+    int64_t total = 0;
+};
+
+int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+TrsmLayout trsm_layout(int64_t n, int64_t m, int64_t leaf)
+{
+    TrsmLayout L;
+    if (n == 0 || m == 0)
+        return L;
+    trsm_leaves(0, n, leaf, L.leaves);
+    int64_t smax = 0;
+    for (const auto &x : L.leaves)
+        smax = std::max(smax, x.second);
+    L.ld = (int32_t)round_up(smax, 8);
+    L.v_bytes = round_up((int64_t)L.leaves.size() * L.ld * L.ld * 2, 256);
+    L.ldw = round_up(n, 8);
+    L.total = L.v_bytes + round_up(L.ldw * m * 2, 256);
+    return L;
+}
+
+struct TrsmRun {
+    const _Float16 *A, *B;
+    int64_t lda, ldb, ldo, ldw, m;
+    float *Out;
+    _Float16 *V, *W;
+    int32_t ld;
+    float alpha;
+    const std::vector<std::pair<int64_t, int64_t>> *leaves;
+    int64_t leaf;
+    hipStream_t stream;
+
+    int leaf_step(int64_t o, int64_t s, bool touched) const
+    {
+        const auto it = std::lower_bound(leaves->begin(), leaves->end(), std::make_pair(o, (int64_t)0));
+        const int64_t idx = it - leaves->begin();
+        hg::TrsmLeafParams p{};
+        p.B = B;
+        p.ldb = ldb;
+        p.Out = Out;
+        p.ldo = ldo;
+        p.W = W;
+        p.ldw = ldw;
+        p.V = V + idx * ld * ld;
+        p.ldv = ld;
+        p.s = (int32_t)s;
+        p.o = o;
+        p.m = (int32_t)m;
+        p.alpha = alpha;
+        p.touched = touched ? 1 : 0;
+        const bool vec = aligned16(B) && aligned16(Out) && aligned16(W) && o % 8 == 0 &&
+                         ldb % 8 == 0 && ldo % 4 == 0 && ldw % 4 == 0;
+        return hip_status(hg::launch_trsm_leaf(p, vec, stream));
+    }
+
+    // Rows o..o+h-1 of the right-hand side: S = beta·S − A21ᵀ·X2 with
+    // A21 = A[o+h:o+s, o:o+h] and X2 from W, in the row-major view
+    //   C'(i, j) = Out(o+j, i),  A'(i, k) = W(o+h+k, i),  B'(j, k) = A(o+h+k, o+j).
+    int update(int64_t o, int64_t s, bool touched) const
+    {
+        const int64_t h = s / 2;
+        hg::GemmParams p{};
+        p.A = W;
+        p.B = A;
+        p.C = Out;
+        p.lda = ldw;
+        p.ldb = lda;
+        p.ldc = ldo;
+        p.M = (int32_t)m;
+        p.nbatch = 1;
+        p.alpha = -1.0f;
+        p.beta = touched ? 1.0f : 0.0f;
+        p.e[0] = {o + h, (o + h) + o * lda, o, (int32_t)h, (int32_t)(s - h)};
+        hg::LaunchOpts op{};
+        op.out_f16 = false;
+        op.beta_read = touched;
+        op.tri = false;
+        op.vec = aligned16(W) && aligned16(A) && ldw % 8 == 0 && lda % 8 == 0 &&
+                 p.e[0].a_off % 8 == 0 && p.e[0].b_off % 8 == 0;
+        op.tile = hg::choose_tile(m, h, s - h);
+        return hip_status(hg::launch_gemm(p, op, stream));
+    }
+
+    // `touched`: some update has already written rows o..o+s-1 of Out.
+    int solve(int64_t o, int64_t s, bool touched) const
+    {
+        if (s <= leaf)
+            return leaf_step(o, s, touched);
+        const int64_t h = s / 2;
+        int st = solve(o + h, s - h, touched);
+        if (st == HG_OK)
+            st = update(o, s, touched);
+        if (st == HG_OK)
+            st = solve(o, h, true);
+        return st;
+    }
+};
+
+}  // namespace
+
+extern "C" {
+
+int64_t hg_trsm_workspace_size(int64_t n, int64_t m, int64_t leaf)
+{
+    if (n < 0)
+        return -1;
+    if (m < 0)
+        return -2;
+    if (leaf <= 0)
+        leaf = 256;
+    if (leaf > hg::kTrsmLeafMax)
+        return -3;
+    return trsm_layout(n, m, leaf).total;
+}
+
+int trsm_lower_trans(int64_t n, int64_t m, float alpha, const void *A, int64_t lda, const void *B,
+                     int64_t ldb, void *Out, int64_t ldo, int out_dtype, int64_t leaf, void *work,
+                     int64_t work_bytes, void *stream)
+{
+    if (n < 0 || n > kI32Max)
+        return -1;
+    if (m < 0 || m > kI32Max)
+        return -2;
+    if (lda < std::max<int64_t>(1, n))
+        return -5;
+    if (ldb < std::max<int64_t>(1, n))
+        return -7;
+    if (ldo < std::max<int64_t>(1, n))
+        return -9;
+    if (out_dtype != HG_F32)
+        return -10;
+    if (leaf <= 0)
+        leaf = 256;
+    if (leaf > hg::kTrsmLeafMax)
+        return -11;
+    if (n == 0 || m == 0)
+        return HG_OK;
+    if (Out == nullptr)
+        return -8;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (alpha == 0.0f)
+        return hip_status(hg::launch_scale(Out, ldo, m, n, 0.0f, false, st));
+    if (A == nullptr)
+        return -4;
+    if (B == nullptr)
+        return -6;
+    const Extent eo = extent(Out, m, ldo, n, 4);
+    const Extent ea = extent(A, n, lda, n, 2);
+    const Extent eb = extent(B, m, ldb, n, 2);
+    if (overlap(eo, ea) || overlap(eo, eb))
+        return -8;
+    const TrsmLayout L = trsm_layout(n, m, leaf);
+    if (work == nullptr || !aligned16(work))
+        return -12;
+    if (work_bytes < L.total)
+        return -13;
+    const Extent ew = {reinterpret_cast<uintptr_t>(work), reinterpret_cast<uintptr_t>(work) + (uintptr_t)L.total};
+    if (overlap(ew, eo) || overlap(ew, ea) || overlap(ew, eb))
+        return -12;
+
+    TrsmRun r{};
+    r.A = static_cast<const _Float16 *>(A);
+    r.B = static_cast<const _Float16 *>(B);
+    r.lda = lda;
+    r.ldb = ldb;
+    r.ldo = ldo;
+    r.ldw = L.ldw;
+    r.m = m;
+    r.Out = static_cast<float *>(Out);
+    r.V = static_cast<_Float16 *>(work);
+    r.W = reinterpret_cast<_Float16 *>(static_cast<unsigned char *>(work) + L.v_bytes);
+    r.ld = L.ld;
+    r.alpha = alpha;
+    r.leaves = &L.leaves;
+    r.leaf = leaf;
+    r.stream = st;
+
+    // Every leaf's inverse first (they depend on A only).
+    for (size_t first = 0; first < L.leaves.size(); first += hg::kTrsmInvBatch) {
+        hg::TrsmInvParams p{};
+        p.A = r.A;
+        p.lda = lda;
+        p.V = r.V;
+        p.ld = L.ld;
+        p.nleaf = (int32_t)std::min<size_t>(hg::kTrsmInvBatch, L.leaves.size() - first);
+        for (int i = 0; i < p.nleaf; ++i) {
+            p.o[i] = L.leaves[first + i].first;
+            p.s[i] = (int32_t)L.leaves[first + i].second;
+            p.voff[i] = (int64_t)(first + i) * L.ld * L.ld;
+        }
+        const int s = hip_status(hg::launch_trsm_inv(p, st));
+        if (s != HG_OK)
+            return s;
+    }
+    return r.solve(0, n, false);
 }
 
 }  // extern "C"

@@ -69,6 +69,48 @@ hipError_t launch_gemm_ring(const GemmParams &p, const LaunchOpts &o, hipStream_
 bool trmm_fused_ok(const GemmParams &p);
 hipError_t launch_trmm_fused(const GemmParams &p, hipStream_t stream);
 
+// Recursive triangular solve X = alpha·A⁻ᵀ·B (hg_trsm.hip).  Leaves are at
+// most kTrsmLeafMax rows; their inverses V_L = A_LL⁻¹ are stored in fp16 as
+// full ld×ld column-major blocks (zeros above the diagonal and outside the
+// leaf), block l at V + voff[l].
+constexpr int kTrsmLeafMax = 256;
+constexpr int kTrsmInvBatch = 64;
+
+struct TrsmInvParams {
+    const _Float16 *A;     // n×n column-major, lower triangle read
+    int64_t lda;
+    _Float16 *V;           // workspace
+    int32_t ld;            // leading dimension (and size) of every V block, multiple of 8
+    int32_t nleaf;         // leaves in this launch (<= kTrsmInvBatch)
+    int64_t o[kTrsmInvBatch];     // leaf offsets (first row/column in A)
+    int64_t voff[kTrsmInvBatch];  // element offset of each V block
+    int32_t s[kTrsmInvBatch];     // leaf sizes (<= ld)
+};
+
+// One leaf of the solve, rows o..o+s-1 of X:
+//   R = fp16(alpha·B + S) (S = Out rows, the updates so far, when `touched`),
+//   X = V_Lᵀ·R with fp32 accumulation, Out = X (fp32), W = fp16(X).
+struct TrsmLeafParams {
+    const _Float16 *B;     // n×m column-major right-hand side
+    int64_t ldb;
+    float *Out;            // n×m column-major fp32 result / running update sums
+    int64_t ldo;
+    _Float16 *W;           // n×m column-major fp16 copy of X (operand of the updates)
+    int64_t ldw;
+    const _Float16 *V;     // this leaf's inverse block
+    int32_t ldv;
+    int32_t s;             // leaf size, 1..kTrsmLeafMax
+    int64_t o;             // leaf offset
+    int32_t m;             // columns of B
+    float alpha;
+    int32_t touched;       // nonzero: add S = Out rows to alpha·B
+};
+
+hipError_t launch_trsm_inv(const TrsmInvParams &p, hipStream_t stream);
+// vec: B, Out, W 16-byte aligned, o % 8 == 0, ldb % 8 == 0, ldo % 4 == 0,
+// ldw % 4 == 0 (vector loads and stores).
+hipError_t launch_trsm_leaf(const TrsmLeafParams &p, bool vec, hipStream_t stream);
+
 // C = beta·C over an M×N window (beta == 0 writes zeros without reading).
 hipError_t launch_scale(void *C, int64_t ldc, int64_t M, int64_t N, float beta,
                         bool out_f16, hipStream_t stream);

@@ -1,0 +1,344 @@
+// hg_trsm.hip — gfx950 kernels of the recursive triangular solve
+// X = alpha·A⁻ᵀ·B with A lower triangular ("异构计算中高性能TRMM与TRSM的递归算法实现"
+// §2.1 blocking, §2.3 triangular solve).
+//
+// The host driver (hg_api.cpp) runs the recursion: for a diagonal block of
+// size s > leaf split at h = floor(s/2), solve the lower half first, update
+// the upper half's right-hand side with the GEMM kernels (alpha = -1), then
+// solve the upper half.  This file holds the two pieces the GEMM kernels do
+// not cover:
+//
+//   * trsm_inv_kernel — the inverse V_L = A_LL⁻¹ of every leaf's diagonal
+//     block, in fp32 by block forward substitution, stored as fp16.  It
+//     depends on A only, so all leaves are inverted up front in one launch.
+//   * trsm_leaf_kernel — the leaf step X_L = V_Lᵀ·R_L as a matrix-core
+//     product (v_mfma_f32_32x32x16_f16, fp32 accumulation), where
+//     R_L = fp16(alpha·B_L + S_L) and S_L holds the sum of the updates already
+//     applied to these rows.  It writes X_L in fp32 and an fp16 copy that the
+//     updates above it take as their GEMM operand.
+//
+// The page solves each leaf by column-parallel substitution with a light
+// synchronisation after every row.  On the matrix cores a 256-row leaf is
+// instead one small GEMM against the precomputed inverse: every one of the
+// m columns of B is independent, as in the page's scheme, and the
+// row-by-row dependence moves into the inversion, which is done once per
+// leaf instead of once per column.
+#include "hg_internal.h"
+
+namespace hg {
+namespace {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef _Float16 halfx4 __attribute__((ext_vector_type(4)));
+
+// ---- Diagonal block inverses -------------------------------------------------
+//
+// Workgroup (leaf l, column block J) computes columns c0 = 32·J .. c0+31 of
+// V = A_LL⁻¹ (lower triangular) over 32-row blocks I = J, J+1, …:
+//   T = E_IJ − Σ_{K=J}^{I−1} A_IK·V_KJ      (E = identity)
+//   A_II·V_IJ = T                            (forward substitution, 32 columns)
+// All arithmetic is fp32; the block is written as fp16, each element exactly
+// once: the computed lower part, zeros above the diagonal, outside the leaf
+// and in the padding up to ld, so that the leaf kernel needs no masks.
+constexpr int kInvCols = 32;
+
+__global__ void __launch_bounds__(256) trsm_inv_kernel(const TrsmInvParams p)
+{
+    __shared__ float vs[kTrsmLeafMax][kInvCols + 1];  // this column block of V
+    __shared__ float as[kInvCols][kTrsmLeafMax + 1];  // A row panel of block I
+
+    const int nj = (p.ld + kInvCols - 1) / kInvCols;
+    const int l = blockIdx.x / nj;
+    const int J = blockIdx.x - l * nj;
+    const int ld = p.ld;
+    const int s = p.s[l];
+    const int64_t o = p.o[l];
+    const _Float16 *__restrict__ A = p.A;
+    const int64_t lda = p.lda;
+    _Float16 *__restrict__ V = p.V + p.voff[l];
+    const int t = threadIdx.x;
+    const int c0 = J * kInvCols;
+    const int ncol = min(kInvCols, ld - c0);
+    const int nrb = (ld + kInvCols - 1) / kInvCols;   // row blocks of the ld×ld block
+    const int nb = (s + kInvCols - 1) / kInvCols;     // row blocks holding leaf rows
+
+    // Rows [r0, r0+32) of this column block: zeros, or the values in vs.
+    auto store_rows = [&](int r0, bool zero) {
+        for (int idx = t; idx < kInvCols * ncol; idx += 256) {
+            const int rr = idx % kInvCols, c = idx / kInvCols;
+            const int r = r0 + rr, col = c0 + c;
+            if (r >= ld)
+                continue;
+            const bool inside = !zero && r < s && col < s && r >= col;
+            V[r + (int64_t)col * ld] = (_Float16)(inside ? vs[r][c] : 0.0f);
+        }
+    };
+
+    if (c0 >= s) {
+        for (int I = 0; I < nrb; ++I)
+            store_rows(I * kInvCols, true);
+        return;
+    }
+    for (int I = 0; I < J; ++I)
+        store_rows(I * kInvCols, true);
+
+    const int c = t % kInvCols;   // column of the block this thread works on
+    const int g = t / kInvCols;   // row group: rows g, g+8, g+16, g+24 of a block
+    for (int I = J; I < nb; ++I) {
+        const int r0 = I * kInvCols;
+        // A panel: rows r0..r0+31, columns c0..r0+31 (the diagonal block last).
+        const int ka = r0 + kInvCols - c0;
+        for (int idx = t; idx < kInvCols * ka; idx += 256) {
+            const int rr = idx % kInvCols, k = c0 + idx / kInvCols;
+            const int r = r0 + rr;
+            as[rr][k] = (r < s && k <= r) ? (float)A[(o + r) + (o + k) * lda] : 0.0f;
+        }
+        __syncthreads();
+        // T for rows of block I, into vs (those rows are not read yet).
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int rr = g + 8 * q;
+            float acc = (r0 + rr == c0 + c) ? 1.0f : 0.0f;
+            for (int k = c0; k < r0; ++k)
+                acc = __builtin_fmaf(-as[rr][k], vs[k][c], acc);
+            vs[r0 + rr][c] = acc;
+        }
+        __syncthreads();
+        // A_II·Y = T, one column per thread of the first 32.
+        if (t < kInvCols) {
+            for (int rr = 0; rr < kInvCols && r0 + rr < s; ++rr) {
+                float y = vs[r0 + rr][t];
+                for (int kk = 0; kk < rr; ++kk)
+                    y = __builtin_fmaf(-as[rr][r0 + kk], vs[r0 + kk][t], y);
+                vs[r0 + rr][t] = y / as[rr][r0 + rr];
+            }
+        }
+        __syncthreads();
+        store_rows(r0, false);
+    }
+    for (int I = nb; I < nrb; ++I)
+        store_rows(I * kInvCols, true);
+}
+
+// ---- Leaf step ---------------------------------------------------------------
+//
+// GEMM view: C(i, j) = Σ_k R(i, k)·V(k, j) with i over the m columns of B and
+// j, k over the s leaf rows; C(i, j) is X(o+j, i).  One workgroup owns 64
+// consecutive i and all j < 256, so the rows of Out it reads as S (columns k
+// of its own i) are exactly the ones it overwrites, after its last read.
+// K is walked in 64-wide stages, double-buffered in LDS; wave w owns
+// j ∈ [64w, 64w+64) and skips stages before its first nonzero row of V
+// (V(k, j) = 0 for k < j).
+constexpr int LBM = 64, LBN = 256, LBK = 64;
+constexpr int LDS_A = LBM * LBK * 2;
+constexpr int LDS_STAGE = LDS_A + LBN * LBK * 2;
+
+__device__ __forceinline__ int lds_chunk(int row, int kc) { return row * 8 + (kc ^ (row & 7)); }
+
+template <bool VEC>
+__global__ void __launch_bounds__(256, 1) trsm_leaf_kernel(const TrsmLeafParams p)
+{
+    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * LDS_STAGE];
+
+    const int m0 = blockIdx.x * LBM;
+    const int t = threadIdx.x;
+    const int lane = t & 63;
+    const int wave = t >> 6;
+    const int lkc = t & 7;
+    const int lrow = t >> 3;
+    const int s = p.s;
+    const int M = p.m;
+    const int nk = (s + LBK - 1) / LBK;
+    const int64_t o = p.o;
+    const float alpha = p.alpha;
+    const bool touched = p.touched != 0;
+
+    uint4 ra[2];
+    uint4 rb[8];
+
+    // R(i, k..k+7) = fp16(alpha·B(o+k.., i) + S(o+k.., i)), zero past the
+    // leaf or past the last column of B.
+    auto load_r = [&](int i, int k) -> uint4 {
+        half8 h;
+        if (i >= M || k >= s)
+            return make_uint4(0u, 0u, 0u, 0u);
+        const _Float16 *bp = p.B + (o + k) + (int64_t)i * p.ldb;
+        const float *sp = p.Out + (o + k) + (int64_t)i * p.ldo;
+        if (VEC && k + 8 <= s) {
+            const half8 b = *reinterpret_cast<const half8 *>(bp);
+            if (touched) {
+                const floatx4 s0 = *reinterpret_cast<const floatx4 *>(sp);
+                const floatx4 s1 = *reinterpret_cast<const floatx4 *>(sp + 4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    h[e] = (_Float16)__builtin_fmaf(alpha, (float)b[e], s0[e]);
+                    h[e + 4] = (_Float16)__builtin_fmaf(alpha, (float)b[e + 4], s1[e]);
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    h[e] = (_Float16)(alpha * (float)b[e]);
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                float v = 0.0f;
+                if (k + e < s) {
+                    v = alpha * (float)bp[e];
+                    if (touched)
+                        v = __builtin_fmaf(alpha, (float)bp[e], sp[e]);
+                }
+                h[e] = (_Float16)v;
+            }
+        }
+        return __builtin_bit_cast(uint4, h);
+    };
+
+    // Stage kt: R rows m0 + lrow + 32u (u < 2); V rows j = lrow + 32u (u < 8)
+    // for the j that have a nonzero in this stage (j < 64·(kt+1)).
+    auto gload = [&](int kt) {
+        const int k = kt * LBK + lkc * 8;
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+            ra[u] = load_r(m0 + lrow + 32 * u, k);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int j = lrow + 32 * u;
+            if (32 * u < LBK * (kt + 1))
+                rb[u] = (k < s && j < s)
+                            ? *reinterpret_cast<const uint4 *>(p.V + (int64_t)j * p.ldv + k)
+                            : make_uint4(0u, 0u, 0u, 0u);
+        }
+    };
+    auto sstore = [&](int buf, int kt) {
+        unsigned char *As = smem + buf * LDS_STAGE;
+        unsigned char *Bs = As + LDS_A;
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+            *reinterpret_cast<uint4 *>(As + lds_chunk(lrow + 32 * u, lkc) * 16) = ra[u];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            if (32 * u < LBK * (kt + 1))
+                *reinterpret_cast<uint4 *>(Bs + lds_chunk(lrow + 32 * u, lkc) * 16) = rb[u];
+    };
+
+    floatx16 acc[2][2];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+            acc[a][b] = floatx16{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+
+    // Fragments: lane l supplies row (l mod 32) of a 32-row block and the 8
+    // consecutive k from 8·(l div 32) of the current 16-wide k step, for both
+    // operands; the B fragment goes first, so each 32×32 result is Cᵀ.
+    const int frow = lane & 31;
+    const int fkc = lane >> 5;
+    const bool wave_live = 64 * wave < s;
+    auto compute = [&](int buf, int kt) {
+        if (!wave_live || wave > kt)
+            return;
+        const unsigned char *As = smem + buf * LDS_STAGE;
+        const unsigned char *Bs = As + LDS_A;
+#pragma unroll
+        for (int st = 0; st < LBK / 16; ++st) {
+            const int kc = 2 * st + fkc;
+            half8 af[2], bf[2];
+#pragma unroll
+            for (int a = 0; a < 2; ++a)
+                af[a] = *reinterpret_cast<const half8 *>(As + lds_chunk(32 * a + frow, kc) * 16);
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+                bf[b] = *reinterpret_cast<const half8 *>(
+                    Bs + lds_chunk(64 * wave + 32 * b + frow, kc) * 16);
+#pragma unroll
+            for (int a = 0; a < 2; ++a)
+#pragma unroll
+                for (int b = 0; b < 2; ++b)
+                    acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[b], af[a], acc[a][b], 0, 0, 0);
+        }
+    };
+
+    gload(0);
+    sstore(0, 0);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+        const int buf = kt & 1;
+        const bool more = kt + 1 < nk;
+        if (more)
+            gload(kt + 1);
+        compute(buf, kt);
+        if (more)
+            sstore(buf ^ 1, kt + 1);
+        __syncthreads();
+    }
+
+    // Epilogue: block (a, b) of this wave holds C(i, j..j+3) for
+    // i = m0 + 32a + (lane mod 32) and, in register group g,
+    // j = 64·wave + 32b + 8g + 4·(lane div 32).
+    if (!wave_live)
+        return;
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+        const int i = m0 + 32 * a + frow;
+        if (i >= M)
+            continue;
+        float *orow = p.Out + o + (int64_t)i * p.ldo;
+        _Float16 *wrow = p.W + o + (int64_t)i * p.ldw;
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int j = 64 * wave + 32 * b + 8 * g + 4 * fkc;
+                const floatx4 v = {acc[a][b][4 * g + 0], acc[a][b][4 * g + 1],
+                                   acc[a][b][4 * g + 2], acc[a][b][4 * g + 3]};
+                if (VEC && j + 4 <= s) {
+                    *reinterpret_cast<floatx4 *>(orow + j) = v;
+                    const halfx4 h = {(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
+                    *reinterpret_cast<halfx4 *>(wrow + j) = h;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (j + e < s) {
+                            orow[j + e] = v[e];
+                            wrow[j + e] = (_Float16)v[e];
+                        }
+                }
+            }
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_trsm_inv(const TrsmInvParams &p, hipStream_t stream)
+{
+    if (p.nleaf <= 0)
+        return hipSuccess;
+    if (p.nleaf > kTrsmInvBatch || p.ld <= 0 || p.ld > kTrsmLeafMax || p.ld % 8 != 0)
+        return hipErrorInvalidValue;
+    for (int l = 0; l < p.nleaf; ++l)
+        if (p.s[l] <= 0 || p.s[l] > p.ld)
+            return hipErrorInvalidValue;
+    const int nj = (p.ld + kInvCols - 1) / kInvCols;
+    hipLaunchKernelGGL(trsm_inv_kernel, dim3((unsigned)(p.nleaf * nj)), dim3(256), 0, stream, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_trsm_leaf(const TrsmLeafParams &p, bool vec, hipStream_t stream)
+{
+    if (p.m <= 0)
+        return hipSuccess;
+    if (p.s <= 0 || p.s > kTrsmLeafMax || p.s > p.ldv || p.ldv % 8 != 0)
+        return hipErrorInvalidValue;
+    const unsigned grid = (unsigned)((p.m + LBM - 1) / LBM);
+    if (vec)
+        hipLaunchKernelGGL(trsm_leaf_kernel<true>, dim3(grid), dim3(256), 0, stream, p);
+    else
+        hipLaunchKernelGGL(trsm_leaf_kernel<false>, dim3(grid), dim3(256), 0, stream, p);
+    return hipGetLastError();
+}
+
+}  // namespace hg

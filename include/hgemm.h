@@ -18,11 +18,19 @@
  *                     by a triangle-masked kernel, and every A21ᵀ·B2 update by
  *                     the GEMM kernel of hgemm with beta = 1.
  *
+ *   trsm_lower_trans  X = alpha·A⁻ᵀ·B with A lower triangular: the triangular
+ *                     solve of the same page, §2.3, by the same recursion
+ *                     (§2.1): the lower half is solved first, the upper
+ *                     half's right-hand side is updated by the GEMM kernel
+ *                     (alpha = -1), leaves are multiplied by the inverse of
+ *                     their diagonal block on the matrix cores.
+ *
  * All matrix pointers are DEVICE pointers on the current HIP device.  Calls
  * are asynchronous on `stream` (a hipStream_t; NULL = the default stream);
  * results are valid once the stream has been synchronised.  The library
  * allocates nothing, never copies between host and device, keeps no state
- * and is thread-safe.  The caller owns every buffer.
+ * and is thread-safe.  The caller owns every buffer, including the device
+ * workspace trsm_lower_trans takes.
  *
  * Return value: 0 on success.  A negative value -i means argument i (1-based,
  * in the order of the prototype) is invalid, following the BLAS xerbla
@@ -129,6 +137,60 @@ int hg_trmm_lower_trans_by_level(int64_t n, int64_t m, float alpha,
                                  const void *B, int64_t ldb,
                                  void *Out, int64_t ldo, int out_dtype,
                                  int64_t leaf, void *stream);
+
+/*
+ * trsm_lower_trans — Out = X = alpha·A⁻ᵀ·B, i.e. the X with Aᵀ·X = alpha·B,
+ * A lower triangular.
+ *
+ *  1 n, 2 m      : A is n×n, B and Out are n×m; each >= 0.
+ *  3 alpha       : scale of the right-hand side (fp32).
+ *  4 A, 5 lda    : fp16, n×n column-major, element (r,c) at A[r + c*lda];
+ *                  lda >= max(1, n).  Only the lower triangle (r >= c) is
+ *                  read.  The diagonal is not checked: a zero on it gives
+ *                  inf/NaN, as the arithmetic does (no singularity test, as
+ *                  in BLAS).
+ *  6 B, 7 ldb    : fp16, n×m column-major right-hand side; ldb >= max(1, n).
+ *  8 Out, 9 ldo  : n×m column-major fp32 solution; ldo >= max(1, n);
+ *                  write-only for the caller (the solve keeps running sums
+ *                  in it).  Must not overlap A or B (error -8).
+ * 10 out_dtype   : HG_F32 (HG_F16 is rejected with -10).
+ * 11 leaf        : recursion cut-off, 1..256 (leaf <= 0 selects 256; larger
+ *                  values are rejected with -11).  A diagonal block of size
+ *                  <= leaf is solved by the leaf step.
+ * 12 work        : device workspace, 16-byte aligned, of at least
+ * 13 work_bytes    hg_trsm_workspace_size(n, m, leaf) bytes; must not overlap
+ *                  A, B or Out (error -12; too small: -13).  Its contents on
+ *                  entry are ignored and on return are unspecified.
+ * 14 stream      : hipStream_t to launch on.
+ *
+ * Arithmetic (half precision operands, fp32 accumulation, as in hgemm):
+ *   - each leaf's diagonal block is inverted in fp32 and rounded to fp16;
+ *   - a leaf's right-hand side alpha·B + (updates so far) is formed in fp32
+ *     and rounded to fp16, multiplied by the fp16 inverse with fp32
+ *     accumulation, and stored in Out as fp32;
+ *   - every update (alpha = -1) takes the solved rows rounded to fp16 as its
+ *     GEMM operand and accumulates in fp32 into Out.
+ * Each fp16 rounding has relative error <= 2^-11, so X carries an error of
+ * order 2^-11 times the condition of the system (ill-conditioned A loses
+ * accordingly).  alpha == 0 sets Out = 0 without reading A, B or work.
+ * Alignment: A and B 16-byte aligned, lda, ldb multiples of 8 and
+ * recursion boundaries (n split down by halving) on multiples of 8 take the
+ * vector paths; anything else runs element-wise paths with the same result.
+ */
+int trsm_lower_trans(int64_t n, int64_t m, float alpha,
+                     const void *A, int64_t lda,
+                     const void *B, int64_t ldb,
+                     void *Out, int64_t ldo, int out_dtype,
+                     int64_t leaf, void *work, int64_t work_bytes,
+                     void *stream);
+
+/*
+ * hg_trsm_workspace_size — bytes of device workspace trsm_lower_trans needs
+ * for (n, m, leaf): the fp16 inverses of the leaf blocks plus an fp16 copy
+ * of X.  Host only.  Returns 0 when n or m is 0, -1 for n < 0, -2 for
+ * m < 0, -3 for leaf > 256 (leaf <= 0 selects 256).
+ */
+int64_t hg_trsm_workspace_size(int64_t n, int64_t m, int64_t leaf);
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char *hg_strerror(int status);

@@ -30,7 +30,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == ["hg_strerror", "hg_trmm_lower_trans_by_level", "hg_trmm_plan",
-                                    "hgemm", "trmm_lower_trans"]
+                                    "hg_trsm_workspace_size", "hgemm", "trmm_lower_trans",
+                                    "trsm_lower_trans"]
 
 
 def test_library_exports_every_declared_symbol(hg):
@@ -102,8 +103,68 @@ def test_trmm_argument_errors(lib, args, code):
     assert lib.trmm_lower_trans(*args, None) == code
 
 
+W = 0x60000000   # fake workspace address
+
+
+def _trsm_need(lib, n, m, leaf):
+    return lib.hg_trsm_workspace_size(n, m, leaf)
+
+
+@pytest.mark.parametrize("args,code", [
+    ((-1, 4, 1.0, P, 8, Q, 8, R, 8, 1, 256, W, 1 << 30), -1),
+    ((8, -1, 1.0, P, 8, Q, 8, R, 8, 1, 256, W, 1 << 30), -2),
+    ((2 ** 31, 4, 1.0, P, 2 ** 31, Q, 2 ** 31, R, 2 ** 31, 1, 256, W, 1 << 30), -1),
+    ((8, 4, 1.0, P, 7, Q, 8, R, 8, 1, 256, W, 1 << 30), -5),
+    ((8, 4, 1.0, P, 8, Q, 7, R, 8, 1, 256, W, 1 << 30), -7),
+    ((8, 4, 1.0, P, 8, Q, 8, R, 7, 1, 256, W, 1 << 30), -9),
+    ((8, 4, 1.0, P, 8, Q, 8, R, 8, 0, 256, W, 1 << 30), -10),
+    ((8, 4, 1.0, P, 8, Q, 8, R, 8, 1, 257, W, 1 << 30), -11),
+    ((8, 4, 1.0, P, 8, Q, 8, None, 8, 1, 256, W, 1 << 30), -8),
+    ((8, 4, 1.0, None, 8, Q, 8, R, 8, 1, 256, W, 1 << 30), -4),
+    ((8, 4, 1.0, P, 8, None, 8, R, 8, 1, 256, W, 1 << 30), -6),
+    ((8, 4, 1.0, P, 8, Q, 8, Q + 16, 8, 1, 256, W, 1 << 30), -8),   # Out overlaps B
+    ((8, 4, 1.0, P, 8, Q, 8, R, 8, 1, 256, None, 1 << 30), -12),
+    ((8, 4, 1.0, P, 8, Q, 8, R, 8, 1, 256, W + 8, 1 << 30), -12),    # misaligned
+    ((8, 4, 1.0, P, 8, Q, 8, R, 8, 1, 256, R + 64, 1 << 30), -12),   # overlaps Out
+    ((8, 4, 1.0, P, 8, Q, 8, R, 8, 1, 256, W, 16), -13),             # too small
+    ((0, 4, 1.0, None, 1, None, 1, None, 1, 1, 256, None, 0), 0),
+    ((8, 0, 1.0, None, 8, None, 8, None, 8, 1, 256, None, 0), 0),
+])
+def test_trsm_argument_errors(lib, args, code):
+    assert lib.trsm_lower_trans(*args, None) == code
+
+
+@pytest.mark.parametrize("n,m,leaf", [(8192, 8192, 256), (1000, 77, 256), (300, 5, 100), (13, 3, 1),
+                                      (257, 9, 0)])
+def test_trsm_workspace_size(lib, n, m, leaf):
+    """Leaf inverses (ld×ld fp16 blocks, ld = largest leaf rounded up to 8)
+    plus the fp16 copy of X (ldw = n rounded up to 8), each 256-byte padded."""
+    L = 256 if leaf <= 0 else leaf
+    leaves = []
+
+    def rec(o, s):
+        if s <= L:
+            leaves.append(s)
+            return
+        rec(o, s // 2)
+        rec(o + s // 2, s - s // 2)
+    rec(0, n)
+    ld = -(-max(leaves) // 8) * 8
+    up = lambda x: -(-x // 256) * 256
+    expect = up(len(leaves) * ld * ld * 2) + up(-(-n // 8) * 8 * m * 2)
+    assert _trsm_need(lib, n, m, leaf) == expect
+
+
+def test_trsm_workspace_size_errors(lib):
+    assert _trsm_need(lib, -1, 4, 256) == -1
+    assert _trsm_need(lib, 4, -1, 256) == -2
+    assert _trsm_need(lib, 4, 4, 300) == -3
+    assert _trsm_need(lib, 0, 4, 256) == 0 and _trsm_need(lib, 4, 0, 256) == 0
+
+
 def test_strerror(hg):
     assert hg.strerror(0) == "success"
+    assert "argument 14" in hg.strerror(-14)
     assert "argument 6" in hg.strerror(-6)
     assert hg.strerror(-99) == "unknown status"
     assert isinstance(hg.strerror(1000 + 1), str)
@@ -179,3 +240,18 @@ def test_plan_errors(hg):
     assert hg.lib.hg_trmm_plan(10, 256, None, 5) == -2
     assert hg.trmm_plan(0) == []
     assert hg.trmm_plan(10, 0) == [(0, 0, 10, 0)]     # leaf <= 0 means 256
+
+
+def test_one_hip_runtime_in_the_process():
+    """Importing the binding loads torch before the library, so the library
+    binds to torch's HIP runtime and the process maps a single one."""
+    import subprocess
+    import sys
+    code = ("import half_precision_gemm_amd\n"
+            "maps = open('/proc/self/maps').read().splitlines()\n"
+            "libs = {l.split()[-1] for l in maps if 'libamdhip64' in l}\n"
+            "print(len(libs))\n")
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True,
+                       timeout=300)
+    assert r.returncode == 0, r.stderr[-2000:]
+    assert r.stdout.strip().splitlines()[-1] == "1"
