@@ -397,7 +397,7 @@ struct TrsmRun {
         p.alpha = alpha;
         p.touched = touched ? 1 : 0;
         const bool vec = aligned16(B) && aligned16(Out) && aligned16(W) && o % 8 == 0 &&
-                         ldb % 8 == 0 && ldo % 4 == 0 && ldw % 4 == 0;
+                         s % 8 == 0 && ldb % 8 == 0 && ldo % 4 == 0 && ldw % 4 == 0;
         return hip_status(hg::launch_trsm_leaf(p, vec, stream));
     }
 

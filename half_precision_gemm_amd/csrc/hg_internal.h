@@ -107,8 +107,8 @@ struct TrsmLeafParams {
 };
 
 hipError_t launch_trsm_inv(const TrsmInvParams &p, hipStream_t stream);
-// vec: B, Out, W 16-byte aligned, o % 8 == 0, ldb % 8 == 0, ldo % 4 == 0,
-// ldw % 4 == 0 (vector loads and stores).
+// vec: B, Out, W 16-byte aligned, o % 8 == 0, s % 8 == 0, ldb % 8 == 0,
+// ldo % 4 == 0, ldw % 4 == 0 (vector loads and stores).
 hipError_t launch_trsm_leaf(const TrsmLeafParams &p, bool vec, hipStream_t stream);
 
 // C = beta·C over an M×N window (beta == 0 writes zeros without reading).

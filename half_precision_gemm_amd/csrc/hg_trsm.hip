@@ -106,14 +106,28 @@ __global__ void __launch_bounds__(256) trsm_inv_kernel(const TrsmInvParams p)
             vs[r0 + rr][c] = acc;
         }
         __syncthreads();
-        // A_II·Y = T, one column per thread of the first 32.
+        // A_II·Y = T, one column per thread of the first 32: the column's 32
+        // values stay in registers (loops unrolled), the coefficients are LDS
+        // broadcasts independent of the substitution chain.  Rows past the
+        // leaf are left as they are (they are stored as zeros).
         if (t < kInvCols) {
-            for (int rr = 0; rr < kInvCols && r0 + rr < s; ++rr) {
-                float y = vs[r0 + rr][t];
-                for (int kk = 0; kk < rr; ++kk)
-                    y = __builtin_fmaf(-as[rr][r0 + kk], vs[r0 + kk][t], y);
-                vs[r0 + rr][t] = y / as[rr][r0 + rr];
+            float y[kInvCols];
+#pragma unroll
+            for (int rr = 0; rr < kInvCols; ++rr)
+                y[rr] = vs[r0 + rr][t];
+#pragma unroll
+            for (int rr = 0; rr < kInvCols; ++rr) {
+                if (r0 + rr < s) {
+                    float acc = y[rr];
+#pragma unroll
+                    for (int kk = 0; kk < rr; ++kk)
+                        acc = __builtin_fmaf(-as[rr][r0 + kk], y[kk], acc);
+                    y[rr] = acc / as[rr][r0 + rr];
+                }
             }
+#pragma unroll
+            for (int rr = 0; rr < kInvCols; ++rr)
+                vs[r0 + rr][t] = y[rr];
         }
         __syncthreads();
         store_rows(r0, false);
@@ -125,38 +139,46 @@ __global__ void __launch_bounds__(256) trsm_inv_kernel(const TrsmInvParams p)
 // ---- Leaf step ---------------------------------------------------------------
 //
 // GEMM view: C(i, j) = Σ_k R(i, k)·V(k, j) with i over the m columns of B and
-// j, k over the s leaf rows; C(i, j) is X(o+j, i).  One workgroup owns 64
+// j, k over the s leaf rows; C(i, j) is X(o+j, i).  One workgroup owns 32
 // consecutive i and all j < 256, so the rows of Out it reads as S (columns k
 // of its own i) are exactly the ones it overwrites, after its last read.
-// K is walked in 64-wide stages, double-buffered in LDS; wave w owns
-// j ∈ [64w, 64w+64) and skips stages before its first nonzero row of V
-// (V(k, j) = 0 for k < j).
-constexpr int LBM = 64, LBN = 256, LBK = 64;
-constexpr int LDS_A = LBM * LBK * 2;
-constexpr int LDS_STAGE = LDS_A + LBN * LBK * 2;
+// The whole K range fits in LDS (R: 32×256, V: 256×256 fp16, 144 KB), so
+// every load is issued up front — one global round trip — then one barrier
+// and the products.  V(k, j) = 0 for k < j: a 16-wide k step whose k are all
+// below a 32-row j block is neither loaded nor multiplied.  Wave w owns
+// j ∈ [64w, 64w+64).
+constexpr int LBM = 32, LBN = 256, LBK = 256;
+constexpr int LKC = LBK / 8;                 // 16-byte chunks per LDS row
+constexpr int LDS_R = LBM * LBK * 2;         // 16 KB
+constexpr int LDS_V = LBN * LBK * 2;         // 128 KB
+constexpr int R_PER_T = LBM * LKC / 256;     // 4
+constexpr int V_PER_T = LBN * LKC / 256;     // 32
 
-__device__ __forceinline__ int lds_chunk(int row, int kc) { return row * 8 + (kc ^ (row & 7)); }
+// 16-byte chunk kc of row `row` in a 32-chunk row: XOR-swizzled so that the
+// fragment reads of 32 consecutive rows at one kc hit distinct bank groups.
+__device__ __forceinline__ int lds_chunk(int row, int kc) { return row * LKC + (kc ^ (row & 31)); }
+
+// Chunk kc (8 consecutive k) of V row j is read by the MFMA k step kc/2 of
+// j block j/32, which runs when that step reaches the block: 16·(kc/2) + 16
+// > 32·(j/32).
+__device__ __forceinline__ bool v_chunk_used(int j, int kc) { return 8 * (kc & ~1) + 16 > (j & ~31); }
 
 template <bool VEC>
 __global__ void __launch_bounds__(256, 1) trsm_leaf_kernel(const TrsmLeafParams p)
 {
-    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * LDS_STAGE];
+    __shared__ __attribute__((aligned(16))) unsigned char smem[LDS_R + LDS_V];
+    unsigned char *Rs = smem;
+    unsigned char *Vs = smem + LDS_R;
 
     const int m0 = blockIdx.x * LBM;
     const int t = threadIdx.x;
     const int lane = t & 63;
     const int wave = t >> 6;
-    const int lkc = t & 7;
-    const int lrow = t >> 3;
     const int s = p.s;
     const int M = p.m;
-    const int nk = (s + LBK - 1) / LBK;
     const int64_t o = p.o;
     const float alpha = p.alpha;
     const bool touched = p.touched != 0;
-
-    uint4 ra[2];
-    uint4 rb[8];
 
     // R(i, k..k+7) = fp16(alpha·B(o+k.., i) + S(o+k.., i)), zero past the
     // leaf or past the last column of B.
@@ -196,116 +218,138 @@ __global__ void __launch_bounds__(256, 1) trsm_leaf_kernel(const TrsmLeafParams 
         return __builtin_bit_cast(uint4, h);
     };
 
-    // Stage kt: R rows m0 + lrow + 32u (u < 2); V rows j = lrow + 32u (u < 8)
-    // for the j that have a nonzero in this stage (j < 64·(kt+1)).
-    auto gload = [&](int kt) {
-        const int k = kt * LBK + lkc * 8;
+    // All loads first.  Thread t takes chunk column t mod 32 of rows
+    // t/32 + 8u: R rows u < 4, V rows u < 32.
+    const int lkc = t & 31;
+    const int lrow = t >> 5;
+    uint4 ra[R_PER_T];
+    uint4 rv[V_PER_T];
+    bool vok[V_PER_T];
+    if constexpr (VEC) {
+        // Branch-free: every load is issued from a valid address (the real
+        // chunk, or a chunk known to be in range) and masked afterwards, so
+        // all of them are in flight together.  VEC implies s % 8 == 0: no
+        // chunk is partial.
+        const int k = lkc * 8;
+        half8 bv[R_PER_T];
+        floatx4 sv[2 * R_PER_T];
+        bool rok[R_PER_T];
+        const int64_t bdummy = o + (int64_t)m0 * p.ldb;
+        const int64_t sdummy = o + (int64_t)m0 * p.ldo;
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
-            ra[u] = load_r(m0 + lrow + 32 * u, k);
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int j = lrow + 32 * u;
-            if (32 * u < LBK * (kt + 1))
-                rb[u] = (k < s && j < s)
-                            ? *reinterpret_cast<const uint4 *>(p.V + (int64_t)j * p.ldv + k)
-                            : make_uint4(0u, 0u, 0u, 0u);
+        for (int u = 0; u < R_PER_T; ++u) {
+            const int i = m0 + lrow + 8 * u;
+            rok[u] = i < M && k < s;
+            bv[u] = *reinterpret_cast<const half8 *>(
+                p.B + (rok[u] ? (o + k) + (int64_t)i * p.ldb : bdummy));
         }
-    };
-    auto sstore = [&](int buf, int kt) {
-        unsigned char *As = smem + buf * LDS_STAGE;
-        unsigned char *Bs = As + LDS_A;
+        if (touched) {
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
-            *reinterpret_cast<uint4 *>(As + lds_chunk(lrow + 32 * u, lkc) * 16) = ra[u];
+            for (int u = 0; u < R_PER_T; ++u) {
+                const int i = m0 + lrow + 8 * u;
+                const float *sp = p.Out + (rok[u] ? (o + k) + (int64_t)i * p.ldo : sdummy);
+                sv[2 * u] = *reinterpret_cast<const floatx4 *>(sp);
+                sv[2 * u + 1] = *reinterpret_cast<const floatx4 *>(sp + 4);
+            }
+        }
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
-            if (32 * u < LBK * (kt + 1))
-                *reinterpret_cast<uint4 *>(Bs + lds_chunk(lrow + 32 * u, lkc) * 16) = rb[u];
-    };
-
-    floatx16 acc[2][2];
+        for (int u = 0; u < V_PER_T; ++u) {
+            const int j = lrow + 8 * u;
+            vok[u] = j < s && k < s && v_chunk_used(j, lkc);
+            rv[u] = *reinterpret_cast<const uint4 *>(p.V + (vok[u] ? (int64_t)j * p.ldv + k : 0));
+        }
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+        for (int u = 0; u < R_PER_T; ++u) {
+            half8 h;
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
-            acc[a][b] = floatx16{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+            for (int e = 0; e < 8; ++e) {
+                const float b = alpha * (float)bv[u][e];
+                const float v = touched ? __builtin_fmaf(alpha, (float)bv[u][e], sv[2 * u + e / 4][e % 4]) : b;
+                h[e] = rok[u] ? (_Float16)v : (_Float16)0.0f;
+            }
+            ra[u] = __builtin_bit_cast(uint4, h);
+        }
+#pragma unroll
+        for (int u = 0; u < V_PER_T; ++u) {
+            const uint32_t keep = vok[u] ? 0xffffffffu : 0u;
+            rv[u] = make_uint4(rv[u].x & keep, rv[u].y & keep, rv[u].z & keep, rv[u].w & keep);
+        }
+    } else {
+#pragma unroll
+        for (int u = 0; u < R_PER_T; ++u)
+            ra[u] = load_r(m0 + lrow + 8 * u, lkc * 8);
+#pragma unroll
+        for (int u = 0; u < V_PER_T; ++u) {
+            const int j = lrow + 8 * u;
+            rv[u] = make_uint4(0u, 0u, 0u, 0u);
+            if (j < s && lkc * 8 < s && v_chunk_used(j, lkc))
+                rv[u] = *reinterpret_cast<const uint4 *>(p.V + (int64_t)j * p.ldv + lkc * 8);
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < R_PER_T; ++u)
+        *reinterpret_cast<uint4 *>(Rs + lds_chunk(lrow + 8 * u, lkc) * 16) = ra[u];
+#pragma unroll
+    for (int u = 0; u < V_PER_T; ++u) {
+        const int j = lrow + 8 * u;
+        if (v_chunk_used(j, lkc))
+            *reinterpret_cast<uint4 *>(Vs + lds_chunk(j, lkc) * 16) = rv[u];
+    }
+    __syncthreads();
 
     // Fragments: lane l supplies row (l mod 32) of a 32-row block and the 8
     // consecutive k from 8·(l div 32) of the current 16-wide k step, for both
-    // operands; the B fragment goes first, so each 32×32 result is Cᵀ.
+    // operands; the V fragment goes first, so each 32×32 result is Cᵀ.
+    if (64 * wave >= s)
+        return;
     const int frow = lane & 31;
     const int fkc = lane >> 5;
-    const bool wave_live = 64 * wave < s;
-    auto compute = [&](int buf, int kt) {
-        if (!wave_live || wave > kt)
-            return;
-        const unsigned char *As = smem + buf * LDS_STAGE;
-        const unsigned char *Bs = As + LDS_A;
+    floatx16 acc[2];
 #pragma unroll
-        for (int st = 0; st < LBK / 16; ++st) {
-            const int kc = 2 * st + fkc;
-            half8 af[2], bf[2];
+    for (int b = 0; b < 2; ++b)
+        acc[b] = floatx16{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+    const int nst = (s + 15) / 16;
 #pragma unroll
-            for (int a = 0; a < 2; ++a)
-                af[a] = *reinterpret_cast<const half8 *>(As + lds_chunk(32 * a + frow, kc) * 16);
-#pragma unroll
-            for (int b = 0; b < 2; ++b)
-                bf[b] = *reinterpret_cast<const half8 *>(
-                    Bs + lds_chunk(64 * wave + 32 * b + frow, kc) * 16);
-#pragma unroll
-            for (int a = 0; a < 2; ++a)
-#pragma unroll
-                for (int b = 0; b < 2; ++b)
-                    acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[b], af[a], acc[a][b], 0, 0, 0);
-        }
-    };
-
-    gload(0);
-    sstore(0, 0);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-        const int buf = kt & 1;
-        const bool more = kt + 1 < nk;
-        if (more)
-            gload(kt + 1);
-        compute(buf, kt);
-        if (more)
-            sstore(buf ^ 1, kt + 1);
-        __syncthreads();
-    }
-
-    // Epilogue: block (a, b) of this wave holds C(i, j..j+3) for
-    // i = m0 + 32a + (lane mod 32) and, in register group g,
-    // j = 64·wave + 32b + 8g + 4·(lane div 32).
-    if (!wave_live)
-        return;
-#pragma unroll
-    for (int a = 0; a < 2; ++a) {
-        const int i = m0 + 32 * a + frow;
-        if (i >= M)
+    for (int st = 0; st < LBK / 16; ++st) {
+        if (st >= nst || 16 * st + 16 <= 64 * wave)
             continue;
-        float *orow = p.Out + o + (int64_t)i * p.ldo;
-        _Float16 *wrow = p.W + o + (int64_t)i * p.ldw;
+        const int kc = 2 * st + fkc;
+        const half8 af = *reinterpret_cast<const half8 *>(Rs + lds_chunk(frow, kc) * 16);
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
+            const int j0 = 64 * wave + 32 * b;
+            if (16 * st + 16 <= j0)
+                continue;
+            const half8 bf = *reinterpret_cast<const half8 *>(Vs + lds_chunk(j0 + frow, kc) * 16);
+            acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf, af, acc[b], 0, 0, 0);
+        }
+    }
+
+    // Epilogue: block b of this wave holds C(i, j..j+3) for
+    // i = m0 + (lane mod 32) and, in register group g,
+    // j = 64·wave + 32b + 8g + 4·(lane div 32).
+    const int i = m0 + frow;
+    if (i >= M)
+        return;
+    float *orow = p.Out + o + (int64_t)i * p.ldo;
+    _Float16 *wrow = p.W + o + (int64_t)i * p.ldw;
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int j = 64 * wave + 32 * b + 8 * g + 4 * fkc;
-                const floatx4 v = {acc[a][b][4 * g + 0], acc[a][b][4 * g + 1],
-                                   acc[a][b][4 * g + 2], acc[a][b][4 * g + 3]};
-                if (VEC && j + 4 <= s) {
-                    *reinterpret_cast<floatx4 *>(orow + j) = v;
-                    const halfx4 h = {(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
-                    *reinterpret_cast<halfx4 *>(wrow + j) = h;
-                } else {
+    for (int b = 0; b < 2; ++b) {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        if (j + e < s) {
-                            orow[j + e] = v[e];
-                            wrow[j + e] = (_Float16)v[e];
-                        }
-                }
+        for (int g = 0; g < 4; ++g) {
+            const int j = 64 * wave + 32 * b + 8 * g + 4 * fkc;
+            const floatx4 v = {acc[b][4 * g + 0], acc[b][4 * g + 1], acc[b][4 * g + 2], acc[b][4 * g + 3]};
+            if (VEC && j + 4 <= s) {
+                *reinterpret_cast<floatx4 *>(orow + j) = v;
+                const halfx4 h = {(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
+                *reinterpret_cast<halfx4 *>(wrow + j) = h;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (j + e < s) {
+                        orow[j + e] = v[e];
+                        wrow[j + e] = (_Float16)v[e];
+                    }
             }
         }
     }
