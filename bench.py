@@ -182,6 +182,32 @@ def config_sweep(hg, stream, main_gemm_ms=None, main_trmm_ms=None):
                            "us_per_entry": round(dt / ri.size * 1e6, 2), "cores": oracle.num_threads()}
             del TA, TB
         res[name] = r
+    for name, w in workloads.TRSM_WORKLOADS.items():
+        print(f"[bench] config {name} ...", file=sys.stderr, flush=True)
+        A_cm, B_cm = workloads.trsm_inputs(w)
+        Ad, Bd = torch.from_numpy(A_cm).to(dev), torch.from_numpy(B_cm).to(dev)
+        Od = torch.empty((w.m, w.n), dtype=torch.float32, device=dev)
+        work = torch.empty(hg.trsm_workspace_size(w.n, w.m, w.leaf), dtype=torch.uint8, device=dev)
+        fn = lambda: hg.trsm_lower_trans(Ad, Bd, Od, w.alpha, w.leaf, work)
+        med, mn, b2b = _time_calls(fn, 5, 20, stream)
+        tf = w.flops / (med * 1e-3) / 1e12
+        # compulsory traffic: A's lower triangle and B read once, X written once (fp32)
+        nbytes = w.n * (w.n + 1) + 2 * w.n * w.m + 4 * w.n * w.m
+        r = {"gpu_ms_median": round(med, 5), "gpu_ms_min": round(mn, 5),
+             "gpu_ms_back_to_back_mean": round(b2b, 5), "reps": 20,
+             "tflops": round(tf, 2), "pct_of_fp16_mfma_peak": round(100 * tf / PEAK_FP16_TFLOPS, 3),
+             "flops": "n^2*m", "compulsory_bytes": nbytes,
+             "note": "triangular solve X = alpha*A^-T*B (next row after the hot path); "
+                     "not part of the timed step"}
+        del Ad, Bd, Od, work
+        cols = np.array([0, w.m // 3, 2 * w.m // 3, w.m - 1], dtype=np.int64)
+        t0 = time.perf_counter()
+        oracle.trsm_lower_trans_cols(A_cm, B_cm, cols, w.alpha)
+        dt = time.perf_counter() - t0
+        r["oracle"] = {"seconds": round(dt, 4), "entries": int(cols.size * w.n),
+                       "mode": f"{cols.size} full columns",
+                       "us_per_column": round(dt / cols.size * 1e6, 1), "cores": oracle.num_threads()}
+        res[name] = r
     return res
 
 
