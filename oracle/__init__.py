@@ -11,8 +11,8 @@ rows); this module only marshals numpy arrays to it through ctypes and builds
 Pages followed (cited by title and section):
   * "Nvidia Tensor Core-MMA PTX编程入门" §4: HGEMM C = A·B, A M×K row-major,
     B K×N column-major, C M×N row-major, fp16 operands.
-  * "GPU架构与CUDA", 共享内存与分块 (masked tiled matmul) and 混合精度核函数
-    (fp16 inputs, wider accumulation).
+  * "GPU架构与CUDA", 共享内存与分块 (masked tiled matmul), 混合精度核函数
+    (fp16 inputs, wider accumulation) and 核函数融合 (matmul + bias + ReLU).
   * "异构计算中高性能TRMM与TRSM的递归算法实现" §2.1–§2.2: B <- α·Aᵀ·B with A
     lower triangular; §2.3: the triangular solve, here X = α·A⁻ᵀ·B.
 
@@ -68,6 +68,10 @@ def _load():
                                                  vp, i64, ctypes.c_int, i64, vp,
                                                  vp, vp]
             lib.oracle_hgemm_sampled.restype = None
+            lib.oracle_hgemm_bias_act.argtypes = [i64, i64, i64, f64, vp, i64, vp, i64,
+                                                  f64, vp, i64, ctypes.c_int, vp,
+                                                  ctypes.c_int, vp, i64]
+            lib.oracle_hgemm_bias_act.restype = None
             lib.oracle_trmm_lower_trans.argtypes = [i64, i64, f64, vp, i64, vp,
                                                     i64, vp, i64]
             lib.oracle_trmm_lower_trans.restype = None
@@ -143,6 +147,44 @@ def hgemm(A: np.ndarray, Bt: np.ndarray, alpha: float = 1.0, beta: float = 0.0,
     if M and N:
         lib.oracle_hgemm(M, N, K, float(alpha), _ptr(A), _ld(A), _ptr(Bt), _ld(Bt),
                          float(beta), cptr, ldc, cin_dtype, _ptr(ref), N)
+    return ref
+
+
+ACT_NONE = 0
+ACT_RELU = 1
+
+
+def hgemm_bias_act(A: np.ndarray, Bt: np.ndarray, alpha: float = 1.0, beta: float = 0.0,
+                   Cin: np.ndarray | None = None, bias: np.ndarray | None = None,
+                   act: int = ACT_NONE) -> np.ndarray:
+    """fp64 reference of act(α·A·B + β·C_in + bias), bias a float32 vector of
+    length N added to every row (None: no bias), act ACT_NONE or ACT_RELU
+    (t < 0 → +0; NaN passes through).  Layouts as in ``hgemm``."""
+    lib = _load()
+    _f16_2d(A, "A")
+    _f16_2d(Bt, "Bt")
+    M, K = A.shape
+    N, K2 = Bt.shape
+    if K2 != K:
+        raise ValueError("inner dimensions differ")
+    if act not in (ACT_NONE, ACT_RELU):
+        raise ValueError("act must be ACT_NONE or ACT_RELU")
+    bptr = None
+    if bias is not None:
+        bias = np.ascontiguousarray(bias, dtype=np.float32)
+        if bias.shape != (N,):
+            raise ValueError("bias must have shape (N,)")
+        bptr = _ptr(bias)
+    ref = np.empty((M, N), dtype=np.float64)
+    cin_dtype, cptr, ldc = F16, None, max(1, N)
+    if beta != 0.0:
+        if Cin is None or Cin.shape != (M, N) or Cin.strides[1] != Cin.itemsize:
+            raise ValueError("Cin of shape (M, N) with unit column stride needed when beta != 0")
+        cin_dtype = F16 if Cin.dtype == np.float16 else F32
+        cptr, ldc = _ptr(Cin), _ld(Cin)
+    if M and N:
+        lib.oracle_hgemm_bias_act(M, N, K, float(alpha), _ptr(A), _ld(A), _ptr(Bt), _ld(Bt),
+                                  float(beta), cptr, ldc, cin_dtype, bptr, int(act), _ptr(ref), N)
     return ref
 
 

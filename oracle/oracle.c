@@ -12,8 +12,9 @@
  *    statement, C = A·B with A M×K row-major, B K×N column-major (element
  *    (k, n) at B[k + n·K]) and C M×N row-major, all operands fp16.
  *  - "GPU架构与CUDA", section 共享内存与分块 (tiled matmul): out-of-range
- *    operands contribute nothing and only in-range outputs are written; and
- *    section 混合精度核函数: fp16 products accumulated in a wider type.
+ *    operands contribute nothing and only in-range outputs are written;
+ *    section 混合精度核函数: fp16 products accumulated in a wider type; and
+ *    section 核函数融合: matmul, bias addition and ReLU as one operation.
  *  - "异构计算中高性能TRMM与TRSM的递归算法实现", §2.1–§2.2: B <- α·Aᵀ·B for
  *    lower-triangular A; §2.3: the triangular solve, here X = α·A⁻ᵀ·B.
  *
@@ -126,6 +127,41 @@ void oracle_hgemm_sampled(int64_t K, double alpha,
         if (beta != 0.0)
             r += beta * cin_value(Cin, cin_dtype, i * ldc + j);
         ref[s] = r;
+    }
+}
+
+/* ---- HGEMM with a fused bias and activation -------------------------------
+ * "GPU架构与CUDA", section 核函数融合: a matmul followed by a bias addition and a
+ * ReLU, done as one operation.  Here, per output element
+ *   t = α·Σ_k A(i,k)·B(k,j) + β·C_in(i,j) + bias[j],   ref(i,j) = act(t)
+ * with bias a length-N vector (one value per column of C; NULL means 0),
+ * act 0 = identity and act 1 = ReLU, taken as (t < 0 ? +0 : t) so that a NaN
+ * passes through.  Same layouts and α/β conventions as oracle_hgemm.
+ */
+void oracle_hgemm_bias_act(int64_t M, int64_t N, int64_t K, double alpha,
+                           const uint16_t *A, int64_t lda,
+                           const uint16_t *B, int64_t ldb,
+                           double beta, const void *Cin, int64_t ldc, int cin_dtype,
+                           const float *bias, int act, double *ref, int64_t ldr)
+{
+    h2d_init();
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < M; ++i) {
+        for (int64_t j = 0; j < N; ++j) {
+            double acc = 0.0;
+            if (alpha != 0.0) {
+                for (int64_t k = 0; k < K; ++k)
+                    acc += g_h2d[A[i * lda + k]] * g_h2d[B[j * ldb + k]];
+            }
+            double t = alpha * acc;
+            if (beta != 0.0)
+                t += beta * cin_value(Cin, cin_dtype, i * ldc + j);
+            if (bias)
+                t += (double)bias[j];
+            if (act == 1 && t < 0.0)
+                t = 0.0;
+            ref[i * ldr + j] = t;
+        }
     }
 }
 

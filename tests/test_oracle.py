@@ -352,3 +352,56 @@ def test_trsm_cols_equals_full():
     full = oracle.trsm_lower_trans(Acm, Bcm, -1.5)
     cols = np.array([11, 0, 5, 5, 3])
     assert np.array_equal(oracle.trsm_lower_trans_cols(Acm, Bcm, cols, -1.5), full[cols])
+
+
+# ---- HGEMM with fused bias and ReLU ("GPU架构与CUDA", 核函数融合) ----
+
+def test_bias_act_matches_numpy():
+    rng = np.random.default_rng(50)
+    M, N, K = 13, 9, 21
+    A = workloads.uniform_f16(rng, (M, K))
+    Bt = workloads.uniform_f16(rng, (N, K))
+    C = workloads.uniform_f16(rng, (M, N))
+    bias = rng.uniform(-2, 2, N).astype(np.float32)
+    t = 1.5 * (A.astype(np.float64) @ Bt.astype(np.float64).T) + 0.25 * C.astype(np.float64) \
+        + bias.astype(np.float64)
+    got = oracle.hgemm_bias_act(A, Bt, 1.5, 0.25, C, bias, oracle.ACT_RELU)
+    np.testing.assert_allclose(got, np.maximum(t, 0.0), rtol=1e-13, atol=1e-13)
+    got = oracle.hgemm_bias_act(A, Bt, 1.5, 0.25, C, bias, oracle.ACT_NONE)
+    np.testing.assert_allclose(got, t, rtol=1e-13, atol=1e-13)
+
+
+def test_bias_act_brute_force_python_loops():
+    rng = np.random.default_rng(51)
+    A = workloads.integer_f16(rng, (4, 6))
+    Bt = workloads.integer_f16(rng, (5, 6))
+    bias = np.array([3.5, -7.0, 0.0, 100.0, -100.0], np.float32)
+    got = oracle.hgemm_bias_act(A, Bt, 2.0, 0.0, None, bias, oracle.ACT_RELU)
+    for i in range(4):
+        for j in range(5):
+            t = 2.0 * sum(float(A[i, k]) * float(Bt[j, k]) for k in range(6)) + float(bias[j])
+            assert got[i, j] == (0.0 if t < 0 else t)
+
+
+def test_bias_act_reduces_to_hgemm():
+    """No bias and no activation is the plain HGEMM (an independent routine)."""
+    rng = np.random.default_rng(52)
+    A = workloads.uniform_f16(rng, (17, 33))
+    Bt = workloads.uniform_f16(rng, (11, 33))
+    C = workloads.uniform_f16(rng, (17, 11)).astype(np.float32)
+    assert np.array_equal(oracle.hgemm_bias_act(A, Bt, 0.75, -1.0, C),
+                          oracle.hgemm(A, Bt, 0.75, -1.0, C))
+
+
+def test_bias_only_rows_and_relu_threshold():
+    """alpha = 0: every row is the bias (+0 plus the bias: a -0 bias gives +0);
+    ReLU zeroes exactly the negative entries, to +0, and a NaN passes
+    through."""
+    A = np.full((3, 4), np.nan, np.float16)
+    Bt = np.full((6, 4), np.nan, np.float16)
+    bias = np.array([-1.0, -0.0, 0.0, 1e-30, np.nan, 5.0], np.float32)
+    got = oracle.hgemm_bias_act(A, Bt, 0.0, 0.0, None, bias, oracle.ACT_RELU)
+    expect = np.array([0.0, 0.0, 0.0, np.float32(1e-30), np.nan, 5.0])
+    for row in got:
+        assert np.array_equal(row, expect, equal_nan=True)
+        assert not np.signbit(row[0]) and not np.signbit(row[1])

@@ -47,6 +47,12 @@ MUTANTS = {
     # TRSM: last row's term dropped from every sum
     "trsm_last_term_dropped": ("for (int64_t k = i + 1; k < n; ++k)\n                acc -= ",
                                "for (int64_t k = i + 1; k + 1 < n; ++k)\n                acc -= "),
+    # fused epilogue: bias dropped
+    "epi_bias_dropped": ("            if (bias)\n                t += (double)bias[j];\n", ""),
+    # fused epilogue: ReLU threshold inverted
+    "epi_relu_inverted": ("if (act == 1 && t < 0.0)", "if (act == 1 && t > 0.0)"),
+    # fused epilogue: bias indexed by row instead of column
+    "epi_bias_by_row": ("t += (double)bias[j];", "t += (double)bias[i % N];"),
     # fp16 decoding: subnormal scale off by one binade
     "decode_subnormal_scale": ("v = ldexp((double)frac, -24);", "v = ldexp((double)frac, -25);"),
     # fp16 decoding: exponent bias off by one
