@@ -182,6 +182,34 @@ def config_sweep(hg, stream, main_gemm_ms=None, main_trmm_ms=None):
                            "us_per_entry": round(dt / ri.size * 1e6, 2), "cores": oracle.num_threads()}
             del TA, TB
         res[name] = r
+    # Fused bias + ReLU epilogue (next row), on the 8192³ inputs with fp16 out:
+    # one launch, against the plain GEMM and the unfused sequence (GEMM, then
+    # a bias-add pass and a ReLU pass over C).
+    print("[bench] config hgemm_bias_relu_8192 ...", file=sys.stderr, flush=True)
+    w = workloads.WORKLOADS["hgemm_8192"]
+    A, Bt, _ = workloads.gemm_inputs(w)
+    Ad, Btd = torch.from_numpy(A).to(dev), torch.from_numpy(Bt).to(dev)
+    biasd = torch.from_numpy(np.random.default_rng(w.seed + 7).uniform(-1, 1, w.N)
+                             .astype(np.float32)).to(dev)
+    Cd = torch.empty((w.M, w.N), dtype=torch.float16, device=dev)
+    fused = lambda: hg.hgemm_bias_act(Ad, Btd, Cd, biasd, True)
+    plain = lambda: hg.hgemm(Ad, Btd, Cd)
+
+    def unfused():
+        hg.hgemm(Ad, Btd, Cd)
+        Cd.add_(biasd)
+        Cd.relu_()
+    tf_ms = _time_calls(fused, 20, 30, stream)
+    tp_ms = _time_calls(plain, 20, 30, stream)
+    tu_ms = _time_calls(unfused, 5, 30, stream)
+    res["hgemm_bias_relu_8192"] = {
+        "gpu_ms_median": round(tf_ms[0], 5), "gpu_ms_min": round(tf_ms[1], 5),
+        "tflops": round(w.flops / (tf_ms[0] * 1e-3) / 1e12, 2),
+        "plain_hgemm_fp16_out_ms_median": round(tp_ms[0], 5),
+        "unfused_gemm_then_bias_then_relu_ms_median": round(tu_ms[0], 5),
+        "note": "C = relu(A*B + bias), 8192^3, fp16 out, one launch; the unfused sequence adds "
+                "two passes over C (torch elementwise ops)"}
+    del Ad, Btd, Cd, biasd
     for name, w in workloads.TRSM_WORKLOADS.items():
         print(f"[bench] config {name} ...", file=sys.stderr, flush=True)
         A_cm, B_cm = workloads.trsm_inputs(w)

@@ -12,6 +12,10 @@ importing this package raises.
         float32, row-major.  Each needs unit stride along its last axis; row
         strides become lda / ldb / ldc.
 
+    hgemm_bias_act(A, Bt, C, bias=None, relu=False, alpha=1.0, beta=0.0)
+        C = act(alpha·A·B + beta·C + bias) in one launch, bias a float32
+        device vector of length N added to every row, act ReLU or none.
+
     trmm_lower_trans(A, B, Out, alpha=1.0, leaf=256)
     trmm_lower_trans_by_level(A, B, Out, alpha=1.0, leaf=256)
         Out = alpha·Aᵀ·B with A lower triangular (strict upper never read);
@@ -54,6 +58,9 @@ lib = ctypes.CDLL(LIB_PATH)
 _i64, _f32, _vp, _int = ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_int
 lib.hgemm.argtypes = [_i64, _i64, _i64, _f32, _vp, _i64, _vp, _i64, _f32, _vp, _i64, _int, _vp]
 lib.hgemm.restype = _int
+lib.hgemm_bias_act.argtypes = [_i64, _i64, _i64, _f32, _vp, _i64, _vp, _i64, _f32, _vp, _i64, _int,
+                               _vp, _int, _vp]
+lib.hgemm_bias_act.restype = _int
 lib.trmm_lower_trans.argtypes = [_i64, _i64, _f32, _vp, _i64, _vp, _i64, _vp, _i64, _int, _i64,
                                  _vp]
 lib.trmm_lower_trans.restype = _int
@@ -69,8 +76,11 @@ lib.hg_strerror.restype = ctypes.c_char_p
 lib.hg_trmm_plan.argtypes = [_i64, _i64, ctypes.POINTER(_i64), _i64]
 lib.hg_trmm_plan.restype = _i64
 
-EXPORTS = ("hgemm", "trmm_lower_trans", "hg_trmm_lower_trans_by_level", "hg_strerror",
-           "hg_trmm_plan", "trsm_lower_trans", "hg_trsm_workspace_size")
+EXPORTS = ("hgemm", "hgemm_bias_act", "trmm_lower_trans", "hg_trmm_lower_trans_by_level",
+           "hg_strerror", "hg_trmm_plan", "trsm_lower_trans", "hg_trsm_workspace_size")
+
+ACT_NONE = 0
+ACT_RELU = 1
 
 
 class HgError(RuntimeError):
@@ -124,6 +134,35 @@ def hgemm(A, Bt, C, alpha: float = 1.0, beta: float = 0.0):
                    _stream_handle(C))
     if st != 0:
         raise HgError("hgemm", st)
+    return C
+
+
+def hgemm_bias_act(A, Bt, C, bias=None, relu: bool = False, alpha: float = 1.0,
+                   beta: float = 0.0):
+    """C = act(alpha·A·B + beta·C + bias) in one launch; bias a float32 device
+    vector of length N (or None), act ReLU when `relu`.  Returns C."""
+    import torch
+    _check_matrix(A, "A", (torch.float16,))
+    _check_matrix(Bt, "Bt", (torch.float16,))
+    _check_matrix(C, "C", (torch.float16, torch.float32))
+    M, K = A.shape
+    N = Bt.shape[0]
+    if Bt.shape[1] != K or tuple(C.shape) != (M, N):
+        raise ValueError(f"shape mismatch: A {tuple(A.shape)}, Bt {tuple(Bt.shape)}, "
+                         f"C {tuple(C.shape)}")
+    bptr = None
+    if bias is not None:
+        if not (isinstance(bias, torch.Tensor) and bias.is_cuda and bias.dtype == torch.float32
+                and bias.dim() == 1 and bias.shape[0] == N and bias.is_contiguous()):
+            raise ValueError("bias must be a contiguous float32 device vector of length N")
+        bptr = bias.data_ptr() or None
+    out_dtype = HG_F16 if C.dtype == torch.float16 else HG_F32
+    st = lib.hgemm_bias_act(M, N, K, float(alpha), A.data_ptr() or None, _ld(A),
+                            Bt.data_ptr() or None, _ld(Bt), float(beta), C.data_ptr() or None,
+                            _ld(C), out_dtype, bptr, ACT_RELU if relu else ACT_NONE,
+                            _stream_handle(C))
+    if st != 0:
+        raise HgError("hgemm_bias_act", st)
     return C
 
 

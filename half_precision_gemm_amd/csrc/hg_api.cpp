@@ -93,12 +93,19 @@ const char *hg_strerror(int status)
     case -12: return "invalid argument 12";
     case -13: return "invalid argument 13";
     case -14: return "invalid argument 14";
+    case -15: return "invalid argument 15";
     default: return "unknown status";
     }
 }
 
-int hgemm(int64_t M, int64_t N, int64_t K, float alpha, const void *A, int64_t lda, const void *B,
-          int64_t ldb, float beta, void *C, int64_t ldc, int out_dtype, void *stream)
+}  // extern "C"
+
+namespace {
+
+// hgemm and hgemm_bias_act: the plain call is bias == nullptr, act == 0.
+int hgemm_impl(int64_t M, int64_t N, int64_t K, float alpha, const void *A, int64_t lda,
+               const void *B, int64_t ldb, float beta, void *C, int64_t ldc, int out_dtype,
+               const float *bias, int act, void *stream)
 {
     if (M < 0 || M > kI32Max)
         return -1;
@@ -114,6 +121,8 @@ int hgemm(int64_t M, int64_t N, int64_t K, float alpha, const void *A, int64_t l
         return -11;
     if (out_dtype != HG_F16 && out_dtype != HG_F32)
         return -12;
+    if (act != HG_ACT_NONE && act != HG_ACT_RELU)
+        return -14;
     if (M == 0 || N == 0)
         return HG_OK;
     if (C == nullptr)
@@ -121,13 +130,15 @@ int hgemm(int64_t M, int64_t N, int64_t K, float alpha, const void *A, int64_t l
     const bool out_f16 = out_dtype == HG_F16;
     const int64_t esize = out_f16 ? 2 : 4;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    const Extent ec = extent(C, M, ldc, N, esize);
+    if (bias != nullptr && overlap(ec, extent(bias, 1, N, N, 4)))
+        return -13;
     if (alpha == 0.0f || K == 0)
-        return hip_status(hg::launch_scale(C, ldc, M, N, beta, out_f16, s));
+        return hip_status(hg::launch_scale(C, ldc, M, N, beta, out_f16, s, bias, act));
     if (A == nullptr)
         return -5;
     if (B == nullptr)
         return -7;
-    const Extent ec = extent(C, M, ldc, N, esize);
     if (overlap(ec, extent(A, M, lda, K, 2)) || overlap(ec, extent(B, N, ldb, K, 2)))
         return -10;
 
@@ -142,14 +153,35 @@ int hgemm(int64_t M, int64_t N, int64_t K, float alpha, const void *A, int64_t l
     p.nbatch = 1;
     p.alpha = alpha;
     p.beta = beta;
+    p.bias = bias;
+    p.act = act;
     p.e[0] = {0, 0, 0, (int32_t)N, (int32_t)K};
     hg::LaunchOpts o{};
     o.out_f16 = out_f16;
     o.beta_read = beta != 0.0f;
     o.tri = false;
     o.vec = aligned16(A) && aligned16(B) && lda % 8 == 0 && ldb % 8 == 0;
+    o.epi = bias != nullptr || act != HG_ACT_NONE;
     o.tile = hg::choose_tile(M, N, K);
     return hip_status(hg::launch_gemm(p, o, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+int hgemm(int64_t M, int64_t N, int64_t K, float alpha, const void *A, int64_t lda, const void *B,
+          int64_t ldb, float beta, void *C, int64_t ldc, int out_dtype, void *stream)
+{
+    return hgemm_impl(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, out_dtype, nullptr,
+                      HG_ACT_NONE, stream);
+}
+
+int hgemm_bias_act(int64_t M, int64_t N, int64_t K, float alpha, const void *A, int64_t lda,
+                   const void *B, int64_t ldb, float beta, void *C, int64_t ldc, int out_dtype,
+                   const float *bias, int act, void *stream)
+{
+    return hgemm_impl(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, out_dtype, bias, act, stream);
 }
 
 int64_t hg_trmm_plan(int64_t n, int64_t leaf, int64_t *nodes, int64_t cap)

@@ -345,7 +345,7 @@ __device__ __forceinline__ bool fused_item(const GemmParams &p, int w, int G, in
     return true;
 }
 
-template <bool OUT_F16, bool BETA, bool TRI, bool KCHK, bool FUSED>
+template <bool OUT_F16, bool BETA, bool TRI, bool KCHK, bool FUSED, bool EPI>
 __global__ void __launch_bounds__(THREADS, 1)
 hgemm_fast_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int cvec)
 {
@@ -623,6 +623,15 @@ hgemm_fast_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int c
                         for (int j = 0; j < TN; ++j)
                             cin[i][j] = *reinterpret_cast<const cvec *>(crow(i) + j * FB);
                 }
+                // EPI: this lane's 4 columns of each column block, once per tile.
+                float bv[EPI ? TN : 1][4];
+                if constexpr (EPI) {
+#pragma unroll
+                    for (int j = 0; j < TN; ++j)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            bv[j][e] = p.bias ? p.bias[T.n0 + wn * WTN + j * FB + 4 * fhi + e] : -0.0f;
+                }
 #pragma unroll
                 for (int i = 0; i < TM; ++i) {
                     celt *cr = crow(i);
@@ -632,8 +641,11 @@ hgemm_fast_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int c
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
                             const float v = acc[i][j][e];
-                            r[e] = (celt)(RD ? __builtin_fmaf(alpha, v, beta * (float)cin[i % CP][j][e])
-                                             : alpha * v);
+                            float t = RD ? __builtin_fmaf(alpha, v, beta * (float)cin[i % CP][j][e])
+                                         : alpha * v;
+                            if constexpr (EPI)
+                                t = epi_apply(t, bv[j][e], p.act);
+                            r[e] = (celt)t;
                         }
                         *reinterpret_cast<cvec *>(cr + j * FB) = r;
                     }
@@ -659,13 +671,19 @@ hgemm_fast_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int c
                             if (col + e >= T.N)
                                 continue;
                             const float v = acc[i][j][e];
+                            const float b = EPI && p.bias ? p.bias[col + e] : -0.0f;
                             if (OUT_F16) {
                                 _Float16 *cp = static_cast<_Float16 *>(p.C) + off + e;
-                                *cp = (_Float16)(RD ? __builtin_fmaf(alpha, v, beta * (float)*cp)
-                                                      : alpha * v);
+                                float t = RD ? __builtin_fmaf(alpha, v, beta * (float)*cp) : alpha * v;
+                                if constexpr (EPI)
+                                    t = epi_apply(t, b, p.act);
+                                *cp = (_Float16)t;
                             } else {
                                 float *cp = static_cast<float *>(p.C) + off + e;
-                                *cp = RD ? __builtin_fmaf(alpha, v, beta * *cp) : alpha * v;
+                                float t = RD ? __builtin_fmaf(alpha, v, beta * *cp) : alpha * v;
+                                if constexpr (EPI)
+                                    t = epi_apply(t, b, p.act);
+                                *cp = t;
                             }
                         }
                     }
@@ -704,7 +722,7 @@ int cu_count()
     return cached[dev];
 }
 
-template <bool OUT_F16, bool BETA, bool TRI>
+template <bool OUT_F16, bool BETA, bool TRI, bool EPI>
 hipError_t launch(const GemmParams &p, hipStream_t stream)
 {
     int maxN = 0;
@@ -739,10 +757,10 @@ hipError_t launch(const GemmParams &p, hipStream_t stream)
     for (int b = 0; b < p.nbatch; ++b)
         kchk = kchk || p.e[b].K % BK != 0;
     if (kchk)
-        hipLaunchKernelGGL((hgemm_fast_kernel<OUT_F16, BETA, TRI, true, false>), dim3((unsigned)grid),
+        hipLaunchKernelGGL((hgemm_fast_kernel<OUT_F16, BETA, TRI, true, false, EPI>), dim3((unsigned)grid),
                            dim3(THREADS), 0, stream, p, tiles_m, tiles_n, (int)total64, cvec);
     else
-        hipLaunchKernelGGL((hgemm_fast_kernel<OUT_F16, BETA, TRI, false, false>), dim3((unsigned)grid),
+        hipLaunchKernelGGL((hgemm_fast_kernel<OUT_F16, BETA, TRI, false, false, EPI>), dim3((unsigned)grid),
                            dim3(THREADS), 0, stream, p, tiles_m, tiles_n, (int)total64, cvec);
     return hipGetLastError();
 }
@@ -763,7 +781,7 @@ hipError_t launch_trmm_fused(const GemmParams &p, hipStream_t stream)
     grid = grid / 8 * 8 > 0 ? grid / 8 * 8 : grid;
     if (grid > total64)
         grid = total64;
-    hipLaunchKernelGGL((hgemm_fast_kernel<false, true, true, false, true>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((hgemm_fast_kernel<false, true, true, false, true, false>), dim3((unsigned)grid),
                        dim3(THREADS), 0, stream, p, tiles_m, tiles_n, (int)total64, cvec);
     return hipGetLastError();
 }
@@ -802,7 +820,7 @@ bool trmm_fused_ok(const GemmParams &p)
 
 bool fast_path_ok(const GemmParams &p, const LaunchOpts &o)
 {
-    if (!o.vec || (o.tri && (o.out_f16 || o.beta_read)))
+    if (!o.vec || (o.tri && (o.out_f16 || o.beta_read || o.epi)))
         return false;
     // 32-bit buffer offsets: every tile's byte range must stay below 2^31.
     if (p.lda > (1 << 21) || p.ldb > (1 << 21))
@@ -816,12 +834,19 @@ bool fast_path_ok(const GemmParams &p, const LaunchOpts &o)
 hipError_t launch_gemm_fast(const GemmParams &p, const LaunchOpts &o, hipStream_t stream)
 {
     if (o.tri)
-        return launch<false, false, true>(p, stream);     // TRMM leaves: fp32, written once
+        return launch<false, false, true, false>(p, stream);     // TRMM leaves: fp32, written once
+    if (o.epi) {
+        if (o.out_f16)
+            return o.beta_read ? launch<true, true, false, true>(p, stream)
+                               : launch<true, false, false, true>(p, stream);
+        return o.beta_read ? launch<false, true, false, true>(p, stream)
+                           : launch<false, false, false, true>(p, stream);
+    }
     if (o.out_f16)
-        return o.beta_read ? launch<true, true, false>(p, stream)
-                           : launch<true, false, false>(p, stream);
-    return o.beta_read ? launch<false, true, false>(p, stream)
-                       : launch<false, false, false>(p, stream);
+        return o.beta_read ? launch<true, true, false, false>(p, stream)
+                           : launch<true, false, false, false>(p, stream);
+    return o.beta_read ? launch<false, true, false, false>(p, stream)
+                       : launch<false, false, false, false>(p, stream);
 }
 
 }  // namespace hg

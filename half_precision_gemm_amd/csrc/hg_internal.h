@@ -31,8 +31,19 @@ struct GemmParams {
     int32_t nbatch;
     float alpha, beta;
     int32_t leaf;    // recursive TRMM in one launch: the recursion's leaf size
+    const float *bias;   // fused epilogue: per-column bias (nullptr: none)
+    int32_t act;         // fused epilogue: 0 identity, 1 ReLU
     BatchEntry e[kMaxBatch];
 };
+
+// Fused epilogue of hgemm_bias_act: t + bias, then the activation.  A missing
+// bias is passed as -0, which leaves every t unchanged (also ±0); ReLU maps
+// t < 0 to +0 and lets NaN through.
+__device__ __forceinline__ float epi_apply(float t, float bias, int act)
+{
+    t += bias;
+    return (act == 1 && t < 0.0f) ? 0.0f : t;
+}
 
 // Kernel families the launcher can pick.
 enum class Tile { Big, Mid, Small };
@@ -42,6 +53,7 @@ struct LaunchOpts {
     bool beta_read;   // beta != 0: read C
     bool tri;         // TRMM leaf: B operand element (j, k) is zero for k < j
     bool vec;         // 16-byte aligned operands: vector loads
+    bool epi;         // fused bias / activation (p.bias, p.act)
     Tile tile;
 };
 
@@ -111,9 +123,12 @@ hipError_t launch_trsm_inv(const TrsmInvParams &p, hipStream_t stream);
 // ldo % 4 == 0, ldw % 4 == 0 (vector loads and stores).
 hipError_t launch_trsm_leaf(const TrsmLeafParams &p, bool vec, hipStream_t stream);
 
-// C = beta·C over an M×N window (beta == 0 writes zeros without reading).
+// C = beta·C over an M×N window (beta == 0 writes zeros without reading);
+// with `bias` or `act`, C = act(beta·C + bias[j]) (the alpha = 0 / K = 0
+// case of the fused epilogue).
 hipError_t launch_scale(void *C, int64_t ldc, int64_t M, int64_t N, float beta,
-                        bool out_f16, hipStream_t stream);
+                        bool out_f16, hipStream_t stream, const float *bias = nullptr,
+                        int act = 0);
 
 // Tile family the launcher would choose for a single M×N GEMM.
 Tile choose_tile(int64_t M, int64_t N, int64_t K);

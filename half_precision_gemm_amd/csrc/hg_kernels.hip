@@ -257,6 +257,7 @@ hgemm_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int cvec)
     const float beta = p.beta;
     const int64_t ldc = p.ldc;
     const bool full = full_m && full_n;
+    const bool epi = p.bias != nullptr || p.act != 0;
 #pragma unroll
     for (int i = 0; i < CF::TM; ++i) {
         const int row = m0 + wm * CF::WTM + i * 32 + frow;
@@ -282,6 +283,11 @@ hgemm_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int cvec)
                             for (int e = 0; e < 4; ++e)
                                 r[e] = alpha * v[e];
                         }
+                        if (epi) {
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                r[e] = epi_apply(r[e], p.bias ? p.bias[col + e] : -0.0f, p.act);
+                        }
                         halfx4 h;
 #pragma unroll
                         for (int e = 0; e < 4; ++e)
@@ -300,21 +306,31 @@ hgemm_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int cvec)
                             for (int e = 0; e < 4; ++e)
                                 r[e] = alpha * v[e];
                         }
+                        if (epi) {
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                r[e] = epi_apply(r[e], p.bias ? p.bias[col + e] : -0.0f, p.act);
+                        }
                         *cp = r;
                     }
                 } else if (row < M) {
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         if (col + e < N) {
+                            const float b = epi && p.bias ? p.bias[col + e] : -0.0f;
                             if (OUT_F16) {
                                 _Float16 *cp = static_cast<_Float16 *>(p.C) + off + e;
-                                const float r = BETA ? __builtin_fmaf(alpha, v[e], beta * (float)*cp)
-                                                     : alpha * v[e];
+                                float r = BETA ? __builtin_fmaf(alpha, v[e], beta * (float)*cp)
+                                               : alpha * v[e];
+                                if (epi)
+                                    r = epi_apply(r, b, p.act);
                                 *cp = (_Float16)r;
                             } else {
                                 float *cp = static_cast<float *>(p.C) + off + e;
-                                const float r = BETA ? __builtin_fmaf(alpha, v[e], beta * *cp)
-                                                     : alpha * v[e];
+                                float r = BETA ? __builtin_fmaf(alpha, v[e], beta * *cp)
+                                               : alpha * v[e];
+                                if (epi)
+                                    r = epi_apply(r, b, p.act);
                                 *cp = r;
                             }
                         }
@@ -328,18 +344,25 @@ hgemm_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int cvec)
 // C = beta·C over the M×N window; beta == 0 writes zeros without reading C.
 template <bool OUT_F16>
 __global__ void __launch_bounds__(256) scale_kernel(void *C, int64_t ldc, int64_t M, int64_t N,
-                                                    float beta)
+                                                    float beta, const float *bias, int act)
 {
     const int64_t total = M * N;
+    const bool epi = bias != nullptr || act != 0;
     for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
          idx += (int64_t)gridDim.x * blockDim.x) {
         const int64_t i = idx / N, j = idx - i * N;
         if (OUT_F16) {
             _Float16 *cp = static_cast<_Float16 *>(C) + i * ldc + j;
-            *cp = beta == 0.0f ? (_Float16)0.0f : (_Float16)(beta * (float)*cp);
+            float t = beta == 0.0f ? 0.0f : beta * (float)*cp;
+            if (epi)
+                t = epi_apply(t, bias ? bias[j] : -0.0f, act);
+            *cp = (_Float16)t;
         } else {
             float *cp = static_cast<float *>(C) + i * ldc + j;
-            *cp = beta == 0.0f ? 0.0f : beta * *cp;
+            float t = beta == 0.0f ? 0.0f : beta * *cp;
+            if (epi)
+                t = epi_apply(t, bias ? bias[j] : -0.0f, act);
+            *cp = t;
         }
     }
 }
@@ -427,7 +450,7 @@ hipError_t launch_gemm(const GemmParams &p, const LaunchOpts &o, hipStream_t str
 }
 
 hipError_t launch_scale(void *C, int64_t ldc, int64_t M, int64_t N, float beta, bool out_f16,
-                        hipStream_t stream)
+                        hipStream_t stream, const float *bias, int act)
 {
     const int64_t total = M * N;
     int64_t blocks = (total + 255) / 256;
@@ -437,10 +460,10 @@ hipError_t launch_scale(void *C, int64_t ldc, int64_t M, int64_t N, float beta, 
         return hipSuccess;
     if (out_f16)
         hipLaunchKernelGGL(scale_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream, C,
-                           ldc, M, N, beta);
+                           ldc, M, N, beta, bias, act);
     else
         hipLaunchKernelGGL(scale_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream, C,
-                           ldc, M, N, beta);
+                           ldc, M, N, beta, bias, act);
     return hipGetLastError();
 }
 

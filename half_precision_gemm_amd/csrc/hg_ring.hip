@@ -78,7 +78,7 @@ __device__ __forceinline__ void ring_map(int wg, int total, int tiles_m, int til
     tn = r / gsz;
 }
 
-template <int BM, int BN, bool OUT_F16, bool BETA, bool KCHK>
+template <int BM, int BN, bool OUT_F16, bool BETA, bool KCHK, bool EPI>
 __global__ void __launch_bounds__(THREADS, 1)
 hgemm_ring_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int cvec)
 {
@@ -215,7 +215,11 @@ hgemm_ring_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int c
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const float v = acc[i][j][e];
-                    r[e] = (celt)(BETA ? __builtin_fmaf(alpha, v, beta * (float)cin[j][e]) : alpha * v);
+                    float t = BETA ? __builtin_fmaf(alpha, v, beta * (float)cin[j][e]) : alpha * v;
+                    if constexpr (EPI)
+                        t = epi_apply(t, p.bias ? p.bias[n0 + wn * WTN + j * 16 + 4 * fhi + e] : -0.0f,
+                                      p.act);
+                    r[e] = (celt)t;
                 }
                 *reinterpret_cast<cvec_t *>(cr + j * 16) = r;
             }
@@ -235,14 +239,17 @@ hgemm_ring_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int c
                         continue;
                     celt *cp = Cb + (int64_t)row * ldc + col + e;
                     const float v = acc[i][j][e];
-                    *cp = (celt)(BETA ? __builtin_fmaf(alpha, v, beta * (float)*cp) : alpha * v);
+                    float t = BETA ? __builtin_fmaf(alpha, v, beta * (float)*cp) : alpha * v;
+                    if constexpr (EPI)
+                        t = epi_apply(t, p.bias ? p.bias[col + e] : -0.0f, p.act);
+                    *cp = (celt)t;
                 }
             }
         }
     }
 }
 
-template <int BM, int BN, bool OUT_F16, bool BETA>
+template <int BM, int BN, bool OUT_F16, bool BETA, bool EPI>
 hipError_t launch_ring_cfg(const GemmParams &p, hipStream_t stream)
 {
     int maxN = 0;
@@ -263,22 +270,28 @@ hipError_t launch_ring_cfg(const GemmParams &p, hipStream_t stream)
     for (int b = 0; b < p.nbatch; ++b)
         cvec = cvec && (p.e[b].c_off % 4 == 0);
     if (kchk)
-        hipLaunchKernelGGL((hgemm_ring_kernel<BM, BN, OUT_F16, BETA, true>), dim3((unsigned)total64),
+        hipLaunchKernelGGL((hgemm_ring_kernel<BM, BN, OUT_F16, BETA, true, EPI>), dim3((unsigned)total64),
                            dim3(THREADS), 0, stream, p, tiles_m, tiles_n, (int)total64, cvec);
     else
-        hipLaunchKernelGGL((hgemm_ring_kernel<BM, BN, OUT_F16, BETA, false>), dim3((unsigned)total64),
+        hipLaunchKernelGGL((hgemm_ring_kernel<BM, BN, OUT_F16, BETA, false, EPI>), dim3((unsigned)total64),
                            dim3(THREADS), 0, stream, p, tiles_m, tiles_n, (int)total64, cvec);
     return hipGetLastError();
+}
+
+template <int BM, int BN, bool EPI>
+hipError_t launch_ring_epi(const GemmParams &p, const LaunchOpts &o, hipStream_t s)
+{
+    if (o.out_f16)
+        return o.beta_read ? launch_ring_cfg<BM, BN, true, true, EPI>(p, s)
+                           : launch_ring_cfg<BM, BN, true, false, EPI>(p, s);
+    return o.beta_read ? launch_ring_cfg<BM, BN, false, true, EPI>(p, s)
+                       : launch_ring_cfg<BM, BN, false, false, EPI>(p, s);
 }
 
 template <int BM, int BN>
 hipError_t launch_ring_tile(const GemmParams &p, const LaunchOpts &o, hipStream_t s)
 {
-    if (o.out_f16)
-        return o.beta_read ? launch_ring_cfg<BM, BN, true, true>(p, s)
-                           : launch_ring_cfg<BM, BN, true, false>(p, s);
-    return o.beta_read ? launch_ring_cfg<BM, BN, false, true>(p, s)
-                       : launch_ring_cfg<BM, BN, false, false>(p, s);
+    return o.epi ? launch_ring_epi<BM, BN, true>(p, o, s) : launch_ring_epi<BM, BN, false>(p, o, s);
 }
 
 }  // namespace

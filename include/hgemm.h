@@ -50,6 +50,10 @@ extern "C" {
 #define HG_F16 0
 #define HG_F32 1
 
+/* Activation of hgemm_bias_act. */
+#define HG_ACT_NONE 0
+#define HG_ACT_RELU 1
+
 #define HG_OK 0
 #define HG_ERR_HIP_BASE 1000
 
@@ -86,6 +90,30 @@ int hgemm(int64_t M, int64_t N, int64_t K, float alpha,
           const void *B, int64_t ldb,
           float beta, void *C, int64_t ldc,
           int out_dtype, void *stream);
+
+/*
+ * hgemm_bias_act — C = act(alpha·A·B + beta·C + bias), the matmul, bias
+ * addition and activation fused into one launch as in "GPU架构与CUDA",
+ * section 核函数融合: the sum and the biased value never leave the chip; the
+ * only memory traffic beyond hgemm's is the bias vector.
+ *
+ *  1–12, 15      : as hgemm (13 → 15: stream).
+ * 13 bias        : DEVICE pointer to N fp32 values, bias[j] added to every
+ *                  element of column j; NULL adds nothing.  Must not overlap
+ *                  C (error -13).
+ * 14 act         : HG_ACT_NONE, or HG_ACT_RELU: t < 0 becomes +0, NaN passes
+ *                  through; anything else is rejected (-14).
+ *
+ * Per element, in fp32: t = alpha·acc + beta·C_in (as hgemm), t = t + bias[j],
+ * t = act(t), then the conversion to out_dtype.  alpha == 0 or K == 0 reads
+ * neither A nor B: C = act(beta·C + bias).  With bias NULL and HG_ACT_NONE the
+ * result is hgemm's, bit for bit.
+ */
+int hgemm_bias_act(int64_t M, int64_t N, int64_t K, float alpha,
+                   const void *A, int64_t lda,
+                   const void *B, int64_t ldb,
+                   float beta, void *C, int64_t ldc,
+                   int out_dtype, const float *bias, int act, void *stream);
 
 /*
  * trmm_lower_trans — Out = alpha·Aᵀ·B, A lower triangular.

@@ -30,8 +30,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == ["hg_strerror", "hg_trmm_lower_trans_by_level", "hg_trmm_plan",
-                                    "hg_trsm_workspace_size", "hgemm", "trmm_lower_trans",
-                                    "trsm_lower_trans"]
+                                    "hg_trsm_workspace_size", "hgemm", "hgemm_bias_act",
+                                    "trmm_lower_trans", "trsm_lower_trans"]
 
 
 def test_library_exports_every_declared_symbol(hg):
@@ -64,6 +64,23 @@ def gemm(lib, M=4, N=4, K=4, alpha=1.0, A=P, lda=None, B=Q, ldb=None, beta=0.0, 
 ])
 def test_hgemm_argument_errors(lib, kw, code):
     assert gemm(lib, **kw) == code
+
+
+def bias_act(lib, M=4, N=4, K=4, A=P, B=Q, C=R, bias=None, act=1, dt=1):
+    return lib.hgemm_bias_act(M, N, K, 1.0, A, max(1, K), B, max(1, K), 0.0, C, max(1, N), dt,
+                              bias, act, None)
+
+
+def test_hgemm_bias_act_argument_errors(lib):
+    assert bias_act(lib, act=2) == -14
+    assert bias_act(lib, act=-1) == -14
+    assert bias_act(lib, M=-1) == -1
+    assert bias_act(lib, dt=5) == -12
+    assert bias_act(lib, C=None) == -10
+    assert bias_act(lib, A=None) == -5
+    assert bias_act(lib, bias=R + 8) == -13          # bias inside C
+    assert bias_act(lib, C=P + 8) == -10             # C overlaps A
+    assert bias_act(lib, M=0, A=None, B=None, C=None) == 0
 
 
 def test_hgemm_first_bad_argument_wins(lib):
