@@ -68,6 +68,14 @@ def _load():
                                                  vp, i64, ctypes.c_int, i64, vp,
                                                  vp, vp]
             lib.oracle_hgemm_sampled.restype = None
+            lib.oracle_bf16_to_double.argtypes = [ctypes.c_uint16]
+            lib.oracle_bf16_to_double.restype = f64
+            lib.oracle_gemm_bf16.argtypes = [i64, i64, i64, f64, vp, i64, vp, i64,
+                                             f64, vp, i64, ctypes.c_int, vp, i64]
+            lib.oracle_gemm_bf16.restype = None
+            lib.oracle_gemm_bf16_sampled.argtypes = [i64, f64, vp, i64, vp, i64, i64,
+                                                     vp, vp, vp]
+            lib.oracle_gemm_bf16_sampled.restype = None
             lib.oracle_hgemm_bias_act.argtypes = [i64, i64, i64, f64, vp, i64, vp, i64,
                                                   f64, vp, i64, ctypes.c_int, vp,
                                                   ctypes.c_int, vp, i64]
@@ -152,6 +160,70 @@ def hgemm(A: np.ndarray, Bt: np.ndarray, alpha: float = 1.0, beta: float = 0.0,
 
 ACT_NONE = 0
 ACT_RELU = 1
+BF16 = 2
+
+
+def bf16_to_double(bits: int) -> float:
+    """Decode one bfloat16 bit pattern (the oracle's own decoder)."""
+    return _load().oracle_bf16_to_double(bits)
+
+
+def _bf16_2d(x: np.ndarray, name: str) -> np.ndarray:
+    if x.dtype != np.uint16 or x.ndim != 2:
+        raise TypeError(f"{name} must be a 2-D uint16 array of bf16 bit patterns")
+    if x.size and x.shape[1] > 1 and x.strides[1] != 2:
+        raise ValueError(f"{name} must have unit stride along its last axis")
+    return x
+
+
+def gemm_bf16(A: np.ndarray, Bt: np.ndarray, alpha: float = 1.0, beta: float = 0.0,
+              Cin: np.ndarray | None = None, cin_bf16: bool = False) -> np.ndarray:
+    """fp64 reference of α·A·B + β·C_in with bf16 operands.
+
+    ``A`` (M, K) and ``Bt`` (N, K) are uint16 arrays of bf16 bit patterns in
+    the layouts of ``hgemm``; ``Cin`` (M, N) is float32, or bf16 bit patterns
+    (uint16) when ``cin_bf16``.  Returns the (M, N) fp64 result.
+    """
+    lib = _load()
+    _bf16_2d(A, "A")
+    _bf16_2d(Bt, "Bt")
+    M, K = A.shape
+    N, K2 = Bt.shape
+    if K2 != K:
+        raise ValueError("inner dimensions differ")
+    ref = np.empty((M, N), dtype=np.float64)
+    cin_dtype, cptr, ldc = F32, None, max(1, N)
+    if beta != 0.0:
+        if Cin is None or Cin.shape != (M, N) or Cin.strides[1] != Cin.itemsize:
+            raise ValueError("Cin of shape (M, N) with unit column stride needed when beta != 0")
+        if cin_bf16:
+            if Cin.dtype != np.uint16:
+                raise TypeError("bf16 Cin must be uint16 bit patterns")
+            cin_dtype = BF16
+        elif Cin.dtype != np.float32:
+            raise TypeError("Cin must be float32 (or bf16 bit patterns with cin_bf16)")
+        cptr, ldc = _ptr(Cin), _ld(Cin)
+    if M and N:
+        lib.oracle_gemm_bf16(M, N, K, float(alpha), _ptr(A), _ld(A), _ptr(Bt), _ld(Bt),
+                             float(beta), cptr, ldc, cin_dtype, _ptr(ref), N)
+    return ref
+
+
+def gemm_bf16_sampled(A: np.ndarray, Bt: np.ndarray, rows: np.ndarray, cols: np.ndarray,
+                      alpha: float = 1.0) -> np.ndarray:
+    """``gemm_bf16`` (β = 0) at entries (rows[s], cols[s])."""
+    lib = _load()
+    _bf16_2d(A, "A")
+    _bf16_2d(Bt, "Bt")
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    cols = np.ascontiguousarray(cols, dtype=np.int64)
+    if rows.size and (rows.min() < 0 or rows.max() >= A.shape[0] or
+                      cols.min() < 0 or cols.max() >= Bt.shape[0]):
+        raise IndexError("sample index out of range")
+    ref = np.empty(rows.shape, dtype=np.float64)
+    lib.oracle_gemm_bf16_sampled(A.shape[1], float(alpha), _ptr(A), _ld(A), _ptr(Bt), _ld(Bt),
+                                 rows.size, _ptr(rows), _ptr(cols), _ptr(ref))
+    return ref
 
 
 def hgemm_bias_act(A: np.ndarray, Bt: np.ndarray, alpha: float = 1.0, beta: float = 0.0,

@@ -53,6 +53,28 @@ double oracle_half_to_double(uint16_t h)
     return sign ? -v : v;
 }
 
+/* ---- bfloat16 decoding, from the format definition --------------------------
+ * 1 sign bit, 8 exponent bits (bias 127), 7 fraction bits (the upper half of an
+ * IEEE binary32).
+ *   exponent 0        : subnormal, value = fraction · 2^-133
+ *   exponent 1..254   : normal,    value = (128 + fraction) · 2^(exponent-134)
+ *   exponent 255      : infinity (fraction 0) or NaN
+ */
+double oracle_bf16_to_double(uint16_t h)
+{
+    const int sign = (h >> 15) & 1;
+    const int expo = (h >> 7) & 0xff;
+    const int frac = h & 0x7f;
+    double v;
+    if (expo == 0)
+        v = ldexp((double)frac, -133);
+    else if (expo == 255)
+        v = frac ? NAN : INFINITY;
+    else
+        v = ldexp((double)(128 + frac), expo - 134);
+    return sign ? -v : v;
+}
+
 /* Decoding every pattern once keeps the triple loops below affordable; each
  * entry is exactly oracle_half_to_double of its index. */
 static double g_h2d[65536];
@@ -67,10 +89,25 @@ static void h2d_init(void)
     g_h2d_ready = 1;
 }
 
+static double g_b2d[65536];
+static int g_b2d_ready = 0;
+
+static void b2d_init(void)
+{
+    if (g_b2d_ready)
+        return;
+    for (int i = 0; i < 65536; ++i)
+        g_b2d[i] = oracle_bf16_to_double((uint16_t)i);
+    g_b2d_ready = 1;
+}
+
+/* cin_dtype: 0 fp16, 1 fp32, 2 bf16 */
 static double cin_value(const void *Cin, int cin_dtype, int64_t idx)
 {
     if (cin_dtype == 0)
         return g_h2d[((const uint16_t *)Cin)[idx]];
+    if (cin_dtype == 2)
+        return oracle_bf16_to_double(((const uint16_t *)Cin)[idx]);
     return (double)((const float *)Cin)[idx];
 }
 
@@ -127,6 +164,53 @@ void oracle_hgemm_sampled(int64_t K, double alpha,
         if (beta != 0.0)
             r += beta * cin_value(Cin, cin_dtype, i * ldc + j);
         ref[s] = r;
+    }
+}
+
+/* ---- GEMM on bf16 operands --------------------------------------------------
+ * "GPU架构与CUDA", section 混合精度核函数: the products in a lower-precision type,
+ * the sum in a wider one.  The same definition as oracle_hgemm with A and B
+ * holding bf16 bit patterns: ref = α·Σ_k A(i,k)·B(k,j) + β·C_in(i,j).
+ */
+void oracle_gemm_bf16(int64_t M, int64_t N, int64_t K, double alpha,
+                      const uint16_t *A, int64_t lda,
+                      const uint16_t *B, int64_t ldb,
+                      double beta, const void *Cin, int64_t ldc, int cin_dtype,
+                      double *ref, int64_t ldr)
+{
+    h2d_init();
+    b2d_init();
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < M; ++i) {
+        for (int64_t j = 0; j < N; ++j) {
+            double acc = 0.0;
+            if (alpha != 0.0) {
+                for (int64_t k = 0; k < K; ++k)
+                    acc += g_b2d[A[i * lda + k]] * g_b2d[B[j * ldb + k]];
+            }
+            double r = alpha * acc;
+            if (beta != 0.0)
+                r += beta * cin_value(Cin, cin_dtype, i * ldc + j);
+            ref[i * ldr + j] = r;
+        }
+    }
+}
+
+/* The bf16 definition at the listed (rows[s], cols[s]) only. */
+void oracle_gemm_bf16_sampled(int64_t K, double alpha,
+                              const uint16_t *A, int64_t lda,
+                              const uint16_t *B, int64_t ldb,
+                              int64_t nsamp, const int64_t *rows,
+                              const int64_t *cols, double *ref)
+{
+    b2d_init();
+#pragma omp parallel for schedule(dynamic, 8)
+    for (int64_t s = 0; s < nsamp; ++s) {
+        const int64_t i = rows[s], j = cols[s];
+        double acc = 0.0;
+        for (int64_t k = 0; k < K; ++k)
+            acc += g_b2d[A[i * lda + k]] * g_b2d[B[j * ldb + k]];
+        ref[s] = alpha * acc;
     }
 }
 

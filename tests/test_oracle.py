@@ -405,3 +405,53 @@ def test_bias_only_rows_and_relu_threshold():
     for row in got:
         assert np.array_equal(row, expect, equal_nan=True)
         assert not np.signbit(row[0]) and not np.signbit(row[1])
+
+
+# ---- GEMM on bf16 operands ("GPU架构与CUDA", 混合精度核函数) ----
+
+def _bf16_values(bits):
+    """numpy's reading of bf16 bit patterns: the upper half of a float32."""
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def test_bf16_decode_matches_numpy_for_every_pattern():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = _bf16_values(bits)
+    got = np.array([oracle.bf16_to_double(int(b)) for b in bits])
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 1), (7, 5, 33), (16, 24, 64)])
+def test_gemm_bf16_matches_numpy(M, N, K):
+    rng = np.random.default_rng(M * N + K)
+    A = workloads.uniform_bf16(rng, (M, K))
+    Bt = workloads.uniform_bf16(rng, (N, K))
+    C32 = rng.uniform(-1, 1, (M, N)).astype(np.float32)
+    C16 = workloads.uniform_bf16(rng, (M, N))
+    prod = _bf16_values(A) @ _bf16_values(Bt).T
+    np.testing.assert_allclose(oracle.gemm_bf16(A, Bt, 1.5, 0.5, C32),
+                               1.5 * prod + 0.5 * C32.astype(np.float64), rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(oracle.gemm_bf16(A, Bt, -1.0, 2.0, C16, cin_bf16=True),
+                               -prod + 2.0 * _bf16_values(C16), rtol=1e-13, atol=1e-13)
+
+
+def test_gemm_bf16_equals_fp16_routine_on_common_values():
+    """Integers in [-4, 4] are exact in both formats: the bf16 routine and the
+    fp16 routine (independent decoders and loops) agree exactly."""
+    rng = np.random.default_rng(60)
+    A16 = workloads.integer_f16(rng, (20, 50))
+    B16 = workloads.integer_f16(rng, (15, 50))
+    Abf = workloads.to_bf16_bits(A16.astype(np.float32))
+    Bbf = workloads.to_bf16_bits(B16.astype(np.float32))
+    assert np.array_equal(oracle.gemm_bf16(Abf, Bbf, 2.0), oracle.hgemm(A16, B16, 2.0))
+
+
+def test_gemm_bf16_sampled_equals_full():
+    rng = np.random.default_rng(61)
+    A = workloads.uniform_bf16(rng, (40, 70))
+    Bt = workloads.uniform_bf16(rng, (30, 70))
+    full = oracle.gemm_bf16(A, Bt, 0.75)
+    ri, cj = workloads.sample_indices(2, 40, 30, 64)
+    assert np.array_equal(oracle.gemm_bf16_sampled(A, Bt, ri, cj, 0.75), full[ri, cj])

@@ -53,6 +53,13 @@ MUTANTS = {
     "epi_relu_inverted": ("if (act == 1 && t < 0.0)", "if (act == 1 && t > 0.0)"),
     # fused epilogue: bias indexed by row instead of column
     "epi_bias_by_row": ("t += (double)bias[j];", "t += (double)bias[i % N];"),
+    # bf16 decoding: exponent bias off by one
+    "bf16_decode_bias": ("v = ldexp((double)(128 + frac), expo - 134);", "v = ldexp((double)(128 + frac), expo - 133);"),
+    # bf16 decoding: fraction field one bit short
+    "bf16_decode_frac": ("const int frac = h & 0x7f;", "const int frac = h & 0x3f;"),
+    # bf16 GEMM: B read at reversed k (a misindexed operand)
+    "bf16_gemm_B_k_reversed": ("acc += g_b2d[A[i * lda + k]] * g_b2d[B[j * ldb + k]];",
+                               "acc += g_b2d[A[i * lda + k]] * g_b2d[B[j * ldb + (K - 1 - k)]];"),
     # fp16 decoding: subnormal scale off by one binade
     "decode_subnormal_scale": ("v = ldexp((double)frac, -24);", "v = ldexp((double)frac, -25);"),
     # fp16 decoding: exponent bias off by one

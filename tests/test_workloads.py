@@ -42,3 +42,19 @@ def test_sample_indices_include_corners():
     ri, cj = workloads.sample_indices(3, 8192, 8192)
     assert ri.size == 1024
     assert set(zip(ri[-4:].tolist(), cj[-4:].tolist())) == {(0, 0), (0, 8191), (8191, 0), (8191, 8191)}
+
+
+def test_bf16_rounding_matches_torch():
+    """The generator's bf16 rounding (nearest even on the dropped bits) agrees
+    with torch's float32 -> bfloat16 conversion, ties and specials included."""
+    import torch
+    rng = np.random.default_rng(1)
+    x = np.concatenate([rng.uniform(-3, 3, 20000).astype(np.float32),
+                        np.array([1.0, 1 + 2 ** -8, 1 + 3 * 2 ** -8, -(1 + 2 ** -8), 0.0, -0.0,
+                                  np.inf, -np.inf, 3e38, 1e-40], np.float32)])
+    ours = workloads.to_bf16_bits(x)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, ref)
+    assert workloads.to_bf16_bits(np.array([1 + 2 ** -8], np.float32))[0] == 0x3F80   # tie to even
+    nanbits = workloads.to_bf16_bits(np.array([np.nan], np.float32))[0]
+    assert (nanbits & 0x7F80) == 0x7F80 and (nanbits & 0x7F) != 0

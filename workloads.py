@@ -100,6 +100,21 @@ def uniform_f16(rng: np.random.Generator, shape, lo: float = -1.0, hi: float = 1
     return rng.uniform(lo, hi, shape).astype(np.float16)
 
 
+def to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round values to bfloat16 (via float32, round to nearest even on the
+    dropped 16 bits; NaN kept quiet) and return the bit patterns as uint16."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    nan = (u & 0x7FFFFFFF) > 0x7F800000
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) & 0xFFFF
+    r = np.where(nan, (u >> 16) | 0x40, r)
+    return r.astype(np.uint16)
+
+
+def uniform_bf16(rng: np.random.Generator, shape, lo: float = -1.0, hi: float = 1.0) -> np.ndarray:
+    """uniform[lo, hi) in float64, rounded to bf16; returns bit patterns (uint16)."""
+    return to_bf16_bits(rng.uniform(lo, hi, shape))
+
+
 def integer_f16(rng: np.random.Generator, shape, lo: int = -4, hi: int = 4) -> np.ndarray:
     """Integers drawn uniformly from [lo, hi], stored as fp16 (exact)."""
     return rng.integers(lo, hi + 1, size=shape).astype(np.float16)
