@@ -210,6 +210,23 @@ def config_sweep(hg, stream, main_gemm_ms=None, main_trmm_ms=None):
         "note": "C = relu(A*B + bias), 8192^3, fp16 out, one launch; the unfused sequence adds "
                 "two passes over C (torch elementwise ops)"}
     del Ad, Btd, Cd, biasd
+    # bf16 operands (next row): the 8192³ shape, values drawn as the HGEMM
+    # workload's and rounded to bf16, fp32 C.
+    print("[bench] config hgemm_bf16_8192 ...", file=sys.stderr, flush=True)
+    rng = np.random.default_rng(w.seed)
+    Ab = workloads.uniform_bf16(rng, (w.M, w.K))
+    Bb = workloads.uniform_bf16(rng, (w.N, w.K))
+    Ad = torch.from_numpy(Ab.view(np.int16)).to(dev).view(torch.bfloat16)
+    Btd = torch.from_numpy(Bb.view(np.int16)).to(dev).view(torch.bfloat16)
+    Cd = torch.empty((w.M, w.N), dtype=torch.float32, device=dev)
+    tb = _time_calls(lambda: hg.hgemm_bf16(Ad, Btd, Cd), 20, 30, stream)
+    tfb = w.flops / (tb[0] * 1e-3) / 1e12
+    res["hgemm_bf16_8192"] = {
+        "gpu_ms_median": round(tb[0], 5), "gpu_ms_min": round(tb[1], 5), "tflops": round(tfb, 2),
+        "pct_of_bf16_mfma_peak": round(100 * tfb / PEAK_FP16_TFLOPS, 3),
+        "note": "bf16 A, B (v_mfma_f32_16x16x32_bf16), fp32 accumulation and C; dense bf16 peak "
+                "equals the fp16 one"}
+    del Ad, Btd, Cd, Ab, Bb
     for name, w in workloads.TRSM_WORKLOADS.items():
         print(f"[bench] config {name} ...", file=sys.stderr, flush=True)
         A_cm, B_cm = workloads.trsm_inputs(w)

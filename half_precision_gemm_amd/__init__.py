@@ -12,6 +12,9 @@ importing this package raises.
         float32, row-major.  Each needs unit stride along its last axis; row
         strides become lda / ldb / ldc.
 
+    hgemm_bf16(A, Bt, C, alpha=1.0, beta=0.0)
+        hgemm with bfloat16 A and Bt; C bfloat16 or float32.
+
     hgemm_bias_act(A, Bt, C, bias=None, relu=False, alpha=1.0, beta=0.0)
         C = act(alpha·A·B + beta·C + bias) in one launch, bias a float32
         device vector of length N added to every row, act ReLU or none.
@@ -41,6 +44,7 @@ LIB_PATH = os.path.join(_PKG, "libhgemm.so")
 
 HG_F16 = 0
 HG_F32 = 1
+HG_BF16 = 2
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
@@ -61,6 +65,8 @@ lib.hgemm.restype = _int
 lib.hgemm_bias_act.argtypes = [_i64, _i64, _i64, _f32, _vp, _i64, _vp, _i64, _f32, _vp, _i64, _int,
                                _vp, _int, _vp]
 lib.hgemm_bias_act.restype = _int
+lib.hgemm_bf16.argtypes = lib.hgemm.argtypes
+lib.hgemm_bf16.restype = _int
 lib.trmm_lower_trans.argtypes = [_i64, _i64, _f32, _vp, _i64, _vp, _i64, _vp, _i64, _int, _i64,
                                  _vp]
 lib.trmm_lower_trans.restype = _int
@@ -76,7 +82,7 @@ lib.hg_strerror.restype = ctypes.c_char_p
 lib.hg_trmm_plan.argtypes = [_i64, _i64, ctypes.POINTER(_i64), _i64]
 lib.hg_trmm_plan.restype = _i64
 
-EXPORTS = ("hgemm", "hgemm_bias_act", "trmm_lower_trans", "hg_trmm_lower_trans_by_level",
+EXPORTS = ("hgemm", "hgemm_bias_act", "hgemm_bf16", "trmm_lower_trans", "hg_trmm_lower_trans_by_level",
            "hg_strerror", "hg_trmm_plan", "trsm_lower_trans", "hg_trsm_workspace_size")
 
 ACT_NONE = 0
@@ -134,6 +140,27 @@ def hgemm(A, Bt, C, alpha: float = 1.0, beta: float = 0.0):
                    _stream_handle(C))
     if st != 0:
         raise HgError("hgemm", st)
+    return C
+
+
+def hgemm_bf16(A, Bt, C, alpha: float = 1.0, beta: float = 0.0):
+    """C = alpha·A·B + beta·C with bf16 A and Bt (layouts as hgemm), C bf16 or
+    float32; returns C."""
+    import torch
+    _check_matrix(A, "A", (torch.bfloat16,))
+    _check_matrix(Bt, "Bt", (torch.bfloat16,))
+    _check_matrix(C, "C", (torch.bfloat16, torch.float32))
+    M, K = A.shape
+    N = Bt.shape[0]
+    if Bt.shape[1] != K or tuple(C.shape) != (M, N):
+        raise ValueError(f"shape mismatch: A {tuple(A.shape)}, Bt {tuple(Bt.shape)}, "
+                         f"C {tuple(C.shape)}")
+    out_dtype = HG_BF16 if C.dtype == torch.bfloat16 else HG_F32
+    st = lib.hgemm_bf16(M, N, K, float(alpha), A.data_ptr() or None, _ld(A), Bt.data_ptr() or None,
+                        _ld(Bt), float(beta), C.data_ptr() or None, _ld(C), out_dtype,
+                        _stream_handle(C))
+    if st != 0:
+        raise HgError("hgemm_bf16", st)
     return C
 
 

@@ -102,10 +102,11 @@ const char *hg_strerror(int status)
 
 namespace {
 
-// hgemm and hgemm_bias_act: the plain call is bias == nullptr, act == 0.
+// hgemm, hgemm_bias_act and hgemm_bf16: the plain call is bias == nullptr,
+// act == 0, fp16 operands; bf16 operands take out_dtype HG_BF16 or HG_F32.
 int hgemm_impl(int64_t M, int64_t N, int64_t K, float alpha, const void *A, int64_t lda,
                const void *B, int64_t ldb, float beta, void *C, int64_t ldc, int out_dtype,
-               const float *bias, int act, void *stream)
+               const float *bias, int act, void *stream, bool in_bf16 = false)
 {
     if (M < 0 || M > kI32Max)
         return -1;
@@ -119,7 +120,8 @@ int hgemm_impl(int64_t M, int64_t N, int64_t K, float alpha, const void *A, int6
         return -8;
     if (ldc < std::max<int64_t>(1, N))
         return -11;
-    if (out_dtype != HG_F16 && out_dtype != HG_F32)
+    if (in_bf16 ? (out_dtype != HG_BF16 && out_dtype != HG_F32)
+                : (out_dtype != HG_F16 && out_dtype != HG_F32))
         return -12;
     if (act != HG_ACT_NONE && act != HG_ACT_RELU)
         return -14;
@@ -127,14 +129,14 @@ int hgemm_impl(int64_t M, int64_t N, int64_t K, float alpha, const void *A, int6
         return HG_OK;
     if (C == nullptr)
         return -10;
-    const bool out_f16 = out_dtype == HG_F16;
+    const bool out_f16 = out_dtype == HG_F16 || out_dtype == HG_BF16;   // 16-bit C
     const int64_t esize = out_f16 ? 2 : 4;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const Extent ec = extent(C, M, ldc, N, esize);
     if (bias != nullptr && overlap(ec, extent(bias, 1, N, N, 4)))
         return -13;
     if (alpha == 0.0f || K == 0)
-        return hip_status(hg::launch_scale(C, ldc, M, N, beta, out_f16, s, bias, act));
+        return hip_status(hg::launch_scale(C, ldc, M, N, beta, out_f16, s, bias, act, in_bf16));
     if (A == nullptr)
         return -5;
     if (B == nullptr)
@@ -162,6 +164,7 @@ int hgemm_impl(int64_t M, int64_t N, int64_t K, float alpha, const void *A, int6
     o.tri = false;
     o.vec = aligned16(A) && aligned16(B) && lda % 8 == 0 && ldb % 8 == 0;
     o.epi = bias != nullptr || act != HG_ACT_NONE;
+    o.in_bf16 = in_bf16;
     o.tile = hg::choose_tile(M, N, K);
     return hip_status(hg::launch_gemm(p, o, s));
 }
@@ -182,6 +185,14 @@ int hgemm_bias_act(int64_t M, int64_t N, int64_t K, float alpha, const void *A, 
                    const float *bias, int act, void *stream)
 {
     return hgemm_impl(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, out_dtype, bias, act, stream);
+}
+
+int hgemm_bf16(int64_t M, int64_t N, int64_t K, float alpha, const void *A, int64_t lda,
+               const void *B, int64_t ldb, float beta, void *C, int64_t ldc, int out_dtype,
+               void *stream)
+{
+    return hgemm_impl(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, out_dtype, nullptr,
+                      HG_ACT_NONE, stream, true);
 }
 
 int64_t hg_trmm_plan(int64_t n, int64_t leaf, int64_t *nodes, int64_t cap)

@@ -56,7 +56,21 @@ namespace {
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef _Float16 halfx4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// v_mfma_f32_16x16x32 on 16-byte fragments holding fp16 or bf16 values (the
+// staging and the fragment reads move bytes and do not depend on the type).
+template <bool BF16>
+__device__ __forceinline__ floatx4 mfma_16x16x32(const half8 &a, const half8 &b, const floatx4 &c)
+{
+    if constexpr (BF16)
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
 
 #ifndef HG_FAST_XCD
 #define HG_FAST_XCD 1
@@ -345,7 +359,7 @@ __device__ __forceinline__ bool fused_item(const GemmParams &p, int w, int G, in
     return true;
 }
 
-template <bool OUT_F16, bool BETA, bool TRI, bool KCHK, bool FUSED, bool EPI>
+template <bool OUT_F16, bool BETA, bool TRI, bool KCHK, bool FUSED, bool EPI, bool IN_BF16>
 __global__ void __launch_bounds__(THREADS, 1)
 hgemm_fast_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int cvec)
 {
@@ -549,8 +563,7 @@ hgemm_fast_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int c
                         __builtin_amdgcn_sched_barrier(0);
                     }
                     constexpr int a = k % TMQ, j = k / TMQ;
-                    acc[h * TMQ + a][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                        fb[s][j], fa[h][a], acc[h * TMQ + a][j], 0, 0, 0);
+                    acc[h * TMQ + a][j] = mfma_16x16x32<IN_BF16>(fb[s][j], fa[h][a], acc[h * TMQ + a][j]);
                     constexpr int op = sched(q, k);
                     if constexpr (op >= kLD) {
                         issue(T, lb, kt + 2, lsl, lfirst + op - kLD);
@@ -602,13 +615,16 @@ hgemm_fast_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int c
         // tile's first).
         auto epilogue = [&](auto rdc) __attribute__((always_inline)) {
             constexpr bool RD = decltype(rdc)::value;
+            // 16-bit C has the input's type (fp16 or bf16).
+            typedef typename std::conditional<IN_BF16, __bf16, _Float16>::type e16;
             prev = T.rows_a == BM && T.rows_b == BN && cvec ? 1 : 2;
             if (prev == 1) {
                 // Interior tile.  When C is read, its loads run CP row blocks
                 // ahead of the stores (the fragment registers are free here),
                 // so the epilogue waits on memory about TM/CP times, not TM.
-                typedef typename std::conditional<OUT_F16, halfx4, floatx4>::type cvec;
-                typedef typename std::conditional<OUT_F16, _Float16, float>::type celt;
+                typedef typename std::conditional<IN_BF16, bf16x4, halfx4>::type vec16;
+                typedef typename std::conditional<OUT_F16, vec16, floatx4>::type cvec;
+                typedef typename std::conditional<OUT_F16, e16, float>::type celt;
                 constexpr int CP = RD ? HG_FAST_EPI_PREFETCH : 1;
                 cvec cin[CP][TN];
                 auto crow = [&](int i) -> celt * {
@@ -673,11 +689,11 @@ hgemm_fast_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int c
                             const float v = acc[i][j][e];
                             const float b = EPI && p.bias ? p.bias[col + e] : -0.0f;
                             if (OUT_F16) {
-                                _Float16 *cp = static_cast<_Float16 *>(p.C) + off + e;
+                                e16 *cp = static_cast<e16 *>(p.C) + off + e;
                                 float t = RD ? __builtin_fmaf(alpha, v, beta * (float)*cp) : alpha * v;
                                 if constexpr (EPI)
                                     t = epi_apply(t, b, p.act);
-                                *cp = (_Float16)t;
+                                *cp = (e16)t;
                             } else {
                                 float *cp = static_cast<float *>(p.C) + off + e;
                                 float t = RD ? __builtin_fmaf(alpha, v, beta * *cp) : alpha * v;
@@ -722,7 +738,7 @@ int cu_count()
     return cached[dev];
 }
 
-template <bool OUT_F16, bool BETA, bool TRI, bool EPI>
+template <bool OUT_F16, bool BETA, bool TRI, bool EPI, bool IN_BF16 = false>
 hipError_t launch(const GemmParams &p, hipStream_t stream)
 {
     int maxN = 0;
@@ -757,10 +773,10 @@ hipError_t launch(const GemmParams &p, hipStream_t stream)
     for (int b = 0; b < p.nbatch; ++b)
         kchk = kchk || p.e[b].K % BK != 0;
     if (kchk)
-        hipLaunchKernelGGL((hgemm_fast_kernel<OUT_F16, BETA, TRI, true, false, EPI>), dim3((unsigned)grid),
+        hipLaunchKernelGGL((hgemm_fast_kernel<OUT_F16, BETA, TRI, true, false, EPI, IN_BF16>), dim3((unsigned)grid),
                            dim3(THREADS), 0, stream, p, tiles_m, tiles_n, (int)total64, cvec);
     else
-        hipLaunchKernelGGL((hgemm_fast_kernel<OUT_F16, BETA, TRI, false, false, EPI>), dim3((unsigned)grid),
+        hipLaunchKernelGGL((hgemm_fast_kernel<OUT_F16, BETA, TRI, false, false, EPI, IN_BF16>), dim3((unsigned)grid),
                            dim3(THREADS), 0, stream, p, tiles_m, tiles_n, (int)total64, cvec);
     return hipGetLastError();
 }
@@ -781,7 +797,7 @@ hipError_t launch_trmm_fused(const GemmParams &p, hipStream_t stream)
     grid = grid / 8 * 8 > 0 ? grid / 8 * 8 : grid;
     if (grid > total64)
         grid = total64;
-    hipLaunchKernelGGL((hgemm_fast_kernel<false, true, true, false, true, false>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((hgemm_fast_kernel<false, true, true, false, true, false, false>), dim3((unsigned)grid),
                        dim3(THREADS), 0, stream, p, tiles_m, tiles_n, (int)total64, cvec);
     return hipGetLastError();
 }
@@ -820,7 +836,7 @@ bool trmm_fused_ok(const GemmParams &p)
 
 bool fast_path_ok(const GemmParams &p, const LaunchOpts &o)
 {
-    if (!o.vec || (o.tri && (o.out_f16 || o.beta_read || o.epi)))
+    if (!o.vec || (o.tri && (o.out_f16 || o.beta_read || o.epi)) || (o.in_bf16 && (o.tri || o.epi)))
         return false;
     // 32-bit buffer offsets: every tile's byte range must stay below 2^31.
     if (p.lda > (1 << 21) || p.ldb > (1 << 21))
@@ -835,6 +851,13 @@ hipError_t launch_gemm_fast(const GemmParams &p, const LaunchOpts &o, hipStream_
 {
     if (o.tri)
         return launch<false, false, true, false>(p, stream);     // TRMM leaves: fp32, written once
+    if (o.in_bf16) {
+        if (o.out_f16)
+            return o.beta_read ? launch<true, true, false, false, true>(p, stream)
+                               : launch<true, false, false, false, true>(p, stream);
+        return o.beta_read ? launch<false, true, false, false, true>(p, stream)
+                           : launch<false, false, false, false, true>(p, stream);
+    }
     if (o.epi) {
         if (o.out_f16)
             return o.beta_read ? launch<true, true, false, true>(p, stream)

@@ -54,6 +54,7 @@ struct LaunchOpts {
     bool tri;         // TRMM leaf: B operand element (j, k) is zero for k < j
     bool vec;         // 16-byte aligned operands: vector loads
     bool epi;         // fused bias / activation (p.bias, p.act)
+    bool in_bf16;     // A and B (and a 16-bit C) are bf16 instead of fp16
     Tile tile;
 };
 
@@ -128,7 +129,7 @@ hipError_t launch_trsm_leaf(const TrsmLeafParams &p, bool vec, hipStream_t strea
 // case of the fused epilogue).
 hipError_t launch_scale(void *C, int64_t ldc, int64_t M, int64_t N, float beta,
                         bool out_f16, hipStream_t stream, const float *bias = nullptr,
-                        int act = 0);
+                        int act = 0, bool bf16 = false);
 
 // Tile family the launcher would choose for a single M×N GEMM.
 Tile choose_tile(int64_t M, int64_t N, int64_t K);

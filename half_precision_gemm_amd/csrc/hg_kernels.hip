@@ -42,6 +42,19 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef _Float16 halfx4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+// v_mfma_f32_32x32x16 on 16-byte fragments of fp16 or bf16 values.
+template <bool BF16>
+__device__ __forceinline__ floatx16 mfma_32x32x16(const half8 &a, const half8 &b, const floatx16 &c)
+{
+    if constexpr (BF16)
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
 
 template <int BM_, int BN_, int BK_, int WM_, int WN_>
 struct Cfg {
@@ -119,7 +132,7 @@ __device__ __forceinline__ void map_tile(int wg, int total, int tiles_m, int til
     tn = r / gsz;
 }
 
-template <class CF, bool OUT_F16, bool BETA, bool TRI, bool VEC>
+template <class CF, bool OUT_F16, bool BETA, bool TRI, bool VEC, bool IN_BF16>
 __global__ void __launch_bounds__(CF::THREADS, 1)
 hgemm_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int cvec)
 {
@@ -227,7 +240,7 @@ hgemm_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int cvec)
             for (int i = 0; i < CF::TM; ++i)
 #pragma unroll
                 for (int j = 0; j < CF::TN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[j], af[i], acc[i][j], 0, 0, 0);
+                    acc[i][j] = mfma_32x32x16<IN_BF16>(bf[j], af[i], acc[i][j]);
         }
     };
 
@@ -258,6 +271,9 @@ hgemm_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int cvec)
     const int64_t ldc = p.ldc;
     const bool full = full_m && full_n;
     const bool epi = p.bias != nullptr || p.act != 0;
+    // 16-bit C has the input's type (fp16 or bf16).
+    typedef typename std::conditional<IN_BF16, __bf16, _Float16>::type e16;
+    typedef typename std::conditional<IN_BF16, bf16x4, halfx4>::type vec16;
 #pragma unroll
     for (int i = 0; i < CF::TM; ++i) {
         const int row = m0 + wm * CF::WTM + i * 32 + frow;
@@ -271,10 +287,10 @@ hgemm_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int cvec)
                 const int64_t off = p.e[batch].c_off + (int64_t)row * ldc + col;
                 if (full && cvec) {
                     if (OUT_F16) {
-                        halfx4 *cp = reinterpret_cast<halfx4 *>(static_cast<_Float16 *>(p.C) + off);
+                        vec16 *cp = reinterpret_cast<vec16 *>(static_cast<e16 *>(p.C) + off);
                         floatx4 r;
                         if (BETA) {
-                            const halfx4 c = *cp;
+                            const vec16 c = *cp;
 #pragma unroll
                             for (int e = 0; e < 4; ++e)
                                 r[e] = __builtin_fmaf(alpha, v[e], beta * (float)c[e]);
@@ -288,10 +304,10 @@ hgemm_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int cvec)
                             for (int e = 0; e < 4; ++e)
                                 r[e] = epi_apply(r[e], p.bias ? p.bias[col + e] : -0.0f, p.act);
                         }
-                        halfx4 h;
+                        vec16 h;
 #pragma unroll
                         for (int e = 0; e < 4; ++e)
-                            h[e] = (_Float16)r[e];
+                            h[e] = (e16)r[e];
                         *cp = h;
                     } else {
                         floatx4 *cp = reinterpret_cast<floatx4 *>(static_cast<float *>(p.C) + off);
@@ -319,12 +335,12 @@ hgemm_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int cvec)
                         if (col + e < N) {
                             const float b = epi && p.bias ? p.bias[col + e] : -0.0f;
                             if (OUT_F16) {
-                                _Float16 *cp = static_cast<_Float16 *>(p.C) + off + e;
+                                e16 *cp = static_cast<e16 *>(p.C) + off + e;
                                 float r = BETA ? __builtin_fmaf(alpha, v[e], beta * (float)*cp)
                                                : alpha * v[e];
                                 if (epi)
                                     r = epi_apply(r, b, p.act);
-                                *cp = (_Float16)r;
+                                *cp = (e16)r;
                             } else {
                                 float *cp = static_cast<float *>(p.C) + off + e;
                                 float r = BETA ? __builtin_fmaf(alpha, v[e], beta * *cp)
@@ -342,21 +358,22 @@ hgemm_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int cvec)
 }
 
 // C = beta·C over the M×N window; beta == 0 writes zeros without reading C.
-template <bool OUT_F16>
+template <bool OUT_F16, bool BF16>
 __global__ void __launch_bounds__(256) scale_kernel(void *C, int64_t ldc, int64_t M, int64_t N,
                                                     float beta, const float *bias, int act)
 {
+    typedef typename std::conditional<BF16, __bf16, _Float16>::type e16;
     const int64_t total = M * N;
     const bool epi = bias != nullptr || act != 0;
     for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
          idx += (int64_t)gridDim.x * blockDim.x) {
         const int64_t i = idx / N, j = idx - i * N;
         if (OUT_F16) {
-            _Float16 *cp = static_cast<_Float16 *>(C) + i * ldc + j;
+            e16 *cp = static_cast<e16 *>(C) + i * ldc + j;
             float t = beta == 0.0f ? 0.0f : beta * (float)*cp;
             if (epi)
                 t = epi_apply(t, bias ? bias[j] : -0.0f, act);
-            *cp = (_Float16)t;
+            *cp = (e16)t;
         } else {
             float *cp = static_cast<float *>(C) + i * ldc + j;
             float t = beta == 0.0f ? 0.0f : beta * *cp;
@@ -367,7 +384,7 @@ __global__ void __launch_bounds__(256) scale_kernel(void *C, int64_t ldc, int64_
     }
 }
 
-template <class CF, bool OUT_F16, bool BETA, bool TRI, bool VEC>
+template <class CF, bool OUT_F16, bool BETA, bool TRI, bool VEC, bool IN_BF16 = false>
 hipError_t launch_cfg(const GemmParams &p, hipStream_t stream)
 {
     int maxN = 0;
@@ -386,7 +403,7 @@ hipError_t launch_cfg(const GemmParams &p, hipStream_t stream)
     int cvec = (reinterpret_cast<uintptr_t>(p.C) % align == 0) && (p.ldc % 4 == 0);
     for (int b = 0; b < p.nbatch; ++b)
         cvec = cvec && (p.e[b].c_off % 4 == 0);
-    hipLaunchKernelGGL((hgemm_kernel<CF, OUT_F16, BETA, TRI, VEC>), dim3((unsigned)total64),
+    hipLaunchKernelGGL((hgemm_kernel<CF, OUT_F16, BETA, TRI, VEC, IN_BF16>), dim3((unsigned)total64),
                        dim3(CF::THREADS), 0, stream, p, tiles_m, tiles_n, (int)total64, cvec);
     return hipGetLastError();
 }
@@ -400,6 +417,17 @@ hipError_t launch_tile(const GemmParams &p, const LaunchOpts &o, hipStream_t s)
             return hipErrorInvalidValue;
         return o.vec ? launch_cfg<CF, false, false, true, true>(p, s)
                      : launch_cfg<CF, false, false, true, false>(p, s);
+    }
+    if (o.in_bf16) {
+        if (o.out_f16)
+            return o.beta_read ? (o.vec ? launch_cfg<CF, true, true, false, true, true>(p, s)
+                                        : launch_cfg<CF, true, true, false, false, true>(p, s))
+                               : (o.vec ? launch_cfg<CF, true, false, false, true, true>(p, s)
+                                        : launch_cfg<CF, true, false, false, false, true>(p, s));
+        return o.beta_read ? (o.vec ? launch_cfg<CF, false, true, false, true, true>(p, s)
+                                    : launch_cfg<CF, false, true, false, false, true>(p, s))
+                           : (o.vec ? launch_cfg<CF, false, false, false, true, true>(p, s)
+                                    : launch_cfg<CF, false, false, false, false, true>(p, s));
     }
     if (o.out_f16) {
         if (o.beta_read)
@@ -450,7 +478,7 @@ hipError_t launch_gemm(const GemmParams &p, const LaunchOpts &o, hipStream_t str
 }
 
 hipError_t launch_scale(void *C, int64_t ldc, int64_t M, int64_t N, float beta, bool out_f16,
-                        hipStream_t stream, const float *bias, int act)
+                        hipStream_t stream, const float *bias, int act, bool bf16)
 {
     const int64_t total = M * N;
     int64_t blocks = (total + 255) / 256;
@@ -458,11 +486,14 @@ hipError_t launch_scale(void *C, int64_t ldc, int64_t M, int64_t N, float beta, 
         blocks = 65536;
     if (blocks < 1)
         return hipSuccess;
-    if (out_f16)
-        hipLaunchKernelGGL(scale_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream, C,
+    if (out_f16 && bf16)
+        hipLaunchKernelGGL((scale_kernel<true, true>), dim3((unsigned)blocks), dim3(256), 0, stream, C,
+                           ldc, M, N, beta, bias, act);
+    else if (out_f16)
+        hipLaunchKernelGGL((scale_kernel<true, false>), dim3((unsigned)blocks), dim3(256), 0, stream, C,
                            ldc, M, N, beta, bias, act);
     else
-        hipLaunchKernelGGL(scale_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream, C,
+        hipLaunchKernelGGL((scale_kernel<false, false>), dim3((unsigned)blocks), dim3(256), 0, stream, C,
                            ldc, M, N, beta, bias, act);
     return hipGetLastError();
 }

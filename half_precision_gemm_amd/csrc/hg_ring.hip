@@ -35,6 +35,19 @@ namespace {
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef _Float16 halfx4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+// v_mfma_f32_16x16x32 on 16-byte fragments of fp16 or bf16 values.
+template <bool BF16>
+__device__ __forceinline__ floatx4 mfma_16x16x32(const half8 &a, const half8 &b, const floatx4 &c)
+{
+    if constexpr (BF16)
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
 
 constexpr int BK = 64, RB = 128, KC = 8, THREADS = 256, NWAVES = 4;
 constexpr uint32_t OOB = 0x80000000u;
@@ -78,7 +91,7 @@ __device__ __forceinline__ void ring_map(int wg, int total, int tiles_m, int til
     tn = r / gsz;
 }
 
-template <int BM, int BN, bool OUT_F16, bool BETA, bool KCHK, bool EPI>
+template <int BM, int BN, bool OUT_F16, bool BETA, bool KCHK, bool EPI, bool IN_BF16>
 __global__ void __launch_bounds__(THREADS, 1)
 hgemm_ring_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int cvec)
 {
@@ -186,7 +199,7 @@ hgemm_ring_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int c
             for (int j = 0; j < TN; ++j)
 #pragma unroll
                 for (int i = 0; i < TM; ++i)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+                    acc[i][j] = mfma_16x16x32<IN_BF16>(fb[j], fa[i], acc[i][j]);
         }
     }
     wait_vmcnt<0>();   // the ring's last zero-fill loads (none reach memory) drain before exit
@@ -195,8 +208,11 @@ hgemm_ring_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int c
     // n0 + wn·WTN + 16j + 4·(lane div 16) + 0..3.
     const float alpha = p.alpha, beta = p.beta;
     const int64_t ldc = p.ldc;
-    typedef typename std::conditional<OUT_F16, halfx4, floatx4>::type cvec_t;
-    typedef typename std::conditional<OUT_F16, _Float16, float>::type celt;
+    // 16-bit C has the input's type (fp16 or bf16).
+    typedef typename std::conditional<IN_BF16, bf16x4, halfx4>::type vec16;
+    typedef typename std::conditional<IN_BF16, __bf16, _Float16>::type e16;
+    typedef typename std::conditional<OUT_F16, vec16, floatx4>::type cvec_t;
+    typedef typename std::conditional<OUT_F16, e16, float>::type celt;
     celt *Cb = static_cast<celt *>(p.C) + p.e[batch].c_off;
     if (rows_a == BM && rows_b == BN && cvec) {
 #pragma unroll
@@ -249,7 +265,7 @@ hgemm_ring_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int c
     }
 }
 
-template <int BM, int BN, bool OUT_F16, bool BETA, bool EPI>
+template <int BM, int BN, bool OUT_F16, bool BETA, bool EPI, bool IN_BF16>
 hipError_t launch_ring_cfg(const GemmParams &p, hipStream_t stream)
 {
     int maxN = 0;
@@ -270,35 +286,38 @@ hipError_t launch_ring_cfg(const GemmParams &p, hipStream_t stream)
     for (int b = 0; b < p.nbatch; ++b)
         cvec = cvec && (p.e[b].c_off % 4 == 0);
     if (kchk)
-        hipLaunchKernelGGL((hgemm_ring_kernel<BM, BN, OUT_F16, BETA, true, EPI>), dim3((unsigned)total64),
+        hipLaunchKernelGGL((hgemm_ring_kernel<BM, BN, OUT_F16, BETA, true, EPI, IN_BF16>), dim3((unsigned)total64),
                            dim3(THREADS), 0, stream, p, tiles_m, tiles_n, (int)total64, cvec);
     else
-        hipLaunchKernelGGL((hgemm_ring_kernel<BM, BN, OUT_F16, BETA, false, EPI>), dim3((unsigned)total64),
+        hipLaunchKernelGGL((hgemm_ring_kernel<BM, BN, OUT_F16, BETA, false, EPI, IN_BF16>), dim3((unsigned)total64),
                            dim3(THREADS), 0, stream, p, tiles_m, tiles_n, (int)total64, cvec);
     return hipGetLastError();
 }
 
-template <int BM, int BN, bool EPI>
+template <int BM, int BN, bool EPI, bool IN_BF16>
 hipError_t launch_ring_epi(const GemmParams &p, const LaunchOpts &o, hipStream_t s)
 {
     if (o.out_f16)
-        return o.beta_read ? launch_ring_cfg<BM, BN, true, true, EPI>(p, s)
-                           : launch_ring_cfg<BM, BN, true, false, EPI>(p, s);
-    return o.beta_read ? launch_ring_cfg<BM, BN, false, true, EPI>(p, s)
-                       : launch_ring_cfg<BM, BN, false, false, EPI>(p, s);
+        return o.beta_read ? launch_ring_cfg<BM, BN, true, true, EPI, IN_BF16>(p, s)
+                           : launch_ring_cfg<BM, BN, true, false, EPI, IN_BF16>(p, s);
+    return o.beta_read ? launch_ring_cfg<BM, BN, false, true, EPI, IN_BF16>(p, s)
+                       : launch_ring_cfg<BM, BN, false, false, EPI, IN_BF16>(p, s);
 }
 
 template <int BM, int BN>
 hipError_t launch_ring_tile(const GemmParams &p, const LaunchOpts &o, hipStream_t s)
 {
-    return o.epi ? launch_ring_epi<BM, BN, true>(p, o, s) : launch_ring_epi<BM, BN, false>(p, o, s);
+    if (o.in_bf16)
+        return launch_ring_epi<BM, BN, false, true>(p, o, s);
+    return o.epi ? launch_ring_epi<BM, BN, true, false>(p, o, s)
+                 : launch_ring_epi<BM, BN, false, false>(p, o, s);
 }
 
 }  // namespace
 
 bool ring_path_ok(const GemmParams &p, const LaunchOpts &o)
 {
-    if (!o.vec || o.tri)
+    if (!o.vec || o.tri || (o.in_bf16 && o.epi))
         return false;
     if (p.lda > (1 << 21) || p.ldb > (1 << 21))
         return false;

@@ -46,9 +46,10 @@
 extern "C" {
 #endif
 
-/* Element type of C (hgemm) and Out (trmm_lower_trans). */
+/* Element type of C (hgemm, hgemm_bf16) and Out (trmm_lower_trans). */
 #define HG_F16 0
 #define HG_F32 1
+#define HG_BF16 2
 
 /* Activation of hgemm_bias_act. */
 #define HG_ACT_NONE 0
@@ -114,6 +115,23 @@ int hgemm_bias_act(int64_t M, int64_t N, int64_t K, float alpha,
                    const void *B, int64_t ldb,
                    float beta, void *C, int64_t ldc,
                    int out_dtype, const float *bias, int act, void *stream);
+
+/*
+ * hgemm_bf16 — hgemm with bf16 A and B ("GPU架构与CUDA", section 混合精度核函数:
+ * a lower-precision type for the products, fp32 for the accumulation; bf16
+ * keeps fp32's exponent range with an 8-bit significand).
+ *
+ * Arguments, layouts, quick returns and status codes as hgemm, except:
+ *  5 A, 7 B      : bf16 (the upper 16 bits of an IEEE binary32).
+ * 12 out_dtype   : HG_BF16 (rounded to nearest even) or HG_F32; HG_F16 is
+ *                  rejected (-12).
+ * Each bf16×bf16 product is exact in fp32 and summed in fp32, as in hgemm.
+ */
+int hgemm_bf16(int64_t M, int64_t N, int64_t K, float alpha,
+               const void *A, int64_t lda,
+               const void *B, int64_t ldb,
+               float beta, void *C, int64_t ldc,
+               int out_dtype, void *stream);
 
 /*
  * trmm_lower_trans — Out = alpha·Aᵀ·B, A lower triangular.

@@ -30,8 +30,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == ["hg_strerror", "hg_trmm_lower_trans_by_level", "hg_trmm_plan",
-                                    "hg_trsm_workspace_size", "hgemm", "hgemm_bias_act",
-                                    "trmm_lower_trans", "trsm_lower_trans"]
+                                    "hg_trsm_workspace_size", "hgemm", "hgemm_bf16",
+                                    "hgemm_bias_act", "trmm_lower_trans", "trsm_lower_trans"]
 
 
 def test_library_exports_every_declared_symbol(hg):
@@ -81,6 +81,16 @@ def test_hgemm_bias_act_argument_errors(lib):
     assert bias_act(lib, bias=R + 8) == -13          # bias inside C
     assert bias_act(lib, C=P + 8) == -10             # C overlaps A
     assert bias_act(lib, M=0, A=None, B=None, C=None) == 0
+
+
+def test_hgemm_bf16_output_types(lib):
+    """bf16 operands take HG_BF16 or HG_F32 output; HG_F16 is rejected, and
+    the fp16 entry point rejects HG_BF16."""
+    args = (4, 4, 4, 1.0, P, 4, Q, 4, 0.0, R, 4)
+    assert lib.hgemm_bf16(*args, 0, None) == -12
+    assert lib.hgemm_bf16(*args, 3, None) == -12
+    assert lib.hgemm(*args, 2, None) == -12
+    assert lib.hgemm_bf16(0, 4, 4, 1.0, None, 4, None, 4, 0.0, None, 4, 2, None) == 0
 
 
 def test_hgemm_first_bad_argument_wins(lib):

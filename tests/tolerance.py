@@ -7,16 +7,21 @@ term covers the final rounding to fp16 (at most 2^-11·|ref|).
 import numpy as np
 
 
-def bound(K, ref):
-    return 1e-3 * np.sqrt(max(int(K), 1)) + 2.0 ** -10 * np.abs(ref)
+def bound(K, ref, rel=2.0 ** -10):
+    return 1e-3 * np.sqrt(max(int(K), 1)) + rel * np.abs(ref)
 
 
-def check_close(out, ref, K, what=""):
+# bf16 output: rounding to bf16 (8-bit significand) is off by at most
+# 2^-9·|ref|; the relative term doubles it as the fp16 rule doubles 2^-11.
+REL_BF16 = 2.0 ** -8
+
+
+def check_close(out, ref, K, what="", rel=2.0 ** -10):
     out = np.asarray(out, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     assert out.shape == ref.shape, (out.shape, ref.shape)
     err = np.abs(out - ref)
-    lim = bound(K, ref)
+    lim = bound(K, ref, rel)
     bad = ~(err <= lim)          # NaN in out counts as a failure
     if bad.any():
         idx = np.argwhere(bad)[:5]
