@@ -227,6 +227,19 @@ def config_sweep(hg, stream, main_gemm_ms=None, main_trmm_ms=None):
         "note": "bf16 A, B (v_mfma_f32_16x16x32_bf16), fp32 accumulation and C; dense bf16 peak "
                 "equals the fp16 one"}
     del Ad, Btd, Cd, Ab, Bb
+    # Skinny right-hand side (next row): the TRMM page's usage example,
+    # n = 4096, m = 256.
+    print("[bench] config trmm_4096x256 ...", file=sys.stderr, flush=True)
+    w = workloads.TrmmWorkload("trmm_4096x256", 4096, 256, 1.0, 256, 6)
+    TA, TB = workloads.trmm_inputs(w)
+    Ad, Bd = torch.from_numpy(TA).to(dev), torch.from_numpy(TB).to(dev)
+    Od = torch.empty((w.m, w.n), dtype=torch.float32, device=dev)
+    ts = _time_calls(lambda: hg.trmm_lower_trans(Ad, Bd, Od, w.alpha, w.leaf), 20, 50, stream)
+    res["trmm_4096x256"] = {"gpu_ms_median": round(ts[0], 5), "gpu_ms_min": round(ts[1], 5),
+                            "gpu_ms_back_to_back_mean": round(ts[2], 5),
+                            "effective_tflops": round(w.flops / (ts[0] * 1e-3) / 1e12, 2),
+                            "note": "B 4096x256 (the TRMM page's usage example), level-by-level launches"}
+    del Ad, Bd, Od, TA, TB
     for name, w in workloads.TRSM_WORKLOADS.items():
         print(f"[bench] config {name} ...", file=sys.stderr, flush=True)
         A_cm, B_cm = workloads.trsm_inputs(w)

@@ -806,6 +806,12 @@ bool trmm_fused_ok(const GemmParams &p)
 {
     if (p.lda > (1 << 21) || p.ldb > (1 << 21) || p.leaf < BN)
         return false;
+    // One persistent workgroup per tile at a time: with fewer than two tiles
+    // per CU (skinny B: m = 256 gives 16 tiles at n = 4096) the per-level
+    // launches, which spread every level over its own grid, are 2–3× faster.
+    const int64_t tiles = (int64_t)((p.M + BM - 1) / BM) * (p.e[0].N / BN);
+    if (tiles < 2 * (int64_t)cu_count())
+        return false;
     if (reinterpret_cast<uintptr_t>(p.A) % 16 != 0 || reinterpret_cast<uintptr_t>(p.B) % 16 != 0 ||
         p.lda % 8 != 0 || p.ldb % 8 != 0)
         return false;

@@ -77,8 +77,9 @@ hipError_t launch_gemm_ring(const GemmParams &p, const LaunchOpts &o, hipStream_
 // C = Outᵀ (M = m, N = K = n; p.A = B, p.B = A, p.C = Out, p.e[0] = {0, 0,
 // 0, n, n}, p.leaf): every output tile walks its leaf and then the recursion's
 // updates that touch it, deepest first, in one persistent workgroup.
-// trmm_fused_ok: the operands suit the fast path and every recursion
-// boundary falls on a 256-column tile edge.
+// trmm_fused_ok: the operands suit the fast path, every recursion boundary
+// falls on a 256-column tile edge, and there are at least two output tiles
+// per CU.
 bool trmm_fused_ok(const GemmParams &p);
 hipError_t launch_trmm_fused(const GemmParams &p, hipStream_t stream);
 

@@ -158,10 +158,11 @@ int hgemm_bf16(int64_t M, int64_t N, int64_t K, float alpha,
  * recursion.  Each term is a GEMM computed in fp32 and added as
  * Out = alpha·acc (leaf) or Out = fma(alpha, acc, Out) (update, beta = 1).
  * When every recursion boundary falls on a multiple of 256 (n a multiple of
- * 256 split down to leaves of at least 256) and the operands are 16-byte
- * aligned with lda, ldb multiples of 8, all terms run in one launch in which
- * each 256×256 output tile walks its own terms in that order; otherwise one
- * batched launch runs all leaves and one each update level.  Both schedules
+ * 256 split down to leaves of at least 256), the operands are 16-byte
+ * aligned with lda, ldb multiples of 8 and there are at least two 256×256
+ * output tiles per compute unit, all terms run in one launch in which each
+ * output tile walks its own terms in that order; otherwise one batched
+ * launch runs all leaves and one each update level.  Both schedules
  * give the same bits (see hg_trmm_lower_trans_by_level).
  */
 int trmm_lower_trans(int64_t n, int64_t m, float alpha,

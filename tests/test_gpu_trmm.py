@@ -154,33 +154,41 @@ def test_deterministic(hg):
 # ---- the one-launch schedule (every recursion boundary on a 256-column tile
 # edge) against the level-by-level schedule: same terms, same order, same
 # bits; and against the oracle.
-@pytest.mark.parametrize("n,m,leaf", [(2048, 300, 256), (4096, 512, 256), (1024, 1000, 512),
-                                      (1280, 256, 1280), (1536, 70, 256), (512, 33, 256),
-                                      (256, 1, 256), (3072, 64, 256), (2560, 100, 256)])
+# The one-launch schedule runs when the recursion's boundaries fall on the
+# 256 grid and there are at least two 256×256 output tiles per CU (m·n >=
+# 512·256²); the shapes below with m·n of 2^25 take it, 3072 and 2560 (their
+# boundaries are off the grid) run level by level in both calls.
+@pytest.mark.parametrize("n,m,leaf", [(4096, 8192, 256), (2048, 16384, 256), (4096, 8192, 512),
+                                      (8192, 4096, 256), (3072, 64, 256), (2560, 100, 256)])
 def test_schedules_bit_identical(hg, n, m, leaf):
-    """n = 3072 and 2560 have recursion boundaries off the 256 grid (both calls
-    then run level by level); the others run the one-launch schedule."""
     print(f"[case] trmm schedules n={n} m={m} leaf={leaf}", flush=True)
     A_cm, B_cm = trmm_inputs(n, m, n + 3 * m + leaf)
     one = run(hg, A_cm, B_cm, 1.25, leaf)
     lev = run(hg, A_cm, B_cm, 1.25, leaf, by_level=True)
     assert np.array_equal(one.view(np.uint32), lev.view(np.uint32))
-    check_close(one, oracle.trmm_lower_trans(A_cm, B_cm, 1.25), n, f"n={n} m={m} leaf={leaf}")
+    if n * m <= 2 ** 20:
+        check_close(one, oracle.trmm_lower_trans(A_cm, B_cm, 1.25), n, f"n={n} m={m} leaf={leaf}")
+    else:
+        ri, cj = workloads.sample_indices(n + m, n, m)
+        ref = oracle.trmm_lower_trans_sampled(A_cm, B_cm, ri, cj, 1.25)
+        check_close(one[cj, ri], ref, n, f"n={n} m={m} leaf={leaf} sampled")
 
 
 def test_one_launch_integer_bit_exact(hg):
     rng = np.random.default_rng(23)
-    n, m = 2048, 200
+    n, m = 2048, 16384
     A = np.tril(workloads.integer_f16(rng, (n, n)))
     B = workloads.integer_f16(rng, (n, m))
-    out = run(hg, np.ascontiguousarray(A.T), np.ascontiguousarray(B.T))
-    exact = A.astype(np.int64).T @ B.astype(np.int64)
-    assert np.array_equal(out, exact.T.astype(np.float32))
+    A_cm, B_cm = np.ascontiguousarray(A.T), np.ascontiguousarray(B.T)
+    out = run(hg, A_cm, B_cm)
+    ri, cj = workloads.sample_indices(7, n, m, 4096)
+    exact = oracle.trmm_lower_trans_sampled(A_cm, B_cm, ri, cj)      # integers, exact in fp64
+    assert np.array_equal(out[cj, ri].astype(np.float64), exact)
 
 
 @pytest.mark.parametrize("fill", [np.nan, -np.inf])
 def test_one_launch_upper_triangle_never_read(hg, fill):
-    n, m = 1024, 96
+    n, m = 4096, 8192
     A0, B_cm = trmm_inputs(n, m, 8, 0.0)
     Ax, _ = trmm_inputs(n, m, 8, fill)
     base = run(hg, A0, B_cm)
@@ -189,8 +197,17 @@ def test_one_launch_upper_triangle_never_read(hg, fill):
 
 
 def test_one_launch_tril_ones_closed_form(hg):
-    n, m = 2048, 40
+    n, m = 2048, 16384
     A = np.tril(np.ones((n, n), np.float16))
     out = run(hg, np.ascontiguousarray(A.T), np.ones((m, n), np.float16), 0.5)
     expect = 0.5 * (n - np.arange(n, dtype=np.float32))
     assert np.array_equal(out, np.tile(expect, (m, 1)))
+
+
+@pytest.mark.parametrize("n,m", [(4096, 256), (8192, 256), (4096, 1024)])
+def test_skinny_b(hg, n, m):
+    """Skinny right-hand sides ("异构计算中高性能TRMM与TRSM的递归算法实现" §5.1
+    uses n = 4096, m = 256): level-by-level launches, against the oracle in full."""
+    A_cm, B_cm = trmm_inputs(n, m, n + m)
+    out = run(hg, A_cm, B_cm, 0.75)
+    check_close(out, oracle.trmm_lower_trans(A_cm, B_cm, 0.75), n, f"skinny n={n} m={m}")
