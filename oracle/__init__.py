@@ -87,6 +87,9 @@ def _load():
                                                             vp, i64, i64, vp,
                                                             vp, vp]
             lib.oracle_trmm_lower_trans_sampled.restype = None
+            lib.oracle_trmm.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, f64, vp, i64,
+                                        vp, i64, vp, i64]
+            lib.oracle_trmm.restype = None
             lib.oracle_trsm_lower_trans.argtypes = [i64, i64, f64, vp, i64, vp,
                                                     i64, vp, i64]
             lib.oracle_trsm_lower_trans.restype = None
@@ -324,6 +327,31 @@ def trmm_lower_trans_sampled(A_cm: np.ndarray, B_cm: np.ndarray, rows: np.ndarra
     lib.oracle_trmm_lower_trans_sampled(n, float(alpha), _ptr(A_cm), _ld(A_cm),
                                         _ptr(B_cm), _ld(B_cm), rows.size,
                                         _ptr(rows), _ptr(cols), _ptr(ref))
+    return ref
+
+
+LOWER, UPPER = 0, 1
+NOTRANS, TRANS = 0, 1
+
+
+def trmm(A_cm: np.ndarray, B_cm: np.ndarray, alpha: float = 1.0, uplo: int = LOWER,
+         trans: int = TRANS) -> np.ndarray:
+    """fp64 reference of Out = α·op(A)·B, A triangular (uplo LOWER or UPPER;
+    only that triangle read), op = transpose when trans == TRANS.  Same
+    column-major convention as ``trmm_lower_trans``."""
+    lib = _load()
+    _f16_2d(A_cm, "A_cm")
+    _f16_2d(B_cm, "B_cm")
+    n = A_cm.shape[0]
+    if A_cm.shape != (n, n) or B_cm.shape[1] != n:
+        raise ValueError("shape mismatch")
+    if uplo not in (LOWER, UPPER) or trans not in (NOTRANS, TRANS):
+        raise ValueError("uplo / trans out of range")
+    m = B_cm.shape[0]
+    ref = np.empty((m, n), dtype=np.float64)
+    if n and m:
+        lib.oracle_trmm(int(uplo), int(trans), n, m, float(alpha), _ptr(A_cm), _ld(A_cm),
+                        _ptr(B_cm), _ld(B_cm), _ptr(ref), n)
     return ref
 
 

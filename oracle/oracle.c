@@ -273,6 +273,35 @@ void oracle_trmm_lower_trans(int64_t n, int64_t m, double alpha,
     }
 }
 
+/* ---- TRMM, left side, any triangle and transposition -----------------------
+ * ref(i,j) = α · Σ_k op(A)(i,k) · B(k,j),  op(A) = A or Aᵀ,
+ * where only A's stored triangle is read: lower (uplo 0) holds A(r,c) for
+ * r >= c, upper (uplo 1) for r <= c; the other triangle counts as zero.
+ * ("异构计算中高性能TRMM与TRSM的递归算法实现" §2.1 shows the lower and upper
+ * blockings; its §5.1 usage calls the lower, non-transposed product.)
+ * A : n×n column-major fp16; B : n×m column-major fp16; ref : n×m column-major.
+ */
+void oracle_trmm(int uplo, int trans, int64_t n, int64_t m, double alpha,
+                 const uint16_t *A, int64_t lda,
+                 const uint16_t *B, int64_t ldb,
+                 double *ref, int64_t ldr)
+{
+    h2d_init();
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t j = 0; j < m; ++j) {
+        for (int64_t i = 0; i < n; ++i) {
+            double acc = 0.0;
+            for (int64_t k = 0; k < n; ++k) {
+                const int64_t r = trans ? k : i, c = trans ? i : k;   /* op(A)(i,k) = A(r,c) */
+                const int stored = uplo == 0 ? r >= c : r <= c;
+                if (stored)
+                    acc += g_h2d[A[r + c * lda]] * g_h2d[B[k + j * ldb]];
+            }
+            ref[i + j * ldr] = alpha * acc;
+        }
+    }
+}
+
 /* Same definition at the listed (rows[s], cols[s]) = (i, j) pairs. */
 void oracle_trmm_lower_trans_sampled(int64_t n, double alpha,
                                      const uint16_t *A, int64_t lda,

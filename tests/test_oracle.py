@@ -455,3 +455,51 @@ def test_gemm_bf16_sampled_equals_full():
     full = oracle.gemm_bf16(A, Bt, 0.75)
     ri, cj = workloads.sample_indices(2, 40, 30, 64)
     assert np.array_equal(oracle.gemm_bf16_sampled(A, Bt, ri, cj, 0.75), full[ri, cj])
+
+
+# ---- TRMM variants: op(A) = A or Aᵀ, A lower or upper ----
+
+@pytest.mark.parametrize("uplo", [oracle.LOWER, oracle.UPPER])
+@pytest.mark.parametrize("trans", [oracle.NOTRANS, oracle.TRANS])
+def test_trmm_variants_match_numpy(uplo, trans):
+    rng = np.random.default_rng(70 + 2 * uplo + trans)
+    n, m = 37, 6
+    A = workloads.uniform_f16(rng, (n, n))
+    B = workloads.uniform_f16(rng, (n, m))
+    T = (np.tril if uplo == oracle.LOWER else np.triu)(A.astype(np.float64))
+    op = T.T if trans == oracle.TRANS else T
+    got = oracle.trmm(np.ascontiguousarray(A.T), np.ascontiguousarray(B.T), -1.5, uplo, trans)
+    np.testing.assert_allclose(got.T, -1.5 * (op @ B.astype(np.float64)), rtol=1e-12, atol=1e-12)
+
+
+def test_trmm_lower_trans_variant_equals_dedicated_routine():
+    A, B = _trmm_inputs(60, 9, 71)
+    Acm, Bcm = np.ascontiguousarray(A.T), np.ascontiguousarray(B.T)
+    assert np.array_equal(oracle.trmm(Acm, Bcm, 0.5, oracle.LOWER, oracle.TRANS),
+                          oracle.trmm_lower_trans(Acm, Bcm, 0.5))
+
+
+@pytest.mark.parametrize("uplo", [oracle.LOWER, oracle.UPPER])
+@pytest.mark.parametrize("trans", [oracle.NOTRANS, oracle.TRANS])
+def test_trmm_variants_other_triangle_not_referenced(uplo, trans):
+    rng = np.random.default_rng(72)
+    n, m = 25, 4
+    A = workloads.uniform_f16(rng, (n, n))
+    B = workloads.uniform_f16(rng, (n, m))
+    other = np.triu_indices(n, 1) if uplo == oracle.LOWER else np.tril_indices(n, -1)
+    Ax = A.copy()
+    Ax[other] = np.nan
+    ref = oracle.trmm(np.ascontiguousarray(A.T), np.ascontiguousarray(B.T), 1.0, uplo, trans)
+    got = oracle.trmm(np.ascontiguousarray(Ax.T), np.ascontiguousarray(B.T), 1.0, uplo, trans)
+    assert np.array_equal(got, ref)
+
+
+def test_trmm_upper_notrans_brute_force():
+    rng = np.random.default_rng(73)
+    A = workloads.integer_f16(rng, (5, 5))
+    B = workloads.integer_f16(rng, (5, 3))
+    got = oracle.trmm(np.ascontiguousarray(A.T), np.ascontiguousarray(B.T), 2.0, oracle.UPPER,
+                      oracle.NOTRANS)
+    for i in range(5):
+        for j in range(3):
+            assert got[j, i] == 2.0 * sum(float(A[i, k]) * float(B[k, j]) for k in range(i, 5))

@@ -60,6 +60,12 @@ MUTANTS = {
     # bf16 GEMM: B read at reversed k (a misindexed operand)
     "bf16_gemm_B_k_reversed": ("acc += g_b2d[A[i * lda + k]] * g_b2d[B[j * ldb + k]];",
                                "acc += g_b2d[A[i * lda + k]] * g_b2d[B[j * ldb + (K - 1 - k)]];"),
+    # TRMM variants: the triangle test inverted for upper
+    "trmm_variant_upper_inverted": ("const int stored = uplo == 0 ? r >= c : r <= c;",
+                                    "const int stored = uplo == 0 ? r >= c : r < c;"),
+    # TRMM variants: transposition ignored
+    "trmm_variant_no_trans": ("const int64_t r = trans ? k : i, c = trans ? i : k;",
+                              "const int64_t r = i, c = k;"),
     # fp16 decoding: subnormal scale off by one binade
     "decode_subnormal_scale": ("v = ldexp((double)frac, -24);", "v = ldexp((double)frac, -25);"),
     # fp16 decoding: exponent bias off by one
