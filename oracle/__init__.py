@@ -90,6 +90,9 @@ def _load():
             lib.oracle_trmm.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, f64, vp, i64,
                                         vp, i64, vp, i64]
             lib.oracle_trmm.restype = None
+            lib.oracle_trmm_sampled.argtypes = [ctypes.c_int, ctypes.c_int, i64, f64, vp, i64,
+                                                vp, i64, i64, vp, vp, vp]
+            lib.oracle_trmm_sampled.restype = None
             lib.oracle_trsm_lower_trans.argtypes = [i64, i64, f64, vp, i64, vp,
                                                     i64, vp, i64]
             lib.oracle_trsm_lower_trans.restype = None
@@ -352,6 +355,24 @@ def trmm(A_cm: np.ndarray, B_cm: np.ndarray, alpha: float = 1.0, uplo: int = LOW
     if n and m:
         lib.oracle_trmm(int(uplo), int(trans), n, m, float(alpha), _ptr(A_cm), _ld(A_cm),
                         _ptr(B_cm), _ld(B_cm), _ptr(ref), n)
+    return ref
+
+
+def trmm_sampled(A_cm: np.ndarray, B_cm: np.ndarray, rows: np.ndarray, cols: np.ndarray,
+                 alpha: float = 1.0, uplo: int = LOWER, trans: int = TRANS) -> np.ndarray:
+    """``trmm`` at entries (row i, column j) = (rows[s], cols[s])."""
+    lib = _load()
+    _f16_2d(A_cm, "A_cm")
+    _f16_2d(B_cm, "B_cm")
+    n = A_cm.shape[0]
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    cols = np.ascontiguousarray(cols, dtype=np.int64)
+    if rows.size and (rows.min() < 0 or rows.max() >= n or
+                      cols.min() < 0 or cols.max() >= B_cm.shape[0]):
+        raise IndexError("sample index out of range")
+    ref = np.empty(rows.shape, dtype=np.float64)
+    lib.oracle_trmm_sampled(int(uplo), int(trans), n, float(alpha), _ptr(A_cm), _ld(A_cm),
+                            _ptr(B_cm), _ld(B_cm), rows.size, _ptr(rows), _ptr(cols), _ptr(ref))
     return ref
 
 

@@ -302,6 +302,28 @@ void oracle_trmm(int uplo, int trans, int64_t n, int64_t m, double alpha,
     }
 }
 
+/* oracle_trmm's definition at the listed (rows[s], cols[s]) = (i, j). */
+void oracle_trmm_sampled(int uplo, int trans, int64_t n, double alpha,
+                         const uint16_t *A, int64_t lda,
+                         const uint16_t *B, int64_t ldb,
+                         int64_t nsamp, const int64_t *rows,
+                         const int64_t *cols, double *ref)
+{
+    h2d_init();
+#pragma omp parallel for schedule(dynamic, 8)
+    for (int64_t s = 0; s < nsamp; ++s) {
+        const int64_t i = rows[s], j = cols[s];
+        double acc = 0.0;
+        for (int64_t k = 0; k < n; ++k) {
+            const int64_t r = trans ? k : i, c = trans ? i : k;
+            const int stored = uplo == 0 ? r >= c : r <= c;
+            if (stored)
+                acc += g_h2d[A[r + c * lda]] * g_h2d[B[k + j * ldb]];
+        }
+        ref[s] = alpha * acc;
+    }
+}
+
 /* Same definition at the listed (rows[s], cols[s]) = (i, j) pairs. */
 void oracle_trmm_lower_trans_sampled(int64_t n, double alpha,
                                      const uint16_t *A, int64_t lda,

@@ -503,3 +503,16 @@ def test_trmm_upper_notrans_brute_force():
     for i in range(5):
         for j in range(3):
             assert got[j, i] == 2.0 * sum(float(A[i, k]) * float(B[k, j]) for k in range(i, 5))
+
+
+@pytest.mark.parametrize("uplo", [oracle.LOWER, oracle.UPPER])
+@pytest.mark.parametrize("trans", [oracle.NOTRANS, oracle.TRANS])
+def test_trmm_variants_sampled_equals_full(uplo, trans):
+    rng = np.random.default_rng(74)
+    n, m = 45, 13
+    A = workloads.uniform_f16(rng, (n, n))
+    B = workloads.uniform_f16(rng, (n, m))
+    Acm, Bcm = np.ascontiguousarray(A.T), np.ascontiguousarray(B.T)
+    full = oracle.trmm(Acm, Bcm, 0.5, uplo, trans)
+    ri, cj = workloads.sample_indices(4, n, m, 100)
+    assert np.array_equal(oracle.trmm_sampled(Acm, Bcm, ri, cj, 0.5, uplo, trans), full[cj, ri])
