@@ -240,6 +240,21 @@ def config_sweep(hg, stream, main_gemm_ms=None, main_trmm_ms=None):
                             "effective_tflops": round(w.flops / (ts[0] * 1e-3) / 1e12, 2),
                             "note": "B 4096x256 (the TRMM page's usage example), level-by-level launches"}
     del Ad, Bd, Od, TA, TB
+    # The page's usage call is the lower, non-transposed product (next row):
+    # n = m = 8192 through hg_trmm (index map of A, B and Out row-reversed).
+    print("[bench] config trmm_8192_lower_notrans ...", file=sys.stderr, flush=True)
+    w = workloads.WORKLOADS["trmm_8192"]
+    TA, TB = workloads.trmm_inputs(w)
+    Ad, Bd = torch.from_numpy(TA).to(dev), torch.from_numpy(TB).to(dev)
+    Od = torch.empty((w.m, w.n), dtype=torch.float32, device=dev)
+    work = torch.empty(hg.trmm_workspace_size(w.n, w.m, "L", False), dtype=torch.uint8, device=dev)
+    ts = _time_calls(lambda: hg.trmm(Ad, Bd, Od, w.alpha, "L", False, w.leaf, work), 5, 20, stream)
+    res["trmm_8192_lower_notrans"] = {
+        "gpu_ms_median": round(ts[0], 5), "gpu_ms_min": round(ts[1], 5),
+        "effective_tflops": round(w.flops / (ts[0] * 1e-3) / 1e12, 2),
+        "note": "Out = A*B, A lower (the TRMM page's usage call): transpose-and-reverse copy of A, "
+                "B and Out row-reversed around the lower-transposed recursion"}
+    del Ad, Bd, Od, TA, TB, work
     for name, w in workloads.TRSM_WORKLOADS.items():
         print(f"[bench] config {name} ...", file=sys.stderr, flush=True)
         A_cm, B_cm = workloads.trsm_inputs(w)

@@ -19,6 +19,10 @@ importing this package raises.
         C = act(alpha·A·B + beta·C + bias) in one launch, bias a float32
         device vector of length N added to every row, act ReLU or none.
 
+    trmm(A, B, Out, alpha=1.0, uplo="L", trans=True, leaf=256, work=None)
+        Out = alpha·op(A)·B for every triangle / transposition (the other
+        three variants through an index map of A into a workspace).
+
     trmm_lower_trans(A, B, Out, alpha=1.0, leaf=256)
     trmm_lower_trans_by_level(A, B, Out, alpha=1.0, leaf=256)
         Out = alpha·Aᵀ·B with A lower triangular (strict upper never read);
@@ -70,6 +74,11 @@ lib.hgemm_bf16.restype = _int
 lib.trmm_lower_trans.argtypes = [_i64, _i64, _f32, _vp, _i64, _vp, _i64, _vp, _i64, _int, _i64,
                                  _vp]
 lib.trmm_lower_trans.restype = _int
+lib.hg_trmm.argtypes = [_int, _int, _i64, _i64, _f32, _vp, _i64, _vp, _i64, _vp, _i64, _int, _i64,
+                        _vp, _i64, _vp]
+lib.hg_trmm.restype = _int
+lib.hg_trmm_workspace_size.argtypes = [_int, _int, _i64, _i64]
+lib.hg_trmm_workspace_size.restype = _i64
 lib.hg_trmm_lower_trans_by_level.argtypes = lib.trmm_lower_trans.argtypes
 lib.hg_trmm_lower_trans_by_level.restype = _int
 lib.trsm_lower_trans.argtypes = [_i64, _i64, _f32, _vp, _i64, _vp, _i64, _vp, _i64, _int, _i64,
@@ -83,7 +92,8 @@ lib.hg_trmm_plan.argtypes = [_i64, _i64, ctypes.POINTER(_i64), _i64]
 lib.hg_trmm_plan.restype = _i64
 
 EXPORTS = ("hgemm", "hgemm_bias_act", "hgemm_bf16", "trmm_lower_trans", "hg_trmm_lower_trans_by_level",
-           "hg_strerror", "hg_trmm_plan", "trsm_lower_trans", "hg_trsm_workspace_size")
+           "hg_strerror", "hg_trmm_plan", "trsm_lower_trans", "hg_trsm_workspace_size", "hg_trmm",
+           "hg_trmm_workspace_size")
 
 ACT_NONE = 0
 ACT_RELU = 1
@@ -253,6 +263,45 @@ def trsm_lower_trans(A, B, Out, alpha: float = 1.0, leaf: int = 256, work=None):
     if st != 0:
         raise HgError("trsm_lower_trans", st)
     return Out
+
+
+def trmm(A, B, Out, alpha: float = 1.0, uplo: str = "L", trans: bool = True, leaf: int = 256,
+         work=None):
+    """Out = alpha·op(A)·B, A lower (uplo "L") or upper ("U") triangular, op
+    the transpose when `trans`; conventions as trmm_lower_trans.  `work` is a
+    device uint8 tensor of at least trmm_workspace_size(...) bytes (allocated
+    with torch for the call when None)."""
+    import torch
+    _check_matrix(A, "A", (torch.float16,))
+    _check_matrix(B, "B", (torch.float16,))
+    _check_matrix(Out, "Out", (torch.float32,))
+    n = A.shape[0]
+    m = B.shape[0]
+    if tuple(A.shape) != (n, n) or B.shape[1] != n or tuple(Out.shape) != (m, n):
+        raise ValueError(f"shape mismatch: A {tuple(A.shape)}, B {tuple(B.shape)}, "
+                         f"Out {tuple(Out.shape)}")
+    if uplo not in ("L", "U"):
+        raise ValueError("uplo must be 'L' or 'U'")
+    u = 0 if uplo == "L" else 1
+    t = 1 if trans else 0
+    need = trmm_workspace_size(n, m, uplo, trans)
+    if work is None and need > 0:
+        work = torch.empty(need, dtype=torch.uint8, device=Out.device)
+    wptr = work.data_ptr() if work is not None else None
+    wbytes = work.numel() * work.element_size() if work is not None else 0
+    st = lib.hg_trmm(u, t, n, m, float(alpha), A.data_ptr() or None, _ld(A), B.data_ptr() or None,
+                     _ld(B), Out.data_ptr() or None, _ld(Out), HG_F32, int(leaf), wptr, wbytes,
+                     _stream_handle(Out))
+    if st != 0:
+        raise HgError("hg_trmm", st)
+    return Out
+
+
+def trmm_workspace_size(n: int, m: int, uplo: str = "L", trans: bool = True) -> int:
+    sz = lib.hg_trmm_workspace_size(0 if uplo == "L" else 1, 1 if trans else 0, n, m)
+    if sz < 0:
+        raise HgError("hg_trmm_workspace_size", int(sz))
+    return int(sz)
 
 
 def trmm_plan(n: int, leaf: int = 256):

@@ -94,6 +94,7 @@ const char *hg_strerror(int status)
     case -13: return "invalid argument 13";
     case -14: return "invalid argument 14";
     case -15: return "invalid argument 15";
+    case -16: return "invalid argument 16";
     default: return "unknown status";
     }
 }
@@ -584,6 +585,119 @@ int trsm_lower_trans(int64_t n, int64_t m, float alpha, const void *A, int64_t l
             return s;
     }
     return r.solve(0, n, false);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Workspace of hg_trmm: L (ldl×n fp16, ldl = n rounded up to 8), then the
+// row-reversed B (ldl×m fp16) when the variant reverses rows; 256-byte
+// aligned parts.
+struct TrmmVariant {
+    int mode = 0;         // index map of A (0: none)
+    bool reverse = false; // B and Out rows reversed
+    int64_t ldl = 0, l_bytes = 0, total = 0;
+};
+
+TrmmVariant trmm_variant(int uplo, int trans, int64_t n, int64_t m)
+{
+    TrmmVariant v;
+    if (uplo == HG_LOWER && trans == HG_TRANS)
+        return v;
+    v.mode = uplo == HG_UPPER ? (trans == HG_NOTRANS ? 1 : 2) : 3;
+    v.reverse = v.mode != 1;
+    v.ldl = round_up(std::max<int64_t>(n, 1), 8);
+    v.l_bytes = round_up(v.ldl * n * 2, 256);
+    v.total = v.l_bytes + (v.reverse ? round_up(v.ldl * m * 2, 256) : 0);
+    return v;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t hg_trmm_workspace_size(int uplo, int trans, int64_t n, int64_t m)
+{
+    if (uplo != HG_LOWER && uplo != HG_UPPER)
+        return -1;
+    if (trans != HG_NOTRANS && trans != HG_TRANS)
+        return -2;
+    if (n < 0)
+        return -3;
+    if (m < 0)
+        return -4;
+    if (n == 0 || m == 0)
+        return 0;
+    return trmm_variant(uplo, trans, n, m).total;
+}
+
+int hg_trmm(int uplo, int trans, int64_t n, int64_t m, float alpha, const void *A, int64_t lda,
+            const void *B, int64_t ldb, void *Out, int64_t ldo, int out_dtype, int64_t leaf,
+            void *work, int64_t work_bytes, void *stream)
+{
+    if (uplo != HG_LOWER && uplo != HG_UPPER)
+        return -1;
+    if (trans != HG_NOTRANS && trans != HG_TRANS)
+        return -2;
+    if (n < 0 || n > kI32Max)
+        return -3;
+    if (m < 0 || m > kI32Max)
+        return -4;
+    if (lda < std::max<int64_t>(1, n))
+        return -7;
+    if (ldb < std::max<int64_t>(1, n))
+        return -9;
+    if (ldo < std::max<int64_t>(1, n))
+        return -11;
+    if (out_dtype != HG_F32)
+        return -12;
+    if (n == 0 || m == 0)
+        return HG_OK;
+    if (Out == nullptr)
+        return -10;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (alpha == 0.0f)
+        return hip_status(hg::launch_scale(Out, ldo, m, n, 0.0f, false, s));
+    if (A == nullptr)
+        return -6;
+    if (B == nullptr)
+        return -8;
+    const Extent eo = extent(Out, m, ldo, n, 4);
+    const Extent ea = extent(A, n, lda, n, 2);
+    const Extent eb = extent(B, m, ldb, n, 2);
+    if (overlap(eo, ea) || overlap(eo, eb))
+        return -10;
+    const TrmmVariant v = trmm_variant(uplo, trans, n, m);
+    if (v.mode == 0)
+        return trmm_impl(n, m, alpha, A, lda, B, ldb, Out, ldo, out_dtype, leaf, stream, true);
+    if (work == nullptr || !aligned16(work))
+        return -14;
+    if (work_bytes < v.total)
+        return -15;
+    const Extent ew = {reinterpret_cast<uintptr_t>(work), reinterpret_cast<uintptr_t>(work) + (uintptr_t)v.total};
+    if (overlap(ew, eo) || overlap(ew, ea) || overlap(ew, eb))
+        return -14;
+    _Float16 *L = static_cast<_Float16 *>(work);
+    int st = hip_status(hg::launch_tri_xform(v.mode, static_cast<const _Float16 *>(A), lda, L, v.ldl, n, s));
+    if (st != HG_OK)
+        return st;
+    const void *Bin = B;
+    int64_t ldbin = ldb;
+    if (v.reverse) {
+        _Float16 *Bp = reinterpret_cast<_Float16 *>(static_cast<unsigned char *>(work) + v.l_bytes);
+        st = hip_status(hg::launch_row_reverse_copy(static_cast<const _Float16 *>(B), ldb, Bp, v.ldl, n, m, s));
+        if (st != HG_OK)
+            return st;
+        Bin = Bp;
+        ldbin = v.ldl;
+    }
+    st = trmm_impl(n, m, alpha, L, v.ldl, Bin, ldbin, Out, ldo, out_dtype, leaf, stream, true);
+    if (st != HG_OK)
+        return st;
+    if (v.reverse)
+        st = hip_status(hg::launch_row_reverse_inplace(static_cast<float *>(Out), ldo, n, m, s));
+    return st;
 }
 
 }  // extern "C"

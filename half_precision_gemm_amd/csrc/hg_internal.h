@@ -125,6 +125,15 @@ hipError_t launch_trsm_inv(const TrsmInvParams &p, hipStream_t stream);
 // ldo % 4 == 0, ldw % 4 == 0 (vector loads and stores).
 hipError_t launch_trsm_leaf(const TrsmLeafParams &p, bool vec, hipStream_t stream);
 
+// TRMM variants (hg_xform.hip): L = map(A) on L's lower triangle (mode 1:
+// A(c, r), 2: A(n-1-r, n-1-c), 3: A(n-1-c, n-1-r)); B's rows reversed into
+// Bp; Out's rows reversed in place.
+hipError_t launch_tri_xform(int mode, const _Float16 *A, int64_t lda, _Float16 *L, int64_t ldl,
+                            int64_t n, hipStream_t stream);
+hipError_t launch_row_reverse_copy(const _Float16 *B, int64_t ldb, _Float16 *Bp, int64_t ldp, int64_t n,
+                                   int64_t m, hipStream_t stream);
+hipError_t launch_row_reverse_inplace(float *Out, int64_t ldo, int64_t n, int64_t m, hipStream_t stream);
+
 // C = beta·C over an M×N window (beta == 0 writes zeros without reading);
 // with `bias` or `act`, C = act(beta·C + bias[j]) (the alpha = 0 / K = 0
 // case of the fused epilogue).

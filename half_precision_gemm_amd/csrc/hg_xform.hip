@@ -1,0 +1,154 @@
+// hg_xform.hip — the index maps that turn every TRMM variant of
+// "异构计算中高性能TRMM与TRSM的递归算法实现" (§2.1 shows the lower and the upper
+// blocking; §5.1 calls the lower, non-transposed product) into the lower
+// transposed one the recursive driver runs.
+//
+// With P the reversal permutation ((P·X)(r, ·) = X(n-1-r, ·)), U upper and
+// A lower triangular:
+//   upper, non-transposed:  U·B = (Uᵀ)ᵀ·B                L = Uᵀ
+//   upper, transposed:      P·(Uᵀ·B) = (P·U·P)ᵀ·(P·B)     L = P·U·P
+//   lower, non-transposed:  P·(A·B) = (P·Aᵀ·P)ᵀ·(P·B)     L = P·Aᵀ·P
+// and each L is lower triangular, so the driver runs Lᵀ·B on it, with B and
+// Out row-reversed in the last two cases (lower, transposed needs no map).
+// These are memory-bound copies (the TRMM itself is the compute).
+#include "hg_internal.h"
+
+namespace hg {
+namespace {
+
+constexpr int XT = 64;   // tile edge
+
+// L(r, c) for r >= c tiles only (the driver never reads L's strict upper
+// triangle; the diagonal tiles' upper parts get whatever the map yields):
+//   MODE 1: A(c, r)            transpose
+//   MODE 2: A(n-1-r, n-1-c)    reverse both indices
+//   MODE 3: A(n-1-c, n-1-r)    transpose and reverse
+// One workgroup per 64×64 tile of L's lower triangle; the transposing modes
+// stage the tile in LDS so that reads and writes both run along columns.
+template <int MODE>
+__global__ void __launch_bounds__(256) tri_xform_kernel(const _Float16 *__restrict__ A, int64_t lda,
+                                                        _Float16 *__restrict__ L, int64_t ldl, int n)
+{
+    __shared__ _Float16 tile[XT][XT + 2];
+    // blockIdx.x → (tile row tr >= tile column tc), row-major over the triangle
+    const int b = blockIdx.x;
+    int tr = (int)((__builtin_sqrtf(8.0f * (float)b + 1.0f) - 1.0f) * 0.5f);
+    while ((tr + 1) * (tr + 2) / 2 <= b)
+        ++tr;
+    while (tr * (tr + 1) / 2 > b)
+        --tr;
+    const int tc = b - tr * (tr + 1) / 2;
+    const int r0 = tr * XT, c0 = tc * XT;
+    const int t = threadIdx.x;
+    const int i = t % XT, g = t / XT;   // i: position along a column, g: column group
+    if constexpr (MODE == 2) {
+#pragma unroll 4
+        for (int q = 0; q < XT / 4; ++q) {
+            const int r = r0 + i, c = c0 + g + 4 * q;
+            if (r < n && c < n)
+                L[r + (int64_t)c * ldl] = A[(n - 1 - r) + (int64_t)(n - 1 - c) * lda];
+        }
+    } else {
+        // Source columns are L's rows: load A's tile column by column.
+#pragma unroll 4
+        for (int q = 0; q < XT / 4; ++q) {
+            const int cl = c0 + i;            // L column ...
+            const int rl = r0 + g + 4 * q;    // ... and row of this element
+            if (cl < n && rl < n) {
+                const int64_t src = MODE == 1 ? cl + (int64_t)rl * lda
+                                              : (n - 1 - cl) + (int64_t)(n - 1 - rl) * lda;
+                tile[i][g + 4 * q] = A[src];
+            }
+        }
+        __syncthreads();
+#pragma unroll 4
+        for (int q = 0; q < XT / 4; ++q) {
+            const int rl = r0 + i, cl = c0 + g + 4 * q;
+            if (rl < n && cl < n)
+                L[rl + (int64_t)cl * ldl] = tile[g + 4 * q][i];
+        }
+    }
+}
+
+// Bp(r, j) = B(n-1-r, j), column-major, fp16.
+__global__ void __launch_bounds__(256) row_reverse_copy_kernel(const _Float16 *__restrict__ B, int64_t ldb,
+                                                               _Float16 *__restrict__ Bp, int64_t ldp,
+                                                               int64_t n, int64_t m)
+{
+    const int64_t total = n * m;
+    for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+         idx += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t j = idx / n, r = idx - j * n;
+        Bp[r + j * ldp] = B[(n - 1 - r) + j * ldb];
+    }
+}
+
+// Out(r, j) <-> Out(n-1-r, j) for r < n/2, in place, fp32.
+__global__ void __launch_bounds__(256) row_reverse_inplace_kernel(float *__restrict__ Out, int64_t ldo,
+                                                                  int64_t n, int64_t m)
+{
+    const int64_t h = n / 2;
+    const int64_t total = h * m;
+    for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+         idx += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t j = idx / h, r = idx - j * h;
+        float *col = Out + j * ldo;
+        const float a = col[r], b = col[n - 1 - r];
+        col[r] = b;
+        col[n - 1 - r] = a;
+    }
+}
+
+unsigned grid_for(int64_t total)
+{
+    int64_t blocks = (total + 255) / 256;
+    return (unsigned)(blocks > 65536 ? 65536 : (blocks < 1 ? 1 : blocks));
+}
+
+}  // namespace
+
+hipError_t launch_tri_xform(int mode, const _Float16 *A, int64_t lda, _Float16 *L, int64_t ldl,
+                            int64_t n, hipStream_t stream)
+{
+    if (n <= 0)
+        return hipSuccess;
+    const int64_t nt = (n + XT - 1) / XT;
+    const int64_t tiles = nt * (nt + 1) / 2;
+    if (tiles > 0x7fffffff || n > 0x7fffffff)
+        return hipErrorInvalidValue;
+    switch (mode) {
+    case 1:
+        hipLaunchKernelGGL(tri_xform_kernel<1>, dim3((unsigned)tiles), dim3(256), 0, stream, A, lda, L, ldl, (int)n);
+        break;
+    case 2:
+        hipLaunchKernelGGL(tri_xform_kernel<2>, dim3((unsigned)tiles), dim3(256), 0, stream, A, lda, L, ldl, (int)n);
+        break;
+    case 3:
+        hipLaunchKernelGGL(tri_xform_kernel<3>, dim3((unsigned)tiles), dim3(256), 0, stream, A, lda, L, ldl, (int)n);
+        break;
+    default:
+        return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_row_reverse_copy(const _Float16 *B, int64_t ldb, _Float16 *Bp, int64_t ldp, int64_t n,
+                                   int64_t m, hipStream_t stream)
+{
+    if (n <= 0 || m <= 0)
+        return hipSuccess;
+    hipLaunchKernelGGL(row_reverse_copy_kernel, dim3(grid_for(n * m)), dim3(256), 0, stream, B, ldb, Bp,
+                       ldp, n, m);
+    return hipGetLastError();
+}
+
+hipError_t launch_row_reverse_inplace(float *Out, int64_t ldo, int64_t n, int64_t m, hipStream_t stream)
+{
+    if (n <= 1 || m <= 0)
+        return hipSuccess;
+    hipLaunchKernelGGL(row_reverse_inplace_kernel, dim3(grid_for((n / 2) * m)), dim3(256), 0, stream, Out,
+                       ldo, n, m);
+    return hipGetLastError();
+}
+
+}  // namespace hg

@@ -51,6 +51,12 @@ extern "C" {
 #define HG_F32 1
 #define HG_BF16 2
 
+/* Triangle and transposition of hg_trmm. */
+#define HG_LOWER 0
+#define HG_UPPER 1
+#define HG_NOTRANS 0
+#define HG_TRANS 1
+
 /* Activation of hgemm_bias_act. */
 #define HG_ACT_NONE 0
 #define HG_ACT_RELU 1
@@ -170,6 +176,40 @@ int trmm_lower_trans(int64_t n, int64_t m, float alpha,
                      const void *B, int64_t ldb,
                      void *Out, int64_t ldo, int out_dtype,
                      int64_t leaf, void *stream);
+
+/*
+ * hg_trmm — Out = alpha·op(A)·B for every triangle and transposition
+ * ("异构计算中高性能TRMM与TRSM的递归算法实现" §2.1 shows the lower and upper
+ * blockings; its §5.1 usage calls the lower, non-transposed product).
+ *
+ *  1 uplo        : HG_LOWER (A(r,c) read for r >= c) or HG_UPPER (r <= c);
+ *                  the other triangle is never referenced.
+ *  2 trans       : HG_TRANS (op(A) = Aᵀ) or HG_NOTRANS (op(A) = A).
+ *  3 n, 4 m, 5 alpha, 6 A, 7 lda, 8 B, 9 ldb, 10 Out, 11 ldo, 12 out_dtype,
+ * 13 leaf        : as trmm_lower_trans (column-major, Out fp32, write-only).
+ * 14 work        : device workspace, 16-byte aligned, of at least
+ * 15 work_bytes    hg_trmm_workspace_size(uplo, trans, n, m) bytes (0 for
+ *                  HG_LOWER/HG_TRANS, which is trmm_lower_trans itself and
+ *                  ignores work); must not overlap A, B or Out (-14; too
+ *                  small: -15).
+ * 16 stream      : hipStream_t to launch on.
+ *
+ * The other three variants run the same recursion on a lower triangular L
+ * that one copy kernel builds in the workspace (P reverses the row order):
+ * upper/notrans: L = Aᵀ; upper/trans: P·Out = (P·A·P)ᵀ·(P·B);
+ * lower/notrans: P·Out = (P·Aᵀ·P)ᵀ·(P·B); for the last two B's rows are
+ * reversed into the workspace and Out's rows are reversed in place at the
+ * end.  The arithmetic is trmm_lower_trans's on L.
+ */
+int hg_trmm(int uplo, int trans, int64_t n, int64_t m, float alpha,
+            const void *A, int64_t lda,
+            const void *B, int64_t ldb,
+            void *Out, int64_t ldo, int out_dtype,
+            int64_t leaf, void *work, int64_t work_bytes, void *stream);
+
+/* hg_trmm_workspace_size — bytes of workspace hg_trmm needs (host only);
+ * -1/-2 for a bad uplo/trans, -3/-4 for n/m < 0. */
+int64_t hg_trmm_workspace_size(int uplo, int trans, int64_t n, int64_t m);
 
 /*
  * hg_trmm_lower_trans_by_level — trmm_lower_trans (same arguments, same

@@ -29,7 +29,8 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["hg_strerror", "hg_trmm_lower_trans_by_level", "hg_trmm_plan",
+    assert declared_functions() == ["hg_strerror", "hg_trmm", "hg_trmm_lower_trans_by_level",
+                                    "hg_trmm_plan", "hg_trmm_workspace_size",
                                     "hg_trsm_workspace_size", "hgemm", "hgemm_bf16",
                                     "hgemm_bias_act", "trmm_lower_trans", "trsm_lower_trans"]
 
@@ -187,6 +188,41 @@ def test_trsm_workspace_size_errors(lib):
     assert _trsm_need(lib, 4, -1, 256) == -2
     assert _trsm_need(lib, 4, 4, 300) == -3
     assert _trsm_need(lib, 0, 4, 256) == 0 and _trsm_need(lib, 4, 0, 256) == 0
+
+
+@pytest.mark.parametrize("args,code", [
+    ((2, 1, 8, 4, 1.0, P, 8, Q, 8, R, 8, 1, 256, W, 1 << 30), -1),
+    ((0, 2, 8, 4, 1.0, P, 8, Q, 8, R, 8, 1, 256, W, 1 << 30), -2),
+    ((0, 0, -1, 4, 1.0, P, 8, Q, 8, R, 8, 1, 256, W, 1 << 30), -3),
+    ((0, 0, 8, -1, 1.0, P, 8, Q, 8, R, 8, 1, 256, W, 1 << 30), -4),
+    ((0, 0, 8, 4, 1.0, P, 7, Q, 8, R, 8, 1, 256, W, 1 << 30), -7),
+    ((0, 0, 8, 4, 1.0, P, 8, Q, 7, R, 8, 1, 256, W, 1 << 30), -9),
+    ((0, 0, 8, 4, 1.0, P, 8, Q, 8, R, 7, 1, 256, W, 1 << 30), -11),
+    ((0, 0, 8, 4, 1.0, P, 8, Q, 8, R, 8, 0, 256, W, 1 << 30), -12),
+    ((0, 0, 8, 4, 1.0, P, 8, Q, 8, None, 8, 1, 256, W, 1 << 30), -10),
+    ((0, 0, 8, 4, 1.0, None, 8, Q, 8, R, 8, 1, 256, W, 1 << 30), -6),
+    ((0, 0, 8, 4, 1.0, P, 8, None, 8, R, 8, 1, 256, W, 1 << 30), -8),
+    ((0, 0, 8, 4, 1.0, P, 8, Q, 8, R, 8, 1, 256, None, 1 << 30), -14),
+    ((1, 1, 8, 4, 1.0, P, 8, Q, 8, R, 8, 1, 256, W + 4, 1 << 30), -14),
+    ((1, 0, 8, 4, 1.0, P, 8, Q, 8, R, 8, 1, 256, W, 8), -15),
+    ((0, 0, 0, 4, 1.0, None, 1, None, 1, None, 1, 1, 256, None, 0), 0),
+])
+def test_hg_trmm_argument_errors(lib, args, code):
+    assert lib.hg_trmm(*args, None) == code
+
+
+def test_hg_trmm_workspace_size(lib):
+    up = lambda x: -(-x // 256) * 256
+    ldl = -(-1000 // 8) * 8
+    assert lib.hg_trmm_workspace_size(0, 1, 1000, 77) == 0                   # lower, trans
+    assert lib.hg_trmm_workspace_size(1, 0, 1000, 77) == up(ldl * 1000 * 2)  # upper, notrans
+    both = up(ldl * 1000 * 2) + up(ldl * 77 * 2)
+    assert lib.hg_trmm_workspace_size(1, 1, 1000, 77) == both               # upper, trans
+    assert lib.hg_trmm_workspace_size(0, 0, 1000, 77) == both               # lower, notrans
+    assert lib.hg_trmm_workspace_size(2, 0, 4, 4) == -1
+    assert lib.hg_trmm_workspace_size(0, 2, 4, 4) == -2
+    assert lib.hg_trmm_workspace_size(0, 0, -1, 4) == -3
+    assert lib.hg_trmm_workspace_size(0, 0, 4, -1) == -4
 
 
 def test_strerror(hg):

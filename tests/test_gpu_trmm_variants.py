@@ -1,0 +1,98 @@
+"""GPU parity of hg_trmm, Out = α·op(A)·B for A lower or upper and op = A or
+Aᵀ ("异构计算中高性能TRMM与TRSM的递归算法实现" §2.1 and the §5.1 usage call),
+against the fp64 oracle, through the C ABI.  Same rule as the TRMM:
+|gpu − ref| <= 1e-3·sqrt(n) + 2^-10·|ref|; integer inputs bit-exact."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from tolerance import check_close
+
+pytestmark = pytest.mark.gpu
+
+VARIANTS = [("L", True), ("L", False), ("U", True), ("U", False)]
+
+
+def _inputs(n, m, seed, uplo, other_fill=0.0):
+    rng = np.random.default_rng(seed)
+    S = workloads.uniform_f16(rng, (n, n))
+    D = workloads.uniform_f16(rng, (n,), 0.5, 1.5)
+    B = workloads.uniform_f16(rng, (n, m))
+    A = np.tril(S, -1) if uplo == "L" else np.triu(S, 1)
+    A[np.arange(n), np.arange(n)] = D
+    if other_fill != 0.0:
+        A[np.triu_indices(n, 1) if uplo == "L" else np.tril_indices(n, -1)] = other_fill
+    return np.ascontiguousarray(A.T), np.ascontiguousarray(B.T)
+
+
+def run(hg, A_cm, B_cm, alpha, uplo, trans, leaf=256):
+    import torch
+    dev = torch.device("cuda:0")
+    n, m = A_cm.shape[0], B_cm.shape[0]
+    print(f"[trmm-variant] n={n} m={m} uplo={uplo} trans={trans} leaf={leaf}", flush=True)
+    A = torch.from_numpy(A_cm).to(dev)
+    B = torch.from_numpy(B_cm).to(dev)
+    Out = torch.full((m, n), float("nan"), dtype=torch.float32, device=dev)
+    hg.trmm(A, B, Out, alpha, uplo, trans, leaf)
+    torch.cuda.synchronize()
+    return Out.cpu().numpy()
+
+
+def _ref(A_cm, B_cm, alpha, uplo, trans):
+    return oracle.trmm(A_cm, B_cm, alpha, oracle.LOWER if uplo == "L" else oracle.UPPER,
+                       oracle.TRANS if trans else oracle.NOTRANS)
+
+
+@pytest.mark.parametrize("uplo,trans", VARIANTS)
+@pytest.mark.parametrize("n,m,leaf", [(1, 1, 256), (2, 5, 256), (300, 77, 256), (1000, 50, 100),
+                                      (2048, 300, 256), (4096, 256, 256), (777, 64, 64)])
+def test_parity(hg, uplo, trans, n, m, leaf):
+    A_cm, B_cm = _inputs(n, m, n + m, uplo)
+    got = run(hg, A_cm, B_cm, -0.75, uplo, trans, leaf)
+    check_close(got, _ref(A_cm, B_cm, -0.75, uplo, trans), n, f"{uplo}{'T' if trans else 'N'} n={n} m={m}")
+
+
+@pytest.mark.parametrize("uplo,trans", VARIANTS)
+def test_other_triangle_never_read(hg, uplo, trans):
+    n, m = 700, 33
+    A0, B_cm = _inputs(n, m, 5, uplo)
+    Ax, _ = _inputs(n, m, 5, uplo, np.nan)
+    assert np.array_equal(run(hg, A0, B_cm, 1.0, uplo, trans).view(np.uint32),
+                          run(hg, Ax, B_cm, 1.0, uplo, trans).view(np.uint32))
+
+
+@pytest.mark.parametrize("uplo,trans", VARIANTS)
+def test_integer_bit_exact(hg, uplo, trans):
+    rng = np.random.default_rng(8)
+    n, m = 1024, 96
+    T = (np.tril if uplo == "L" else np.triu)(workloads.integer_f16(rng, (n, n)))
+    B = workloads.integer_f16(rng, (n, m))
+    A_cm, B_cm = np.ascontiguousarray(T.T), np.ascontiguousarray(B.T)
+    got = run(hg, A_cm, B_cm, 1.0, uplo, trans)
+    assert np.array_equal(got.astype(np.float64), _ref(A_cm, B_cm, 1.0, uplo, trans))
+
+
+def test_lower_trans_is_trmm_lower_trans_bits(hg):
+    import torch
+    n, m = 2048, 512
+    A_cm, B_cm = _inputs(n, m, 9, "L")
+    got = run(hg, A_cm, B_cm, 1.25, "L", True)
+    dev = torch.device("cuda:0")
+    Out = torch.empty((m, n), dtype=torch.float32, device=dev)
+    hg.trmm_lower_trans(torch.from_numpy(A_cm).to(dev), torch.from_numpy(B_cm).to(dev), Out, 1.25)
+    torch.cuda.synchronize()
+    assert np.array_equal(got.view(np.uint32), Out.cpu().numpy().view(np.uint32))
+
+
+@pytest.mark.parametrize("uplo,trans", [("L", False), ("U", False)])
+def test_8192_sampled(hg, uplo, trans):
+    """n = m = 8192 for the non-transposed variants (the page's usage call is
+    lower, non-transposed), 1024 sampled entries."""
+    n = m = 8192
+    A_cm, B_cm = _inputs(n, m, 11, uplo)
+    got = run(hg, A_cm, B_cm, 1.0, uplo, trans)
+    ri, cj = workloads.sample_indices(11, n, m)
+    ref = oracle.trmm_sampled(A_cm, B_cm, ri, cj, 1.0, oracle.LOWER if uplo == "L" else oracle.UPPER,
+                              oracle.TRANS if trans else oracle.NOTRANS)
+    check_close(got[cj, ri], ref, n, f"{uplo}N 8192 sampled")
