@@ -300,8 +300,6 @@ __global__ void __launch_bounds__(256, 1) trsm_leaf_kernel(const TrsmLeafParams 
     // Fragments: lane l supplies row (l mod 32) of a 32-row block and the 8
     // consecutive k from 8·(l div 32) of the current 16-wide k step, for both
     // operands; the V fragment goes first, so each 32×32 result is Cᵀ.
-    if (64 * wave >= s)
-        return;
     const int frow = lane & 31;
     const int fkc = lane >> 5;
     floatx16 acc[2];
@@ -311,7 +309,7 @@ __global__ void __launch_bounds__(256, 1) trsm_leaf_kernel(const TrsmLeafParams 
     const int nst = (s + 15) / 16;
 #pragma unroll
     for (int st = 0; st < LBK / 16; ++st) {
-        if (st >= nst || 16 * st + 16 <= 64 * wave)
+        if (64 * wave >= s || st >= nst || 16 * st + 16 <= 64 * wave)
             continue;
         const int kc = 2 * st + fkc;
         const half8 af = *reinterpret_cast<const half8 *>(Rs + lds_chunk(frow, kc) * 16);
@@ -325,32 +323,48 @@ __global__ void __launch_bounds__(256, 1) trsm_leaf_kernel(const TrsmLeafParams 
         }
     }
 
-    // Epilogue: block b of this wave holds C(i, j..j+3) for
+    // Epilogue, staged through LDS (the inverse's area, free once every wave
+    // is past its last MFMA): block b of this wave holds C(i, j..j+3) for
     // i = m0 + (lane mod 32) and, in register group g,
-    // j = 64·wave + 32b + 8g + 4·(lane div 32).
-    const int i = m0 + frow;
-    if (i >= M)
-        return;
-    float *orow = p.Out + o + (int64_t)i * p.ldo;
-    _Float16 *wrow = p.W + o + (int64_t)i * p.ldw;
+    // j = 64·wave + 32b + 8g + 4·(lane div 32).  Written to LDS as rows i of
+    // 256 fp32, then each store instruction writes one column i of X: 64
+    // lanes × 4 rows = the column's 1 KiB of fp32 and 512 B of fp16, whole
+    // cache lines (scattered 16-byte pieces tripled the written bytes).
+    float *Xs = reinterpret_cast<float *>(Vs);
+    constexpr int XLD = LBN + 4;                 // padded row of the staged tile
+    __syncthreads();
+    if (64 * wave < s) {
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
+        for (int b = 0; b < 2; ++b)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const int j = 64 * wave + 32 * b + 8 * g + 4 * fkc;
-            const floatx4 v = {acc[b][4 * g + 0], acc[b][4 * g + 1], acc[b][4 * g + 2], acc[b][4 * g + 3]};
-            if (VEC && j + 4 <= s) {
-                *reinterpret_cast<floatx4 *>(orow + j) = v;
-                const halfx4 h = {(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
-                *reinterpret_cast<halfx4 *>(wrow + j) = h;
-            } else {
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    if (j + e < s) {
-                        orow[j + e] = v[e];
-                        wrow[j + e] = (_Float16)v[e];
-                    }
+            for (int g = 0; g < 4; ++g) {
+                const int j = 64 * wave + 32 * b + 8 * g + 4 * fkc;
+                *reinterpret_cast<floatx4 *>(Xs + frow * XLD + j) =
+                    floatx4{acc[b][4 * g + 0], acc[b][4 * g + 1], acc[b][4 * g + 2], acc[b][4 * g + 3]};
             }
+    }
+    __syncthreads();
+    const int j = 4 * lane;                      // rows j..j+3 of each column
+#pragma unroll
+    for (int c = 0; c < LBM / 4; ++c) {
+        const int il = wave + 4 * c;
+        const int i = m0 + il;
+        if (i >= M || j >= s)
+            continue;
+        const floatx4 v = *reinterpret_cast<const floatx4 *>(Xs + il * XLD + j);
+        float *orow = p.Out + o + (int64_t)i * p.ldo;
+        _Float16 *wrow = p.W + o + (int64_t)i * p.ldw;
+        if (VEC && j + 4 <= s) {
+            *reinterpret_cast<floatx4 *>(orow + j) = v;
+            *reinterpret_cast<halfx4 *>(wrow + j) =
+                halfx4{(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (j + e < s) {
+                    orow[j + e] = v[e];
+                    wrow[j + e] = (_Float16)v[e];
+                }
         }
     }
 }
