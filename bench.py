@@ -227,6 +227,22 @@ def config_sweep(hg, stream, main_gemm_ms=None, main_trmm_ms=None):
         "note": "bf16 A, B (v_mfma_f32_16x16x32_bf16), fp32 accumulation and C; dense bf16 peak "
                 "equals the fp16 one"}
     del Ad, Btd, Cd, Ab, Bb
+    # Row-major B (next row; the GPU architecture page's matmul layout):
+    # 8192³, fp32 C, B transposed into a workspace, then the GEMM.
+    print("[bench] config hgemm_rowmajor_b_8192 ...", file=sys.stderr, flush=True)
+    A, Bt, _ = workloads.gemm_inputs(w)
+    Ad = torch.from_numpy(A).to(dev)
+    Brd = torch.from_numpy(np.ascontiguousarray(Bt.T)).to(dev)
+    Cd = torch.empty((w.M, w.N), dtype=torch.float32, device=dev)
+    work = torch.empty(hg.lib.hg_hgemm_layout_workspace_size(0, 0, w.M, w.N, w.K), dtype=torch.uint8,
+                       device=dev)
+    tl = _time_calls(lambda: hg.hgemm_layout(Ad, Brd, Cd, False, True, work=work), 20, 30, stream)
+    res["hgemm_rowmajor_b_8192"] = {
+        "gpu_ms_median": round(tl[0], 5), "gpu_ms_min": round(tl[1], 5),
+        "tflops": round(w.flops / (tl[0] * 1e-3) / 1e12, 2),
+        "note": "B given K x N row-major: one tiled transpose (128 MiB read + written) into the "
+                "workspace, then the K-contiguous GEMM"}
+    del Ad, Brd, Cd, work, A, Bt
     # Skinny right-hand side (next row): the TRMM page's usage example,
     # n = 4096, m = 256.
     print("[bench] config trmm_4096x256 ...", file=sys.stderr, flush=True)

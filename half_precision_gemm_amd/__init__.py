@@ -15,6 +15,10 @@ importing this package raises.
     hgemm_bf16(A, Bt, C, alpha=1.0, beta=0.0)
         hgemm with bfloat16 A and Bt; C bfloat16 or float32.
 
+    hgemm_layout(A, B, C, a_col_major=False, b_row_major=False, alpha, beta, work)
+        hgemm with A column-major and/or B row-major (transposed into a
+        workspace first).
+
     hgemm_bias_act(A, Bt, C, bias=None, relu=False, alpha=1.0, beta=0.0)
         C = act(alpha·A·B + beta·C + bias) in one launch, bias a float32
         device vector of length N added to every row, act ReLU or none.
@@ -69,6 +73,11 @@ lib.hgemm.restype = _int
 lib.hgemm_bias_act.argtypes = [_i64, _i64, _i64, _f32, _vp, _i64, _vp, _i64, _f32, _vp, _i64, _int,
                                _vp, _int, _vp]
 lib.hgemm_bias_act.restype = _int
+lib.hgemm_layout.argtypes = [_int, _int, _i64, _i64, _i64, _f32, _vp, _i64, _vp, _i64, _f32, _vp,
+                             _i64, _int, _vp, _i64, _vp]
+lib.hgemm_layout.restype = _int
+lib.hg_hgemm_layout_workspace_size.argtypes = [_int, _int, _i64, _i64, _i64]
+lib.hg_hgemm_layout_workspace_size.restype = _i64
 lib.hgemm_bf16.argtypes = lib.hgemm.argtypes
 lib.hgemm_bf16.restype = _int
 lib.trmm_lower_trans.argtypes = [_i64, _i64, _f32, _vp, _i64, _vp, _i64, _vp, _i64, _int, _i64,
@@ -93,7 +102,10 @@ lib.hg_trmm_plan.restype = _i64
 
 EXPORTS = ("hgemm", "hgemm_bias_act", "hgemm_bf16", "trmm_lower_trans", "hg_trmm_lower_trans_by_level",
            "hg_strerror", "hg_trmm_plan", "trsm_lower_trans", "hg_trsm_workspace_size", "hg_trmm",
-           "hg_trmm_workspace_size")
+           "hg_trmm_workspace_size", "hgemm_layout", "hg_hgemm_layout_workspace_size")
+
+ROW_MAJOR = 0
+COL_MAJOR = 1
 
 ACT_NONE = 0
 ACT_RELU = 1
@@ -150,6 +162,40 @@ def hgemm(A, Bt, C, alpha: float = 1.0, beta: float = 0.0):
                    _stream_handle(C))
     if st != 0:
         raise HgError("hgemm", st)
+    return C
+
+
+def hgemm_layout(A, B, C, a_col_major: bool = False, b_row_major: bool = False,
+                 alpha: float = 1.0, beta: float = 0.0, work=None):
+    """C = alpha·A·B + beta·C with A given M×K row-major (a (M, K) tensor) or
+    column-major (a (K, M) tensor holding Aᵀ), and B given K×N column-major
+    (an (N, K) tensor, hgemm's Bt) or row-major (a (K, N) tensor).  C is
+    (M, N).  `work`: device uint8 tensor of at least
+    hgemm_layout_workspace_size(...) bytes (allocated with torch when None)."""
+    import torch
+    _check_matrix(A, "A", (torch.float16,))
+    _check_matrix(B, "B", (torch.float16,))
+    _check_matrix(C, "C", (torch.float16, torch.float32))
+    M, N = C.shape
+    K = A.shape[0] if a_col_major else A.shape[1]
+    if (A.shape[1] if a_col_major else A.shape[0]) != M:
+        raise ValueError(f"A {tuple(A.shape)} does not match C {tuple(C.shape)}")
+    if tuple(B.shape) != ((K, N) if b_row_major else (N, K)):
+        raise ValueError(f"B {tuple(B.shape)} does not match K={K}, N={N}")
+    al, bl = (COL_MAJOR if a_col_major else ROW_MAJOR), (ROW_MAJOR if b_row_major else COL_MAJOR)
+    need = lib.hg_hgemm_layout_workspace_size(al, bl, M, N, K)
+    if need < 0:
+        raise HgError("hg_hgemm_layout_workspace_size", int(need))
+    if work is None and need > 0:
+        work = torch.empty(need, dtype=torch.uint8, device=C.device)
+    wptr = work.data_ptr() if work is not None else None
+    wbytes = work.numel() * work.element_size() if work is not None else 0
+    out_dtype = HG_F16 if C.dtype == torch.float16 else HG_F32
+    st = lib.hgemm_layout(al, bl, M, N, K, float(alpha), A.data_ptr() or None, _ld(A),
+                          B.data_ptr() or None, _ld(B), float(beta), C.data_ptr() or None, _ld(C),
+                          out_dtype, wptr, wbytes, _stream_handle(C))
+    if st != 0:
+        raise HgError("hgemm_layout", st)
     return C
 
 

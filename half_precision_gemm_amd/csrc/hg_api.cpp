@@ -95,6 +95,7 @@ const char *hg_strerror(int status)
     case -14: return "invalid argument 14";
     case -15: return "invalid argument 15";
     case -16: return "invalid argument 16";
+    case -17: return "invalid argument 17";
     default: return "unknown status";
     }
 }
@@ -698,6 +699,126 @@ int hg_trmm(int uplo, int trans, int64_t n, int64_t m, float alpha, const void *
     if (v.reverse)
         st = hip_status(hg::launch_row_reverse_inplace(static_cast<float *>(Out), ldo, n, m, s));
     return st;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Workspace of hgemm_layout: A in the native row-major M×K form when it is
+// given column-major, then B in the native N×K (K-contiguous) form when it
+// is given row-major; ld = K rounded up to 8, parts 256-byte aligned.
+struct GemmLayout {
+    int64_t ldk = 0, a_bytes = 0, b_bytes = 0;
+};
+
+GemmLayout gemm_layout(int a_layout, int b_layout, int64_t M, int64_t N, int64_t K)
+{
+    GemmLayout g;
+    g.ldk = round_up(std::max<int64_t>(K, 1), 8);
+    g.a_bytes = a_layout == HG_COL_MAJOR ? round_up(M * g.ldk * 2, 256) : 0;
+    g.b_bytes = b_layout == HG_ROW_MAJOR ? round_up(N * g.ldk * 2, 256) : 0;
+    return g;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t hg_hgemm_layout_workspace_size(int a_layout, int b_layout, int64_t M, int64_t N, int64_t K)
+{
+    if (a_layout != HG_ROW_MAJOR && a_layout != HG_COL_MAJOR)
+        return -1;
+    if (b_layout != HG_ROW_MAJOR && b_layout != HG_COL_MAJOR)
+        return -2;
+    if (M < 0 || N < 0 || K < 0)
+        return -3;
+    if (M == 0 || N == 0 || K == 0)
+        return 0;
+    const GemmLayout g = gemm_layout(a_layout, b_layout, M, N, K);
+    return g.a_bytes + g.b_bytes;
+}
+
+int hgemm_layout(int a_layout, int b_layout, int64_t M, int64_t N, int64_t K, float alpha,
+                 const void *A, int64_t lda, const void *B, int64_t ldb, float beta, void *C,
+                 int64_t ldc, int out_dtype, void *work, int64_t work_bytes, void *stream)
+{
+    if (a_layout != HG_ROW_MAJOR && a_layout != HG_COL_MAJOR)
+        return -1;
+    if (b_layout != HG_ROW_MAJOR && b_layout != HG_COL_MAJOR)
+        return -2;
+    if (M < 0 || M > kI32Max)
+        return -3;
+    if (N < 0 || N > kI32Max)
+        return -4;
+    if (K < 0 || K > kI32Max)
+        return -5;
+    // A is M×K: row-major needs lda >= K, column-major lda >= M; B is K×N:
+    // column-major needs ldb >= K, row-major ldb >= N.
+    if (lda < std::max<int64_t>(1, a_layout == HG_ROW_MAJOR ? K : M))
+        return -8;
+    if (ldb < std::max<int64_t>(1, b_layout == HG_COL_MAJOR ? K : N))
+        return -10;
+    if (ldc < std::max<int64_t>(1, N))
+        return -13;
+    if (out_dtype != HG_F16 && out_dtype != HG_F32)
+        return -14;
+    if (M == 0 || N == 0)
+        return HG_OK;
+    if (C == nullptr)
+        return -12;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const bool native_a = a_layout == HG_ROW_MAJOR, native_b = b_layout == HG_COL_MAJOR;
+    const bool reads = alpha != 0.0f && K != 0;
+    if (reads && A == nullptr)
+        return -7;
+    if (reads && B == nullptr)
+        return -9;
+    const int64_t esize = out_dtype == HG_F16 ? 2 : 4;
+    const Extent ec = extent(C, M, ldc, N, esize);
+    const Extent ea = native_a ? extent(A, M, lda, K, 2) : extent(A, K, lda, M, 2);
+    const Extent eb = native_b ? extent(B, N, ldb, K, 2) : extent(B, K, ldb, N, 2);
+    if (reads && (overlap(ec, ea) || overlap(ec, eb)))
+        return -12;
+    // Native layouts (and the quick returns, which read neither operand) are
+    // hgemm itself; every argument it checks has been checked above.
+    if ((native_a && native_b) || !reads)
+        return hgemm_impl(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, out_dtype, nullptr,
+                          HG_ACT_NONE, stream);
+    const GemmLayout g = gemm_layout(a_layout, b_layout, M, N, K);
+    if (work == nullptr || !aligned16(work))
+        return -15;
+    if (work_bytes < g.a_bytes + g.b_bytes)
+        return -16;
+    const Extent ew = {reinterpret_cast<uintptr_t>(work),
+                       reinterpret_cast<uintptr_t>(work) + (uintptr_t)(g.a_bytes + g.b_bytes)};
+    if (overlap(ew, ec) || overlap(ew, ea) || overlap(ew, eb))
+        return -15;
+    const void *An = A;
+    int64_t ldan = lda;
+    const void *Bn = B;
+    int64_t ldbn = ldb;
+    unsigned char *wp = static_cast<unsigned char *>(work);
+    if (!native_a) {
+        // A column-major M×K is Aᵀ row-major K×M: transpose it to M×K row-major.
+        _Float16 *Ap = reinterpret_cast<_Float16 *>(wp);
+        const int st = hip_status(hg::launch_transpose(static_cast<const _Float16 *>(A), lda, Ap, g.ldk, K, M, s));
+        if (st != HG_OK)
+            return st;
+        An = Ap;
+        ldan = g.ldk;
+    }
+    if (!native_b) {
+        // B row-major K×N: transpose it to N×K row-major (K-contiguous columns).
+        _Float16 *Bp = reinterpret_cast<_Float16 *>(wp + g.a_bytes);
+        const int st = hip_status(hg::launch_transpose(static_cast<const _Float16 *>(B), ldb, Bp, g.ldk, K, N, s));
+        if (st != HG_OK)
+            return st;
+        Bn = Bp;
+        ldbn = g.ldk;
+    }
+    return hgemm_impl(M, N, K, alpha, An, ldan, Bn, ldbn, beta, C, ldc, out_dtype, nullptr,
+                      HG_ACT_NONE, stream);
 }
 
 }  // extern "C"

@@ -70,6 +70,33 @@ __global__ void __launch_bounds__(256) tri_xform_kernel(const _Float16 *__restri
     }
 }
 
+// D = Sᵀ for row-major fp16 matrices: S is rows×cols (S[r·lds + c]), D is
+// cols×rows (D[c·ldd + r]).  64×64 tiles through LDS so that both the reads
+// (along S's rows) and the writes (along D's rows) are contiguous.
+__global__ void __launch_bounds__(256) transpose_kernel(const _Float16 *__restrict__ S, int64_t lds,
+                                                        _Float16 *__restrict__ D, int64_t ldd, int rows,
+                                                        int cols, int tiles_c)
+{
+    __shared__ _Float16 tile[XT][XT + 2];
+    const int tr = blockIdx.x / tiles_c, tc = blockIdx.x - (blockIdx.x / tiles_c) * tiles_c;
+    const int r0 = tr * XT, c0 = tc * XT;
+    const int t = threadIdx.x;
+    const int i = t % XT, g = t / XT;
+#pragma unroll 4
+    for (int q = 0; q < XT / 4; ++q) {
+        const int r = r0 + g + 4 * q, c = c0 + i;       // read along a row of S
+        if (r < rows && c < cols)
+            tile[g + 4 * q][i] = S[(int64_t)r * lds + c];
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int q = 0; q < XT / 4; ++q) {
+        const int c = c0 + g + 4 * q, r = r0 + i;       // write along a row of D
+        if (r < rows && c < cols)
+            D[(int64_t)c * ldd + r] = tile[i][g + 4 * q];
+    }
+}
+
 // Bp(r, j) = B(n-1-r, j), column-major, fp16.
 __global__ void __launch_bounds__(256) row_reverse_copy_kernel(const _Float16 *__restrict__ B, int64_t ldb,
                                                                _Float16 *__restrict__ Bp, int64_t ldp,
@@ -129,6 +156,19 @@ hipError_t launch_tri_xform(int mode, const _Float16 *A, int64_t lda, _Float16 *
     default:
         return hipErrorInvalidValue;
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_transpose(const _Float16 *S, int64_t lds, _Float16 *D, int64_t ldd, int64_t rows,
+                            int64_t cols, hipStream_t stream)
+{
+    if (rows <= 0 || cols <= 0)
+        return hipSuccess;
+    const int64_t tr = (rows + XT - 1) / XT, tc = (cols + XT - 1) / XT;
+    if (tr * tc > 0x7fffffff || rows > 0x7fffffff || cols > 0x7fffffff)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL(transpose_kernel, dim3((unsigned)(tr * tc)), dim3(256), 0, stream, S, lds, D, ldd,
+                       (int)rows, (int)cols, (int)tc);
     return hipGetLastError();
 }
 

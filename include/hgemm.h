@@ -57,6 +57,10 @@ extern "C" {
 #define HG_NOTRANS 0
 #define HG_TRANS 1
 
+/* Storage order of hgemm_layout's operands. */
+#define HG_ROW_MAJOR 0
+#define HG_COL_MAJOR 1
+
 /* Activation of hgemm_bias_act. */
 #define HG_ACT_NONE 0
 #define HG_ACT_RELU 1
@@ -121,6 +125,35 @@ int hgemm_bias_act(int64_t M, int64_t N, int64_t K, float alpha,
                    const void *B, int64_t ldb,
                    float beta, void *C, int64_t ldc,
                    int out_dtype, const float *bias, int act, void *stream);
+
+/*
+ * hgemm_layout — hgemm with A and B in either storage order (C stays M×N
+ * row-major): A M×K row-major (A[i*lda + k], hgemm's) or column-major
+ * (A[i + k*lda]); B K×N column-major (B[k + j*ldb], hgemm's) or row-major
+ * (B[k*ldb + j], the layout of the matmul in "GPU架构与CUDA").
+ *
+ *  1 a_layout, 2 b_layout : HG_ROW_MAJOR or HG_COL_MAJOR.
+ *  3 M, 4 N, 5 K, 6 alpha, 7 A, 8 lda, 9 B, 10 ldb, 11 beta, 12 C, 13 ldc,
+ * 14 out_dtype   : as hgemm; lda >= K (row-major A) or >= M (column-major),
+ *                  ldb >= K (column-major B) or >= N (row-major).
+ * 15 work        : device workspace, 16-byte aligned, of at least
+ * 16 work_bytes    hg_hgemm_layout_workspace_size(...) bytes (0 for hgemm's
+ *                  own layouts, which ignore it); must not overlap A, B or C
+ *                  (-15; too small: -16).
+ * 17 stream      : hipStream_t.
+ *
+ * An operand that is not K-contiguous is first transposed into the
+ * workspace by a tiled copy kernel; the product then runs on hgemm's kernels
+ * with the same arithmetic (bit-identical to hgemm on the transposed data).
+ */
+int hgemm_layout(int a_layout, int b_layout, int64_t M, int64_t N, int64_t K, float alpha,
+                 const void *A, int64_t lda, const void *B, int64_t ldb,
+                 float beta, void *C, int64_t ldc, int out_dtype,
+                 void *work, int64_t work_bytes, void *stream);
+
+/* hg_hgemm_layout_workspace_size — bytes hgemm_layout needs (host only);
+ * -1/-2 for a bad layout, -3 for a negative size. */
+int64_t hg_hgemm_layout_workspace_size(int a_layout, int b_layout, int64_t M, int64_t N, int64_t K);
 
 /*
  * hgemm_bf16 — hgemm with bf16 A and B ("GPU架构与CUDA", section 混合精度核函数:

@@ -29,10 +29,11 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["hg_strerror", "hg_trmm", "hg_trmm_lower_trans_by_level",
-                                    "hg_trmm_plan", "hg_trmm_workspace_size",
-                                    "hg_trsm_workspace_size", "hgemm", "hgemm_bf16",
-                                    "hgemm_bias_act", "trmm_lower_trans", "trsm_lower_trans"]
+    assert declared_functions() == ["hg_hgemm_layout_workspace_size", "hg_strerror", "hg_trmm",
+                                    "hg_trmm_lower_trans_by_level", "hg_trmm_plan",
+                                    "hg_trmm_workspace_size", "hg_trsm_workspace_size", "hgemm",
+                                    "hgemm_bf16", "hgemm_bias_act", "hgemm_layout",
+                                    "trmm_lower_trans", "trsm_lower_trans"]
 
 
 def test_library_exports_every_declared_symbol(hg):
@@ -223,6 +224,31 @@ def test_hg_trmm_workspace_size(lib):
     assert lib.hg_trmm_workspace_size(0, 2, 4, 4) == -2
     assert lib.hg_trmm_workspace_size(0, 0, -1, 4) == -3
     assert lib.hg_trmm_workspace_size(0, 0, 4, -1) == -4
+
+
+def test_hgemm_layout_argument_errors(lib):
+    L = lambda *a: lib.hgemm_layout(*a, None)
+    assert L(2, 1, 4, 4, 4, 1.0, P, 4, Q, 4, 0.0, R, 4, 1, W, 1 << 20) == -1
+    assert L(0, 2, 4, 4, 4, 1.0, P, 4, Q, 4, 0.0, R, 4, 1, W, 1 << 20) == -2
+    assert L(0, 1, -1, 4, 4, 1.0, P, 4, Q, 4, 0.0, R, 4, 1, W, 1 << 20) == -3
+    assert L(1, 1, 8, 4, 2, 1.0, P, 2, Q, 2, 0.0, R, 4, 1, W, 1 << 20) == -8    # col-major A: lda >= M
+    assert L(0, 0, 4, 8, 2, 1.0, P, 2, Q, 2, 0.0, R, 8, 1, W, 1 << 20) == -10   # row-major B: ldb >= N
+    assert L(0, 1, 4, 4, 4, 1.0, P, 4, Q, 4, 0.0, R, 4, 3, W, 1 << 20) == -14
+    assert L(0, 1, 4, 4, 4, 1.0, P, 4, Q, 4, 0.0, None, 4, 1, W, 1 << 20) == -12
+    assert L(0, 0, 4, 4, 4, 1.0, None, 4, Q, 4, 0.0, R, 4, 1, W, 1 << 20) == -7
+    assert L(0, 0, 4, 4, 4, 1.0, P, 4, Q, 4, 0.0, R, 4, 1, None, 1 << 20) == -15
+    assert L(0, 0, 4, 4, 4, 1.0, P, 4, Q, 4, 0.0, R, 4, 1, W, 8) == -16
+    assert L(1, 1, 0, 4, 4, 1.0, None, 4, None, 4, 0.0, None, 4, 1, None, 0) == 0
+
+
+def test_hgemm_layout_workspace_size(lib):
+    up = lambda x: -(-x // 256) * 256
+    ldk = -(-100 // 8) * 8
+    assert lib.hg_hgemm_layout_workspace_size(0, 1, 30, 40, 100) == 0
+    assert lib.hg_hgemm_layout_workspace_size(1, 1, 30, 40, 100) == up(30 * ldk * 2)
+    assert lib.hg_hgemm_layout_workspace_size(0, 0, 30, 40, 100) == up(40 * ldk * 2)
+    assert lib.hg_hgemm_layout_workspace_size(1, 0, 30, 40, 100) == up(30 * ldk * 2) + up(40 * ldk * 2)
+    assert lib.hg_hgemm_layout_workspace_size(3, 0, 1, 1, 1) == -1
 
 
 def test_strerror(hg):
