@@ -46,6 +46,7 @@ SHAPES = [
     (1, 1, 256), (2, 3, 256), (8, 8, 256), (64, 17, 256), (255, 64, 256), (256, 256, 256),
     (257, 100, 256), (300, 77, 256), (512, 513, 256), (777, 128, 64), (1000, 50, 100),
     (1024, 1000, 256), (2048, 256, 256), (200, 40, 16), (130, 70, 33), (1536, 300, 256),
+    (512, 31, 256), (1024, 33, 256), (4096, 96, 256),
 ]
 
 
@@ -146,3 +147,18 @@ def test_workload_8192_sampled_columns(hg):
     A = A_cm.T.astype(np.float64)
     check_trsm(X[cols].T, A, B_cm[cols].T.astype(np.float64), w.alpha, w.leaf, Xref=ref.T,
                what="trsm_8192")
+
+
+def test_vector_and_elementwise_paths_agree(hg):
+    """n = 1024 with aligned operands (vector loads and stores) against the
+    same system with a leading dimension that is not a multiple of 8 (the
+    element-wise paths of the leaf step and the GEMM updates): both within
+    the rule, and within a few fp16 roundings of each other."""
+    n, m = 1024, 200
+    A_cm, B_cm = _inputs(n, m, 21)
+    vec = run(hg, A_cm, B_cm, 1.0, 256)
+    ew = run(hg, A_cm, B_cm, 1.0, 256, pad=3)
+    ref = oracle.trsm_lower_trans(A_cm, B_cm, 1.0)
+    check_trsm(vec.T, A_cm.T, B_cm.T, 1.0, 256, Xref=ref.T, what="vector paths")
+    check_trsm(ew.T, A_cm.T, B_cm.T, 1.0, 256, Xref=ref.T, what="element-wise paths")
+    assert np.abs(vec - ew).max() <= 8 * 2.0 ** -11 * np.abs(ref).max()
