@@ -117,7 +117,7 @@ def _time_calls(fn, warmup, reps, stream):
     return ts[len(ts) // 2], ts[0], a.elapsed_time(b) / reps
 
 
-def config_sweep(hg, stream, main_gemm_ms=None, main_trmm_ms=None):
+def config_sweep(hg, stream, main_gemm_ms=None, main_trmm_ms=None, only=None):
     """Every configuration of the workload list: GPU median / min per call
     (HIP events on the kernels' stream), TFLOP/s, % of the fp16 MFMA peak and
     GB/s of compulsory traffic, next to the fp64 oracle on this host (in full
@@ -130,8 +130,13 @@ def config_sweep(hg, stream, main_gemm_ms=None, main_trmm_ms=None):
     import workloads
     dev = torch.device("cuda:0")
     res = {}
+
+    def want(name):
+        return only is None or name in only
     reps = {"hgemm_256": 200, "hgemm_1000_ragged": 200, "hgemm_4096": 50}
     for name, w in workloads.WORKLOADS.items():
+        if not want(name):
+            continue
         print(f"[bench] config {name} ...", file=sys.stderr, flush=True)
         r = {}
         if isinstance(w, workloads.GemmWorkload):
@@ -182,96 +187,105 @@ def config_sweep(hg, stream, main_gemm_ms=None, main_trmm_ms=None):
                            "us_per_entry": round(dt / ri.size * 1e6, 2), "cores": oracle.num_threads()}
             del TA, TB
         res[name] = r
-    # Fused bias + ReLU epilogue (next row), on the 8192³ inputs with fp16 out:
-    # one launch, against the plain GEMM and the unfused sequence (GEMM, then
-    # a bias-add pass and a ReLU pass over C).
-    print("[bench] config hgemm_bias_relu_8192 ...", file=sys.stderr, flush=True)
-    w = workloads.WORKLOADS["hgemm_8192"]
-    A, Bt, _ = workloads.gemm_inputs(w)
-    Ad, Btd = torch.from_numpy(A).to(dev), torch.from_numpy(Bt).to(dev)
-    biasd = torch.from_numpy(np.random.default_rng(w.seed + 7).uniform(-1, 1, w.N)
-                             .astype(np.float32)).to(dev)
-    Cd = torch.empty((w.M, w.N), dtype=torch.float16, device=dev)
-    fused = lambda: hg.hgemm_bias_act(Ad, Btd, Cd, biasd, True)
-    plain = lambda: hg.hgemm(Ad, Btd, Cd)
+    if want("hgemm_bias_relu_8192"):
+        # Fused bias + ReLU epilogue (next row), on the 8192³ inputs with fp16 out:
+        # one launch, against the plain GEMM and the unfused sequence (GEMM, then
+        # a bias-add pass and a ReLU pass over C).
+        print("[bench] config hgemm_bias_relu_8192 ...", file=sys.stderr, flush=True)
+        w = workloads.WORKLOADS["hgemm_8192"]
+        A, Bt, _ = workloads.gemm_inputs(w)
+        Ad, Btd = torch.from_numpy(A).to(dev), torch.from_numpy(Bt).to(dev)
+        biasd = torch.from_numpy(np.random.default_rng(w.seed + 7).uniform(-1, 1, w.N)
+                                 .astype(np.float32)).to(dev)
+        Cd = torch.empty((w.M, w.N), dtype=torch.float16, device=dev)
+        fused = lambda: hg.hgemm_bias_act(Ad, Btd, Cd, biasd, True)
+        plain = lambda: hg.hgemm(Ad, Btd, Cd)
 
-    def unfused():
-        hg.hgemm(Ad, Btd, Cd)
-        Cd.add_(biasd)
-        Cd.relu_()
-    tf_ms = _time_calls(fused, 20, 30, stream)
-    tp_ms = _time_calls(plain, 20, 30, stream)
-    tu_ms = _time_calls(unfused, 5, 30, stream)
-    res["hgemm_bias_relu_8192"] = {
-        "gpu_ms_median": round(tf_ms[0], 5), "gpu_ms_min": round(tf_ms[1], 5),
-        "tflops": round(w.flops / (tf_ms[0] * 1e-3) / 1e12, 2),
-        "plain_hgemm_fp16_out_ms_median": round(tp_ms[0], 5),
-        "unfused_gemm_then_bias_then_relu_ms_median": round(tu_ms[0], 5),
-        "note": "C = relu(A*B + bias), 8192^3, fp16 out, one launch; the unfused sequence adds "
-                "two passes over C (torch elementwise ops)"}
-    del Ad, Btd, Cd, biasd
-    # bf16 operands (next row): the 8192³ shape, values drawn as the HGEMM
-    # workload's and rounded to bf16, fp32 C.
-    print("[bench] config hgemm_bf16_8192 ...", file=sys.stderr, flush=True)
-    rng = np.random.default_rng(w.seed)
-    Ab = workloads.uniform_bf16(rng, (w.M, w.K))
-    Bb = workloads.uniform_bf16(rng, (w.N, w.K))
-    Ad = torch.from_numpy(Ab.view(np.int16)).to(dev).view(torch.bfloat16)
-    Btd = torch.from_numpy(Bb.view(np.int16)).to(dev).view(torch.bfloat16)
-    Cd = torch.empty((w.M, w.N), dtype=torch.float32, device=dev)
-    tb = _time_calls(lambda: hg.hgemm_bf16(Ad, Btd, Cd), 20, 30, stream)
-    tfb = w.flops / (tb[0] * 1e-3) / 1e12
-    res["hgemm_bf16_8192"] = {
-        "gpu_ms_median": round(tb[0], 5), "gpu_ms_min": round(tb[1], 5), "tflops": round(tfb, 2),
-        "pct_of_bf16_mfma_peak": round(100 * tfb / PEAK_FP16_TFLOPS, 3),
-        "note": "bf16 A, B (v_mfma_f32_16x16x32_bf16), fp32 accumulation and C; dense bf16 peak "
-                "equals the fp16 one"}
-    del Ad, Btd, Cd, Ab, Bb
-    # Row-major B (next row; the GPU architecture page's matmul layout):
-    # 8192³, fp32 C, B transposed into a workspace, then the GEMM.
-    print("[bench] config hgemm_rowmajor_b_8192 ...", file=sys.stderr, flush=True)
-    A, Bt, _ = workloads.gemm_inputs(w)
-    Ad = torch.from_numpy(A).to(dev)
-    Brd = torch.from_numpy(np.ascontiguousarray(Bt.T)).to(dev)
-    Cd = torch.empty((w.M, w.N), dtype=torch.float32, device=dev)
-    work = torch.empty(hg.lib.hg_hgemm_layout_workspace_size(0, 0, w.M, w.N, w.K), dtype=torch.uint8,
-                       device=dev)
-    tl = _time_calls(lambda: hg.hgemm_layout(Ad, Brd, Cd, False, True, work=work), 20, 30, stream)
-    res["hgemm_rowmajor_b_8192"] = {
-        "gpu_ms_median": round(tl[0], 5), "gpu_ms_min": round(tl[1], 5),
-        "tflops": round(w.flops / (tl[0] * 1e-3) / 1e12, 2),
-        "note": "B given K x N row-major: one tiled transpose (128 MiB read + written) into the "
-                "workspace, then the K-contiguous GEMM"}
-    del Ad, Brd, Cd, work, A, Bt
-    # Skinny right-hand side (next row): the TRMM page's usage example,
-    # n = 4096, m = 256.
-    print("[bench] config trmm_4096x256 ...", file=sys.stderr, flush=True)
-    w = workloads.TrmmWorkload("trmm_4096x256", 4096, 256, 1.0, 256, 6)
-    TA, TB = workloads.trmm_inputs(w)
-    Ad, Bd = torch.from_numpy(TA).to(dev), torch.from_numpy(TB).to(dev)
-    Od = torch.empty((w.m, w.n), dtype=torch.float32, device=dev)
-    ts = _time_calls(lambda: hg.trmm_lower_trans(Ad, Bd, Od, w.alpha, w.leaf), 20, 50, stream)
-    res["trmm_4096x256"] = {"gpu_ms_median": round(ts[0], 5), "gpu_ms_min": round(ts[1], 5),
-                            "gpu_ms_back_to_back_mean": round(ts[2], 5),
-                            "effective_tflops": round(w.flops / (ts[0] * 1e-3) / 1e12, 2),
-                            "note": "B 4096x256 (the TRMM page's usage example), level-by-level launches"}
-    del Ad, Bd, Od, TA, TB
-    # The page's usage call is the lower, non-transposed product (next row):
-    # n = m = 8192 through hg_trmm (index map of A, B and Out row-reversed).
-    print("[bench] config trmm_8192_lower_notrans ...", file=sys.stderr, flush=True)
-    w = workloads.WORKLOADS["trmm_8192"]
-    TA, TB = workloads.trmm_inputs(w)
-    Ad, Bd = torch.from_numpy(TA).to(dev), torch.from_numpy(TB).to(dev)
-    Od = torch.empty((w.m, w.n), dtype=torch.float32, device=dev)
-    work = torch.empty(hg.trmm_workspace_size(w.n, w.m, "L", False), dtype=torch.uint8, device=dev)
-    ts = _time_calls(lambda: hg.trmm(Ad, Bd, Od, w.alpha, "L", False, w.leaf, work), 5, 20, stream)
-    res["trmm_8192_lower_notrans"] = {
-        "gpu_ms_median": round(ts[0], 5), "gpu_ms_min": round(ts[1], 5),
-        "effective_tflops": round(w.flops / (ts[0] * 1e-3) / 1e12, 2),
-        "note": "Out = A*B, A lower (the TRMM page's usage call): transpose-and-reverse copy of A, "
-                "B and Out row-reversed around the lower-transposed recursion"}
-    del Ad, Bd, Od, TA, TB, work
+        def unfused():
+            hg.hgemm(Ad, Btd, Cd)
+            Cd.add_(biasd)
+            Cd.relu_()
+        tf_ms = _time_calls(fused, 20, 30, stream)
+        tp_ms = _time_calls(plain, 20, 30, stream)
+        tu_ms = _time_calls(unfused, 5, 30, stream)
+        res["hgemm_bias_relu_8192"] = {
+            "gpu_ms_median": round(tf_ms[0], 5), "gpu_ms_min": round(tf_ms[1], 5),
+            "tflops": round(w.flops / (tf_ms[0] * 1e-3) / 1e12, 2),
+            "plain_hgemm_fp16_out_ms_median": round(tp_ms[0], 5),
+            "unfused_gemm_then_bias_then_relu_ms_median": round(tu_ms[0], 5),
+            "note": "C = relu(A*B + bias), 8192^3, fp16 out, one launch; the unfused sequence adds "
+                    "two passes over C (torch elementwise ops)"}
+        del Ad, Btd, Cd, biasd
+    if want("hgemm_bf16_8192"):
+        # bf16 operands (next row): the 8192³ shape, values drawn as the HGEMM
+        # workload's and rounded to bf16, fp32 C.
+        print("[bench] config hgemm_bf16_8192 ...", file=sys.stderr, flush=True)
+        w = workloads.WORKLOADS["hgemm_8192"]
+        rng = np.random.default_rng(w.seed)
+        Ab = workloads.uniform_bf16(rng, (w.M, w.K))
+        Bb = workloads.uniform_bf16(rng, (w.N, w.K))
+        Ad = torch.from_numpy(Ab.view(np.int16)).to(dev).view(torch.bfloat16)
+        Btd = torch.from_numpy(Bb.view(np.int16)).to(dev).view(torch.bfloat16)
+        Cd = torch.empty((w.M, w.N), dtype=torch.float32, device=dev)
+        tb = _time_calls(lambda: hg.hgemm_bf16(Ad, Btd, Cd), 20, 30, stream)
+        tfb = w.flops / (tb[0] * 1e-3) / 1e12
+        res["hgemm_bf16_8192"] = {
+            "gpu_ms_median": round(tb[0], 5), "gpu_ms_min": round(tb[1], 5), "tflops": round(tfb, 2),
+            "pct_of_bf16_mfma_peak": round(100 * tfb / PEAK_FP16_TFLOPS, 3),
+            "note": "bf16 A, B (v_mfma_f32_16x16x32_bf16), fp32 accumulation and C; dense bf16 peak "
+                    "equals the fp16 one"}
+        del Ad, Btd, Cd, Ab, Bb
+    if want("hgemm_rowmajor_b_8192"):
+        # Row-major B (next row; the GPU architecture page's matmul layout):
+        # 8192³, fp32 C, B transposed into a workspace, then the GEMM.
+        print("[bench] config hgemm_rowmajor_b_8192 ...", file=sys.stderr, flush=True)
+        w = workloads.WORKLOADS["hgemm_8192"]
+        A, Bt, _ = workloads.gemm_inputs(w)
+        Ad = torch.from_numpy(A).to(dev)
+        Brd = torch.from_numpy(np.ascontiguousarray(Bt.T)).to(dev)
+        Cd = torch.empty((w.M, w.N), dtype=torch.float32, device=dev)
+        work = torch.empty(hg.lib.hg_hgemm_layout_workspace_size(0, 0, w.M, w.N, w.K), dtype=torch.uint8,
+                           device=dev)
+        tl = _time_calls(lambda: hg.hgemm_layout(Ad, Brd, Cd, False, True, work=work), 20, 30, stream)
+        res["hgemm_rowmajor_b_8192"] = {
+            "gpu_ms_median": round(tl[0], 5), "gpu_ms_min": round(tl[1], 5),
+            "tflops": round(w.flops / (tl[0] * 1e-3) / 1e12, 2),
+            "note": "B given K x N row-major: one tiled transpose (128 MiB read + written) into the "
+                    "workspace, then the K-contiguous GEMM"}
+        del Ad, Brd, Cd, work, A, Bt
+    if want("trmm_4096x256"):
+        # Skinny right-hand side (next row): the TRMM page's usage example,
+        # n = 4096, m = 256.
+        print("[bench] config trmm_4096x256 ...", file=sys.stderr, flush=True)
+        w = workloads.TrmmWorkload("trmm_4096x256", 4096, 256, 1.0, 256, 6)
+        TA, TB = workloads.trmm_inputs(w)
+        Ad, Bd = torch.from_numpy(TA).to(dev), torch.from_numpy(TB).to(dev)
+        Od = torch.empty((w.m, w.n), dtype=torch.float32, device=dev)
+        ts = _time_calls(lambda: hg.trmm_lower_trans(Ad, Bd, Od, w.alpha, w.leaf), 20, 50, stream)
+        res["trmm_4096x256"] = {"gpu_ms_median": round(ts[0], 5), "gpu_ms_min": round(ts[1], 5),
+                                "gpu_ms_back_to_back_mean": round(ts[2], 5),
+                                "effective_tflops": round(w.flops / (ts[0] * 1e-3) / 1e12, 2),
+                                "note": "B 4096x256 (the TRMM page's usage example), level-by-level launches"}
+        del Ad, Bd, Od, TA, TB
+    if want("trmm_8192_lower_notrans"):
+        # The page's usage call is the lower, non-transposed product (next row):
+        # n = m = 8192 through hg_trmm (index map of A, B and Out row-reversed).
+        print("[bench] config trmm_8192_lower_notrans ...", file=sys.stderr, flush=True)
+        w = workloads.WORKLOADS["trmm_8192"]
+        TA, TB = workloads.trmm_inputs(w)
+        Ad, Bd = torch.from_numpy(TA).to(dev), torch.from_numpy(TB).to(dev)
+        Od = torch.empty((w.m, w.n), dtype=torch.float32, device=dev)
+        work = torch.empty(hg.trmm_workspace_size(w.n, w.m, "L", False), dtype=torch.uint8, device=dev)
+        ts = _time_calls(lambda: hg.trmm(Ad, Bd, Od, w.alpha, "L", False, w.leaf, work), 5, 20, stream)
+        res["trmm_8192_lower_notrans"] = {
+            "gpu_ms_median": round(ts[0], 5), "gpu_ms_min": round(ts[1], 5),
+            "effective_tflops": round(w.flops / (ts[0] * 1e-3) / 1e12, 2),
+            "note": "Out = A*B, A lower (the TRMM page's usage call): transpose-and-reverse copy of A, "
+                    "B and Out row-reversed around the lower-transposed recursion"}
+        del Ad, Bd, Od, TA, TB, work
     for name, w in workloads.TRSM_WORKLOADS.items():
+        if not want(name):
+            continue
         print(f"[bench] config {name} ...", file=sys.stderr, flush=True)
         A_cm, B_cm = workloads.trsm_inputs(w)
         Ad, Bd = torch.from_numpy(A_cm).to(dev), torch.from_numpy(B_cm).to(dev)
@@ -307,6 +321,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-trmm", action="store_true", help="time the HGEMM alone")
+    ap.add_argument("--config", action="append", default=None, metavar="NAME",
+                    help="run only this entry of the per-configuration sweep (repeatable)")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the per-configuration sweep (GPU and oracle times of every workload)")
     ap.add_argument("--no-ceiling", action="store_true",
@@ -422,7 +438,7 @@ def main():
                           "max": round(max(trmm_ms), 4)}
         out["trmm_effective_tflops"] = round(wt.flops / (tavg * 1e-3) / 1e12, 2)
     if not args.no_configs:
-        out["configs"] = config_sweep(hg, stream, gemm_avg,
+        out["configs"] = config_sweep(hg, stream, gemm_avg, only=args.config, main_trmm_ms=
                                       (sum(trmm_ms) / len(trmm_ms)) if do_trmm else None)
     if not args.no_ceiling:
         out["mfma_ceiling"] = mfma_ceiling()
