@@ -70,17 +70,44 @@ __global__ void __launch_bounds__(256) tri_xform_kernel(const _Float16 *__restri
     }
 }
 
+typedef _Float16 half8v __attribute__((ext_vector_type(8)));
+
 // D = Sᵀ for row-major fp16 matrices: S is rows×cols (S[r·lds + c]), D is
 // cols×rows (D[c·ldd + r]).  64×64 tiles through LDS so that both the reads
-// (along S's rows) and the writes (along D's rows) are contiguous.
+// (along S's rows) and the writes (along D's rows) are contiguous.  With
+// `vec` (16-byte aligned S and D, lds and ldd multiples of 8) full tiles move
+// 16 bytes per lane each way; edge tiles and the other cases go element by
+// element.
 __global__ void __launch_bounds__(256) transpose_kernel(const _Float16 *__restrict__ S, int64_t lds,
                                                         _Float16 *__restrict__ D, int64_t ldd, int rows,
-                                                        int cols, int tiles_c)
+                                                        int cols, int tiles_c, int vec)
 {
-    __shared__ _Float16 tile[XT][XT + 2];
+    __shared__ __attribute__((aligned(16))) _Float16 tile[XT][XT + 8];
     const int tr = blockIdx.x / tiles_c, tc = blockIdx.x - (blockIdx.x / tiles_c) * tiles_c;
     const int r0 = tr * XT, c0 = tc * XT;
     const int t = threadIdx.x;
+    if (vec && r0 + XT <= rows && c0 + XT <= cols) {
+        // Thread t: 16-byte chunk t mod 8 of tile rows t/8 and t/8 + 32.
+        const int ch = t % 8, rr = t / 8;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int row = rr + 32 * u;
+            *reinterpret_cast<half8v *>(&tile[row][8 * ch]) =
+                *reinterpret_cast<const half8v *>(S + (int64_t)(r0 + row) * lds + c0 + 8 * ch);
+        }
+        __syncthreads();
+        // D row c0 + cc holds S's column: chunk ch gathers tile rows 8ch..8ch+7.
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int cc = rr + 32 * u;
+            half8v v;
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                v[e] = tile[8 * ch + e][cc];
+            *reinterpret_cast<half8v *>(D + (int64_t)(c0 + cc) * ldd + r0 + 8 * ch) = v;
+        }
+        return;
+    }
     const int i = t % XT, g = t / XT;
 #pragma unroll 4
     for (int q = 0; q < XT / 4; ++q) {
@@ -97,11 +124,25 @@ __global__ void __launch_bounds__(256) transpose_kernel(const _Float16 *__restri
     }
 }
 
-// Bp(r, j) = B(n-1-r, j), column-major, fp16.
+// Bp(r, j) = B(n-1-r, j), column-major, fp16.  With `vec` (n, ldb, ldp
+// multiples of 8, 16-byte aligned B and Bp) each thread moves 8 rows: one
+// 16-byte load, the halves reversed in registers, one 16-byte store.
 __global__ void __launch_bounds__(256) row_reverse_copy_kernel(const _Float16 *__restrict__ B, int64_t ldb,
                                                                _Float16 *__restrict__ Bp, int64_t ldp,
-                                                               int64_t n, int64_t m)
+                                                               int64_t n, int64_t m, int vec)
 {
+    if (vec) {
+        const int64_t n8 = n / 8;
+        const int64_t total = n8 * m;
+        for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+             idx += (int64_t)gridDim.x * blockDim.x) {
+            const int64_t j = idx / n8, q = idx - j * n8;
+            const half8v v = *reinterpret_cast<const half8v *>(B + j * ldb + (n - 8 - 8 * q));
+            *reinterpret_cast<half8v *>(Bp + j * ldp + 8 * q) =
+                __builtin_shufflevector(v, v, 7, 6, 5, 4, 3, 2, 1, 0);
+        }
+        return;
+    }
     const int64_t total = n * m;
     for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
          idx += (int64_t)gridDim.x * blockDim.x) {
@@ -167,8 +208,10 @@ hipError_t launch_transpose(const _Float16 *S, int64_t lds, _Float16 *D, int64_t
     const int64_t tr = (rows + XT - 1) / XT, tc = (cols + XT - 1) / XT;
     if (tr * tc > 0x7fffffff || rows > 0x7fffffff || cols > 0x7fffffff)
         return hipErrorInvalidValue;
+    const int vec = reinterpret_cast<uintptr_t>(S) % 16 == 0 && reinterpret_cast<uintptr_t>(D) % 16 == 0 &&
+                    lds % 8 == 0 && ldd % 8 == 0;
     hipLaunchKernelGGL(transpose_kernel, dim3((unsigned)(tr * tc)), dim3(256), 0, stream, S, lds, D, ldd,
-                       (int)rows, (int)cols, (int)tc);
+                       (int)rows, (int)cols, (int)tc, vec);
     return hipGetLastError();
 }
 
@@ -177,8 +220,10 @@ hipError_t launch_row_reverse_copy(const _Float16 *B, int64_t ldb, _Float16 *Bp,
 {
     if (n <= 0 || m <= 0)
         return hipSuccess;
-    hipLaunchKernelGGL(row_reverse_copy_kernel, dim3(grid_for(n * m)), dim3(256), 0, stream, B, ldb, Bp,
-                       ldp, n, m);
+    const int vec = n % 8 == 0 && ldb % 8 == 0 && ldp % 8 == 0 && reinterpret_cast<uintptr_t>(B) % 16 == 0 &&
+                    reinterpret_cast<uintptr_t>(Bp) % 16 == 0;
+    hipLaunchKernelGGL(row_reverse_copy_kernel, dim3(grid_for(vec ? (n / 8) * m : n * m)), dim3(256), 0,
+                       stream, B, ldb, Bp, ldp, n, m, vec);
     return hipGetLastError();
 }
 
