@@ -283,6 +283,33 @@ def config_sweep(hg, stream, main_gemm_ms=None, main_trmm_ms=None, only=None):
             "note": "Out = A*B, A lower (the TRMM page's usage call): transpose-and-reverse copy of A, "
                     "B and Out row-reversed around the lower-transposed recursion"}
         del Ad, Bd, Od, TA, TB, work
+    if want("trmm_8192_inplace"):
+        # In-place form B <- A*B (fp16 B overwritten), lower and not transposed.
+        # B is restored from a copy before each timed call, outside the events.
+        print("[bench] config trmm_8192_inplace ...", file=sys.stderr, flush=True)
+        w = workloads.WORKLOADS["trmm_8192"]
+        TA, TB = workloads.trmm_inputs(w)
+        Ad, B0 = torch.from_numpy(TA).to(dev), torch.from_numpy(TB).to(dev)
+        Bd = torch.empty_like(B0)
+        work = torch.empty(hg.lib.hg_trmm_inplace_workspace_size(0, 0, w.n, w.m), dtype=torch.uint8,
+                           device=dev)
+        ts = []
+        for i in range(25):
+            Bd.copy_(B0)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            hg.trmm_inplace(Ad, Bd, w.alpha, "L", False, w.leaf, work)
+            b.record(stream)
+            torch.cuda.synchronize()
+            if i >= 5:
+                ts.append(a.elapsed_time(b))
+        ts.sort()
+        res["trmm_8192_inplace"] = {
+            "gpu_ms_median": round(ts[len(ts) // 2], 5), "gpu_ms_min": round(ts[0], 5),
+            "effective_tflops": round(w.flops / (ts[len(ts) // 2] * 1e-3) / 1e12, 2),
+            "note": "B <- A*B in fp16, A lower: the lower, non-transposed product into an fp32 "
+                    "workspace, then one rounding pass into B"}
+        del Ad, B0, Bd, TA, TB, work
     for name, w in workloads.TRSM_WORKLOADS.items():
         if not want(name):
             continue

@@ -88,6 +88,11 @@ lib.hg_trmm.argtypes = [_int, _int, _i64, _i64, _f32, _vp, _i64, _vp, _i64, _vp,
 lib.hg_trmm.restype = _int
 lib.hg_trmm_workspace_size.argtypes = [_int, _int, _i64, _i64]
 lib.hg_trmm_workspace_size.restype = _i64
+lib.hg_trmm_inplace.argtypes = [_int, _int, _i64, _i64, _f32, _vp, _i64, _vp, _i64, _i64, _vp, _i64,
+                                _vp]
+lib.hg_trmm_inplace.restype = _int
+lib.hg_trmm_inplace_workspace_size.argtypes = [_int, _int, _i64, _i64]
+lib.hg_trmm_inplace_workspace_size.restype = _i64
 lib.hg_trmm_lower_trans_by_level.argtypes = lib.trmm_lower_trans.argtypes
 lib.hg_trmm_lower_trans_by_level.restype = _int
 lib.trsm_lower_trans.argtypes = [_i64, _i64, _f32, _vp, _i64, _vp, _i64, _vp, _i64, _int, _i64,
@@ -102,7 +107,8 @@ lib.hg_trmm_plan.restype = _i64
 
 EXPORTS = ("hgemm", "hgemm_bias_act", "hgemm_bf16", "trmm_lower_trans", "hg_trmm_lower_trans_by_level",
            "hg_strerror", "hg_trmm_plan", "trsm_lower_trans", "hg_trsm_workspace_size", "hg_trmm",
-           "hg_trmm_workspace_size", "hgemm_layout", "hg_hgemm_layout_workspace_size")
+           "hg_trmm_workspace_size", "hgemm_layout", "hg_hgemm_layout_workspace_size",
+           "hg_trmm_inplace", "hg_trmm_inplace_workspace_size")
 
 ROW_MAJOR = 0
 COL_MAJOR = 1
@@ -341,6 +347,33 @@ def trmm(A, B, Out, alpha: float = 1.0, uplo: str = "L", trans: bool = True, lea
     if st != 0:
         raise HgError("hg_trmm", st)
     return Out
+
+
+def trmm_inplace(A, B, alpha: float = 1.0, uplo: str = "L", trans: bool = True, leaf: int = 256,
+                 work=None):
+    """B ← alpha·op(A)·B with B a float16 (m, n) tensor in the column-major
+    convention, overwritten with the product rounded to fp16; returns B."""
+    import torch
+    _check_matrix(A, "A", (torch.float16,))
+    _check_matrix(B, "B", (torch.float16,))
+    n = A.shape[0]
+    m = B.shape[0]
+    if tuple(A.shape) != (n, n) or B.shape[1] != n:
+        raise ValueError(f"shape mismatch: A {tuple(A.shape)}, B {tuple(B.shape)}")
+    if uplo not in ("L", "U"):
+        raise ValueError("uplo must be 'L' or 'U'")
+    u, t = (0 if uplo == "L" else 1), (1 if trans else 0)
+    need = lib.hg_trmm_inplace_workspace_size(u, t, n, m)
+    if need < 0:
+        raise HgError("hg_trmm_inplace_workspace_size", int(need))
+    if work is None:
+        work = torch.empty(max(need, 1), dtype=torch.uint8, device=B.device)
+    st = lib.hg_trmm_inplace(u, t, n, m, float(alpha), A.data_ptr() or None, _ld(A),
+                             B.data_ptr() or None, _ld(B), int(leaf), work.data_ptr(),
+                             work.numel() * work.element_size(), _stream_handle(B))
+    if st != 0:
+        raise HgError("hg_trmm_inplace", st)
+    return B
 
 
 def trmm_workspace_size(n: int, m: int, uplo: str = "L", trans: bool = True) -> int:

@@ -822,3 +822,58 @@ int hgemm_layout(int a_layout, int b_layout, int64_t M, int64_t N, int64_t K, fl
 }
 
 }  // extern "C"
+
+extern "C" {
+
+int64_t hg_trmm_inplace_workspace_size(int uplo, int trans, int64_t n, int64_t m)
+{
+    const int64_t v = hg_trmm_workspace_size(uplo, trans, n, m);
+    if (v < 0 || n == 0 || m == 0)
+        return v;
+    return round_up(round_up(n, 8) * m * 4, 256) + v;
+}
+
+int hg_trmm_inplace(int uplo, int trans, int64_t n, int64_t m, float alpha, const void *A, int64_t lda,
+                    void *B, int64_t ldb, int64_t leaf, void *work, int64_t work_bytes, void *stream)
+{
+    if (uplo != HG_LOWER && uplo != HG_UPPER)
+        return -1;
+    if (trans != HG_NOTRANS && trans != HG_TRANS)
+        return -2;
+    if (n < 0 || n > kI32Max)
+        return -3;
+    if (m < 0 || m > kI32Max)
+        return -4;
+    if (lda < std::max<int64_t>(1, n))
+        return -7;
+    if (ldb < std::max<int64_t>(1, n))
+        return -9;
+    if (n == 0 || m == 0)
+        return HG_OK;
+    if (B == nullptr)
+        return -8;
+    if (alpha != 0.0f && A == nullptr)
+        return -6;
+    const int64_t ldx = round_up(n, 8);
+    const int64_t x_bytes = round_up(ldx * m * 4, 256);
+    const int64_t need = x_bytes + hg_trmm_workspace_size(uplo, trans, n, m);
+    if (work == nullptr || !aligned16(work))
+        return -11;
+    if (work_bytes < need)
+        return -12;
+    const Extent ew = {reinterpret_cast<uintptr_t>(work), reinterpret_cast<uintptr_t>(work) + (uintptr_t)need};
+    if (overlap(ew, extent(B, m, ldb, n, 2)) || (A && overlap(ew, extent(A, n, lda, n, 2))))
+        return -11;
+    if (A && overlap(extent(B, m, ldb, n, 2), extent(A, n, lda, n, 2)))
+        return -8;
+    float *X = static_cast<float *>(work);
+    unsigned char *vwork = static_cast<unsigned char *>(work) + x_bytes;
+    int st = hg_trmm(uplo, trans, n, m, alpha, A, lda, B, ldb, X, ldx, HG_F32, leaf, vwork,
+                     work_bytes - x_bytes, stream);
+    if (st != HG_OK)
+        return st;   // a HIP error: the arguments were checked above
+    return hip_status(hg::launch_f32_to_f16(X, ldx, static_cast<_Float16 *>(B), ldb, n, m,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -133,6 +133,9 @@ hipError_t launch_tri_xform(int mode, const _Float16 *A, int64_t lda, _Float16 *
 hipError_t launch_row_reverse_copy(const _Float16 *B, int64_t ldb, _Float16 *Bp, int64_t ldp, int64_t n,
                                    int64_t m, hipStream_t stream);
 hipError_t launch_row_reverse_inplace(float *Out, int64_t ldo, int64_t n, int64_t m, hipStream_t stream);
+// B = fp16(X) (nearest even), column-major n×m.
+hipError_t launch_f32_to_f16(const float *X, int64_t ldx, _Float16 *B, int64_t ldb, int64_t n, int64_t m,
+                             hipStream_t stream);
 // D = Sᵀ, S rows×cols row-major (lds), D cols×rows row-major (ldd), fp16.
 hipError_t launch_transpose(const _Float16 *S, int64_t lds, _Float16 *D, int64_t ldd, int64_t rows,
                             int64_t cols, hipStream_t stream);

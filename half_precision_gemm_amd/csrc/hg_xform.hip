@@ -167,6 +167,35 @@ __global__ void __launch_bounds__(256) row_reverse_inplace_kernel(float *__restr
     }
 }
 
+// B(r, j) = fp16(X(r, j)) (round to nearest even), column-major n×m.
+// Each thread converts 8 consecutive rows of one column per step; blockIdx.y
+// strides over the columns.  VEC: X and B columns start 16-byte aligned, so
+// whole groups of 8 move as two float4 loads and one 16-byte store.
+template <bool VEC>
+__global__ void __launch_bounds__(256) f32_to_f16_kernel(const float *__restrict__ X, int64_t ldx,
+                                                         _Float16 *__restrict__ B, int64_t ldb, int64_t n,
+                                                         int64_t m)
+{
+    const int64_t r0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
+    if (r0 >= n)
+        return;
+    for (int64_t j = blockIdx.y; j < m; j += gridDim.y) {
+        const float *x = X + j * ldx + r0;
+        _Float16 *b = B + j * ldb + r0;
+        if (VEC && r0 + 8 <= n) {
+            const float4 lo = reinterpret_cast<const float4 *>(x)[0];
+            const float4 hi = reinterpret_cast<const float4 *>(x)[1];
+            typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+            h8 h = {(_Float16)lo.x, (_Float16)lo.y, (_Float16)lo.z, (_Float16)lo.w,
+                    (_Float16)hi.x, (_Float16)hi.y, (_Float16)hi.z, (_Float16)hi.w};
+            *reinterpret_cast<h8 *>(b) = h;
+        } else {
+            for (int i = 0; i < 8 && r0 + i < n; ++i)
+                b[i] = (_Float16)x[i];
+        }
+    }
+}
+
 unsigned grid_for(int64_t total)
 {
     int64_t blocks = (total + 255) / 256;
@@ -224,6 +253,21 @@ hipError_t launch_row_reverse_copy(const _Float16 *B, int64_t ldb, _Float16 *Bp,
                     reinterpret_cast<uintptr_t>(Bp) % 16 == 0;
     hipLaunchKernelGGL(row_reverse_copy_kernel, dim3(grid_for(vec ? (n / 8) * m : n * m)), dim3(256), 0,
                        stream, B, ldb, Bp, ldp, n, m, vec);
+    return hipGetLastError();
+}
+
+hipError_t launch_f32_to_f16(const float *X, int64_t ldx, _Float16 *B, int64_t ldb, int64_t n, int64_t m,
+                             hipStream_t stream)
+{
+    if (n <= 0 || m <= 0)
+        return hipSuccess;
+    const dim3 grid((unsigned)((n + 2047) / 2048), (unsigned)(m < 65535 ? m : 65535));
+    const bool vec = (reinterpret_cast<uintptr_t>(X) & 15) == 0 && (reinterpret_cast<uintptr_t>(B) & 15) == 0 &&
+                     ldx % 4 == 0 && ldb % 8 == 0;
+    if (vec)
+        hipLaunchKernelGGL(f32_to_f16_kernel<true>, grid, dim3(256), 0, stream, X, ldx, B, ldb, n, m);
+    else
+        hipLaunchKernelGGL(f32_to_f16_kernel<false>, grid, dim3(256), 0, stream, X, ldx, B, ldb, n, m);
     return hipGetLastError();
 }
 

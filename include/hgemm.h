@@ -245,6 +245,33 @@ int hg_trmm(int uplo, int trans, int64_t n, int64_t m, float alpha,
 int64_t hg_trmm_workspace_size(int uplo, int trans, int64_t n, int64_t m);
 
 /*
+ * hg_trmm_inplace — B ← alpha·op(A)·B in fp16, the in-place form of
+ * "异构计算中高性能TRMM与TRSM的递归算法实现" §2.2 ("B ←").
+ *
+ *  1 uplo, 2 trans, 3 n, 4 m, 5 alpha, 6 A, 7 lda : as hg_trmm.
+ *  8 B, 9 ldb     : fp16 n×m column-major, read as the right-hand side and
+ *                   overwritten with the product rounded to nearest even.
+ *                   Must not overlap A (-8).
+ * 10 leaf        : as hg_trmm.
+ * 11 work        : device workspace, 16-byte aligned, of at least
+ * 12 work_bytes    hg_trmm_inplace_workspace_size(uplo, trans, n, m) bytes:
+ *                  the fp32 product and hg_trmm's own workspace; must not
+ *                  overlap A or B (-11; too small: -12).
+ * 13 stream      : hipStream_t.
+ *
+ * The product is formed in fp32 (hg_trmm into the workspace) and rounded to
+ * fp16 once, so B receives hg_trmm's result rounded to nearest even; no
+ * intermediate of the recursion is rounded to fp16.
+ */
+int hg_trmm_inplace(int uplo, int trans, int64_t n, int64_t m, float alpha,
+                    const void *A, int64_t lda, void *B, int64_t ldb,
+                    int64_t leaf, void *work, int64_t work_bytes, void *stream);
+
+/* hg_trmm_inplace_workspace_size — bytes hg_trmm_inplace needs (host only);
+ * negative values as hg_trmm_workspace_size. */
+int64_t hg_trmm_inplace_workspace_size(int uplo, int trans, int64_t n, int64_t m);
+
+/*
  * hg_trmm_lower_trans_by_level — trmm_lower_trans (same arguments, same
  * status codes, same result bit for bit) scheduled as in the recursion's
  * description, "异构计算中高性能TRMM与TRSM的递归算法实现" §2.2: one batched

@@ -30,6 +30,7 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == ["hg_hgemm_layout_workspace_size", "hg_strerror", "hg_trmm",
+                                    "hg_trmm_inplace", "hg_trmm_inplace_workspace_size",
                                     "hg_trmm_lower_trans_by_level", "hg_trmm_plan",
                                     "hg_trmm_workspace_size", "hg_trsm_workspace_size", "hgemm",
                                     "hgemm_bf16", "hgemm_bias_act", "hgemm_layout",
@@ -249,6 +250,23 @@ def test_hgemm_layout_workspace_size(lib):
     assert lib.hg_hgemm_layout_workspace_size(0, 0, 30, 40, 100) == up(40 * ldk * 2)
     assert lib.hg_hgemm_layout_workspace_size(1, 0, 30, 40, 100) == up(30 * ldk * 2) + up(40 * ldk * 2)
     assert lib.hg_hgemm_layout_workspace_size(3, 0, 1, 1, 1) == -1
+
+
+def test_hg_trmm_inplace_arguments(lib):
+    up = lambda x: -(-x // 256) * 256
+    assert lib.hg_trmm_inplace_workspace_size(0, 1, 1000, 77) == up(1000 * 77 * 4)
+    assert lib.hg_trmm_inplace_workspace_size(1, 0, 1000, 77) == \
+        up(1000 * 77 * 4) + lib.hg_trmm_workspace_size(1, 0, 1000, 77)
+    assert lib.hg_trmm_inplace_workspace_size(5, 0, 10, 10) == -1
+    I = lambda *a: lib.hg_trmm_inplace(*a, None)
+    assert I(3, 1, 8, 4, 1.0, P, 8, Q, 8, 256, W, 1 << 20) == -1
+    assert I(0, 1, 8, 4, 1.0, P, 7, Q, 8, 256, W, 1 << 20) == -7
+    assert I(0, 1, 8, 4, 1.0, P, 8, Q, 7, 256, W, 1 << 20) == -9
+    assert I(0, 1, 8, 4, 1.0, P, 8, None, 8, 256, W, 1 << 20) == -8
+    assert I(0, 1, 8, 4, 1.0, P, 8, P + 16, 8, 256, W, 1 << 20) == -8     # B overlaps A
+    assert I(0, 1, 8, 4, 1.0, P, 8, Q, 8, 256, None, 1 << 20) == -11
+    assert I(0, 1, 8, 4, 1.0, P, 8, Q, 8, 256, W, 16) == -12
+    assert I(0, 1, 0, 4, 1.0, None, 1, None, 1, 256, None, 0) == 0
 
 
 def test_strerror(hg):
