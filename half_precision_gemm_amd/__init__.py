@@ -262,7 +262,7 @@ def trmm_lower_trans(A, B, Out, alpha: float = 1.0, leaf: int = 256):
 
 def trmm_lower_trans_by_level(A, B, Out, alpha: float = 1.0, leaf: int = 256):
     """trmm_lower_trans scheduled as one batched launch per recursion level
-    (same result, bit for bit); see hg_trmm_lower_trans_by_level."""
+    (same result up to fp32 rounding); see hg_trmm_lower_trans_by_level."""
     return _trmm(lib.hg_trmm_lower_trans_by_level, "hg_trmm_lower_trans_by_level", A, B, Out,
                  alpha, leaf)
 

@@ -8,14 +8,12 @@
 // triangle-masked leaf of the recursive TRMM ("异构计算中高性能TRMM与TRSM的
 // 递归算法实现" §2.2).  Design:
 //
-//  * One workgroup = 8 waves (2 per SIMD) per 256×256 tile, laid out 2×4;
-//    each wave owns a 128×64 sub-tile = 8×4 blocks of
-//    v_mfma_f32_16x16x32_f16, 128 fp32 accumulators per lane.  The 16×16×32
-//    shape draws less power per flop than 32×32×16 on these data, so the
-//    chip holds a higher clock; two waves per SIMD keep the matrix core fed
-//    while the other waits on LDS, whose per-wave throughput (about 27
-//    bytes per clock for reads and direct loads together) would otherwise
-//    bound a single wave.
+//  * One workgroup = 4 waves (one per SIMD) per 256×256 tile, laid out 2×2;
+//    each wave owns a 128×128 sub-tile = 8×8 blocks of
+//    v_mfma_f32_16x16x32_f16, 256 fp32 accumulators per lane (AGPRs).  The
+//    16×16×32 shape draws less power per flop than 32×32×16 on these data,
+//    so the chip holds a higher clock.  (HG_FAST_NW=8 builds the 2×4 layout
+//    with two waves per SIMD and 128×64 sub-tiles; it was not faster.)
 //  * K is walked in BK = 64 stages: one 128-byte cache line per operand row.
 //    Operands reach LDS through the gfx950 direct buffer→LDS path
 //    (buffer_load_dwordx4 … lds; each wave instruction moves 8 rows × 128
@@ -248,9 +246,6 @@ __device__ __forceinline__ void map_tile(int id, int total, int tiles_m, int til
 // Everything a workgroup needs to know about one tile.
 struct TileInfo {
     int batch, m0, n0, N, K, rows_a, rows_b, kt0, nk;
-    int kend;      // FUSED: end of this K segment (stage kt0 + nk, in elements)
-    int first;     // FUSED: the tile's first segment (C written, not read)
-    int tri;       // FUSED: the leaf segment (triangle mask applies)
     hg_int32x4 ra, rb;
 };
 
@@ -291,45 +286,28 @@ __device__ __forceinline__ bool find_tile(const GemmParams &p, int &id, int stri
 // ---- Recursive TRMM in one launch ("异构计算中高性能TRMM与TRSM的递归算法实现"
 // §2.1–§2.2).  In the GEMM view used here (C = Outᵀ, M = m, N = K = n), the
 // recursion splits a diagonal block (o, s) at h = ⌊s/2⌋: the tiles of output
-// columns [o, o+h) receive the update over K = [o+h, o+s) after everything
-// below that node; a block of at most `leaf` columns is a leaf, whose tiles
-// take K from their own first column to the leaf's end under the triangle
-// mask.  For one output tile the leaf and the updates that touch it cover
-// contiguous K ranges in increasing order, ending at the leaf's end and at
-// the ends of the ancestors whose upper half holds the tile, deepest first:
-// exactly the order in which the depth-first recursion accumulates into
-// that tile.  So one workgroup can walk a tile's segments in that order,
-// writing C = α·acc after the first and C = fma(α, acc, C) after each later
-// one -- the same arithmetic, per element, as the level-by-level launches.
-
-// End of the K segment that starts at kpos for the tile whose first column
-// is n0.
-__device__ __forceinline__ int trmm_seg_end(int n0, int kpos, int n, int leaf)
-{
-    int o = 0, s = n, best = n;
-    while (s > leaf) {
-        const int h = s / 2;
-        if (n0 < o + h) {
-            if (o + s > kpos && o + s < best)
-                best = o + s;
-            s = h;
-        } else {
-            o += h;
-            s -= h;
-        }
-    }
-    if (o + s > kpos && o + s < best)
-        best = o + s;
-    return best;
-}
+// columns [o, o+h) receive the update over K = [o+h, o+s) (a GEMM with
+// β = 1) after everything below that node; a block of at most `leaf`
+// columns is a leaf, whose tiles take K from their own first column to the
+// leaf's end under the triangle mask.  With every recursion boundary on a
+// tile edge, the leaf and the updates that reach one output tile cover
+// contiguous K ranges in increasing order -- the leaf's end, then the ends
+// of the ancestors whose upper half holds the tile, deepest first, the last
+// one n -- which is the order in which the depth-first recursion
+// accumulates into that tile.  One workgroup therefore walks K from the
+// tile's first column to n in that order, and each update's β = 1
+// accumulation into the tile happens in the fp32 accumulators rather than
+// through a store and a reload of Out; α, common to the leaf and every
+// update, is applied once when the tile is written.  The level-by-level
+// launches keep the store between updates.
 
 // Work item of workgroup w in round r: output tile q = r·G + w (r even) or
 // r·G + G-1-w (r odd) of the tiles ordered by column, so that the columns
 // with the most K work run first and the rounds of every workgroup add up
 // to about the same work (a tile's work falls linearly with its column).
-// kpos < 0 starts the tile's first segment.  False once q is past the end.
-__device__ __forceinline__ bool fused_item(const GemmParams &p, int w, int G, int round, int kpos,
-                                           int total, int tiles_m, TileInfo &T)
+// False once q is past the end.
+__device__ __forceinline__ bool fused_item(const GemmParams &p, int w, int G, int round, int total,
+                                           int tiles_m, TileInfo &T)
 {
     const int q = round * G + ((round & 1) ? G - 1 - w : w);
     if (q >= total)
@@ -337,9 +315,6 @@ __device__ __forceinline__ bool fused_item(const GemmParams &p, int w, int G, in
     const int tm = q % tiles_m, tn = q / tiles_m;
     const int N = p.e[0].N, K = p.e[0].K;
     const int m0 = tm * BM, n0 = tn * BN;
-    if (kpos < 0)
-        kpos = n0;
-    const int kend = trmm_seg_end(n0, kpos, K, p.leaf);
     T.batch = 0;
     T.m0 = m0;
     T.n0 = n0;
@@ -347,11 +322,8 @@ __device__ __forceinline__ bool fused_item(const GemmParams &p, int w, int G, in
     T.K = K;
     T.rows_a = min(p.M - m0, BM);
     T.rows_b = min(N - n0, BN);
-    T.kt0 = kpos / BK;
-    T.nk = (kend - kpos) / BK;
-    T.kend = kend;
-    T.first = kpos == n0;
-    T.tri = kpos == n0;
+    T.kt0 = n0 / BK;
+    T.nk = (K - n0) / BK;
     const _Float16 *Ab = p.A + (int64_t)m0 * p.lda;
     const _Float16 *Bb = p.B + (int64_t)n0 * p.ldb;
     T.ra = make_rsrc(Ab, (uint32_t)(((int64_t)(T.rows_a - 1) * p.lda + K) * 2));
@@ -474,7 +446,7 @@ hgemm_fast_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int c
 
     int id = blockIdx.x;              // FUSED: the round
     TileInfo T;
-    if (FUSED ? !fused_item(p, blockIdx.x, stride, 0, -1, total, tiles_m, T)
+    if (FUSED ? !fused_item(p, blockIdx.x, stride, 0, total, tiles_m, T)
               : !find_tile<TRI>(p, id, stride, total, tiles_m, tiles_n, T))
         return;
     if (FUSED)
@@ -490,7 +462,7 @@ hgemm_fast_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int c
     // The counter retires in issue order, so waiting until at most
     // (loads after stage 0) + EPI_OPS remain means stage 0 has landed while
     // the epilogue's stores are still draining.
-    constexpr int EPI_OPS = TM * TN * (BETA && !FUSED ? 2 : 1);   // FUSED: the smaller count
+    constexpr int EPI_OPS = TM * TN * (BETA ? 2 : 1);
     constexpr int VM_TILE0 = 2 * LPS;       // stage 1's loads, issued after stage 0's
     constexpr int VM_AFTER_EPI = VM_TILE0 + EPI_OPS < 63 ? VM_TILE0 + EPI_OPS : 63;
     int prev = 0;                      // 0: first tile, 1: after an interior epilogue, 2: after an edge one
@@ -534,8 +506,10 @@ hgemm_fast_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int c
             static_for<NQ>([&](auto qc) __attribute__((always_inline)) {
                 constexpr int q = decltype(qc)::value;
                 constexpr int s = q >> 1, h = q & 1;
+                // Only the first BN/BK stages hold elements with k below
+                // the tile's columns.
                 if constexpr (TRI && h == 0) {
-                    if (!FUSED || T.tri)
+                    if (kt < BN / BK)
                         mask_tri(T, kt, s);
                 }
                 // Ring loads of this quarter: operand, stage, slot, first index.
@@ -592,10 +566,8 @@ hgemm_fast_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int c
         TileInfo Tn;
         bool more;
         if constexpr (FUSED) {
-            // The tile's next segment, or the next round's tile.
-            nid = T.kend < T.K ? id : id + 1;
-            more = fused_item(p, blockIdx.x, stride, nid, T.kend < T.K ? T.kend : -1, total, tiles_m,
-                              Tn);
+            nid = id + 1;                 // the next round's tile
+            more = fused_item(p, blockIdx.x, stride, nid, total, tiles_m, Tn);
         } else {
             more = find_tile<TRI>(p, nid, stride, total, tiles_m, tiles_n, Tn);
         }
@@ -611,8 +583,7 @@ hgemm_fast_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int c
         // (the B fragment is the MFMA's first operand): lane covers row
         // m0 + wm·WTM + 16i + (lane mod 16) and columns
         // n0 + wn·WTN + 16j + 4·(lane div 16) + 0..3.
-        // RD: the epilogue reads C (beta != 0; FUSED: every segment after the
-        // tile's first).
+        // RD: the epilogue reads C (beta != 0).
         auto epilogue = [&](auto rdc) __attribute__((always_inline)) {
             constexpr bool RD = decltype(rdc)::value;
             // 16-bit C has the input's type (fp16 or bf16).
@@ -706,14 +677,7 @@ hgemm_fast_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int c
                 }
             }
         };
-        if constexpr (FUSED) {
-            if (T.first)
-                epilogue(std::false_type{});
-            else
-                epilogue(std::true_type{});
-        } else {
-            epilogue(std::integral_constant<bool, BETA>{});
-        }
+        epilogue(std::integral_constant<bool, BETA>{});
         if (!more)
             break;
         T = Tn;
@@ -797,7 +761,7 @@ hipError_t launch_trmm_fused(const GemmParams &p, hipStream_t stream)
     grid = grid / 8 * 8 > 0 ? grid / 8 * 8 : grid;
     if (grid > total64)
         grid = total64;
-    hipLaunchKernelGGL((hgemm_fast_kernel<false, true, true, false, true, false, false>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((hgemm_fast_kernel<false, false, true, false, true, false, false>), dim3((unsigned)grid),
                        dim3(THREADS), 0, stream, p, tiles_m, tiles_n, (int)total64, cvec);
     return hipGetLastError();
 }

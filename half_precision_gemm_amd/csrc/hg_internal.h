@@ -76,7 +76,8 @@ hipError_t launch_gemm_ring(const GemmParams &p, const LaunchOpts &o, hipStream_
 // Recursive TRMM (Out = alpha·Aᵀ·B, A lower) in one launch, in the GEMM view
 // C = Outᵀ (M = m, N = K = n; p.A = B, p.B = A, p.C = Out, p.e[0] = {0, 0,
 // 0, n, n}, p.leaf): every output tile walks its leaf and then the recursion's
-// updates that touch it, deepest first, in one persistent workgroup.
+// updates that touch it, deepest first, in one persistent workgroup, the
+// updates accumulated in registers (one store per tile).
 // trmm_fused_ok: the operands suit the fast path, every recursion boundary
 // falls on a 256-column tile edge, and there are at least two output tiles
 // per CU.

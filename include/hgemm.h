@@ -200,9 +200,12 @@ int hgemm_bf16(int64_t M, int64_t N, int64_t K, float alpha,
  * 256 split down to leaves of at least 256), the operands are 16-byte
  * aligned with lda, ldb multiples of 8 and there are at least two 256×256
  * output tiles per compute unit, all terms run in one launch in which each
- * output tile walks its own terms in that order; otherwise one batched
- * launch runs all leaves and one each update level.  Both schedules
- * give the same bits (see hg_trmm_lower_trans_by_level).
+ * output tile walks its own terms in that order and adds each update to
+ * the leaf in its fp32 accumulators (alpha applied once, when the tile is
+ * written); otherwise one batched launch runs all leaves and one each
+ * update level, rounding Out to fp32 after every update.  The two
+ * schedules differ only by those fp32 roundings (integer-valued inputs:
+ * the same bits; see hg_trmm_lower_trans_by_level).
  */
 int trmm_lower_trans(int64_t n, int64_t m, float alpha,
                      const void *A, int64_t lda,
@@ -273,7 +276,7 @@ int64_t hg_trmm_inplace_workspace_size(int uplo, int trans, int64_t n, int64_t m
 
 /*
  * hg_trmm_lower_trans_by_level — trmm_lower_trans (same arguments, same
- * status codes, same result bit for bit) scheduled as in the recursion's
+ * status codes, the same result up to fp32 rounding) scheduled as in the recursion's
  * description, "异构计算中高性能TRMM与TRSM的递归算法实现" §2.2: one batched
  * launch for all leaves, then one batched GEMM launch (beta = 1) per
  * recursion level, deepest first.  For verification and comparison of the
