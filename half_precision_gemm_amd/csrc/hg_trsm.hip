@@ -145,8 +145,8 @@ __global__ void __launch_bounds__(256) trsm_inv_kernel(const TrsmInvParams p)
 // The whole K range fits in LDS (R: 32×256, V: 256×256 fp16, 144 KB), so
 // every load is issued up front — one global round trip — then one barrier
 // and the products.  V(k, j) = 0 for k < j: a 16-wide k step whose k are all
-// below a 32-row j block is neither loaded nor multiplied.  Wave w owns
-// j ∈ [64w, 64w+64).
+// below a 32-row j block is not loaded (and enters the product as zero).
+// Wave w owns the j blocks [32w, 32w+32) and [224-32w, 256-32w).
 constexpr int LBM = 32, LBN = 256, LBK = 256;
 constexpr int LKC = LBK / 8;                 // 16-byte chunks per LDS row
 constexpr int LDS_R = LBM * LBK * 2;         // 16 KB
@@ -219,9 +219,15 @@ __global__ void __launch_bounds__(256, 1) trsm_leaf_kernel(const TrsmLeafParams 
     };
 
     // All loads first.  Thread t takes chunk column t mod 32 of rows
-    // t/32 + 8u: R rows u < 4, V rows u < 32.
+    // t/32 + 8u: R rows u < 4, V rows t/32 + 8·((u + rot) mod 32).  Every
+    // workgroup reads the same V; the rotation makes the workgroups of one
+    // XCD (consecutive workgroups go to different XCDs, so those of one XCD
+    // are 8 apart) request different lines (different L2 channels) instead
+    // of queueing on the same ones.
     const int lkc = t & 31;
     const int lrow = t >> 5;
+    const int rot = (blockIdx.x >> 3) & (V_PER_T - 1);
+    auto vrow = [&](int u) { return lrow + 8 * ((u + rot) & (V_PER_T - 1)); };
     uint4 ra[R_PER_T];
     uint4 rv[V_PER_T];
     bool vok[V_PER_T];
@@ -254,7 +260,7 @@ __global__ void __launch_bounds__(256, 1) trsm_leaf_kernel(const TrsmLeafParams 
         }
 #pragma unroll
         for (int u = 0; u < V_PER_T; ++u) {
-            const int j = lrow + 8 * u;
+            const int j = vrow(u);
             vok[u] = j < s && k < s && v_chunk_used(j, lkc);
             rv[u] = *reinterpret_cast<const uint4 *>(p.V + (vok[u] ? (int64_t)j * p.ldv + k : 0));
         }
@@ -280,7 +286,7 @@ __global__ void __launch_bounds__(256, 1) trsm_leaf_kernel(const TrsmLeafParams 
             ra[u] = load_r(m0 + lrow + 8 * u, lkc * 8);
 #pragma unroll
         for (int u = 0; u < V_PER_T; ++u) {
-            const int j = lrow + 8 * u;
+            const int j = vrow(u);
             rv[u] = make_uint4(0u, 0u, 0u, 0u);
             if (j < s && lkc * 8 < s && v_chunk_used(j, lkc))
                 rv[u] = *reinterpret_cast<const uint4 *>(p.V + (int64_t)j * p.ldv + lkc * 8);
@@ -291,7 +297,7 @@ __global__ void __launch_bounds__(256, 1) trsm_leaf_kernel(const TrsmLeafParams 
         *reinterpret_cast<uint4 *>(Rs + lds_chunk(lrow + 8 * u, lkc) * 16) = ra[u];
 #pragma unroll
     for (int u = 0; u < V_PER_T; ++u) {
-        const int j = lrow + 8 * u;
+        const int j = vrow(u);
         if (v_chunk_used(j, lkc))
             *reinterpret_cast<uint4 *>(Vs + lds_chunk(j, lkc) * 16) = rv[u];
     }
@@ -300,25 +306,29 @@ __global__ void __launch_bounds__(256, 1) trsm_leaf_kernel(const TrsmLeafParams 
     // Fragments: lane l supplies row (l mod 32) of a 32-row block and the 8
     // consecutive k from 8·(l div 32) of the current 16-wide k step, for both
     // operands; the V fragment goes first, so each 32×32 result is Cᵀ.
+    // Wave w owns the 32-row j blocks w and 7 - w: block jb needs the k steps
+    // st >= 2·jb (V(k, j) = 0 for k < j), 18 steps per wave in all.  The
+    // loop runs every step with no branch, so the fragment reads can be
+    // issued ahead of the products; a V chunk that was not loaded (k below
+    // the block, or past the leaf) enters as zero.
     const int frow = lane & 31;
     const int fkc = lane >> 5;
+    const int jbs[2] = {wave, 7 - wave};
     floatx16 acc[2];
 #pragma unroll
     for (int b = 0; b < 2; ++b)
         acc[b] = floatx16{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
-    const int nst = (s + 15) / 16;
 #pragma unroll
     for (int st = 0; st < LBK / 16; ++st) {
-        if (64 * wave >= s || st >= nst || 16 * st + 16 <= 64 * wave)
-            continue;
         const int kc = 2 * st + fkc;
         const half8 af = *reinterpret_cast<const half8 *>(Rs + lds_chunk(frow, kc) * 16);
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
-            const int j0 = 64 * wave + 32 * b;
-            if (16 * st + 16 <= j0)
-                continue;
-            const half8 bf = *reinterpret_cast<const half8 *>(Vs + lds_chunk(j0 + frow, kc) * 16);
+            const int jb = jbs[b];
+            const uint4 raw = *reinterpret_cast<const uint4 *>(Vs + lds_chunk(32 * jb + frow, kc) * 16);
+            const uint32_t keep = st >= 2 * jb && 8 * kc < s ? 0xffffffffu : 0u;
+            const half8 bf = __builtin_bit_cast(
+                half8, make_uint4(raw.x & keep, raw.y & keep, raw.z & keep, raw.w & keep));
             acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf, af, acc[b], 0, 0, 0);
         }
     }
@@ -326,19 +336,19 @@ __global__ void __launch_bounds__(256, 1) trsm_leaf_kernel(const TrsmLeafParams 
     // Epilogue, staged through LDS (the inverse's area, free once every wave
     // is past its last MFMA): block b of this wave holds C(i, j..j+3) for
     // i = m0 + (lane mod 32) and, in register group g,
-    // j = 64·wave + 32b + 8g + 4·(lane div 32).  Written to LDS as rows i of
-    // 256 fp32, then each store instruction writes one column i of X: 64
+    // j = 32·jb + 8g + 4·(lane div 32) for its row block jb.  Written to LDS
+    // as rows i of 256 fp32, then each store instruction writes one column i of X: 64
     // lanes × 4 rows = the column's 1 KiB of fp32 and 512 B of fp16, whole
     // cache lines (scattered 16-byte pieces tripled the written bytes).
     float *Xs = reinterpret_cast<float *>(Vs);
     constexpr int XLD = LBN + 4;                 // padded row of the staged tile
     __syncthreads();
-    if (64 * wave < s) {
+    {
 #pragma unroll
         for (int b = 0; b < 2; ++b)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const int j = 64 * wave + 32 * b + 8 * g + 4 * fkc;
+                const int j = 32 * jbs[b] + 8 * g + 4 * fkc;
                 *reinterpret_cast<floatx4 *>(Xs + frow * XLD + j) =
                     floatx4{acc[b][4 * g + 0], acc[b][4 * g + 1], acc[b][4 * g + 2], acc[b][4 * g + 3]};
             }
