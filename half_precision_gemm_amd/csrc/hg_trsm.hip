@@ -38,16 +38,27 @@ typedef _Float16 halfx4 __attribute__((ext_vector_type(4)));
 // Workgroup (leaf l, column block J) computes columns c0 = 32·J .. c0+31 of
 // V = A_LL⁻¹ (lower triangular) over 32-row blocks I = J, J+1, …:
 //   T = E_IJ − Σ_{K=J}^{I−1} A_IK·V_KJ      (E = identity)
-//   A_II·V_IJ = T                            (forward substitution, 32 columns)
-// All arithmetic is fp32; the block is written as fp16, each element exactly
+//   V_IJ = D_I·T,  D_I = A_II⁻¹
+// The D_I of all its blocks are computed first, together (one forward
+// substitution per thread), so that the block-by-block sweep holds no
+// serial substitution, only products.  All arithmetic is fp32; the block is written as fp16, each element exactly
 // once: the computed lower part, zeros above the diagonal, outside the leaf
 // and in the padding up to ld, so that the leaf kernel needs no masks.
 constexpr int kInvCols = 32;
 
 __global__ void __launch_bounds__(256) trsm_inv_kernel(const TrsmInvParams p)
 {
-    __shared__ float vs[kTrsmLeafMax][kInvCols + 1];  // this column block of V
-    __shared__ float as[kInvCols][kTrsmLeafMax + 1];  // A row panel of block I
+    // This column block of V, transposed: vt[c][r] = V(r, c0 + c).  Row
+    // stride 260 floats keeps every row 16-byte aligned for float4 reads.
+    constexpr int VT = kTrsmLeafMax + 4;
+    constexpr int NDB = kTrsmLeafMax / kInvCols;       // diagonal blocks per leaf (8)
+    constexpr int DT = kInvCols + 4;
+    __shared__ __attribute__((aligned(16))) float vt[kInvCols][VT];
+    __shared__ __attribute__((aligned(16))) float as[kInvCols][VT];   // A row panel of block I
+    // D_I = A_II⁻¹ of the diagonal blocks I = J, J+1, …: dd[I - J][r][k].
+    __shared__ __attribute__((aligned(16))) float dd[NDB][kInvCols][DT];
+    // Per-wave partial sums of T.
+    __shared__ float red[4][kInvCols][kInvCols + 1];
 
     const int nj = (p.ld + kInvCols - 1) / kInvCols;
     const int l = blockIdx.x / nj;
@@ -64,7 +75,7 @@ __global__ void __launch_bounds__(256) trsm_inv_kernel(const TrsmInvParams p)
     const int nrb = (ld + kInvCols - 1) / kInvCols;   // row blocks of the ld×ld block
     const int nb = (s + kInvCols - 1) / kInvCols;     // row blocks holding leaf rows
 
-    // Rows [r0, r0+32) of this column block: zeros, or the values in vs.
+    // Rows [r0, r0+32) of this column block: zeros, or the values in vt.
     auto store_rows = [&](int r0, bool zero) {
         for (int idx = t; idx < kInvCols * ncol; idx += 256) {
             const int rr = idx % kInvCols, c = idx / kInvCols;
@@ -72,7 +83,7 @@ __global__ void __launch_bounds__(256) trsm_inv_kernel(const TrsmInvParams p)
             if (r >= ld)
                 continue;
             const bool inside = !zero && r < s && col < s && r >= col;
-            V[r + (int64_t)col * ld] = (_Float16)(inside ? vs[r][c] : 0.0f);
+            V[r + (int64_t)col * ld] = (_Float16)(inside ? vt[c][r] : 0.0f);
         }
     };
 
@@ -86,48 +97,138 @@ __global__ void __launch_bounds__(256) trsm_inv_kernel(const TrsmInvParams p)
 
     const int c = t % kInvCols;   // column of the block this thread works on
     const int g = t / kInvCols;   // row group: rows g, g+8, g+16, g+24 of a block
-    for (int I = J; I < nb; ++I) {
-        const int r0 = I * kInvCols;
-        // A panel: rows r0..r0+31, columns c0..r0+31 (the diagonal block last).
-        const int ka = r0 + kInvCols - c0;
-        for (int idx = t; idx < kInvCols * ka; idx += 256) {
-            const int rr = idx % kInvCols, k = c0 + idx / kInvCols;
-            const int r = r0 + rr;
-            as[rr][k] = (r < s && k <= r) ? (float)A[(o + r) + (o + k) * lda] : 0.0f;
+    const int lane = t & 63, wave = t >> 6;
+    // A panel of block I: rows r0..r0+31, columns c0..r0+31 (the diagonal
+    // block last), at most 32×256 values, 32 per thread: thread t takes row
+    // r0 + t mod 32 of columns c0 + t/32 + 8u.  All 32 loads of a panel are
+    // issued together, and the next block's panel is requested before this
+    // block's arithmetic, so each panel costs one memory round trip that
+    // overlaps the previous block's work.
+    constexpr int kPanelPerT = kInvCols * kTrsmLeafMax / 256;
+    _Float16 pa[kPanelPerT];
+    auto load_panel = [&](int I) {
+        const int r = I * kInvCols + c;
+        const int ka = I * kInvCols + kInvCols - c0;
+#pragma unroll
+        for (int u = 0; u < kPanelPerT; ++u) {
+            const int kk = g + 8 * u;
+            const int k = c0 + kk;
+            pa[u] = (kk < ka && r < s && k <= r) ? A[(o + r) + (o + k) * lda] : (_Float16)0.0f;
+        }
+    };
+    if (J < nb)
+        load_panel(J);
+
+    // Inverses of the diagonal blocks, all at once: thread t solves
+    // A_II·d = e_c for block I = J + t/32, column c = t mod 32, by forward
+    // substitution (fp32, coefficients from LDS); rows past the leaf get a
+    // unit diagonal, so d stays finite there (those rows are stored as zeros).
+    {
+        const int ndb = nb - J;
+#pragma unroll
+        for (int u = 0; u < kPanelPerT; ++u) {
+            const int idx = t + 256 * u;
+            const int bi = idx / (kInvCols * kInvCols);
+            const int kk = (idx / kInvCols) % kInvCols, rr = idx % kInvCols;
+            if (bi < ndb) {
+                const int r = (J + bi) * kInvCols + rr, k = (J + bi) * kInvCols + kk;
+                float a = 0.0f;
+                if (r < s && k <= r)
+                    a = (float)A[(o + r) + (o + k) * lda];
+                else if (r >= s && k == r)
+                    a = 1.0f;
+                dd[bi][rr][kk] = a;
+            }
         }
         __syncthreads();
-        // T for rows of block I, into vs (those rows are not read yet).
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int rr = g + 8 * q;
-            float acc = (r0 + rr == c0 + c) ? 1.0f : 0.0f;
-            for (int k = c0; k < r0; ++k)
-                acc = __builtin_fmaf(-as[rr][k], vs[k][c], acc);
-            vs[r0 + rr][c] = acc;
-        }
-        __syncthreads();
-        // A_II·Y = T, one column per thread of the first 32: the column's 32
-        // values stay in registers (loops unrolled), the coefficients are LDS
-        // broadcasts independent of the substitution chain.  Rows past the
-        // leaf are left as they are (they are stored as zeros).
-        if (t < kInvCols) {
-            float y[kInvCols];
-#pragma unroll
-            for (int rr = 0; rr < kInvCols; ++rr)
-                y[rr] = vs[r0 + rr][t];
+        const int bi = t / kInvCols;
+        float y[kInvCols];
+        if (bi < ndb) {
 #pragma unroll
             for (int rr = 0; rr < kInvCols; ++rr) {
-                if (r0 + rr < s) {
-                    float acc = y[rr];
+                float acc = rr == c ? 1.0f : 0.0f;
 #pragma unroll
-                    for (int kk = 0; kk < rr; ++kk)
-                        acc = __builtin_fmaf(-as[rr][r0 + kk], y[kk], acc);
-                    y[rr] = acc / as[rr][r0 + rr];
-                }
+                for (int kk = 0; kk < rr; ++kk)
+                    acc = __builtin_fmaf(-dd[bi][rr][kk], y[kk], acc);
+                y[rr] = acc / dd[bi][rr][rr];
             }
+        }
+        __syncthreads();
+        if (bi < ndb) {
 #pragma unroll
             for (int rr = 0; rr < kInvCols; ++rr)
-                vs[r0 + rr][t] = y[rr];
+                dd[bi][rr][c] = y[rr];
+        }
+        __syncthreads();
+    }
+
+    for (int I = J; I < nb; ++I) {
+        const int r0 = I * kInvCols;
+        const int ka = r0 + kInvCols - c0;
+#pragma unroll
+        for (int u = 0; u < kPanelPerT; ++u) {
+            const int kk = g + 8 * u;
+            if (kk < ka)
+                as[c][c0 + kk] = (float)pa[u];
+        }
+        __syncthreads();
+        if (I + 1 < nb)
+            load_panel(I + 1);
+        // T for rows of block I, into vt (those rows are not read yet).  The
+        // sum over k in [c0, r0) runs on the matrix cores in fp32
+        // (v_mfma_f32_32x32x2_f32), split evenly over the four waves (a
+        // multiple of 8 k each); in group k0 .. k0+7, step m takes
+        // k = k0 + 4·(lane div 32) + m from both operands, so each lane
+        // reads one float4 of its A row (as) and one of its V column (vt).
+        // The four partial 32×32 sums meet in LDS.
+        {
+            const int kw = (r0 - c0) / 4;
+            const int kb = c0 + wave * kw;
+            const int h = lane >> 5, li = lane & 31;
+            floatx16 acc = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+            for (int k0 = kb; k0 < kb + kw; k0 += 8) {
+                const float4 a = *reinterpret_cast<const float4 *>(&as[li][k0 + 4 * h]);
+                const float4 v = *reinterpret_cast<const float4 *>(&vt[li][k0 + 4 * h]);
+                acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.x, v.x, acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.y, v.y, acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.z, v.z, acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.w, v.w, acc, 0, 0, 0);
+            }
+            // Lane holds column li, rows 8·(v div 4) + 4h + v mod 4.
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+                red[wave][8 * (v >> 2) + 4 * h + (v & 3)][li] = acc[v];
+            __syncthreads();
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int i = g + 8 * q;
+                const float sum = (red[0][i][c] + red[1][i][c]) + (red[2][i][c] + red[3][i][c]);
+                vt[c][r0 + i] = (r0 + i == c0 + c ? 1.0f : 0.0f) - sum;
+            }
+        }
+        __syncthreads();
+        // V_IJ = D_I·T: the thread's four rows of column c, T's column read
+        // as float4 from vt, D's rows from dd; written back over T once every
+        // thread has read it.
+        {
+            const float(*D)[DT] = dd[I - J];
+            float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int kk = 0; kk < kInvCols; kk += 4) {
+                const float4 v = *reinterpret_cast<const float4 *>(&vt[c][r0 + kk]);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float4 d = *reinterpret_cast<const float4 *>(&D[g + 8 * q][kk]);
+                    acc[q] = __builtin_fmaf(d.x, v.x, acc[q]);
+                    acc[q] = __builtin_fmaf(d.y, v.y, acc[q]);
+                    acc[q] = __builtin_fmaf(d.z, v.z, acc[q]);
+                    acc[q] = __builtin_fmaf(d.w, v.w, acc[q]);
+                }
+            }
+            __syncthreads();
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                vt[c][r0 + g + 8 * q] = acc[q];
         }
         __syncthreads();
         store_rows(r0, false);
