@@ -424,7 +424,9 @@ struct TrsmRun {
     int64_t leaf;
     hipStream_t stream;
 
-    int leaf_step(int64_t o, int64_t s, bool touched) const
+    // sb > 0: the leaf also applies the update of the node (o, s + sb) whose
+    // lower half [o+s, o+s+sb) is already solved (see TrsmLeafParams).
+    int leaf_step(int64_t o, int64_t s, bool touched, int64_t sb = 0) const
     {
         const auto it = std::lower_bound(leaves->begin(), leaves->end(), std::make_pair(o, (int64_t)0));
         const int64_t idx = it - leaves->begin();
@@ -442,9 +444,27 @@ struct TrsmRun {
         p.m = (int32_t)m;
         p.alpha = alpha;
         p.touched = touched ? 1 : 0;
-        const bool vec = aligned16(B) && aligned16(Out) && aligned16(W) && o % 8 == 0 &&
-                         s % 8 == 0 && ldb % 8 == 0 && ldo % 4 == 0 && ldw % 4 == 0;
+        p.A = static_cast<const _Float16 *>(A);
+        p.lda = lda;
+        p.sb = (int32_t)sb;
+        const bool vec = leaf_vec(o, s);
         return hip_status(hg::launch_trsm_leaf(p, vec, stream));
+    }
+
+    bool leaf_vec(int64_t o, int64_t s) const
+    {
+        return aligned16(B) && aligned16(Out) && aligned16(W) && o % 8 == 0 && s % 8 == 0 &&
+               ldb % 8 == 0 && ldo % 4 == 0 && ldw % 4 == 0;
+    }
+
+    // The deepest nodes (both halves leaves) run as the lower leaf, then the
+    // upper leaf with the node's update fused in, when the vector paths and
+    // the fused update's alignment allow it.
+    bool fuse_ok(int64_t o, int64_t s) const
+    {
+        const int64_t h = s / 2;
+        return s > leaf && h <= leaf && s - h <= leaf && leaf_vec(o, h) && (s - h) % 8 == 0 &&
+               aligned16(A) && lda % 8 == 0 && ldw % 8 == 0;
     }
 
     // Rows o..o+h-1 of the right-hand side: S = beta·S − A21ᵀ·X2 with
@@ -481,6 +501,10 @@ struct TrsmRun {
         if (s <= leaf)
             return leaf_step(o, s, touched);
         const int64_t h = s / 2;
+        if (fuse_ok(o, s)) {
+            const int st = leaf_step(o + h, s - h, touched);
+            return st == HG_OK ? leaf_step(o, h, touched, s - h) : st;
+        }
         int st = solve(o + h, s - h, touched);
         if (st == HG_OK)
             st = update(o, s, touched);

@@ -119,11 +119,19 @@ struct TrsmLeafParams {
     int32_t m;             // columns of B
     float alpha;
     int32_t touched;       // nonzero: add S = Out rows to alpha·B
+    // Fused update of the recursion node whose upper half is this leaf
+    // (sb > 0, vec only): S -= A21ᵀ·X2 first, A21 = A[o+s : o+s+sb, o : o+s],
+    // X2 = W rows o+s .. o+s+sb-1 (the lower half, already solved).
+    const _Float16 *A;
+    int64_t lda;
+    int32_t sb;
 };
 
 hipError_t launch_trsm_inv(const TrsmInvParams &p, hipStream_t stream);
 // vec: B, Out, W 16-byte aligned, o % 8 == 0, s % 8 == 0, ldb % 8 == 0,
-// ldo % 4 == 0, ldw % 4 == 0 (vector loads and stores).
+// ldo % 4 == 0, ldw % 4 == 0 (vector loads and stores); a fused update
+// (sb > 0) also needs vec, A 16-byte aligned, lda % 8 == 0, ldw % 8 == 0 and
+// sb % 8 == 0.
 hipError_t launch_trsm_leaf(const TrsmLeafParams &p, bool vec, hipStream_t stream);
 
 // TRMM variants (hg_xform.hip): L = map(A) on L's lower triangle (mode 1:

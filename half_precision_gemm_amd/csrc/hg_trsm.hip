@@ -254,6 +254,7 @@ constexpr int LDS_R = LBM * LBK * 2;         // 16 KB
 constexpr int LDS_V = LBN * LBK * 2;         // 128 KB
 constexpr int R_PER_T = LBM * LKC / 256;     // 4
 constexpr int V_PER_T = LBN * LKC / 256;     // 32
+constexpr int XLD = LBN + 4;                 // padded fp32 row of a staged 32×256 result
 
 // 16-byte chunk kc of row `row` in a 32-chunk row: XOR-swizzled so that the
 // fragment reads of 32 consecutive rows at one kc hit distinct bank groups.
@@ -332,7 +333,119 @@ __global__ void __launch_bounds__(256, 1) trsm_leaf_kernel(const TrsmLeafParams 
     uint4 ra[R_PER_T];
     uint4 rv[V_PER_T];
     bool vok[V_PER_T];
-    if constexpr (VEC) {
+    if (VEC && p.sb > 0) {
+        // Fused update of the deepest recursion node above this leaf:
+        // S <- S − A21ᵀ·X2 for the leaf's rows, A21 = A[o+s : o+s+sb, o : o+s]
+        // and X2 the lower half's solved rows (fp16, from W).  Its operands
+        // are staged in LDS first (A21ᵀ in V's area, X2 in R's), the
+        // inverse's loads are issued before its products so that they are in
+        // flight meanwhile, and its 32×s result meets B and S in fp32 through
+        // LDS: S_new = S − U (or −U on rows no update has touched yet), the
+        // arithmetic of the separate beta = 1 GEMM, then R = fp16(alpha·B + S_new).
+        const int sb = p.sb;
+        const int k = lkc * 8;
+        const int64_t ob = o + s;                  // first row of the lower half
+        uint4 ru[V_PER_T];
+        uint4 rx[R_PER_T];
+        half8 bv[R_PER_T];
+        floatx4 sv[2 * R_PER_T];
+        bool rok[R_PER_T];
+        const int64_t bdummy = o + (int64_t)m0 * p.ldb;
+        const int64_t sdummy = o + (int64_t)m0 * p.ldo;
+        const int64_t wdummy = ob + (int64_t)m0 * p.ldw;
+        const int64_t adummy = ob + o * p.lda;
+#pragma unroll
+        for (int u = 0; u < R_PER_T; ++u) {
+            const int i = m0 + lrow + 8 * u;
+            rok[u] = i < M && k < s;
+            bv[u] = *reinterpret_cast<const half8 *>(p.B + (rok[u] ? (o + k) + (int64_t)i * p.ldb : bdummy));
+            const bool xok = i < M && k < sb;
+            const uint4 x = *reinterpret_cast<const uint4 *>(p.W + (xok ? (ob + k) + (int64_t)i * p.ldw : wdummy));
+            const uint32_t keep = xok ? 0xffffffffu : 0u;
+            rx[u] = make_uint4(x.x & keep, x.y & keep, x.z & keep, x.w & keep);
+        }
+        if (touched) {
+#pragma unroll
+            for (int u = 0; u < R_PER_T; ++u) {
+                const int i = m0 + lrow + 8 * u;
+                const float *sp = p.Out + (rok[u] ? (o + k) + (int64_t)i * p.ldo : sdummy);
+                sv[2 * u] = *reinterpret_cast<const floatx4 *>(sp);
+                sv[2 * u + 1] = *reinterpret_cast<const floatx4 *>(sp + 4);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < V_PER_T; ++u) {
+            const int j = vrow(u);
+            const bool aok = j < s && k < sb;
+            const uint4 a = *reinterpret_cast<const uint4 *>(p.A + (aok ? (ob + k) + (o + j) * p.lda : adummy));
+            const uint32_t keep = aok ? 0xffffffffu : 0u;
+            ru[u] = make_uint4(a.x & keep, a.y & keep, a.z & keep, a.w & keep);
+        }
+#pragma unroll
+        for (int u = 0; u < R_PER_T; ++u)
+            *reinterpret_cast<uint4 *>(Rs + lds_chunk(lrow + 8 * u, lkc) * 16) = rx[u];
+#pragma unroll
+        for (int u = 0; u < V_PER_T; ++u)
+            *reinterpret_cast<uint4 *>(Vs + lds_chunk(vrow(u), lkc) * 16) = ru[u];
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < V_PER_T; ++u) {
+            const int j = vrow(u);
+            vok[u] = j < s && k < s && v_chunk_used(j, lkc);
+            rv[u] = *reinterpret_cast<const uint4 *>(p.V + (vok[u] ? (int64_t)j * p.ldv + k : 0));
+        }
+        // U(i, j) = Σ_k' X2(i, k')·A21(k', j), the fragments of the leaf
+        // product below with A21ᵀ in place of the inverse (every chunk of
+        // both operands was written, zeros past sb and s).
+        {
+            const int frow = lane & 31;
+            const int fkc = lane >> 5;
+            const int jbs[2] = {wave, 7 - wave};
+            floatx16 uacc[2];
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+                uacc[b] = floatx16{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+            for (int st = 0; st < LBK / 16; ++st) {
+                const int kc = 2 * st + fkc;
+                const half8 af = *reinterpret_cast<const half8 *>(Rs + lds_chunk(frow, kc) * 16);
+#pragma unroll
+                for (int b = 0; b < 2; ++b) {
+                    const half8 bf = *reinterpret_cast<const half8 *>(Vs + lds_chunk(32 * jbs[b] + frow, kc) * 16);
+                    uacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf, af, uacc[b], 0, 0, 0);
+                }
+            }
+            __syncthreads();                       // every wave is past its reads of Rs, Vs
+            float *Us = reinterpret_cast<float *>(Vs);
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+                    *reinterpret_cast<floatx4 *>(Us + frow * XLD + 32 * jbs[b] + 8 * g + 4 * fkc) =
+                        floatx4{uacc[b][4 * g + 0], uacc[b][4 * g + 1], uacc[b][4 * g + 2], uacc[b][4 * g + 3]};
+            __syncthreads();
+#pragma unroll
+            for (int u = 0; u < R_PER_T; ++u) {
+                const float *ur = Us + (lrow + 8 * u) * XLD + k;
+                const floatx4 u0 = *reinterpret_cast<const floatx4 *>(ur);
+                const floatx4 u1 = *reinterpret_cast<const floatx4 *>(ur + 4);
+                half8 h;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float uv = e < 4 ? u0[e] : u1[e - 4];
+                    const float sn = touched ? __builtin_fmaf(-1.0f, uv, sv[2 * u + e / 4][e % 4]) : -uv;
+                    h[e] = rok[u] ? (_Float16)__builtin_fmaf(alpha, (float)bv[u][e], sn) : (_Float16)0.0f;
+                }
+                ra[u] = __builtin_bit_cast(uint4, h);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < V_PER_T; ++u) {
+            const uint32_t keep = vok[u] ? 0xffffffffu : 0u;
+            rv[u] = make_uint4(rv[u].x & keep, rv[u].y & keep, rv[u].z & keep, rv[u].w & keep);
+        }
+        __syncthreads();                           // U read by every thread before V overwrites it
+    } else if constexpr (VEC) {
         // Branch-free: every load is issued from a valid address (the real
         // chunk, or a chunk known to be in range) and masked afterwards, so
         // all of them are in flight together.  VEC implies s % 8 == 0: no
@@ -442,7 +555,6 @@ __global__ void __launch_bounds__(256, 1) trsm_leaf_kernel(const TrsmLeafParams 
     // lanes × 4 rows = the column's 1 KiB of fp32 and 512 B of fp16, whole
     // cache lines (scattered 16-byte pieces tripled the written bytes).
     float *Xs = reinterpret_cast<float *>(Vs);
-    constexpr int XLD = LBN + 4;                 // padded row of the staged tile
     __syncthreads();
     {
 #pragma unroll
@@ -501,6 +613,10 @@ hipError_t launch_trsm_leaf(const TrsmLeafParams &p, bool vec, hipStream_t strea
     if (p.m <= 0)
         return hipSuccess;
     if (p.s <= 0 || p.s > kTrsmLeafMax || p.s > p.ldv || p.ldv % 8 != 0)
+        return hipErrorInvalidValue;
+    if (p.sb < 0 || p.sb > kTrsmLeafMax ||
+        (p.sb > 0 && (!vec || p.A == nullptr || reinterpret_cast<uintptr_t>(p.A) % 16 != 0 ||
+                      p.lda % 8 != 0 || p.ldw % 8 != 0 || p.sb % 8 != 0)))
         return hipErrorInvalidValue;
     const unsigned grid = (unsigned)((p.m + LBM - 1) / LBM);
     if (vec)
