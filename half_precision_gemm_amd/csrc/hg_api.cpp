@@ -705,6 +705,34 @@ int hg_trmm(int uplo, int trans, int64_t n, int64_t m, float alpha, const void *
     if (overlap(ew, eo) || overlap(ew, ea) || overlap(ew, eb))
         return -14;
     _Float16 *L = static_cast<_Float16 *>(work);
+    // Upper/transposed (L = A) and lower/non-transposed (L = Aᵀ, upper) are,
+    // in the GEMM view, the lower-transposed product with the triangle on the
+    // other side: the one-launch schedule walks each tile's K from 0 to its
+    // diagonal block (tri_up), with no row reversal of B or Out.
+    if ((uplo == HG_UPPER && trans == HG_TRANS) || (uplo == HG_LOWER && trans == HG_NOTRANS)) {
+        const bool copy = uplo == HG_LOWER;
+        hg::GemmParams p{};
+        p.A = static_cast<const _Float16 *>(B);
+        p.B = copy ? L : static_cast<const _Float16 *>(A);
+        p.C = Out;
+        p.lda = ldb;
+        p.ldb = copy ? v.ldl : lda;
+        p.ldc = ldo;
+        p.M = (int32_t)m;
+        p.alpha = alpha;
+        p.leaf = (int32_t)std::min<int64_t>(leaf <= 0 ? 256 : leaf, kI32Max);
+        p.tri_up = 1;
+        p.nbatch = 1;
+        p.e[0] = {0, 0, 0, (int32_t)n, (int32_t)n};
+        if (hg::trmm_fused_ok(p)) {
+            if (copy) {
+                const int st = hip_status(hg::launch_tri_xform(4, static_cast<const _Float16 *>(A), lda, L, v.ldl, n, s));
+                if (st != HG_OK)
+                    return st;
+            }
+            return hip_status(hg::launch_trmm_fused(p, s));
+        }
+    }
     int st = hip_status(hg::launch_tri_xform(v.mode, static_cast<const _Float16 *>(A), lda, L, v.ldl, n, s));
     if (st != HG_OK)
         return st;

@@ -304,7 +304,8 @@ __device__ __forceinline__ bool find_tile(const GemmParams &p, int &id, int stri
 // Work item of workgroup w in round r: output tile q = r·G + w (r even) or
 // r·G + G-1-w (r odd) of the tiles ordered by column, so that the columns
 // with the most K work run first and the rounds of every workgroup add up
-// to about the same work (a tile's work falls linearly with its column).
+// to about the same work (a tile's work falls linearly with its column;
+// with tri_up it rises, and the columns are taken from the last).
 // False once q is past the end.
 __device__ __forceinline__ bool fused_item(const GemmParams &p, int w, int G, int round, int total,
                                            int tiles_m, TileInfo &T)
@@ -312,7 +313,8 @@ __device__ __forceinline__ bool fused_item(const GemmParams &p, int w, int G, in
     const int q = round * G + ((round & 1) ? G - 1 - w : w);
     if (q >= total)
         return false;
-    const int tm = q % tiles_m, tn = q / tiles_m;
+    const int tm = q % tiles_m;
+    const int tn = p.tri_up ? (total / tiles_m) - 1 - q / tiles_m : q / tiles_m;
     const int N = p.e[0].N, K = p.e[0].K;
     const int m0 = tm * BM, n0 = tn * BN;
     T.batch = 0;
@@ -322,8 +324,8 @@ __device__ __forceinline__ bool fused_item(const GemmParams &p, int w, int G, in
     T.K = K;
     T.rows_a = min(p.M - m0, BM);
     T.rows_b = min(N - n0, BN);
-    T.kt0 = n0 / BK;
-    T.nk = (K - n0) / BK;
+    T.kt0 = p.tri_up ? 0 : n0 / BK;
+    T.nk = p.tri_up ? (n0 + BN) / BK : (K - n0) / BK;
     const _Float16 *Ab = p.A + (int64_t)m0 * p.lda;
     const _Float16 *Bb = p.B + (int64_t)n0 * p.ldb;
     T.ra = make_rsrc(Ab, (uint32_t)(((int64_t)(T.rows_a - 1) * p.lda + K) * 2));
@@ -422,11 +424,12 @@ hgemm_fast_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int c
     // A fragments: one set per quarter parity (TMQ blocks each); B
     // fragments: one set per k-step of the stage (all TN blocks).
     half8 fa[2][TMQ], fb[SPS][TN];
-    // TRI: zero the B fragment elements (j, k) with k < j.  Block j of k-step
-    // s holds row jrow = n0 + wn·WTN + 16j + (lane mod 16) and the 8 k from
-    // kfirst = (kt0+kt)·BK + 32s + 8·(lane div 16); the first
-    // clamp(jrow - kfirst, 0, 8) of them are zeroed by a select (so NaN or
-    // Inf stored above the diagonal cannot reach the MFMA).
+    // TRI: zero the B fragment elements (j, k) with k < j (tri_up: k > j).
+    // Block j of k-step s holds row jrow = n0 + wn·WTN + 16j + (lane mod 16)
+    // and the 8 k from kfirst = (kt0+kt)·BK + 32s + 8·(lane div 16); element
+    // e is zeroed when e < jrow - kfirst (tri_up: e > jrow - kfirst) by a
+    // mask (so NaN or Inf stored in the other triangle cannot reach the
+    // MFMA).
     auto mask_tri = [&](const TileInfo &T, int kt, int s) {
         const int frow = lane & 15;
         const int fhi = lane >> 4;
@@ -435,10 +438,18 @@ hgemm_fast_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int c
         for (int j = 0; j < TN; ++j) {
             const int t = T.n0 + wn * WTN + j * FB + frow - kfirst;   // elements to zero
             u32x4 w = __builtin_bit_cast(u32x4, fb[s][j]);
+            if (p.tri_up) {
 #pragma unroll
-            for (int d = 0; d < 4; ++d) {
-                const uint32_t m = (2 * d >= t ? 0x0000ffffu : 0u) | (2 * d + 1 >= t ? 0xffff0000u : 0u);
-                w[d] &= m;
+                for (int d = 0; d < 4; ++d) {
+                    const uint32_t m = (2 * d <= t ? 0x0000ffffu : 0u) | (2 * d + 1 <= t ? 0xffff0000u : 0u);
+                    w[d] &= m;
+                }
+            } else {
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    const uint32_t m = (2 * d >= t ? 0x0000ffffu : 0u) | (2 * d + 1 >= t ? 0xffff0000u : 0u);
+                    w[d] &= m;
+                }
             }
             fb[s][j] = __builtin_bit_cast(half8, w);
         }
@@ -506,10 +517,11 @@ hgemm_fast_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int c
             static_for<NQ>([&](auto qc) __attribute__((always_inline)) {
                 constexpr int q = decltype(qc)::value;
                 constexpr int s = q >> 1, h = q & 1;
-                // Only the first BN/BK stages hold elements with k below
-                // the tile's columns.
+                // Only the BN/BK stages of the tile's diagonal block hold
+                // elements on the wrong side of its columns: the first ones
+                // of the walk, or (tri_up) the last.
                 if constexpr (TRI && h == 0) {
-                    if (kt < BN / BK)
+                    if (p.tri_up ? kt >= T.nk - BN / BK : kt < BN / BK)
                         mask_tri(T, kt, s);
                 }
                 // Ring loads of this quarter: operand, stage, slot, first index.

@@ -31,6 +31,9 @@ struct GemmParams {
     int32_t nbatch;
     float alpha, beta;
     int32_t leaf;    // recursive TRMM in one launch: the recursion's leaf size
+    int32_t tri_up;  // recursive TRMM in one launch: B element (j, k) counts for
+                     // k <= j (an upper-triangular operand in the GEMM view)
+                     // instead of k >= j
     const float *bias;   // fused epilogue: per-column bias (nullptr: none)
     int32_t act;         // fused epilogue: 0 identity, 1 ReLU
     BatchEntry e[kMaxBatch];
@@ -78,6 +81,9 @@ hipError_t launch_gemm_ring(const GemmParams &p, const LaunchOpts &o, hipStream_
 // 0, n, n}, p.leaf): every output tile walks its leaf and then the recursion's
 // updates that touch it, deepest first, in one persistent workgroup, the
 // updates accumulated in registers (one store per tile).
+// With p.tri_up the GEMM view's B element (j, k) counts for k <= j: a tile
+// walks K from 0 to its own diagonal block (the outermost update first, the
+// leaf last).
 // trmm_fused_ok: the operands suit the fast path, every recursion boundary
 // falls on a 256-column tile edge, and there are at least two output tiles
 // per CU.
@@ -135,7 +141,8 @@ hipError_t launch_trsm_inv(const TrsmInvParams &p, hipStream_t stream);
 hipError_t launch_trsm_leaf(const TrsmLeafParams &p, bool vec, hipStream_t stream);
 
 // TRMM variants (hg_xform.hip): L = map(A) on L's lower triangle (mode 1:
-// A(c, r), 2: A(n-1-r, n-1-c), 3: A(n-1-c, n-1-r)); B's rows reversed into
+// A(c, r), 2: A(n-1-r, n-1-c), 3: A(n-1-c, n-1-r)), or mode 4: A(c, r) on
+// L's upper triangle; B's rows reversed into
 // Bp; Out's rows reversed in place.
 hipError_t launch_tri_xform(int mode, const _Float16 *A, int64_t lda, _Float16 *L, int64_t ldl,
                             int64_t n, hipStream_t stream);

@@ -23,6 +23,7 @@ constexpr int XT = 64;   // tile edge
 //   MODE 1: A(c, r)            transpose
 //   MODE 2: A(n-1-r, n-1-c)    reverse both indices
 //   MODE 3: A(n-1-c, n-1-r)    transpose and reverse
+//   MODE 4: A(c, r) on the r <= c tiles instead (L upper triangular)
 // One workgroup per 64×64 tile of L's lower triangle; the transposing modes
 // stage the tile in LDS so that reads and writes both run along columns.
 template <int MODE>
@@ -38,7 +39,7 @@ __global__ void __launch_bounds__(256) tri_xform_kernel(const _Float16 *__restri
     while (tr * (tr + 1) / 2 > b)
         --tr;
     const int tc = b - tr * (tr + 1) / 2;
-    const int r0 = tr * XT, c0 = tc * XT;
+    const int r0 = (MODE == 4 ? tc : tr) * XT, c0 = (MODE == 4 ? tr : tc) * XT;
     const int t = threadIdx.x;
     const int i = t % XT, g = t / XT;   // i: position along a column, g: column group
     if constexpr (MODE == 2) {
@@ -55,8 +56,8 @@ __global__ void __launch_bounds__(256) tri_xform_kernel(const _Float16 *__restri
             const int cl = c0 + i;            // L column ...
             const int rl = r0 + g + 4 * q;    // ... and row of this element
             if (cl < n && rl < n) {
-                const int64_t src = MODE == 1 ? cl + (int64_t)rl * lda
-                                              : (n - 1 - cl) + (int64_t)(n - 1 - rl) * lda;
+                const int64_t src = MODE == 1 || MODE == 4 ? cl + (int64_t)rl * lda
+                                                           : (n - 1 - cl) + (int64_t)(n - 1 - rl) * lda;
                 tile[i][g + 4 * q] = A[src];
             }
         }
@@ -222,6 +223,9 @@ hipError_t launch_tri_xform(int mode, const _Float16 *A, int64_t lda, _Float16 *
         break;
     case 3:
         hipLaunchKernelGGL(tri_xform_kernel<3>, dim3((unsigned)tiles), dim3(256), 0, stream, A, lda, L, ldl, (int)n);
+        break;
+    case 4:
+        hipLaunchKernelGGL(tri_xform_kernel<4>, dim3((unsigned)tiles), dim3(256), 0, stream, A, lda, L, ldl, (int)n);
         break;
     default:
         return hipErrorInvalidValue;

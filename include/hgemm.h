@@ -230,12 +230,16 @@ int trmm_lower_trans(int64_t n, int64_t m, float alpha,
  *                  small: -15).
  * 16 stream      : hipStream_t to launch on.
  *
- * The other three variants run the same recursion on a lower triangular L
- * that one copy kernel builds in the workspace (P reverses the row order):
- * upper/notrans: L = Aᵀ; upper/trans: P·Out = (P·A·P)ᵀ·(P·B);
- * lower/notrans: P·Out = (P·Aᵀ·P)ᵀ·(P·B); for the last two B's rows are
- * reversed into the workspace and Out's rows are reversed in place at the
- * end.  The arithmetic is trmm_lower_trans's on L.
+ * upper/notrans runs the same recursion on L = Aᵀ, which one copy kernel
+ * builds in the workspace.  upper/trans and lower/notrans, when the
+ * one-launch schedule applies (see trmm_lower_trans), run it with the
+ * triangle on the other side of the GEMM view: each output tile walks K from
+ * 0 up to its diagonal block (the recursion's outermost update first, the
+ * leaf last), on A itself (upper/trans) or on an upper triangular copy of Aᵀ
+ * (lower/notrans).  Otherwise they run on a lower triangular L with the row
+ * order reversed by P: upper/trans: P·Out = (P·A·P)ᵀ·(P·B); lower/notrans:
+ * P·Out = (P·Aᵀ·P)ᵀ·(P·B), B's rows reversed into the workspace and Out's
+ * rows reversed in place at the end.
  */
 int hg_trmm(int uplo, int trans, int64_t n, int64_t m, float alpha,
             const void *A, int64_t lda,

@@ -96,3 +96,45 @@ def test_8192_sampled(hg, uplo, trans):
     ref = oracle.trmm_sampled(A_cm, B_cm, ri, cj, 1.0, oracle.LOWER if uplo == "L" else oracle.UPPER,
                               oracle.TRANS if trans else oracle.NOTRANS)
     check_close(got[cj, ri], ref, n, f"{uplo}N 8192 sampled")
+
+
+# ---- The one-launch schedule of all four variants (at least two 256×256
+# output tiles per CU: m·n >= 2^25).  Upper/transposed and lower/non-transposed
+# walk each tile's K from 0 up to its diagonal block (the triangle on the other
+# side of the GEMM view); the other two walk down from it.
+ONE_LAUNCH = [(4096, 8192, 256), (2048, 16384, 256), (4096, 8192, 512)]
+
+
+@pytest.mark.parametrize("uplo,trans", VARIANTS)
+@pytest.mark.parametrize("n,m,leaf", ONE_LAUNCH)
+def test_one_launch_sampled(hg, uplo, trans, n, m, leaf):
+    A_cm, B_cm = _inputs(n, m, n + m + leaf, uplo)
+    got = run(hg, A_cm, B_cm, 0.5, uplo, trans, leaf)
+    assert np.isfinite(got).all()
+    ri, cj = workloads.sample_indices(n + leaf, n, m)
+    ref = oracle.trmm_sampled(A_cm, B_cm, ri, cj, 0.5, oracle.LOWER if uplo == "L" else oracle.UPPER,
+                              oracle.TRANS if trans else oracle.NOTRANS)
+    check_close(got[cj, ri], ref, n, f"{uplo}{'T' if trans else 'N'} one launch n={n} m={m} leaf={leaf}")
+
+
+@pytest.mark.parametrize("uplo,trans", VARIANTS)
+def test_one_launch_integer_bit_exact(hg, uplo, trans):
+    rng = np.random.default_rng(41)
+    n, m = 2048, 16384
+    T = (np.tril if uplo == "L" else np.triu)(workloads.integer_f16(rng, (n, n)))
+    B = workloads.integer_f16(rng, (n, m))
+    A_cm, B_cm = np.ascontiguousarray(T.T), np.ascontiguousarray(B.T)
+    got = run(hg, A_cm, B_cm, 1.0, uplo, trans)
+    ri, cj = workloads.sample_indices(43, n, m, 4096)
+    exact = oracle.trmm_sampled(A_cm, B_cm, ri, cj, 1.0, oracle.LOWER if uplo == "L" else oracle.UPPER,
+                                oracle.TRANS if trans else oracle.NOTRANS)
+    assert np.array_equal(got[cj, ri].astype(np.float64), exact)
+
+
+@pytest.mark.parametrize("uplo,trans", VARIANTS)
+def test_one_launch_other_triangle_never_read(hg, uplo, trans):
+    n, m = 4096, 8192
+    A0, B_cm = _inputs(n, m, 6, uplo)
+    Ax, _ = _inputs(n, m, 6, uplo, np.nan)
+    assert np.array_equal(run(hg, A0, B_cm, 1.0, uplo, trans).view(np.uint32),
+                          run(hg, Ax, B_cm, 1.0, uplo, trans).view(np.uint32))
