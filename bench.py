@@ -283,6 +283,28 @@ def config_sweep(hg, stream, main_gemm_ms=None, main_trmm_ms=None, only=None):
             "note": "Out = A*B, A lower (the TRMM page's usage call): transpose-and-reverse copy of A, "
                     "B and Out row-reversed around the lower-transposed recursion"}
         del Ad, Bd, Od, TA, TB, work
+    if want("hgemm_splitk_512x512x65536"):
+        # Split-K (next row): a 512×512 C has 16 tiles of 128×128 for 256 CUs
+        # while K = 65536 is long; hgemm_splitk (slices chosen from the shape)
+        # against the plain call.
+        print("[bench] config hgemm_splitk_512x512x65536 ...", file=sys.stderr, flush=True)
+        M = N = 512
+        K = 65536
+        rng = np.random.default_rng(8)
+        Ad = torch.from_numpy(workloads.uniform_f16(rng, (M, K))).to(dev)
+        Btd = torch.from_numpy(workloads.uniform_f16(rng, (N, K))).to(dev)
+        Cd = torch.empty((M, N), dtype=torch.float32, device=dev)
+        work = torch.empty(hg.splitk_workspace_size(M, N, K, 0), dtype=torch.uint8, device=dev)
+        plain = _time_calls(lambda: hg.hgemm(Ad, Btd, Cd), 5, 20, stream)
+        split = _time_calls(lambda: hg.hgemm_splitk(Ad, Btd, Cd, 1.0, 0.0, 0, work), 5, 20, stream)
+        flops = 2.0 * M * N * K
+        res["hgemm_splitk_512x512x65536"] = {
+            "gpu_ms_median": round(split[0], 5), "gpu_ms_min": round(split[1], 5),
+            "tflops": round(flops / (split[0] * 1e-3) / 1e12, 2),
+            "plain_hgemm_ms_median": round(plain[0], 5),
+            "plain_hgemm_tflops": round(flops / (plain[0] * 1e-3) / 1e12, 2),
+            "note": "fp32 C; K cut into slices run side by side, partials summed in order in fp32"}
+        del Ad, Btd, Cd, work
     if want("trmm_8192_inplace"):
         # In-place form B <- A*B (fp16 B overwritten), lower and not transposed.
         # B is restored from a copy before each timed call, outside the events.

@@ -88,6 +88,11 @@ lib.hg_trmm.argtypes = [_int, _int, _i64, _i64, _f32, _vp, _i64, _vp, _i64, _vp,
 lib.hg_trmm.restype = _int
 lib.hg_trmm_workspace_size.argtypes = [_int, _int, _i64, _i64]
 lib.hg_trmm_workspace_size.restype = _i64
+lib.hgemm_splitk.argtypes = [_i64, _i64, _i64, _f32, _vp, _i64, _vp, _i64, _f32, _vp, _i64, _int, _int, _vp,
+                             _i64, _vp]
+lib.hgemm_splitk.restype = _int
+lib.hg_hgemm_splitk_workspace_size.argtypes = [_i64, _i64, _i64, _int]
+lib.hg_hgemm_splitk_workspace_size.restype = _i64
 lib.hg_trmm_inplace.argtypes = [_int, _int, _i64, _i64, _f32, _vp, _i64, _vp, _i64, _i64, _vp, _i64,
                                 _vp]
 lib.hg_trmm_inplace.restype = _int
@@ -108,7 +113,8 @@ lib.hg_trmm_plan.restype = _i64
 EXPORTS = ("hgemm", "hgemm_bias_act", "hgemm_bf16", "trmm_lower_trans", "hg_trmm_lower_trans_by_level",
            "hg_strerror", "hg_trmm_plan", "trsm_lower_trans", "hg_trsm_workspace_size", "hg_trmm",
            "hg_trmm_workspace_size", "hgemm_layout", "hg_hgemm_layout_workspace_size",
-           "hg_trmm_inplace", "hg_trmm_inplace_workspace_size")
+           "hg_trmm_inplace", "hg_trmm_inplace_workspace_size", "hgemm_splitk",
+           "hg_hgemm_splitk_workspace_size")
 
 ROW_MAJOR = 0
 COL_MAJOR = 1
@@ -169,6 +175,42 @@ def hgemm(A, Bt, C, alpha: float = 1.0, beta: float = 0.0):
     if st != 0:
         raise HgError("hgemm", st)
     return C
+
+
+def hgemm_splitk(A, Bt, C, alpha: float = 1.0, beta: float = 0.0, splits: int = 0, work=None):
+    """hgemm with K split into `splits` slices (0: chosen from the shape and
+    the device) summed in order in fp32; `work`: device uint8 tensor of at
+    least splitk_workspace_size(M, N, K, splits) bytes (allocated with torch
+    when None).  Returns C."""
+    import torch
+    _check_matrix(A, "A", (torch.float16,))
+    _check_matrix(Bt, "Bt", (torch.float16,))
+    _check_matrix(C, "C", (torch.float16, torch.float32))
+    M, K = A.shape
+    N = Bt.shape[0]
+    if Bt.shape[1] != K or tuple(C.shape) != (M, N):
+        raise ValueError(f"shape mismatch: A {tuple(A.shape)}, Bt {tuple(Bt.shape)}, "
+                         f"C {tuple(C.shape)}")
+    need = lib.hg_hgemm_splitk_workspace_size(M, N, K, int(splits))
+    if need < 0:
+        raise HgError("hg_hgemm_splitk_workspace_size", int(need))
+    if work is None:
+        work = torch.empty(max(need, 1), dtype=torch.uint8, device=C.device)
+    out_dtype = HG_F16 if C.dtype == torch.float16 else HG_F32
+    st = lib.hgemm_splitk(M, N, K, float(alpha), A.data_ptr() or None, _ld(A), Bt.data_ptr() or None,
+                          _ld(Bt), float(beta), C.data_ptr() or None, _ld(C), out_dtype, int(splits),
+                          work.data_ptr(), work.numel() * work.element_size(), _stream_handle(C))
+    if st != 0:
+        raise HgError("hgemm_splitk", st)
+    return C
+
+
+def splitk_workspace_size(M: int, N: int, K: int, splits: int = 0) -> int:
+    """Bytes of workspace hgemm_splitk needs on the current device."""
+    need = lib.hg_hgemm_splitk_workspace_size(M, N, K, int(splits))
+    if need < 0:
+        raise HgError("hg_hgemm_splitk_workspace_size", int(need))
+    return int(need)
 
 
 def hgemm_layout(A, B, C, a_col_major: bool = False, b_row_major: bool = False,

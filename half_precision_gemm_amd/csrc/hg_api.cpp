@@ -930,3 +930,135 @@ int hg_trmm_inplace(int uplo, int trans, int64_t n, int64_t m, float alpha, cons
 }
 
 }  // extern "C"
+
+namespace {
+
+// ---- Split-K: K cut into S slices of Ks (a multiple of 64) columns; the
+// slices run as one batched GEMM into fp32 partials (alpha = 1, beta = 0),
+// then one reduction kernel sums them in slice order and applies alpha,
+// beta and the output conversion.
+struct SplitK {
+    int64_t S = 1, Ks = 0, bytes = 0;
+};
+
+int device_cus()
+{
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+        return 256;
+    return n;
+}
+
+// splits > 0: that many slices (at most 32, each at least 64 columns of K);
+// 0: enough slices to give every CU a 128×128 tile, each slice at least 256
+// columns of K.
+SplitK splitk_plan(int64_t M, int64_t N, int64_t K, int splits)
+{
+    SplitK p;
+    int64_t want = splits;
+    if (splits == 0) {
+        const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
+        want = std::max<int64_t>(1, device_cus() / std::max<int64_t>(tiles, 1));
+        want = std::min<int64_t>(want, std::max<int64_t>(1, K / 256));
+    }
+    want = std::max<int64_t>(1, std::min<int64_t>({want, 32, std::max<int64_t>(1, K / 64)}));
+    p.Ks = round_up((K + want - 1) / want, 64);
+    p.S = std::max<int64_t>(1, (K + p.Ks - 1) / p.Ks);
+    p.bytes = round_up(p.S * M * N * 4, 256);
+    return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t hg_hgemm_splitk_workspace_size(int64_t M, int64_t N, int64_t K, int splits)
+{
+    if (M < 0 || M > kI32Max)
+        return -1;
+    if (N < 0 || N > kI32Max)
+        return -2;
+    if (K < 0 || K > kI32Max)
+        return -3;
+    if (splits < 0 || splits > 32)
+        return -4;
+    if (M == 0 || N == 0 || K == 0)
+        return 0;
+    return splitk_plan(M, N, K, splits).bytes;
+}
+
+int hgemm_splitk(int64_t M, int64_t N, int64_t K, float alpha, const void *A, int64_t lda, const void *B,
+                 int64_t ldb, float beta, void *C, int64_t ldc, int out_dtype, int splits, void *work,
+                 int64_t work_bytes, void *stream)
+{
+    if (M < 0 || M > kI32Max)
+        return -1;
+    if (N < 0 || N > kI32Max)
+        return -2;
+    if (K < 0 || K > kI32Max)
+        return -3;
+    if (lda < std::max<int64_t>(1, K))
+        return -6;
+    if (ldb < std::max<int64_t>(1, K))
+        return -8;
+    if (ldc < std::max<int64_t>(1, N))
+        return -11;
+    if (out_dtype != HG_F16 && out_dtype != HG_F32)
+        return -12;
+    if (splits < 0 || splits > 32)
+        return -13;
+    if (M == 0 || N == 0)
+        return HG_OK;
+    if (C == nullptr)
+        return -10;
+    const bool out_f16 = out_dtype == HG_F16;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const Extent ec = extent(C, M, ldc, N, out_f16 ? 2 : 4);
+    if (alpha == 0.0f || K == 0)
+        return hip_status(hg::launch_scale(C, ldc, M, N, beta, out_f16, s));
+    if (A == nullptr)
+        return -5;
+    if (B == nullptr)
+        return -7;
+    const Extent ea = extent(A, M, lda, K, 2), eb = extent(B, N, ldb, K, 2);
+    if (overlap(ec, ea) || overlap(ec, eb))
+        return -10;
+    const SplitK plan = splitk_plan(M, N, K, splits);
+    if (work == nullptr || !aligned16(work))
+        return -14;
+    if (work_bytes < plan.bytes)
+        return -15;
+    const Extent ew = {reinterpret_cast<uintptr_t>(work), reinterpret_cast<uintptr_t>(work) + (uintptr_t)plan.bytes};
+    if (overlap(ew, ec) || overlap(ew, ea) || overlap(ew, eb))
+        return -14;
+    float *P = static_cast<float *>(work);
+    hg::GemmParams p{};
+    p.A = static_cast<const _Float16 *>(A);
+    p.B = static_cast<const _Float16 *>(B);
+    p.C = P;
+    p.lda = lda;
+    p.ldb = ldb;
+    p.ldc = N;
+    p.M = (int32_t)M;
+    p.alpha = 1.0f;
+    p.beta = 0.0f;
+    p.nbatch = (int32_t)plan.S;
+    bool vec = aligned16(A) && aligned16(B) && lda % 8 == 0 && ldb % 8 == 0;
+    for (int64_t q = 0; q < plan.S; ++q) {
+        const int64_t k0 = q * plan.Ks;
+        p.e[q] = {k0, k0, q * M * N, (int32_t)N, (int32_t)std::min(plan.Ks, K - k0)};
+    }
+    hg::LaunchOpts o{};
+    o.out_f16 = false;
+    o.beta_read = false;
+    o.tri = false;
+    o.vec = vec;
+    o.tile = choose_batched_tile(M, N, plan.S);
+    int st = hip_status(hg::launch_gemm(p, o, s));
+    if (st != HG_OK)
+        return st;
+    return hip_status(hg::launch_splitk_reduce(P, M * N, (int)plan.S, M, N, alpha, beta, C, ldc, out_f16, s));
+}
+
+}  // extern "C"

@@ -149,6 +149,10 @@ hipError_t launch_tri_xform(int mode, const _Float16 *A, int64_t lda, _Float16 *
 hipError_t launch_row_reverse_copy(const _Float16 *B, int64_t ldb, _Float16 *Bp, int64_t ldp, int64_t n,
                                    int64_t m, hipStream_t stream);
 hipError_t launch_row_reverse_inplace(float *Out, int64_t ldo, int64_t n, int64_t m, hipStream_t stream);
+// Split-K: C = alpha·Σ_s P_s + beta·C over S fp32 partials (M×N row-major,
+// ld N, `slice` elements apart), in slice order.
+hipError_t launch_splitk_reduce(const float *P, int64_t slice, int S, int64_t M, int64_t N, float alpha,
+                                float beta, void *C, int64_t ldc, bool out_f16, hipStream_t stream);
 // B = fp16(X) (nearest even), column-major n×m.
 hipError_t launch_f32_to_f16(const float *X, int64_t ldx, _Float16 *B, int64_t ldb, int64_t n, int64_t m,
                              hipStream_t stream);

@@ -13,6 +13,8 @@
 // These are memory-bound copies (the TRMM itself is the compute).
 #include "hg_internal.h"
 
+#include <type_traits>
+
 namespace hg {
 namespace {
 
@@ -197,6 +199,54 @@ __global__ void __launch_bounds__(256) f32_to_f16_kernel(const float *__restrict
     }
 }
 
+// C = alpha·Σ_s P_s + beta·C over S fp32 partial products P_s (row-major
+// M×N, ld N, slice elements apart), summed in slice order; the epilogue is the
+// GEMM kernels' (fma(alpha, sum, beta·c), or alpha·sum without beta), with
+// BETA a compile-time choice as there, so that the same instructions round
+// the result (a 16-bit C with beta: one v_fma_mixlo_f16, a single rounding).
+// VEC: 4 columns per thread (N % 4 == 0, 16-byte aligned P, C aligned to its
+// 4-element vector, ldc % 4 == 0).  blockIdx.y strides over the rows.
+template <bool OUT_F16, bool VEC, bool BETA>
+__global__ void __launch_bounds__(256) splitk_reduce_kernel(const float *__restrict__ P, int64_t slice, int S,
+                                                            int64_t M, int64_t N, float alpha, float beta,
+                                                            void *__restrict__ C, int64_t ldc)
+{
+    typedef typename std::conditional<OUT_F16, _Float16, float>::type celt;
+    const int64_t ncg = VEC ? N / 4 : N;
+    const int64_t cg = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (cg >= ncg)
+        return;
+    constexpr int W = VEC ? 4 : 1;
+    for (int64_t i = blockIdx.y; i < M; i += gridDim.y) {
+        const int64_t j = cg * W;
+        float acc[W];
+#pragma unroll
+        for (int e = 0; e < W; ++e)
+            acc[e] = P[i * N + j + e];
+        for (int s = 1; s < S; ++s) {
+            if constexpr (VEC) {
+                const float4 v = *reinterpret_cast<const float4 *>(P + s * slice + i * N + j);
+                acc[0] += v.x;
+                acc[1] += v.y;
+                acc[2] += v.z;
+                acc[3] += v.w;
+            } else {
+                acc[0] += P[s * slice + i * N + j];
+            }
+        }
+        celt *cp = static_cast<celt *>(C) + i * ldc + j;
+        celt out[W];
+#pragma unroll
+        for (int e = 0; e < W; ++e) {
+            const float t = BETA ? __builtin_fmaf(alpha, acc[e], beta * (float)cp[e]) : alpha * acc[e];
+            out[e] = (celt)t;
+        }
+#pragma unroll
+        for (int e = 0; e < W; ++e)
+            cp[e] = out[e];
+    }
+}
+
 unsigned grid_for(int64_t total)
 {
     int64_t blocks = (total + 255) / 256;
@@ -272,6 +322,34 @@ hipError_t launch_f32_to_f16(const float *X, int64_t ldx, _Float16 *B, int64_t l
         hipLaunchKernelGGL(f32_to_f16_kernel<true>, grid, dim3(256), 0, stream, X, ldx, B, ldb, n, m);
     else
         hipLaunchKernelGGL(f32_to_f16_kernel<false>, grid, dim3(256), 0, stream, X, ldx, B, ldb, n, m);
+    return hipGetLastError();
+}
+
+hipError_t launch_splitk_reduce(const float *P, int64_t slice, int S, int64_t M, int64_t N, float alpha,
+                                float beta, void *C, int64_t ldc, bool out_f16, hipStream_t stream)
+{
+    if (M <= 0 || N <= 0 || S <= 0)
+        return hipSuccess;
+    const uintptr_t calign = out_f16 ? 8 : 16;
+    const bool vec = N % 4 == 0 && reinterpret_cast<uintptr_t>(P) % 16 == 0 && slice % 4 == 0 &&
+                     reinterpret_cast<uintptr_t>(C) % calign == 0 && ldc % 4 == 0;
+    const int64_t ncg = vec ? N / 4 : N;
+    const dim3 grid((unsigned)((ncg + 255) / 256), (unsigned)(M < 65535 ? M : 65535));
+    const int sel = (out_f16 ? 4 : 0) | (vec ? 2 : 0) | (beta != 0.0f ? 1 : 0);
+#define HG_REDUCE(F, V, B)                                                                                     \
+    hipLaunchKernelGGL((splitk_reduce_kernel<F, V, B>), grid, dim3(256), 0, stream, P, slice, S, M, N, alpha, \
+                       beta, C, ldc)
+    switch (sel) {
+    case 0: HG_REDUCE(false, false, false); break;
+    case 1: HG_REDUCE(false, false, true); break;
+    case 2: HG_REDUCE(false, true, false); break;
+    case 3: HG_REDUCE(false, true, true); break;
+    case 4: HG_REDUCE(true, false, false); break;
+    case 5: HG_REDUCE(true, false, true); break;
+    case 6: HG_REDUCE(true, true, false); break;
+    default: HG_REDUCE(true, true, true); break;
+    }
+#undef HG_REDUCE
     return hipGetLastError();
 }
 

@@ -247,6 +247,40 @@ int hg_trmm(int uplo, int trans, int64_t n, int64_t m, float alpha,
             void *Out, int64_t ldo, int out_dtype,
             int64_t leaf, void *work, int64_t work_bytes, void *stream);
 
+/*
+ * hgemm_splitk — hgemm with K cut into slices that run side by side, for
+ * problems whose C has too few tiles to fill the GPU while K is long (the
+ * tiled product of "GPU架构与CUDA" 共享内存与分块, its K loop partitioned).
+ *
+ *  1..12          : as hgemm (fp16 A row-major, B column-major; out_dtype
+ *                   HG_F16 or HG_F32).
+ * 13 splits       : number of K slices, 1..32 (each at least 64 columns of K,
+ *                   fewer if K is short); 0 picks enough slices to give every
+ *                   compute unit a 128×128 tile, each slice at least 256
+ *                   columns long.  Outside 0..32: -13.
+ * 14 work         : device workspace, 16-byte aligned, of at least
+ * 15 work_bytes     hg_hgemm_splitk_workspace_size(M, N, K, splits) bytes
+ *                   (the fp32 partial products); must not overlap A, B or C
+ *                   (-14; too small: -15).
+ * 16 stream       : hipStream_t.
+ *
+ * Each slice's product is accumulated in fp32 as in hgemm and stored in fp32;
+ * the slices are then summed in order in fp32 and C = fma(alpha, sum,
+ * beta·C) (alpha·sum when beta = 0) is rounded to out_dtype once.  The
+ * result depends only on the arguments (no atomics).  With one slice it is
+ * hgemm's, bit for bit.
+ */
+int hgemm_splitk(int64_t M, int64_t N, int64_t K, float alpha,
+                 const void *A, int64_t lda, const void *B, int64_t ldb,
+                 float beta, void *C, int64_t ldc, int out_dtype, int splits,
+                 void *work, int64_t work_bytes, void *stream);
+
+/* hg_hgemm_splitk_workspace_size — bytes hgemm_splitk needs for (M, N, K,
+ * splits) on the current device (host only; splits = 0 depends on the
+ * device's compute-unit count); -1/-2/-3 for M/N/K out of range, -4 for
+ * splits outside 0..32. */
+int64_t hg_hgemm_splitk_workspace_size(int64_t M, int64_t N, int64_t K, int splits);
+
 /* hg_trmm_workspace_size — bytes of workspace hg_trmm needs (host only);
  * -1/-2 for a bad uplo/trans, -3/-4 for n/m < 0. */
 int64_t hg_trmm_workspace_size(int uplo, int trans, int64_t n, int64_t m);

@@ -29,11 +29,12 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["hg_hgemm_layout_workspace_size", "hg_strerror", "hg_trmm",
+    assert declared_functions() == ["hg_hgemm_layout_workspace_size", "hg_hgemm_splitk_workspace_size",
+                                    "hg_strerror", "hg_trmm",
                                     "hg_trmm_inplace", "hg_trmm_inplace_workspace_size",
                                     "hg_trmm_lower_trans_by_level", "hg_trmm_plan",
                                     "hg_trmm_workspace_size", "hg_trsm_workspace_size", "hgemm",
-                                    "hgemm_bf16", "hgemm_bias_act", "hgemm_layout",
+                                    "hgemm_bf16", "hgemm_bias_act", "hgemm_layout", "hgemm_splitk",
                                     "trmm_lower_trans", "trsm_lower_trans"]
 
 
@@ -362,3 +363,26 @@ def test_one_hip_runtime_in_the_process():
                        timeout=300)
     assert r.returncode == 0, r.stderr[-2000:]
     assert r.stdout.strip().splitlines()[-1] == "1"
+
+
+def test_hgemm_splitk_workspace_and_arguments(lib):
+    up = lambda x: -(-x // 256) * 256
+    # explicit splits: Ks = ceil(K / s) rounded up to 64, S = ceil(K / Ks)
+    assert lib.hg_hgemm_splitk_workspace_size(512, 512, 65536, 8) == up(8 * 512 * 512 * 4)
+    assert lib.hg_hgemm_splitk_workspace_size(100, 60, 1000, 3) == up(3 * 100 * 60 * 4)
+    assert lib.hg_hgemm_splitk_workspace_size(100, 60, 100, 32) == up(100 * 60 * 4)       # slices >= 64 columns
+    assert lib.hg_hgemm_splitk_workspace_size(100, 60, 200, 32) == up(2 * 100 * 60 * 4)   # 3 asked: 128 + 72
+    assert lib.hg_hgemm_splitk_workspace_size(100, 60, 10, 4) == up(100 * 60 * 4)         # one slice
+    assert lib.hg_hgemm_splitk_workspace_size(0, 60, 10, 4) == 0
+    assert lib.hg_hgemm_splitk_workspace_size(-1, 60, 10, 4) == -1
+    assert lib.hg_hgemm_splitk_workspace_size(4, 4, 4, 33) == -4
+    assert lib.hg_hgemm_splitk_workspace_size(4, 4, 4, -1) == -4
+    S = lambda *a: lib.hgemm_splitk(*a, None)
+    assert S(4, 4, 4, 1.0, P, 4, Q, 4, 0.0, R, 4, 1, 33, W, 1 << 20) == -13
+    assert S(4, 4, 4, 1.0, P, 4, Q, 4, 0.0, R, 4, 2, 2, W, 1 << 20) == -12
+    assert S(4, 4, 4, 1.0, P, 3, Q, 4, 0.0, R, 4, 1, 2, W, 1 << 20) == -6
+    assert S(4, 4, 4, 1.0, P, 4, Q, 4, 0.0, R, 3, 1, 2, W, 1 << 20) == -11
+    assert S(4, 4, 4, 1.0, P, 4, Q, 4, 0.0, R, 4, 1, 2, None, 1 << 20) == -14
+    assert S(4, 4, 4, 1.0, P, 4, Q, 4, 0.0, R, 4, 1, 2, W, 16) == -15
+    assert S(4, 4, 4, 1.0, P, 4, Q, 4, 0.0, R, 4, 1, 2, R, 1 << 20) == -14        # work overlaps C
+    assert S(0, 4, 4, 1.0, None, 4, None, 4, 0.0, None, 4, 1, 2, None, 0) == 0
