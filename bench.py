@@ -229,9 +229,16 @@ def config_sweep(hg, stream, main_gemm_ms=None, main_trmm_ms=None, only=None):
         Cd = torch.empty((w.M, w.N), dtype=torch.float32, device=dev)
         tb = _time_calls(lambda: hg.hgemm_bf16(Ad, Btd, Cd), 20, 30, stream)
         tfb = w.flops / (tb[0] * 1e-3) / 1e12
+        # the same with the fused bias + ReLU and a bf16 C
+        biasd = torch.from_numpy(np.random.default_rng(w.seed + 7).uniform(-1, 1, w.N)
+                                 .astype(np.float32)).to(dev)
+        Cb = torch.empty((w.M, w.N), dtype=torch.bfloat16, device=dev)
+        tbe = _time_calls(lambda: hg.hgemm_bias_act(Ad, Btd, Cb, biasd, True), 20, 30, stream)
         res["hgemm_bf16_8192"] = {
             "gpu_ms_median": round(tb[0], 5), "gpu_ms_min": round(tb[1], 5), "tflops": round(tfb, 2),
             "pct_of_bf16_mfma_peak": round(100 * tfb / PEAK_FP16_TFLOPS, 3),
+            "bias_relu_bf16_out_ms_median": round(tbe[0], 5),
+            "bias_relu_bf16_out_tflops": round(w.flops / (tbe[0] * 1e-3) / 1e12, 2),
             "note": "bf16 A, B (v_mfma_f32_16x16x32_bf16), fp32 accumulation and C; dense bf16 peak "
                     "equals the fp16 one"}
         del Ad, Btd, Cd, Ab, Bb

@@ -88,6 +88,8 @@ lib.hg_trmm.argtypes = [_int, _int, _i64, _i64, _f32, _vp, _i64, _vp, _i64, _vp,
 lib.hg_trmm.restype = _int
 lib.hg_trmm_workspace_size.argtypes = [_int, _int, _i64, _i64]
 lib.hg_trmm_workspace_size.restype = _i64
+lib.hgemm_bf16_bias_act.argtypes = lib.hgemm_bias_act.argtypes
+lib.hgemm_bf16_bias_act.restype = _int
 lib.hgemm_splitk.argtypes = [_i64, _i64, _i64, _f32, _vp, _i64, _vp, _i64, _f32, _vp, _i64, _int, _int, _vp,
                              _i64, _vp]
 lib.hgemm_splitk.restype = _int
@@ -113,7 +115,7 @@ lib.hg_trmm_plan.restype = _i64
 EXPORTS = ("hgemm", "hgemm_bias_act", "hgemm_bf16", "trmm_lower_trans", "hg_trmm_lower_trans_by_level",
            "hg_strerror", "hg_trmm_plan", "trsm_lower_trans", "hg_trsm_workspace_size", "hg_trmm",
            "hg_trmm_workspace_size", "hgemm_layout", "hg_hgemm_layout_workspace_size",
-           "hg_trmm_inplace", "hg_trmm_inplace_workspace_size", "hgemm_splitk",
+           "hg_trmm_inplace", "hg_trmm_inplace_workspace_size", "hgemm_splitk", "hgemm_bf16_bias_act",
            "hg_hgemm_splitk_workspace_size")
 
 ROW_MAJOR = 0
@@ -271,11 +273,13 @@ def hgemm_bf16(A, Bt, C, alpha: float = 1.0, beta: float = 0.0):
 def hgemm_bias_act(A, Bt, C, bias=None, relu: bool = False, alpha: float = 1.0,
                    beta: float = 0.0):
     """C = act(alpha·A·B + beta·C + bias) in one launch; bias a float32 device
-    vector of length N (or None), act ReLU when `relu`.  Returns C."""
+    vector of length N (or None), act ReLU when `relu`.  A and Bt float16 (C
+    float16 or float32) or both bfloat16 (C bfloat16 or float32).  Returns C."""
     import torch
-    _check_matrix(A, "A", (torch.float16,))
-    _check_matrix(Bt, "Bt", (torch.float16,))
-    _check_matrix(C, "C", (torch.float16, torch.float32))
+    _check_matrix(A, "A", (torch.float16, torch.bfloat16))
+    _check_matrix(Bt, "Bt", (A.dtype,))
+    bf = A.dtype == torch.bfloat16
+    _check_matrix(C, "C", (torch.bfloat16 if bf else torch.float16, torch.float32))
     M, K = A.shape
     N = Bt.shape[0]
     if Bt.shape[1] != K or tuple(C.shape) != (M, N):
@@ -287,13 +291,13 @@ def hgemm_bias_act(A, Bt, C, bias=None, relu: bool = False, alpha: float = 1.0,
                 and bias.dim() == 1 and bias.shape[0] == N and bias.is_contiguous()):
             raise ValueError("bias must be a contiguous float32 device vector of length N")
         bptr = bias.data_ptr() or None
-    out_dtype = HG_F16 if C.dtype == torch.float16 else HG_F32
-    st = lib.hgemm_bias_act(M, N, K, float(alpha), A.data_ptr() or None, _ld(A),
-                            Bt.data_ptr() or None, _ld(Bt), float(beta), C.data_ptr() or None,
-                            _ld(C), out_dtype, bptr, ACT_RELU if relu else ACT_NONE,
-                            _stream_handle(C))
+    out_dtype = HG_F32 if C.dtype == torch.float32 else (HG_BF16 if bf else HG_F16)
+    fn = lib.hgemm_bf16_bias_act if bf else lib.hgemm_bias_act
+    st = fn(M, N, K, float(alpha), A.data_ptr() or None, _ld(A), Bt.data_ptr() or None, _ld(Bt),
+            float(beta), C.data_ptr() or None, _ld(C), out_dtype, bptr, ACT_RELU if relu else ACT_NONE,
+            _stream_handle(C))
     if st != 0:
-        raise HgError("hgemm_bias_act", st)
+        raise HgError("hgemm_bf16_bias_act" if bf else "hgemm_bias_act", st)
     return C
 
 

@@ -189,6 +189,13 @@ int hgemm_bias_act(int64_t M, int64_t N, int64_t K, float alpha, const void *A, 
     return hgemm_impl(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, out_dtype, bias, act, stream);
 }
 
+int hgemm_bf16_bias_act(int64_t M, int64_t N, int64_t K, float alpha, const void *A, int64_t lda,
+                        const void *B, int64_t ldb, float beta, void *C, int64_t ldc, int out_dtype,
+                        const float *bias, int act, void *stream)
+{
+    return hgemm_impl(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, out_dtype, bias, act, stream, true);
+}
+
 int hgemm_bf16(int64_t M, int64_t N, int64_t K, float alpha, const void *A, int64_t lda,
                const void *B, int64_t ldb, float beta, void *C, int64_t ldc, int out_dtype,
                void *stream)

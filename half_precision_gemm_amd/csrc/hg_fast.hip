@@ -818,7 +818,7 @@ bool trmm_fused_ok(const GemmParams &p)
 
 bool fast_path_ok(const GemmParams &p, const LaunchOpts &o)
 {
-    if (!o.vec || (o.tri && (o.out_f16 || o.beta_read || o.epi)) || (o.in_bf16 && (o.tri || o.epi)))
+    if (!o.vec || (o.tri && (o.out_f16 || o.beta_read || o.epi)) || (o.in_bf16 && o.tri))
         return false;
     // 32-bit buffer offsets: every tile's byte range must stay below 2^31.
     if (p.lda > (1 << 21) || p.ldb > (1 << 21))
@@ -834,6 +834,13 @@ hipError_t launch_gemm_fast(const GemmParams &p, const LaunchOpts &o, hipStream_
     if (o.tri)
         return launch<false, false, true, false>(p, stream);     // TRMM leaves: fp32, written once
     if (o.in_bf16) {
+        if (o.epi) {
+            if (o.out_f16)
+                return o.beta_read ? launch<true, true, false, true, true>(p, stream)
+                                   : launch<true, false, false, true, true>(p, stream);
+            return o.beta_read ? launch<false, true, false, true, true>(p, stream)
+                               : launch<false, false, false, true, true>(p, stream);
+        }
         if (o.out_f16)
             return o.beta_read ? launch<true, true, false, false, true>(p, stream)
                                : launch<true, false, false, false, true>(p, stream);

@@ -308,7 +308,7 @@ template <int BM, int BN>
 hipError_t launch_ring_tile(const GemmParams &p, const LaunchOpts &o, hipStream_t s)
 {
     if (o.in_bf16)
-        return launch_ring_epi<BM, BN, false, true>(p, o, s);
+        return o.epi ? launch_ring_epi<BM, BN, true, true>(p, o, s) : launch_ring_epi<BM, BN, false, true>(p, o, s);
     return o.epi ? launch_ring_epi<BM, BN, true, false>(p, o, s)
                  : launch_ring_epi<BM, BN, false, false>(p, o, s);
 }
@@ -317,7 +317,7 @@ hipError_t launch_ring_tile(const GemmParams &p, const LaunchOpts &o, hipStream_
 
 bool ring_path_ok(const GemmParams &p, const LaunchOpts &o)
 {
-    if (!o.vec || o.tri || (o.in_bf16 && o.epi))
+    if (!o.vec || o.tri)
         return false;
     if (p.lda > (1 << 21) || p.ldb > (1 << 21))
         return false;

@@ -173,6 +173,18 @@ int hgemm_bf16(int64_t M, int64_t N, int64_t K, float alpha,
                int out_dtype, void *stream);
 
 /*
+ * hgemm_bf16_bias_act — hgemm_bias_act with bf16 A and B: C = act(alpha·A·B
+ * + beta·C + bias) in one launch, the products as in hgemm_bf16 and the bias
+ * and activation as in hgemm_bias_act ("GPU架构与CUDA", sections 混合精度核函数
+ * and 核函数融合).  Arguments, layouts and status codes as hgemm_bias_act,
+ * except A and B are bf16 and out_dtype is HG_BF16 or HG_F32 (-12).
+ */
+int hgemm_bf16_bias_act(int64_t M, int64_t N, int64_t K, float alpha,
+                        const void *A, int64_t lda, const void *B, int64_t ldb,
+                        float beta, void *C, int64_t ldc, int out_dtype,
+                        const float *bias, int act, void *stream);
+
+/*
  * trmm_lower_trans — Out = alpha·Aᵀ·B, A lower triangular.
  *
  *  1 n, 2 m      : A is n×n, B and Out are n×m; each >= 0.

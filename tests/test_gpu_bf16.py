@@ -105,3 +105,58 @@ def test_8192_sampled(hg):
     got = run(hg, A, Bt, np.zeros((w.M, w.N), np.float32), 1.0, 0.0, "f32")
     ri, cj = workloads.sample_indices(w.seed, w.M, w.N)
     check_close(got[ri, cj], oracle.gemm_bf16_sampled(A, Bt, ri, cj), w.K, "bf16 8192 sampled")
+
+
+# ---- bf16 operands with the fused bias and ReLU (hgemm_bf16_bias_act):
+# C = act(alpha·A·B + beta·C + bias) in one launch.  The reference is the
+# oracle's bf16 GEMM, biased and rectified by the definition (t + bias, then
+# t < 0 -> +0), so the bias add and the ReLU are the only arithmetic the test
+# itself does.
+def run_epi(hg, A, Bt, C0, bias, relu, alpha, beta, out):
+    import torch
+    dev = torch.device("cuda:0")
+    M, K = A.shape
+    N = Bt.shape[0]
+    print(f"[bf16-epi] M={M} N={N} K={K} relu={relu} beta={beta} out={out}", flush=True)
+    Ad = _bf16_tensor(A, dev)
+    Bd = _bf16_tensor(Bt, dev)
+    Cd = _bf16_tensor(C0, dev) if out == "bf16" else torch.from_numpy(C0).to(dev)
+    bd = torch.from_numpy(bias).to(dev)
+    hg.hgemm_bias_act(Ad, Bd, Cd, bd, relu, alpha, beta)
+    torch.cuda.synchronize()
+    if out == "bf16":
+        bits = Cd.view(torch.int16).cpu().numpy().view(np.uint16)
+        return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return Cd.cpu().numpy().astype(np.float64)
+
+
+def _biased(ref, bias, relu):
+    t = ref + bias.astype(np.float64)[None, :]
+    return np.where(t < 0, 0.0, t) if relu else t
+
+
+@pytest.mark.parametrize("M,N,K,out,beta", CASES)
+@pytest.mark.parametrize("relu", [False, True])
+def test_bias_act_parity(hg, M, N, K, out, beta, relu):
+    rng = np.random.default_rng(M + N + K + 7 * relu)
+    A = workloads.uniform_bf16(rng, (M, K))
+    Bt = workloads.uniform_bf16(rng, (N, K))
+    C0 = workloads.uniform_bf16(rng, (M, N)) if out == "bf16" else rng.uniform(-1, 1, (M, N)).astype(np.float32)
+    bias = rng.uniform(-2, 2, N).astype(np.float32)
+    got = run_epi(hg, A, Bt, C0, bias, relu, 1.25, beta, out)
+    ref = _biased(oracle.gemm_bf16(A, Bt, 1.25, beta, C0 if beta else None, cin_bf16=(out == "bf16")), bias, relu)
+    check_close(got, ref, K, f"bf16 bias {M}x{N}x{K} {out} relu={relu}",
+                rel=REL_BF16 if out == "bf16" else 2.0 ** -10)
+    if relu:
+        assert (got >= 0).all()
+
+
+@pytest.mark.parametrize("M,N,K", [(4096, 4096, 512), (1000, 1000, 1000), (77, 50, 24)])
+def test_bias_act_integer_bit_exact(hg, M, N, K):
+    rng = np.random.default_rng(K + 3)
+    A = workloads.to_bf16_bits(rng.integers(-4, 5, (M, K)).astype(np.float32))
+    Bt = workloads.to_bf16_bits(rng.integers(-4, 5, (N, K)).astype(np.float32))
+    C0 = rng.integers(-4, 5, (M, N)).astype(np.float32)
+    bias = rng.integers(-40, 41, N).astype(np.float32)
+    got = run_epi(hg, A, Bt, C0, bias, True, 1.0, 2.0, "f32")
+    assert np.array_equal(got, _biased(oracle.gemm_bf16(A, Bt, 1.0, 2.0, C0), bias, True))
