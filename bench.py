@@ -35,10 +35,14 @@ PEAK_HBM_GBS = 8000.0
 
 
 def kernel_source_hash():
+    """Hash of the HGEMM kernels' code: the sources with // comments and
+    blank lines removed, so that a comment edit keeps the profiles valid."""
+    import re
     h = hashlib.sha256()
     for f in ("hg_fast.hip", "hg_ring.hip", "hg_kernels.hip", "hg_api.cpp", "hg_internal.h"):
-        with open(os.path.join(ROOT, "half_precision_gemm_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "half_precision_gemm_amd", "csrc", f), encoding="utf-8") as fh:
+            code = [re.sub(r"//.*$", "", line).rstrip() for line in fh]
+        h.update("\n".join(line for line in code if line).encode())
     return h.hexdigest()[:16]
 
 

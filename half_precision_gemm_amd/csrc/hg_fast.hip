@@ -6,7 +6,8 @@
 // tiled matmul of "GPU架构与CUDA" 共享内存与分块), for operands whose rows
 // are 16-byte aligned and K a multiple of 8; with TRI it is also the
 // triangle-masked leaf of the recursive TRMM ("异构计算中高性能TRMM与TRSM的
-// 递归算法实现" §2.2).  Design:
+// 递归算法实现" §2.2), and with TRI and FUSED the whole recursion in one
+// launch (see the section on the recursive TRMM below).  Design:
 //
 //  * One workgroup = 4 waves (one per SIMD) per 256×256 tile, laid out 2×2;
 //    each wave owns a 128×128 sub-tile = 8×8 blocks of
