@@ -21,11 +21,19 @@ importing this package raises.
 
     hgemm_bias_act(A, Bt, C, bias=None, relu=False, alpha=1.0, beta=0.0)
         C = act(alpha·A·B + beta·C + bias) in one launch, bias a float32
-        device vector of length N added to every row, act ReLU or none.
+        device vector of length N added to every row, act ReLU or none;
+        float16 or bfloat16 operands.
+
+    hgemm_splitk(A, Bt, C, alpha=1.0, beta=0.0, splits=0, work=None)
+        hgemm with K cut into slices run side by side (few output tiles,
+        long K); partial products summed in order in fp32.
 
     trmm(A, B, Out, alpha=1.0, uplo="L", trans=True, leaf=256, work=None)
-        Out = alpha·op(A)·B for every triangle / transposition (the other
-        three variants through an index map of A into a workspace).
+        Out = alpha·op(A)·B for every triangle / transposition.
+
+    trmm_inplace(A, B, alpha=1.0, uplo="L", trans=True, leaf=256, work=None)
+        B = alpha·op(A)·B with B float16, overwritten (the product formed in
+        fp32 and rounded once).
 
     trmm_lower_trans(A, B, Out, alpha=1.0, leaf=256)
     trmm_lower_trans_by_level(A, B, Out, alpha=1.0, leaf=256)
