@@ -25,6 +25,13 @@
 // leaf instead of once per column.
 #include "hg_internal.h"
 
+typedef int32_t hg_trsm_i32x4 __attribute__((ext_vector_type(4)));
+
+// Raw buffer load of 16 bytes per lane (LLVM intrinsic).  An offset past the
+// resource's range returns zeros without a memory request.
+extern "C" __device__ hg_trsm_i32x4 hg_trsm_buffer_load_b128(hg_trsm_i32x4 rsrc, int voffset, int soffset,
+                                                            int aux) __asm("llvm.amdgcn.raw.buffer.load.v4i32");
+
 namespace hg {
 namespace {
 
@@ -260,6 +267,19 @@ constexpr int XLD = LBN + 4;                 // padded fp32 row of a staged 32×
 // fragment reads of 32 consecutive rows at one kc hit distinct bank groups.
 __device__ __forceinline__ int lds_chunk(int row, int kc) { return row * LKC + (kc ^ (row & 31)); }
 
+// Buffer resource over `bytes` bytes from `base` (no stride; the offset of a
+// load is checked against `bytes`).
+__device__ __forceinline__ hg_trsm_i32x4 buffer_rsrc(const void *base, uint32_t bytes)
+{
+    const uint64_t b = reinterpret_cast<uint64_t>(base);
+    hg_trsm_i32x4 r;
+    r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+    r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
+    r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+    r[3] = 0x00020000;
+    return r;
+}
+
 // Chunk kc (8 consecutive k) of V row j is read by the MFMA k step kc/2 of
 // j block j/32, which runs when that step reaches the block: 16·(kc/2) + 16
 // > 32·(j/32).
@@ -281,6 +301,7 @@ __global__ void __launch_bounds__(256, 1) trsm_leaf_kernel(const TrsmLeafParams 
     const int64_t o = p.o;
     const float alpha = p.alpha;
     const bool touched = p.touched != 0;
+    const hg_trsm_i32x4 vrs = buffer_rsrc(p.V, (uint32_t)p.ldv * (uint32_t)p.ldv * 2u);
 
     // R(i, k..k+7) = fp16(alpha·B(o+k.., i) + S(o+k.., i)), zero past the
     // leaf or past the last column of B.
@@ -392,7 +413,9 @@ __global__ void __launch_bounds__(256, 1) trsm_leaf_kernel(const TrsmLeafParams 
         for (int u = 0; u < V_PER_T; ++u) {
             const int j = vrow(u);
             vok[u] = j < s && k < s && v_chunk_used(j, lkc);
-            rv[u] = *reinterpret_cast<const uint4 *>(p.V + (vok[u] ? (int64_t)j * p.ldv + k : 0));
+            // unused chunks: an out-of-range offset, so no memory request
+            const uint32_t voff = vok[u] ? (uint32_t)(j * p.ldv + k) * 2u : 0x80000000u;
+            rv[u] = __builtin_bit_cast(uint4, hg_trsm_buffer_load_b128(vrs, (int)voff, 0, 0));
         }
         // U(i, j) = Σ_k' X2(i, k')·A21(k', j), the fragments of the leaf
         // product below with A21ᵀ in place of the inverse (every chunk of
@@ -476,7 +499,9 @@ __global__ void __launch_bounds__(256, 1) trsm_leaf_kernel(const TrsmLeafParams 
         for (int u = 0; u < V_PER_T; ++u) {
             const int j = vrow(u);
             vok[u] = j < s && k < s && v_chunk_used(j, lkc);
-            rv[u] = *reinterpret_cast<const uint4 *>(p.V + (vok[u] ? (int64_t)j * p.ldv + k : 0));
+            // unused chunks: an out-of-range offset, so no memory request
+            const uint32_t voff = vok[u] ? (uint32_t)(j * p.ldv + k) * 2u : 0x80000000u;
+            rv[u] = __builtin_bit_cast(uint4, hg_trsm_buffer_load_b128(vrs, (int)voff, 0, 0));
         }
 #pragma unroll
         for (int u = 0; u < R_PER_T; ++u) {
