@@ -273,12 +273,18 @@ def config_sweep(hg, stream, main_gemm_ms=None, main_trmm_ms=None, only=None):
         Ad, Bd = torch.from_numpy(TA).to(dev), torch.from_numpy(TB).to(dev)
         Od = torch.empty((w.m, w.n), dtype=torch.float32, device=dev)
         ts = _time_calls(lambda: hg.trmm_lower_trans(Ad, Bd, Od, w.alpha, w.leaf), 20, 50, stream)
+        # the same recursion with each phase's launches on 4 streams (the page's
+        # usage notes) instead of one batched launch per phase
+        streams4 = [torch.cuda.current_stream()] + [torch.cuda.Stream() for _ in range(3)]
+        t4 = _time_calls(lambda: hg.trmm_lower_trans_streams(Ad, Bd, Od, streams4, w.alpha, w.leaf), 20, 50,
+                         stream)
         # compulsory traffic: A's lower triangle and B read once, Out written once (fp32)
         nb = w.n * (w.n + 1) + 2 * w.n * w.m + 4 * w.n * w.m
         res["trmm_4096x256"] = {"gpu_ms_median": round(ts[0], 5), "gpu_ms_min": round(ts[1], 5),
                                 "gpu_ms_back_to_back_mean": round(ts[2], 5),
                                 "effective_tflops": round(w.flops / (ts[0] * 1e-3) / 1e12, 2),
                                 "compulsory_bytes": nb, "gbs": round(nb / (ts[0] * 1e-3) / 1e9, 1),
+                                "four_streams_ms_median": round(t4[0], 5),
                                 "note": "B 4096x256 (the TRMM page's usage example), level-by-level launches"}
         del Ad, Bd, Od, TA, TB
     if want("trmm_8192_lower_notrans"):

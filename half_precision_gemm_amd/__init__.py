@@ -109,6 +109,9 @@ lib.hg_trmm_inplace.restype = _int
 lib.hg_trmm_inplace_workspace_size.argtypes = [_int, _int, _i64, _i64]
 lib.hg_trmm_inplace_workspace_size.restype = _i64
 lib.hg_trmm_lower_trans_by_level.argtypes = lib.trmm_lower_trans.argtypes
+lib.hg_trmm_lower_trans_streams.argtypes = [_i64, _i64, _f32, _vp, _i64, _vp, _i64, _vp, _i64, _int, _i64,
+                                            ctypes.POINTER(_vp), _int]
+lib.hg_trmm_lower_trans_streams.restype = _int
 lib.hg_trmm_lower_trans_by_level.restype = _int
 lib.trsm_lower_trans.argtypes = [_i64, _i64, _f32, _vp, _i64, _vp, _i64, _vp, _i64, _int, _i64,
                                  _vp, _i64, _vp]
@@ -124,6 +127,7 @@ EXPORTS = ("hgemm", "hgemm_bias_act", "hgemm_bf16", "trmm_lower_trans", "hg_trmm
            "hg_strerror", "hg_trmm_plan", "trsm_lower_trans", "hg_trsm_workspace_size", "hg_trmm",
            "hg_trmm_workspace_size", "hgemm_layout", "hg_hgemm_layout_workspace_size",
            "hg_trmm_inplace", "hg_trmm_inplace_workspace_size", "hgemm_splitk", "hgemm_bf16_bias_act",
+           "hg_trmm_lower_trans_streams",
            "hg_hgemm_splitk_workspace_size")
 
 ROW_MAJOR = 0
@@ -319,6 +323,27 @@ def trmm_lower_trans_by_level(A, B, Out, alpha: float = 1.0, leaf: int = 256):
     (same result up to fp32 rounding); see hg_trmm_lower_trans_by_level."""
     return _trmm(lib.hg_trmm_lower_trans_by_level, "hg_trmm_lower_trans_by_level", A, B, Out,
                  alpha, leaf)
+
+
+def trmm_lower_trans_streams(A, B, Out, streams, alpha: float = 1.0, leaf: int = 256):
+    """trmm_lower_trans_by_level with each phase's launches spread over the
+    torch streams in `streams` (1 to 8; the first is where the result is
+    ordered); the same bits as trmm_lower_trans_by_level.  Returns Out."""
+    import torch
+    _check_matrix(A, "A", (torch.float16,))
+    _check_matrix(B, "B", (torch.float16,))
+    _check_matrix(Out, "Out", (torch.float32,))
+    n = A.shape[0]
+    m = B.shape[0]
+    if tuple(A.shape) != (n, n) or B.shape[1] != n or tuple(Out.shape) != (m, n):
+        raise ValueError(f"shape mismatch: A {tuple(A.shape)}, B {tuple(B.shape)}, Out {tuple(Out.shape)}")
+    arr = (ctypes.c_void_p * len(streams))(*[ctypes.c_void_p(st.cuda_stream) for st in streams])
+    st = lib.hg_trmm_lower_trans_streams(n, m, float(alpha), A.data_ptr() or None, _ld(A),
+                                         B.data_ptr() or None, _ld(B), Out.data_ptr() or None, _ld(Out),
+                                         HG_F32, int(leaf), arr, len(streams))
+    if st != 0:
+        raise HgError("hg_trmm_lower_trans_streams", st)
+    return Out
 
 
 def _trmm(fn, fname, A, B, Out, alpha, leaf):

@@ -233,9 +233,12 @@ namespace {
 // updates in its accumulators); without
 // it, or when the recursion's boundaries do not fall on tile edges, one
 // batched launch per recursion level.
+// With `streams` (nstreams > 1, fused off) the per-level schedule puts each
+// leaf and each update of a level on its own stream, round-robin, with the
+// streams joined between levels (hg_trmm_lower_trans_streams).
 int trmm_impl(int64_t n, int64_t m, float alpha, const void *A, int64_t lda, const void *B,
               int64_t ldb, void *Out, int64_t ldo, int out_dtype, int64_t leaf, void *stream,
-              bool fused)
+              bool fused, const hipStream_t *streams = nullptr, int nstreams = 0)
 {
     if (n < 0 || n > kI32Max)
         return -1;
@@ -299,6 +302,49 @@ int trmm_impl(int64_t n, int64_t m, float alpha, const void *A, int64_t lda, con
             return hip_status(hg::launch_trmm_fused(p, s));
     }
 
+    // Several streams: events to join them between levels (every stream
+    // waits for the others' work so far); the first stream is the caller's.
+    std::vector<hipEvent_t> evs;
+    auto cleanup = [&]() {
+        for (hipEvent_t e : evs)
+            (void)hipEventDestroy(e);
+        evs.clear();
+    };
+    auto join = [&]() -> int {
+        for (int i = 0; i < nstreams; ++i) {
+            const hipError_t e = hipEventRecord(evs[i], streams[i]);
+            if (e != hipSuccess)
+                return hip_status(e);
+        }
+        for (int i = 0; i < nstreams; ++i)
+            for (int k = 0; k < nstreams; ++k) {
+                if (k == i)
+                    continue;
+                const hipError_t e = hipStreamWaitEvent(streams[i], evs[k], 0);
+                if (e != hipSuccess)
+                    return hip_status(e);
+            }
+        return HG_OK;
+    };
+    if (nstreams > 1) {
+        for (int i = 0; i < nstreams; ++i) {
+            hipEvent_t e;
+            const hipError_t err = hipEventCreateWithFlags(&e, hipEventDisableTiming);
+            if (err != hipSuccess) {
+                cleanup();
+                return hip_status(err);
+            }
+            evs.push_back(e);
+        }
+        // the other streams start after the caller's stream's earlier work
+        const int stj = join();
+        if (stj != HG_OK) {
+            cleanup();
+            return stj;
+        }
+    }
+    int rr = 0;   // next stream, round-robin
+
     auto run_batch = [&](const std::vector<hg::BatchEntry> &ents, bool tri, float beta) -> int {
         for (size_t first = 0; first < ents.size(); first += hg::kMaxBatch) {
             hg::GemmParams p = base;
@@ -318,11 +364,24 @@ int trmm_impl(int64_t n, int64_t m, float alpha, const void *A, int64_t lda, con
             o.tri = tri;
             o.vec = vec;
             o.tile = choose_batched_tile(m, maxN, (int64_t)cnt);
+            if (nstreams > 1) {
+                // each entry alone, with the tile family of the whole batch:
+                // the same kernel computes every tile as in the batched launch
+                for (size_t i = 0; i < cnt; ++i) {
+                    hg::GemmParams q = p;
+                    q.nbatch = 1;
+                    q.e[0] = p.e[i];
+                    const hipError_t e = hg::launch_gemm(q, o, streams[rr++ % nstreams]);
+                    if (e != hipSuccess)
+                        return hip_status(e);
+                }
+                continue;
+            }
             const hipError_t e = hg::launch_gemm(p, o, s);
             if (e != hipSuccess)
                 return hip_status(e);
         }
-        return HG_OK;
+        return nstreams > 1 ? join() : HG_OK;
     };
 
     // Leaves: Out(o+i, j) = alpha·Σ_{k>=i} A(o+k, o+i)·B(o+k, j), written once.
@@ -331,8 +390,10 @@ int trmm_impl(int64_t n, int64_t m, float alpha, const void *A, int64_t lda, con
         if (x.kind == 0)
             ents.push_back({x.o, x.o * lda + x.o, x.o, (int32_t)x.s, (int32_t)x.s});
     int st = run_batch(ents, true, 0.0f);
-    if (st != HG_OK)
+    if (st != HG_OK) {
+        cleanup();
         return st;
+    }
     // Updates, deepest level first; within a level they write disjoint rows.
     for (int64_t d = max_depth; d >= 0; --d) {
         ents.clear();
@@ -345,9 +406,12 @@ int trmm_impl(int64_t n, int64_t m, float alpha, const void *A, int64_t lda, con
         if (ents.empty())
             continue;
         st = run_batch(ents, false, 1.0f);
-        if (st != HG_OK)
+        if (st != HG_OK) {
+            cleanup();
             return st;
+        }
     }
+    cleanup();
     return HG_OK;
 }
 
@@ -367,6 +431,20 @@ int hg_trmm_lower_trans_by_level(int64_t n, int64_t m, float alpha, const void *
                                  int64_t leaf, void *stream)
 {
     return trmm_impl(n, m, alpha, A, lda, B, ldb, Out, ldo, out_dtype, leaf, stream, false);
+}
+
+int hg_trmm_lower_trans_streams(int64_t n, int64_t m, float alpha, const void *A, int64_t lda,
+                                const void *B, int64_t ldb, void *Out, int64_t ldo, int out_dtype,
+                                int64_t leaf, void *const *streams, int nstreams)
+{
+    if (nstreams < 1 || nstreams > 8)
+        return -13;
+    if (streams == nullptr)
+        return -12;
+    hipStream_t ss[8];
+    for (int i = 0; i < nstreams; ++i)
+        ss[i] = static_cast<hipStream_t>(streams[i]);
+    return trmm_impl(n, m, alpha, A, lda, B, ldb, Out, ldo, out_dtype, leaf, ss[0], false, ss, nstreams);
 }
 
 }  // extern "C"

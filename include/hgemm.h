@@ -339,6 +339,33 @@ int hg_trmm_lower_trans_by_level(int64_t n, int64_t m, float alpha,
                                  int64_t leaf, void *stream);
 
 /*
+ * hg_trmm_lower_trans_streams — hg_trmm_lower_trans_by_level with the
+ * independent launches of each phase spread over several streams, as the
+ * recursion's usage notes suggest ("异构计算中高性能TRMM与TRSM的递归算法实现"
+ * §5.2: several streams for the independent branches): every leaf, then
+ * every update of a level, deepest level first, goes to the next stream in
+ * turn, and the streams are joined (events) at entry, between phases and at
+ * the end.
+ *
+ *  1..11         : as trmm_lower_trans (no stream argument).
+ * 12 streams     : array of nstreams hipStream_t; streams[0] is the caller's:
+ *                  the work starts after what is queued on it and, on return,
+ *                  everything queued later on it runs after the product.
+ *                  NULL: -12.
+ * 13 nstreams    : 1..8 (-13 otherwise).
+ *
+ * Each launch runs the kernel the batched launch of its phase runs, so the
+ * result equals hg_trmm_lower_trans_by_level's bit for bit.  The level's
+ * batched launch already runs all its branches side by side; this entry
+ * point is there to measure the stream form against it.
+ */
+int hg_trmm_lower_trans_streams(int64_t n, int64_t m, float alpha,
+                                const void *A, int64_t lda,
+                                const void *B, int64_t ldb,
+                                void *Out, int64_t ldo, int out_dtype,
+                                int64_t leaf, void *const *streams, int nstreams);
+
+/*
  * trsm_lower_trans — Out = X = alpha·A⁻ᵀ·B, i.e. the X with Aᵀ·X = alpha·B,
  * A lower triangular.
  *

@@ -32,7 +32,8 @@ def test_header_declares_the_entry_points():
     assert declared_functions() == ["hg_hgemm_layout_workspace_size", "hg_hgemm_splitk_workspace_size",
                                     "hg_strerror", "hg_trmm",
                                     "hg_trmm_inplace", "hg_trmm_inplace_workspace_size",
-                                    "hg_trmm_lower_trans_by_level", "hg_trmm_plan",
+                                    "hg_trmm_lower_trans_by_level", "hg_trmm_lower_trans_streams",
+                                    "hg_trmm_plan",
                                     "hg_trmm_workspace_size", "hg_trsm_workspace_size", "hgemm",
                                     "hgemm_bf16", "hgemm_bf16_bias_act", "hgemm_bias_act", "hgemm_layout",
                                     "hgemm_splitk",
@@ -387,3 +388,14 @@ def test_hgemm_splitk_workspace_and_arguments(lib):
     assert S(4, 4, 4, 1.0, P, 4, Q, 4, 0.0, R, 4, 1, 2, W, 16) == -15
     assert S(4, 4, 4, 1.0, P, 4, Q, 4, 0.0, R, 4, 1, 2, R, 1 << 20) == -14        # work overlaps C
     assert S(0, 4, 4, 1.0, None, 4, None, 4, 0.0, None, 4, 1, 2, None, 0) == 0
+
+
+def test_trmm_streams_arguments(lib):
+    import ctypes
+    arr = (ctypes.c_void_p * 2)(None, None)
+    T = lambda ns, streams=arr: lib.hg_trmm_lower_trans_streams(8, 4, 1.0, P, 8, Q, 8, R, 8, 1, 256, streams, ns)
+    assert T(0) == -13
+    assert T(9) == -13
+    assert T(2, None) == -12
+    assert lib.hg_trmm_lower_trans_streams(8, 4, 1.0, P, 8, Q, 8, R, 8, 2, 256, arr, 2) == -10   # fp16 Out
+    assert lib.hg_trmm_lower_trans_streams(0, 4, 1.0, None, 1, None, 1, None, 1, 1, 256, arr, 2) == 0

@@ -233,3 +233,21 @@ def test_skinny_b(hg, n, m):
     A_cm, B_cm = trmm_inputs(n, m, n + m)
     out = run(hg, A_cm, B_cm, 0.75)
     check_close(out, oracle.trmm_lower_trans(A_cm, B_cm, 0.75), n, f"skinny n={n} m={m}")
+
+
+# ---- the per-level schedule spread over several streams
+# (hg_trmm_lower_trans_streams): every launch runs the kernel of its
+# phase's batched launch, so the bits equal the level-by-level entry point's.
+@pytest.mark.parametrize("n,m,leaf,nstreams", [(4096, 256, 256, 4), (2048, 1000, 256, 2),
+                                               (1000, 300, 100, 3), (8192, 512, 256, 8),
+                                               (600, 70, 128, 1)])
+def test_streams_equal_by_level(hg, n, m, leaf, nstreams):
+    print(f"[case] trmm streams n={n} m={m} leaf={leaf} streams={nstreams}", flush=True)
+    A_cm, B_cm = trmm_inputs(n, m, n + m + nstreams)
+    lev = run(hg, A_cm, B_cm, 0.75, leaf, by_level=True)
+    streams = [torch.cuda.current_stream()] + [torch.cuda.Stream() for _ in range(nstreams - 1)]
+    Out = torch.full((m, n), float("nan"), dtype=torch.float32, device=DEV)
+    hg.trmm_lower_trans_streams(dev(A_cm), dev(B_cm), Out, streams, 0.75, leaf)
+    torch.cuda.synchronize()
+    got = Out.cpu().numpy()
+    assert np.array_equal(got.view(np.uint32), lev.view(np.uint32))
