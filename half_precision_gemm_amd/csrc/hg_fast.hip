@@ -637,6 +637,17 @@ hgemm_fast_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int c
                         for (int e = 0; e < 4; ++e)
                             bv[j][e] = p.bias ? p.bias[T.n0 + wn * WTN + j * FB + 4 * fhi + e] : -0.0f;
                 }
+                // With 128-column wave sub-tiles each 16-row block goes
+                // through LDS (A ring slot 2, which the next tile's prologue
+                // leaves free; 8 KiB per wave) so that each store instruction
+                // writes two whole 128-column rows, i.e. complete 128-byte
+                // lines, instead of a half (fp32) or quarter (16-bit) line in
+                // each of 16 rows.  The number of stores is unchanged.
+                constexpr bool STAGE = TN == 8;
+                constexpr int UB = sizeof(cvec);       // one lane's 4 columns
+                constexpr int SROW = 32 * UB;          // one staged 128-column row
+                constexpr int SSW = OUT_F16 ? 2 : 1;   // bank swizzle: piece ^ (row · SSW)
+                unsigned char *stg = smem + 2 * SLOT + wave * (FB * SROW);
 #pragma unroll
                 for (int i = 0; i < TM; ++i) {
                     celt *cr = crow(i);
@@ -652,7 +663,24 @@ hgemm_fast_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int c
                                 t = epi_apply(t, bv[j][e], p.act);
                             r[e] = (celt)t;
                         }
-                        *reinterpret_cast<cvec *>(cr + j * FB) = r;
+                        if constexpr (STAGE)
+                            *reinterpret_cast<cvec *>(stg + frow * SROW + ((4 * j + fhi) ^ (frow * SSW)) * UB) = r;
+                        else
+                            *reinterpret_cast<cvec *>(cr + j * FB) = r;
+                    }
+                    if constexpr (STAGE) {
+                        // A wave's LDS accesses execute in issue order, so the
+                        // reads see this block's writes; the fences keep the
+                        // compiler from moving LDS accesses across.
+                        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+                        celt *c0 = crow(i) - frow * ldc - 4 * fhi;   // row 0, column 0 of the block
+#pragma unroll
+                        for (int t = 0; t < TN; ++t) {
+                            const int rr = 2 * t + (lane >> 5), uu = lane & 31;
+                            const cvec v = *reinterpret_cast<const cvec *>(stg + rr * SROW + (uu ^ (rr * SSW)) * UB);
+                            *reinterpret_cast<cvec *>(c0 + (int64_t)rr * ldc + 4 * uu) = v;
+                        }
+                        __atomic_signal_fence(__ATOMIC_SEQ_CST);
                     }
                     if (RD && i + CP < TM) {
 #pragma unroll
