@@ -302,3 +302,25 @@ def test_empty(hg):
     C = torch.empty((3, 0), dtype=torch.float32, device=DEV)
     hg.hgemm(A, Bt, C)
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("odt", [np.float16, np.float32])
+def test_big_tiles_padded_window(hg, odt):
+    """256×256-tile kernel (≥ 256 tiles) writing into a window of a larger
+    buffer: ldc ≠ N, a nonzero element offset, ragged M and N (interior tiles
+    and edge tiles side by side); the padding keeps its sentinels and every
+    element of the window matches the oracle."""
+    M, N, K, pad = 4096 + 37, 4096 + 64, 192, 12
+    print(f"[case] big-tile window M={M} N={N} K={K} ldc={N + pad + 4} {np.dtype(odt).name}", flush=True)
+    A = rnd(21, (M, K))
+    Bt = rnd(22, (N, K))
+    sentinel = odt(-12345.0) if odt == np.float32 else np.float16(-1234.0)
+    big = np.full((M + 2, N + pad + 4), sentinel, odt)
+    bigd = dev(big)
+    view = bigd[1:M + 1, 4:N + 4]            # element offset ldc + 4 (a multiple of 4)
+    hg.hgemm(dev(A), dev(Bt), view, 0.5, 0.0)
+    torch.cuda.synchronize()
+    got = bigd.cpu().numpy()
+    assert np.all(got[0] == sentinel) and np.all(got[M + 1] == sentinel)
+    assert np.all(got[:, :4] == sentinel) and np.all(got[:, N + 4:] == sentinel)
+    check_close(got[1:M + 1, 4:N + 4], 0.5 * oracle.hgemm(A, Bt), K, "window")
