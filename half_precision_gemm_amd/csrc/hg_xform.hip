@@ -283,6 +283,42 @@ hipError_t launch_tri_xform(int mode, const _Float16 *A, int64_t lda, _Float16 *
     return hipGetLastError();
 }
 
+typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+
+// D = Sᵀ when rows and cols are multiples of 64 and rows are 16-byte
+// aligned, without LDS: each wave moves one 64×64 tile.  Lane (rb, cb) =
+// (lane / 8, lane % 8) loads the 8×8 block at S rows 8rb.., columns 8cb..
+// (eight 16-byte loads; the 8 lanes of one rb read one whole 128-byte line
+// of each row), transposes it in registers and stores 8 rows of D (the 8
+// lanes of one cb write one whole 128-byte line of each).
+__global__ void __launch_bounds__(256) transpose64_kernel(const _Float16 *__restrict__ S, int64_t lds,
+                                                          _Float16 *__restrict__ D, int64_t ldd, int tiles_c,
+                                                          int ntiles)
+{
+    const int tile = blockIdx.x * 4 + (int)(threadIdx.x >> 6);
+    if (tile >= ntiles)
+        return;
+    const int lane = threadIdx.x & 63, rb = lane >> 3, cb = lane & 7;
+    const int64_t r0 = (int64_t)(tile / tiles_c) * 64 + 8 * rb;
+    const int64_t c0 = (int64_t)(tile % tiles_c) * 64 + 8 * cb;
+    u32x4v in[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+        in[k] = *reinterpret_cast<const u32x4v *>(S + (r0 + k) * lds + c0);
+    // Output row k2 is S column c0 + k2: element e = S(r0 + e, c0 + k2),
+    // i.e. half k2 of in[e]; dword d packs elements 2d (low) and 2d + 1.
+#pragma unroll
+    for (int k2 = 0; k2 < 8; ++k2) {
+        u32x4v o;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            const uint32_t a = in[2 * d][k2 >> 1], b = in[2 * d + 1][k2 >> 1];
+            o[d] = (k2 & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
+        }
+        *reinterpret_cast<u32x4v *>(D + (c0 + k2) * ldd + r0) = o;
+    }
+}
+
 hipError_t launch_transpose(const _Float16 *S, int64_t lds, _Float16 *D, int64_t ldd, int64_t rows,
                             int64_t cols, hipStream_t stream)
 {
@@ -293,6 +329,12 @@ hipError_t launch_transpose(const _Float16 *S, int64_t lds, _Float16 *D, int64_t
         return hipErrorInvalidValue;
     const int vec = reinterpret_cast<uintptr_t>(S) % 16 == 0 && reinterpret_cast<uintptr_t>(D) % 16 == 0 &&
                     lds % 8 == 0 && ldd % 8 == 0;
+    if (vec && rows % 64 == 0 && cols % 64 == 0) {
+        const int64_t nt = (rows / 64) * (cols / 64);
+        hipLaunchKernelGGL(transpose64_kernel, dim3((unsigned)((nt + 3) / 4)), dim3(256), 0, stream, S, lds, D,
+                           ldd, (int)(cols / 64), (int)nt);
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL(transpose_kernel, dim3((unsigned)(tr * tc)), dim3(256), 0, stream, S, lds, D, ldd,
                        (int)rows, (int)cols, (int)tc, vec);
     return hipGetLastError();
