@@ -31,6 +31,12 @@
 //  * Persistent workgroups (short K): one per CU walks a strided list of
 //    tiles; the next tile's first stages are requested before the current
 //    tile's epilogue, so loads overlap the stores.
+//  * Epilogue: a lane's accumulators are 4 consecutive columns in each of 8
+//    column blocks of one row; stored as they are, every store instruction
+//    would touch 16 rows with part of a 128-byte line each.  Each 16-row
+//    block is instead passed through LDS (the A slot that the next tile's
+//    prologue leaves idle) and stored two whole 128-column rows per
+//    instruction; the store count is the same.
 //
 // Workgroup→tile order: tile ids are regrouped per XCD (consecutive
 // workgroup ids run on different XCDs, each with its own L2), then each
