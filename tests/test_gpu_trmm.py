@@ -251,3 +251,21 @@ def test_streams_equal_by_level(hg, n, m, leaf, nstreams):
     torch.cuda.synchronize()
     got = Out.cpu().numpy()
     assert np.array_equal(got.view(np.uint32), lev.view(np.uint32))
+
+
+def test_streams_join_onto_first_stream(hg):
+    """Work queued on streams[0] after the call sees the finished product
+    (the final join), also when streams[0] is not the current stream."""
+    n, m, leaf = 2048, 512, 256
+    print(f"[case] trmm streams join n={n} m={m}", flush=True)
+    A_cm, B_cm = trmm_inputs(n, m, 77)
+    lev = run(hg, A_cm, B_cm, 1.0, leaf, by_level=True)
+    s0, s1, s2 = torch.cuda.Stream(), torch.cuda.Stream(), torch.cuda.Stream()
+    Ad, Bd = dev(A_cm), dev(B_cm)
+    Out = torch.full((m, n), float("nan"), dtype=torch.float32, device=DEV)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s0):
+        hg.trmm_lower_trans_streams(Ad, Bd, Out, [s0, s1, s2], 1.0, leaf)
+        copy = Out.clone()          # queued on s0 right behind the product
+    torch.cuda.synchronize()
+    assert np.array_equal(copy.cpu().numpy().view(np.uint32), lev.view(np.uint32))
