@@ -101,6 +101,16 @@ def _load():
             lib.oracle_trsm_lower_trans_cols.restype = None
             lib.oracle_num_threads.argtypes = []
             lib.oracle_num_threads.restype = ctypes.c_int
+            lib.oracle_gemm_bf16_bias_act.argtypes = [i64, i64, i64, f64, vp, i64, vp, i64,
+                                                      f64, vp, i64, ctypes.c_int, vp,
+                                                      ctypes.c_int, vp, i64]
+            lib.oracle_gemm_bf16_bias_act.restype = None
+            lib.oracle_gemm_bias_act_sampled.argtypes = [ctypes.c_int, i64, f64, vp, i64, vp,
+                                                         i64, f64, vp, i64, ctypes.c_int, vp,
+                                                         ctypes.c_int, i64, vp, vp, vp]
+            lib.oracle_gemm_bias_act_sampled.restype = None
+            lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
+            lib.oracle_set_num_threads.restype = None
             _lib = lib
     return _lib
 
@@ -264,6 +274,105 @@ def hgemm_bias_act(A: np.ndarray, Bt: np.ndarray, alpha: float = 1.0, beta: floa
         lib.oracle_hgemm_bias_act(M, N, K, float(alpha), _ptr(A), _ld(A), _ptr(Bt), _ld(Bt),
                                   float(beta), cptr, ldc, cin_dtype, bptr, int(act), _ptr(ref), N)
     return ref
+
+
+def gemm_bf16_bias_act(A: np.ndarray, Bt: np.ndarray, alpha: float = 1.0, beta: float = 0.0,
+                       Cin: np.ndarray | None = None, bias: np.ndarray | None = None,
+                       act: int = ACT_NONE, cin_bf16: bool = False) -> np.ndarray:
+    """fp64 reference of act(α·A·B + β·C_in + bias) with bf16 operands.
+
+    ``A`` (M, K) and ``Bt`` (N, K) are uint16 arrays of bf16 bit patterns in
+    the layouts of ``hgemm``; ``Cin`` (M, N) is float32, or bf16 bit patterns
+    when ``cin_bf16``, read only when ``beta != 0``; ``bias`` a float32
+    vector of length N (None: no bias); ``act`` ACT_NONE or ACT_RELU."""
+    lib = _load()
+    _bf16_2d(A, "A")
+    _bf16_2d(Bt, "Bt")
+    M, K = A.shape
+    N, K2 = Bt.shape
+    if K2 != K:
+        raise ValueError("inner dimensions differ")
+    if act not in (ACT_NONE, ACT_RELU):
+        raise ValueError("act must be ACT_NONE or ACT_RELU")
+    bptr = None
+    if bias is not None:
+        bias = np.ascontiguousarray(bias, dtype=np.float32)
+        if bias.shape != (N,):
+            raise ValueError("bias must have shape (N,)")
+        bptr = _ptr(bias)
+    ref = np.empty((M, N), dtype=np.float64)
+    cin_dtype, cptr, ldc = F32, None, max(1, N)
+    if beta != 0.0:
+        cin_dtype, cptr, ldc = _cin_args(Cin, (M, N), cin_bf16)
+    if M and N:
+        lib.oracle_gemm_bf16_bias_act(M, N, K, float(alpha), _ptr(A), _ld(A), _ptr(Bt), _ld(Bt),
+                                      float(beta), cptr, ldc, cin_dtype, bptr, int(act),
+                                      _ptr(ref), N)
+    return ref
+
+
+def _cin_args(Cin, shape, cin_bf16):
+    """(cin_dtype, pointer, ldc) of an incoming C: fp16, fp32, or bf16 bit
+    patterns (uint16) when ``cin_bf16``."""
+    if Cin is None or Cin.shape != shape or (Cin.size and Cin.strides[1] != Cin.itemsize):
+        raise ValueError("Cin of shape (M, N) with unit column stride needed when beta != 0")
+    if cin_bf16:
+        if Cin.dtype != np.uint16:
+            raise TypeError("bf16 Cin must be uint16 bit patterns")
+        return BF16, _ptr(Cin), _ld(Cin)
+    if Cin.dtype == np.float16:
+        return F16, _ptr(Cin), _ld(Cin)
+    if Cin.dtype == np.float32:
+        return F32, _ptr(Cin), _ld(Cin)
+    raise TypeError("Cin must be float16 or float32 (or bf16 bit patterns with cin_bf16)")
+
+
+def gemm_bias_act_sampled(A: np.ndarray, Bt: np.ndarray, rows: np.ndarray, cols: np.ndarray,
+                          alpha: float = 1.0, beta: float = 0.0, Cin: np.ndarray | None = None,
+                          bias: np.ndarray | None = None, act: int = ACT_NONE,
+                          bf16: bool = False, cin_bf16: bool = False) -> np.ndarray:
+    """act(α·A·B + β·C_in + bias) evaluated only at entries (rows[s], cols[s]).
+
+    ``A``/``Bt`` are fp16 arrays, or uint16 bf16 bit patterns when ``bf16``;
+    ``Cin`` as in ``gemm_bf16_bias_act`` (fp16 or fp32 for fp16 operands)."""
+    lib = _load()
+    if bf16:
+        _bf16_2d(A, "A")
+        _bf16_2d(Bt, "Bt")
+    else:
+        _f16_2d(A, "A")
+        _f16_2d(Bt, "Bt")
+    if A.shape[1] != Bt.shape[1]:
+        raise ValueError("inner dimensions differ")
+    if act not in (ACT_NONE, ACT_RELU):
+        raise ValueError("act must be ACT_NONE or ACT_RELU")
+    N = Bt.shape[0]
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    cols = np.ascontiguousarray(cols, dtype=np.int64)
+    if rows.shape != cols.shape:
+        raise ValueError("rows and cols differ in length")
+    if rows.size and (rows.min() < 0 or rows.max() >= A.shape[0] or
+                      cols.min() < 0 or cols.max() >= N):
+        raise IndexError("sample index out of range")
+    bptr = None
+    if bias is not None:
+        bias = np.ascontiguousarray(bias, dtype=np.float32)
+        if bias.shape != (N,):
+            raise ValueError("bias must have shape (N,)")
+        bptr = _ptr(bias)
+    cin_dtype, cptr, ldc = F16, None, 1
+    if beta != 0.0:
+        cin_dtype, cptr, ldc = _cin_args(Cin, (A.shape[0], N), cin_bf16)
+    ref = np.empty(rows.shape, dtype=np.float64)
+    lib.oracle_gemm_bias_act_sampled(BF16 if bf16 else F16, A.shape[1], float(alpha), _ptr(A), _ld(A),
+                                     _ptr(Bt), _ld(Bt), float(beta), cptr, ldc, cin_dtype, bptr,
+                                     int(act), rows.size, _ptr(rows), _ptr(cols), _ptr(ref))
+    return ref
+
+
+def set_num_threads(n: int) -> None:
+    """Threads the oracle's parallel loops use from now on (n >= 1)."""
+    _load().oracle_set_num_threads(int(n))
 
 
 def hgemm_sampled(A: np.ndarray, Bt: np.ndarray, rows: np.ndarray, cols: np.ndarray,

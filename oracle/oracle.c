@@ -410,3 +410,85 @@ int oracle_num_threads(void)
     }
     return t;
 }
+
+/* ---- Fused bias and activation on bf16 operands ----------------------------
+ * "GPU架构与CUDA", sections 核函数融合 (matmul, bias addition and ReLU as one
+ * operation) and 混合精度核函数 (a 16-bit operand type, a wider sum): the
+ * definition of oracle_hgemm_bias_act with A and B holding bf16 bit
+ * patterns,
+ *   v = α·Σ_k A(i,k)·B(k,j) + β·C_in(i,j) + bias[j],   ref(i,j) = act(v)
+ * bias NULL adds nothing; act 1 is ReLU (v < 0 becomes +0, NaN passes
+ * through); C_in is read only when β != 0 (cin_dtype 1 fp32, 2 bf16).
+ */
+void oracle_gemm_bf16_bias_act(int64_t M, int64_t N, int64_t K, double alpha,
+                               const uint16_t *A, int64_t lda,
+                               const uint16_t *B, int64_t ldb,
+                               double beta, const void *Cin, int64_t ldc, int cin_dtype,
+                               const float *bias, int act, double *ref, int64_t ldr)
+{
+    h2d_init();
+    b2d_init();
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < M; ++i) {
+        for (int64_t j = 0; j < N; ++j) {
+            double dot = 0.0;
+            if (alpha != 0.0) {
+                for (int64_t k = 0; k < K; ++k)
+                    dot += g_b2d[A[i * lda + k]] * g_b2d[B[j * ldb + k]];
+            }
+            double v = alpha * dot;
+            if (beta != 0.0)
+                v += beta * cin_value(Cin, cin_dtype, i * ldc + j);
+            if (bias != NULL)
+                v += (double)bias[j];
+            if (act == 1 && v < 0.0)
+                v = 0.0;
+            ref[i * ldr + j] = v;
+        }
+    }
+}
+
+/* The fused definition above (and oracle_hgemm_bias_act's) at the listed
+ * entries (rows[s], cols[s]) only, for operands of either 16-bit type:
+ * in_dtype 0 = fp16, 2 = bf16.  ref[s] = act(α·Σ_k A(i,k)·B(k,j)
+ * + β·C_in(i,j) + bias[j]) with i = rows[s], j = cols[s]. */
+void oracle_gemm_bias_act_sampled(int in_dtype, int64_t K, double alpha,
+                                  const uint16_t *A, int64_t lda,
+                                  const uint16_t *B, int64_t ldb,
+                                  double beta, const void *Cin, int64_t ldc, int cin_dtype,
+                                  const float *bias, int act, int64_t nsamp,
+                                  const int64_t *rows, const int64_t *cols, double *ref)
+{
+    h2d_init();
+    b2d_init();
+    const double *dec = in_dtype == 2 ? g_b2d : g_h2d;
+#pragma omp parallel for schedule(dynamic, 8)
+    for (int64_t s = 0; s < nsamp; ++s) {
+        const int64_t i = rows[s], j = cols[s];
+        double dot = 0.0;
+        if (alpha != 0.0) {
+            for (int64_t k = 0; k < K; ++k)
+                dot += dec[A[i * lda + k]] * dec[B[j * ldb + k]];
+        }
+        double u = alpha * dot;
+        if (beta != 0.0)
+            u += beta * cin_value(Cin, cin_dtype, i * ldc + j);
+        if (bias != NULL)
+            u += (double)bias[j];
+        if (act == 1 && u < 0.0)
+            u = 0.0;
+        ref[s] = u;
+    }
+}
+
+/* Threads for the parallel loops above (n >= 1); the benchmark times the
+ * oracle on one thread as well as on all of them.  No arithmetic. */
+void oracle_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    extern void omp_set_num_threads(int);
+    omp_set_num_threads(n > 0 ? n : 1);
+#else
+    (void)n;
+#endif
+}

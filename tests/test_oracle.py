@@ -457,6 +457,118 @@ def test_gemm_bf16_sampled_equals_full():
     assert np.array_equal(oracle.gemm_bf16_sampled(A, Bt, ri, cj, 0.75), full[ri, cj])
 
 
+# ---- Fused bias and ReLU on bf16 operands, and the fused definition at
+# sampled entries ("GPU架构与CUDA", 核函数融合 and 混合精度核函数) ----
+
+def _relu(t):
+    return np.where(t < 0, 0.0, t)
+
+
+def test_bf16_bias_act_matches_numpy():
+    rng = np.random.default_rng(53)
+    M, N, K = 12, 10, 37
+    A = workloads.uniform_bf16(rng, (M, K))
+    Bt = workloads.uniform_bf16(rng, (N, K))
+    C32 = rng.uniform(-1, 1, (M, N)).astype(np.float32)
+    C16 = workloads.uniform_bf16(rng, (M, N))
+    bias = rng.uniform(-2, 2, N).astype(np.float32)
+    prod = _bf16_values(A) @ _bf16_values(Bt).T
+    t = 1.25 * prod + 0.5 * C32.astype(np.float64) + bias.astype(np.float64)
+    got = oracle.gemm_bf16_bias_act(A, Bt, 1.25, 0.5, C32, bias, oracle.ACT_RELU)
+    np.testing.assert_allclose(got, _relu(t), rtol=1e-13, atol=1e-13)
+    got = oracle.gemm_bf16_bias_act(A, Bt, 1.25, 0.5, C32, bias, oracle.ACT_NONE)
+    np.testing.assert_allclose(got, t, rtol=1e-13, atol=1e-13)
+    t16 = -prod + 2.0 * _bf16_values(C16) + bias.astype(np.float64)
+    got = oracle.gemm_bf16_bias_act(A, Bt, -1.0, 2.0, C16, bias, oracle.ACT_RELU, cin_bf16=True)
+    np.testing.assert_allclose(got, _relu(t16), rtol=1e-13, atol=1e-13)
+
+
+def test_bf16_bias_act_brute_force_python_loops():
+    rng = np.random.default_rng(54)
+    A16 = workloads.integer_f16(rng, (4, 6))
+    B16 = workloads.integer_f16(rng, (5, 6))
+    A = workloads.to_bf16_bits(A16.astype(np.float32))
+    Bt = workloads.to_bf16_bits(B16.astype(np.float32))
+    bias = np.array([3.5, -7.0, 0.0, 100.0, -100.0], np.float32)
+    got = oracle.gemm_bf16_bias_act(A, Bt, 2.0, 0.0, None, bias, oracle.ACT_RELU)
+    for i in range(4):
+        for j in range(5):
+            t = 2.0 * sum(float(A16[i, k]) * float(B16[j, k]) for k in range(6)) + float(bias[j])
+            assert got[i, j] == (0.0 if t < 0 else t)
+
+
+def test_bf16_bias_act_reduces_to_gemm_bf16():
+    """No bias and no activation is the plain bf16 GEMM (an independent
+    routine), bit for bit."""
+    rng = np.random.default_rng(55)
+    A = workloads.uniform_bf16(rng, (17, 33))
+    Bt = workloads.uniform_bf16(rng, (11, 33))
+    C = rng.uniform(-1, 1, (17, 11)).astype(np.float32)
+    assert np.array_equal(oracle.gemm_bf16_bias_act(A, Bt, 0.75, -1.0, C),
+                          oracle.gemm_bf16(A, Bt, 0.75, -1.0, C))
+
+
+def test_bf16_bias_act_alpha_zero_rows_are_the_bias():
+    """alpha = 0, beta = 0: A and B (NaN) are not read, every row is act(bias)."""
+    A = np.full((3, 4), 0x7fc0, np.uint16)
+    Bt = np.full((6, 4), 0x7fc0, np.uint16)
+    bias = np.array([-1.0, -0.0, 0.0, 1e-30, np.nan, 5.0], np.float32)
+    got = oracle.gemm_bf16_bias_act(A, Bt, 0.0, 0.0, None, bias, oracle.ACT_RELU)
+    expect = np.array([0.0, 0.0, 0.0, np.float32(1e-30), np.nan, 5.0])
+    for row in got:
+        assert np.array_equal(row, expect, equal_nan=True)
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+def test_bias_act_sampled_matches_numpy(bf16):
+    """The sampled fused definition against numpy at the sampled entries,
+    with beta != 0, a bias and ReLU (fp16 C for fp16 operands, bf16 C for
+    bf16 operands)."""
+    rng = np.random.default_rng(56 + bf16)
+    M, N, K = 40, 30, 70
+    if bf16:
+        A = workloads.uniform_bf16(rng, (M, K))
+        Bt = workloads.uniform_bf16(rng, (N, K))
+        C = workloads.uniform_bf16(rng, (M, N))
+        av, bv, cv = _bf16_values(A), _bf16_values(Bt), _bf16_values(C)
+    else:
+        A = workloads.uniform_f16(rng, (M, K))
+        Bt = workloads.uniform_f16(rng, (N, K))
+        C = workloads.uniform_f16(rng, (M, N))
+        av, bv, cv = A.astype(np.float64), Bt.astype(np.float64), C.astype(np.float64)
+    bias = rng.uniform(-2, 2, N).astype(np.float32)
+    ri, cj = workloads.sample_indices(9, M, N, 200)
+    t = -0.75 * (av @ bv.T) + 1.5 * cv + bias.astype(np.float64)[None, :]
+    got = oracle.gemm_bias_act_sampled(A, Bt, ri, cj, -0.75, 1.5, C, bias, oracle.ACT_RELU,
+                                       bf16=bf16, cin_bf16=bf16)
+    np.testing.assert_allclose(got, _relu(t)[ri, cj], rtol=1e-13, atol=1e-13)
+    got = oracle.gemm_bias_act_sampled(A, Bt, ri, cj, -0.75, 1.5, C, bias, oracle.ACT_NONE,
+                                       bf16=bf16, cin_bf16=bf16)
+    np.testing.assert_allclose(got, t[ri, cj], rtol=1e-13, atol=1e-13)
+
+
+def test_bias_act_sampled_equals_full_routines():
+    """Sampled = the full fp16 and bf16 fused routines (each pinned above) at
+    the sampled entries; beta = 0 does not read a NaN C."""
+    rng = np.random.default_rng(58)
+    M, N, K = 33, 45, 50
+    A = workloads.uniform_f16(rng, (M, K))
+    Bt = workloads.uniform_f16(rng, (N, K))
+    C = workloads.uniform_f16(rng, (M, N)).astype(np.float32)
+    bias = rng.uniform(-2, 2, N).astype(np.float32)
+    ri, cj = workloads.sample_indices(3, M, N, 300)
+    full = oracle.hgemm_bias_act(A, Bt, 1.5, 0.5, C, bias, oracle.ACT_RELU)
+    assert np.array_equal(oracle.gemm_bias_act_sampled(A, Bt, ri, cj, 1.5, 0.5, C, bias,
+                                                       oracle.ACT_RELU), full[ri, cj])
+    Ab = workloads.uniform_bf16(rng, (M, K))
+    Bb = workloads.uniform_bf16(rng, (N, K))
+    full = oracle.gemm_bf16_bias_act(Ab, Bb, 2.0, 0.0, None, bias, oracle.ACT_RELU)
+    nanC = np.full((M, N), np.nan, np.float32)
+    got = oracle.gemm_bias_act_sampled(Ab, Bb, ri, cj, 2.0, 0.0, nanC, bias, oracle.ACT_RELU,
+                                       bf16=True)
+    assert np.array_equal(got, full[ri, cj])
+
+
 # ---- TRMM variants: op(A) = A or Aᵀ, A lower or upper ----
 
 @pytest.mark.parametrize("uplo", [oracle.LOWER, oracle.UPPER])

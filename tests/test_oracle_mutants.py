@@ -53,6 +53,23 @@ MUTANTS = {
     "epi_relu_inverted": ("if (act == 1 && t < 0.0)", "if (act == 1 && t > 0.0)"),
     # fused epilogue: bias indexed by row instead of column
     "epi_bias_by_row": ("t += (double)bias[j];", "t += (double)bias[i % N];"),
+    # bf16 fused epilogue: bias dropped
+    "bf16_epi_bias_dropped": ("            if (bias != NULL)\n                v += (double)bias[j];\n", ""),
+    # bf16 fused epilogue: ReLU threshold inverted
+    "bf16_epi_relu_inverted": ("if (act == 1 && v < 0.0)", "if (act == 1 && v > 0.0)"),
+    # bf16 fused epilogue: bias indexed by row instead of column
+    "bf16_epi_bias_by_row": ("v += (double)bias[j];", "v += (double)bias[i % N];"),
+    # bf16 fused epilogue: the beta·C term dropped
+    "bf16_epi_beta_dropped": ("            if (beta != 0.0)\n                v += beta * cin_value(Cin, cin_dtype, i * ldc + j);\n", ""),
+    # sampled fused definition: bias indexed by row instead of column
+    "sampled_epi_bias_by_row": ("u += (double)bias[j];", "u += (double)bias[i % (j + 1)];"),
+    # sampled fused definition: ReLU never applied
+    "sampled_epi_relu_dropped": ("if (act == 1 && u < 0.0)", "if (act == 2 && u < 0.0)"),
+    # sampled fused definition: bf16 operands decoded as fp16
+    "sampled_epi_decoder_swapped": ("const double *dec = in_dtype == 2 ? g_b2d : g_h2d;",
+                                    "const double *dec = g_h2d;"),
+    # sampled fused definition: the beta·C term dropped
+    "sampled_epi_beta_dropped": ("        if (beta != 0.0)\n            u += beta * cin_value(Cin, cin_dtype, i * ldc + j);\n", ""),
     # bf16 decoding: exponent bias off by one
     "bf16_decode_bias": ("v = ldexp((double)(128 + frac), expo - 134);", "v = ldexp((double)(128 + frac), expo - 133);"),
     # bf16 decoding: fraction field one bit short
