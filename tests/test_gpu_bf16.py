@@ -47,6 +47,8 @@ CASES = [
     (1536, 1024, 512, "f32", 0.0),
     (300, 257, 64, "f32", 1.0),
     (200, 130, 33, "bf16", 0.0),
+    (4096, 4096, 512, "bf16", 0.5),     # fast kernel, 16-bit C read (beta != 0)
+    (4133, 4133, 1000, "bf16", 0.5),    # fast kernel, 16-bit C read, ragged edges, K tail
 ]
 
 
@@ -108,10 +110,8 @@ def test_8192_sampled(hg):
 
 
 # ---- bf16 operands with the fused bias and ReLU (hgemm_bf16_bias_act):
-# C = act(alpha·A·B + beta·C + bias) in one launch.  The reference is the
-# oracle's bf16 GEMM, biased and rectified by the definition (t + bias, then
-# t < 0 -> +0), so the bias add and the ReLU are the only arithmetic the test
-# itself does.
+# C = act(alpha·A·B + beta·C + bias) in one launch, against the oracle's
+# fused bf16 definition.
 def run_epi(hg, A, Bt, C0, bias, relu, alpha, beta, out):
     import torch
     dev = torch.device("cuda:0")
@@ -130,11 +130,6 @@ def run_epi(hg, A, Bt, C0, bias, relu, alpha, beta, out):
     return Cd.cpu().numpy().astype(np.float64)
 
 
-def _biased(ref, bias, relu):
-    t = ref + bias.astype(np.float64)[None, :]
-    return np.where(t < 0, 0.0, t) if relu else t
-
-
 @pytest.mark.parametrize("M,N,K,out,beta", CASES)
 @pytest.mark.parametrize("relu", [False, True])
 def test_bias_act_parity(hg, M, N, K, out, beta, relu):
@@ -144,7 +139,8 @@ def test_bias_act_parity(hg, M, N, K, out, beta, relu):
     C0 = workloads.uniform_bf16(rng, (M, N)) if out == "bf16" else rng.uniform(-1, 1, (M, N)).astype(np.float32)
     bias = rng.uniform(-2, 2, N).astype(np.float32)
     got = run_epi(hg, A, Bt, C0, bias, relu, 1.25, beta, out)
-    ref = _biased(oracle.gemm_bf16(A, Bt, 1.25, beta, C0 if beta else None, cin_bf16=(out == "bf16")), bias, relu)
+    ref = oracle.gemm_bf16_bias_act(A, Bt, 1.25, beta, C0 if beta else None, bias,
+                                    oracle.ACT_RELU if relu else oracle.ACT_NONE, cin_bf16=(out == "bf16"))
     check_close(got, ref, K, f"bf16 bias {M}x{N}x{K} {out} relu={relu}",
                 rel=REL_BF16 if out == "bf16" else 2.0 ** -10)
     if relu:
@@ -159,4 +155,4 @@ def test_bias_act_integer_bit_exact(hg, M, N, K):
     C0 = rng.integers(-4, 5, (M, N)).astype(np.float32)
     bias = rng.integers(-40, 41, N).astype(np.float32)
     got = run_epi(hg, A, Bt, C0, bias, True, 1.0, 2.0, "f32")
-    assert np.array_equal(got, _biased(oracle.gemm_bf16(A, Bt, 1.0, 2.0, C0), bias, True))
+    assert np.array_equal(got, oracle.gemm_bf16_bias_act(A, Bt, 1.0, 2.0, C0, bias, oracle.ACT_RELU))

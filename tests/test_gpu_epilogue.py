@@ -49,6 +49,8 @@ CASES = [
     (1536, 1024, 512, "f32", 0.0),      # ring (128x128)
     (300, 257, 64, "f32", 1.0),         # ring, N not a multiple of 4
     (200, 130, 33, "f16", 0.0),         # general path: K not a multiple of 8
+    (4096, 4096, 512, "f16", 0.5),      # fast, 16-bit C read (beta != 0)
+    (4133, 4133, 1000, "f16", 0.5),     # fast, 16-bit C read, ragged edges, K tail
 ]
 
 
@@ -123,8 +125,7 @@ def test_alpha_zero_bias_and_relu(hg):
 
 def test_workload_8192_sampled(hg):
     """The 8192³ shape as the benchmark runs it (fp16 out, bias, ReLU): 1024
-    sampled entries against the oracle's HGEMM at those entries, biased and
-    rectified by the definition."""
+    sampled entries against the oracle's fused definition at those entries."""
     w = workloads.WORKLOADS["hgemm_8192"]
     A, Bt, _ = workloads.gemm_inputs(w)
     rng = np.random.default_rng(w.seed + 7)
@@ -132,6 +133,5 @@ def test_workload_8192_sampled(hg):
     C0 = np.zeros((w.M, w.N), np.float16)
     got = run(hg, A, Bt, C0, bias, True, 1.0, 0.0, "f16")
     ri, cj = workloads.sample_indices(w.seed, w.M, w.N)
-    t = oracle.hgemm_sampled(A, Bt, ri, cj) + bias[cj].astype(np.float64)
-    ref = np.where(t < 0, 0.0, t)
+    ref = oracle.gemm_bias_act_sampled(A, Bt, ri, cj, 1.0, 0.0, None, bias, oracle.ACT_RELU)
     check_close(got[ri, cj], ref, w.K, "bias_act 8192 sampled")
