@@ -9,9 +9,11 @@ One step = one pass over the whole path on resident synthetic inputs:
 Prints one JSON line.  `value` is the HGEMM throughput in TFLOP/s (2·M·N·K per
 call over the average HGEMM kernel time, measured with HIP events on the
 stream the kernels run on); the TRMM time per call is reported next to it.
-`roofline` prices the HGEMM kernel against the dense fp16 MFMA peak;
-`cpu_baseline` times the fp64 oracle on a bounded row block of the same
-HGEMM on this host's cores.
+`roofline` prices the HGEMM kernel and `trmm_roofline` the one-launch TRMM
+against the dense fp16 MFMA peak; `cpu_baseline` times the fp64 oracle on a
+bounded row block of the same HGEMM on this host's cores, and `check` holds
+the oracle's verdict on 1024 sampled entries of each timed output;
+`inputs_sha256` identifies the inputs.
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 100] [--no-cpu-baseline]
 
@@ -46,24 +48,80 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def traffic_from_profiles(src_hash):
-    """HBM bytes per HGEMM launch from the committed rocprofv3 counter runs,
-    if they were taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", "hgemm_8192_traffic.json")
+def profile_record(name, src_hash):
+    """A committed counter summary (profiles/<name>.json: HBM bytes per launch,
+    shader clock), if it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", name + ".json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         d = json.load(f)
     if d.get("kernel_source_sha256_16") != src_hash:
         return None
-    return d.get("hbm_bytes_per_launch")
+    return d
+
+
+def trmm_phase_bound_us(n, m, leaf, peak_tflops=PEAK_FP16_TFLOPS, hbm_gbs=PEAK_HBM_GBS):
+    """Roofline of the recursion scheduled level by level: all leaves, then
+    one batched GEMM (beta = 1, fp32 Out read and written) per level.  Each
+    phase costs max(flops / MFMA peak, bytes / HBM bandwidth); returns the
+    sum over phases in microseconds and the per-phase list."""
+    phases = []
+    leaves, levels = [], {}
+
+    def rec(o, s_, depth):
+        if s_ <= leaf:
+            leaves.append(s_)
+            return
+        h = s_ // 2
+        rec(o, h, depth + 1)
+        levels.setdefault(depth, []).append((h, s_ - h))
+        rec(o + h, s_ - h, depth + 1)
+    rec(0, n, 0)
+    # leaves: the triangle times B, B read (fp16), Out written (fp32), A's
+    # diagonal blocks read (fp16)
+    f = sum(L * (L + 1) * m for L in leaves)
+    b = 2 * n * m + 4 * n * m + sum(2 * L * L for L in leaves)
+    phases.append(("leaves", f, b))
+    for d in sorted(levels, reverse=True):
+        f = sum(2.0 * m * h * k for h, k in levels[d])
+        # A21 (k×h fp16), B2 (k×m fp16), Out1 (h×m fp32) read and written
+        b = sum(2 * h * k + 2 * k * m + 8 * h * m for h, k in levels[d])
+        phases.append((f"level {d}", f, b))
+    out = []
+    for name, f, b in phases:
+        t = max(f / (peak_tflops * 1e12), b / (hbm_gbs * 1e9)) * 1e6
+        out.append({"phase": name, "flops": f, "bytes": b, "bound_us": round(t, 2)})
+    return sum(p["bound_us"] for p in out), out
+
+
+PROBE_SRC = os.path.join(ROOT, "mfma_ceiling.cpp")
+PROBE_BIN = os.path.join(ROOT, "mfma_ceiling")
+
+
+def build_probe(verbose=False):
+    """Compile the MFMA-only ceiling probe (mfma_ceiling.cpp, a measurement
+    tool of this benchmark, not part of the library) for gfx950."""
+    import subprocess
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    tmp = PROBE_BIN + ".tmp%d" % os.getpid()
+    cmd = [hipcc, "--offload-arch=gfx950", "-O3", "-std=c++17",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-o", tmp, PROBE_SRC]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError("hipcc failed building mfma_ceiling")
+    os.replace(tmp, PROBE_BIN)
+    return PROBE_BIN
 
 
 def mfma_ceiling():
     """Run the MFMA-only ceiling probe (register-resident fp16 operands drawn
     like the benchmark's); None if it is not built or fails."""
     import subprocess
-    exe = os.path.join(ROOT, "half_precision_gemm_amd", "mfma_ceiling")
+    exe = PROBE_BIN
     if not os.path.exists(exe):
         return None
     try:
@@ -171,6 +229,14 @@ def config_sweep(hg, stream, main_gemm_ms=None, main_trmm_ms=None, only=None):
                 dt = time.perf_counter() - t0
                 r["oracle"] = {"seconds": round(dt, 4), "entries": w.M * w.N, "mode": "full",
                                "cores": oracle.num_threads()}
+                if w.M * w.N <= 256 * 256:
+                    # the same on one thread
+                    nt = oracle.num_threads()
+                    oracle.set_num_threads(1)
+                    t0 = time.perf_counter()
+                    oracle.hgemm(A, Bt, w.alpha, w.beta, C)
+                    r["oracle"]["seconds_one_thread"] = round(time.perf_counter() - t0, 4)
+                    oracle.set_num_threads(nt)
             else:
                 ri, cj = workloads.sample_indices(w.seed, w.M, w.N)
                 oracle.hgemm_sampled(A, Bt, ri, cj, w.alpha, w.beta, C)
@@ -179,9 +245,12 @@ def config_sweep(hg, stream, main_gemm_ms=None, main_trmm_ms=None, only=None):
                                "us_per_entry": round(dt / ri.size * 1e6, 2), "cores": oracle.num_threads()}
         else:
             if main_trmm_ms is not None:
+                tf = w.flops / (main_trmm_ms * 1e-3) / 1e12
                 r.update({"gpu_ms_avg": round(main_trmm_ms, 5), "from": "the benchmark's timed steps",
-                          "effective_tflops": round(w.flops / (main_trmm_ms * 1e-3) / 1e12, 2),
-                          "pct_of_342us_phase_bound": round(100 * 0.342 / main_trmm_ms, 1)})
+                          "schedule": "one launch (updates accumulated in registers)",
+                          "effective_tflops": round(tf, 2),
+                          "pct_of_fp16_mfma_peak": round(100 * tf / PEAK_FP16_TFLOPS, 2),
+                          "mfma_bound_us": round(w.flops / (PEAK_FP16_TFLOPS * 1e12) * 1e6, 1)})
             TA, TB = workloads.trmm_inputs(w)
             ri, cj = workloads.sample_indices(w.seed, w.n, w.m)
             t0 = time.perf_counter()
@@ -264,6 +333,27 @@ def config_sweep(hg, stream, main_gemm_ms=None, main_trmm_ms=None, only=None):
             "note": "B given K x N row-major: one tiled transpose (128 MiB read + written) into the "
                     "workspace, then the K-contiguous GEMM"}
         del Ad, Brd, Cd, work, A, Bt
+    if want("trmm_8192_by_level"):
+        # The recursion scheduled as the page describes it: one batched launch
+        # for the 32 leaves, then one batched beta = 1 GEMM launch per level,
+        # deepest first (Out read and written in fp32 at every level); priced
+        # against that schedule's per-phase roofline.
+        print("[bench] config trmm_8192_by_level ...", file=sys.stderr, flush=True)
+        w = workloads.WORKLOADS["trmm_8192"]
+        TA, TB = workloads.trmm_inputs(w)
+        Ad, Bd = torch.from_numpy(TA).to(dev), torch.from_numpy(TB).to(dev)
+        Od = torch.empty((w.m, w.n), dtype=torch.float32, device=dev)
+        ts = _time_calls(lambda: hg.trmm_lower_trans_by_level(Ad, Bd, Od, w.alpha, w.leaf), 5, 20, stream)
+        bound_us, phases = trmm_phase_bound_us(w.n, w.m, w.leaf)
+        res["trmm_8192_by_level"] = {
+            "gpu_ms_median": round(ts[0], 5), "gpu_ms_min": round(ts[1], 5),
+            "effective_tflops": round(w.flops / (ts[0] * 1e-3) / 1e12, 2),
+            "phase_bound_us": round(bound_us, 1),
+            "pct_of_phase_bound": round(100 * bound_us * 1e-3 / ts[0], 1),
+            "phases": phases,
+            "note": "leaves in one launch, then one beta = 1 GEMM launch per recursion level; "
+                    "each phase bounded by max(flops / 2516.6 TFLOP/s, bytes / 8 TB/s)"}
+        del Ad, Bd, Od, TA, TB
     if want("trmm_4096x256"):
         # Skinny right-hand side (next row): the TRMM page's usage example,
         # n = 4096, m = 256.
@@ -417,12 +507,14 @@ def main():
     wg = workloads.WORKLOADS["hgemm_8192"]
     wt = workloads.WORKLOADS["trmm_8192"]
     A, Bt, _ = workloads.gemm_inputs(wg)
+    inputs = {"hgemm_8192": {"A": workloads.sha256(A), "Bt": workloads.sha256(Bt)}}
     Ad = torch.from_numpy(A).to(dev)
     Btd = torch.from_numpy(Bt).to(dev)
     Cd = torch.empty((wg.M, wg.N), dtype=torch.float32, device=dev)
     do_trmm = not args.no_trmm
     if do_trmm:
         TA, TB = workloads.trmm_inputs(wt)
+        inputs["trmm_8192"] = {"A_cm": workloads.sha256(TA), "B_cm": workloads.sha256(TB)}
         TAd = torch.from_numpy(TA).to(dev)
         TBd = torch.from_numpy(TB).to(dev)
         del TA, TB
@@ -471,7 +563,28 @@ def main():
     print(f"[bench] timed {args.steps} steps: hgemm avg {gemm_avg:.4f} ms "
           f"(min {min(gemm_ms):.4f}), {tflops:.1f} TFLOP/s", file=sys.stderr, flush=True)
 
+    # The timed outputs at the 1024 sampled entries of each workload (the
+    # oracle checks them after the sweep, in the CPU-baseline leg).
+    ri_g, cj_g = workloads.sample_indices(wg.seed, wg.M, wg.N)
+    gemm_samples = Cd[torch.from_numpy(ri_g).to(dev), torch.from_numpy(cj_g).to(dev)].cpu().numpy()
+    if do_trmm:
+        ri_t, cj_t = workloads.sample_indices(wt.seed, wt.n, wt.m)
+        # Out(i, j) of the column-major n×m output sits at TOut[j, i]
+        trmm_samples = TOut[torch.from_numpy(cj_t).to(dev), torch.from_numpy(ri_t).to(dev)].cpu().numpy()
+
     src_hash = kernel_source_hash()
+    prof_g = profile_record("hgemm_8192_traffic", src_hash) or {}
+    prof_t = profile_record("trmm_8192_traffic", src_hash) or {}
+
+    def clock_fields(prof, achieved):
+        # shader clock from SQ_BUSY_CYCLES over the kernel's duration in the
+        # counter run, and the peak at that clock (256 CU × 4096 flop/clk)
+        ghz = prof.get("shader_clock_ghz")
+        if not ghz:
+            return {"shader_clock_ghz": None, "frac_of_peak_at_that_clock": None}
+        return {"shader_clock_ghz": ghz,
+                "frac_of_peak_at_that_clock": round(achieved / (256 * 4096 * ghz * 1e-3), 4)}
+
     out = {
         "metric": "HGEMM TFLOP/s + % of MI355X FP16 MFMA peak at 8192^3; TRMM ms at n=8192",
         "value": round(tflops, 2),
@@ -496,16 +609,31 @@ def main():
                      "max": round(max(gemm_ms), 4)},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_FP16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_FP16_TFLOPS, 4),
-                     "traffic": traffic_from_profiles(src_hash),
+                     "traffic": prof_g.get("hbm_bytes_per_launch"),
                      "kernel": "hgemm_fast_kernel (256x256 tile, 4 waves, v_mfma_f32_16x16x32_f16, 64-wide K stages) at M=N=K=8192, fp32 out",
-                     "algorithmic_flops_per_launch": wg.flops},
+                     "algorithmic_flops_per_launch": wg.flops,
+                     "algorithmic_bytes_per_launch": 2 * (wg.M * wg.K + wg.N * wg.K) + 4 * wg.M * wg.N,
+                     **clock_fields(prof_g, tflops)},
         "kernel_source_sha256_16": src_hash,
     }
     if do_trmm:
         tavg = sum(trmm_ms) / len(trmm_ms)
+        ttf = wt.flops / (tavg * 1e-3) / 1e12
         out["trmm_ms"] = {"avg": round(tavg, 4), "min": round(min(trmm_ms), 4),
                           "max": round(max(trmm_ms), 4)}
-        out["trmm_effective_tflops"] = round(wt.flops / (tavg * 1e-3) / 1e12, 2)
+        out["trmm_effective_tflops"] = round(ttf, 2)
+        # The one-launch TRMM is MFMA-bound: n(n+1)m useful flops against
+        # 0.47 GB compulsory traffic (A's lower triangle, B, Out in fp32).
+        out["trmm_roofline"] = {
+            "bound": "mfma", "achieved": round(ttf, 2), "peak": PEAK_FP16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(ttf / PEAK_FP16_TFLOPS, 4),
+            "bound_ms": round(wt.flops / (PEAK_FP16_TFLOPS * 1e12) * 1e3, 4),
+            "traffic": prof_t.get("hbm_bytes_per_launch"),
+            "kernel": "hgemm_fast_kernel, one-launch recursive TRMM (each 256x256 output tile walks its "
+                      "leaf and its updates in recursion order), n = m = 8192, leaf 256, fp32 out",
+            "algorithmic_flops_per_launch": wt.flops,
+            "algorithmic_bytes_per_launch": wt.n * (wt.n + 1) + 2 * wt.n * wt.m + 4 * wt.n * wt.m,
+            **clock_fields(prof_t, ttf)}
     if not args.no_configs:
         out["configs"] = config_sweep(hg, stream, gemm_avg, only=args.config, main_trmm_ms=
                                       (sum(trmm_ms) / len(trmm_ms)) if do_trmm else None)
@@ -514,6 +642,32 @@ def main():
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle) ...", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(A, Bt)
+        # The oracle on the sampled entries of what the timed steps computed.
+        import oracle
+        from tests.tolerance import bound
+        chk = {}
+        ref = oracle.hgemm_sampled(A, Bt, ri_g, cj_g, wg.alpha, wg.beta)
+        err = np.abs(gemm_samples.astype(np.float64) - ref)
+        chk["hgemm_8192"] = {"entries": int(ri_g.size), "max_abs_err": float(np.nanmax(err)),
+                             "max_err_over_tolerance": float(np.nanmax(err / bound(wg.K, ref))),
+                             "pass": bool((err <= bound(wg.K, ref)).all())}
+        if do_trmm:
+            TA, TB = workloads.trmm_inputs(wt)
+            ref = oracle.trmm_lower_trans_sampled(TA, TB, ri_t, cj_t, wt.alpha)
+            err = np.abs(trmm_samples.astype(np.float64) - ref)
+            chk["trmm_8192"] = {"entries": int(ri_t.size), "max_abs_err": float(np.nanmax(err)),
+                                "max_err_over_tolerance": float(np.nanmax(err / bound(wt.n, ref))),
+                                "pass": bool((err <= bound(wt.n, ref)).all())}
+            del TA, TB
+        chk["rule"] = "|gpu - oracle| <= 1e-3*sqrt(K) + 2^-10*|oracle| (K = n for the TRMM)"
+        out["check"] = chk
+    golden = os.path.join(ROOT, "tests", "golden", "input_sha256.json")
+    if os.path.exists(golden):
+        with open(golden) as f:
+            g = json.load(f)
+        inputs["match_pinned_hashes"] = all(g.get(k, {}).get(a) == h for k, v in inputs.items()
+                                            if isinstance(v, dict) for a, h in v.items())
+    out["inputs_sha256"] = inputs
     print(json.dumps(out), flush=True)
 
 

@@ -26,25 +26,6 @@ FLAGS = [
 ]
 
 
-CEILING_SRC = os.path.join(CSRC, "mfma_ceiling.cpp")
-CEILING_BIN = os.path.join(PKG, "mfma_ceiling")
-
-
-def build_ceiling(verbose=False):
-    """The MFMA throughput-ceiling probe (a small standalone program)."""
-    tmp = CEILING_BIN + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17",
-           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-o", tmp, CEILING_SRC]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        sys.stderr.write(r.stdout + r.stderr)
-        raise RuntimeError("hipcc failed building mfma_ceiling")
-    os.replace(tmp, CEILING_BIN)
-    return CEILING_BIN
-
-
 def build(extra=(), out=LIB, verbose=False):
     tmp = out + ".tmp%d" % os.getpid()
     cmd = [HIPCC] + FLAGS + list(extra) + ["-o", tmp] + SOURCES
@@ -60,4 +41,3 @@ def build(extra=(), out=LIB, verbose=False):
 
 if __name__ == "__main__":
     print(build(verbose=True))
-    print(build_ceiling(verbose=True))

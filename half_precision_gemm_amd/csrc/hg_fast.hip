@@ -44,6 +44,7 @@
 // tiles resident on one XCD share A row panels and B column panels.
 #include "hg_internal.h"
 
+#include <atomic>
 #include <type_traits>
 #include <utility>
 
@@ -737,21 +738,23 @@ hgemm_fast_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int c
     }
 }
 
-// Persistent grid size: one workgroup per CU (the 128 KiB ring allows one).
+// Persistent grid size: one workgroup per CU (the 160 KiB ring allows one).
+// The count is cached per device; concurrent first calls may both query it
+// and store the same value (relaxed atomics: no data race).
 int cu_count()
 {
-    static int cached[64] = {0};
+    static std::atomic<int> cached[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
         return 256;
-    if (cached[dev] == 0) {
-        int n = 0;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
         if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
             n <= 0)
             n = 256;
-        cached[dev] = n;
+        cached[dev].store(n, std::memory_order_relaxed);
     }
-    return cached[dev];
+    return n;
 }
 
 template <bool OUT_F16, bool BETA, bool TRI, bool EPI, bool IN_BF16 = false>

@@ -15,8 +15,15 @@
  *                     the recursive 2×2 blocking of
  *                     "异构计算中高性能TRMM与TRSM的递归算法实现" §2.1–§2.2:
  *                     split at n/2 until a block is at most `leaf`, leaf blocks
- *                     by a triangle-masked kernel, and every A21ᵀ·B2 update by
- *                     the GEMM kernel of hgemm with beta = 1.
+ *                     by the triangle-masked GEMM kernel, and the A21ᵀ·B2
+ *                     updates by hgemm's GEMM kernel.  By default (aligned
+ *                     operands, recursion boundaries on 256-column tile edges)
+ *                     the whole recursion is one launch: each output tile
+ *                     walks its leaf and then its updates in recursion order
+ *                     and adds the updates in its fp32 accumulators.
+ *                     hg_trmm_lower_trans_by_level runs the page's schedule
+ *                     literally: one launch for the leaves, then one GEMM
+ *                     launch with beta = 1 per recursion level.
  *
  *   trsm_lower_trans  X = alpha·A⁻ᵀ·B with A lower triangular: the triangular
  *                     solve of the same page, §2.3, by the same recursion
@@ -28,9 +35,11 @@
  * All matrix pointers are DEVICE pointers on the current HIP device.  Calls
  * are asynchronous on `stream` (a hipStream_t; NULL = the default stream);
  * results are valid once the stream has been synchronised.  The library
- * allocates nothing, never copies between host and device, keeps no state
- * and is thread-safe.  The caller owns every buffer, including the device
- * workspace trsm_lower_trans takes.
+ * allocates no memory, never copies between host and device and keeps no
+ * state beyond a per-device cache of the compute-unit count (atomic), so
+ * calls from several host threads are safe; hg_trmm_lower_trans_streams
+ * creates and destroys HIP events within each call.  The caller owns every
+ * buffer, including the device workspaces some entry points take.
  *
  * Return value: 0 on success.  A negative value -i means argument i (1-based,
  * in the order of the prototype) is invalid, following the BLAS xerbla
