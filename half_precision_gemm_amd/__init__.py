@@ -28,6 +28,10 @@ importing this package raises.
         hgemm with K cut into slices run side by side (few output tiles,
         long K); partial products summed in order in fp32.
 
+    hgemm_splitk_noalloc(A, Bt, C, alpha=1.0, beta=0.0, splits=0)
+        the same with the partials in the library's static device array (no
+        workspace, nothing allocated; calls overlapping on one GPU race).
+
     trmm(A, B, Out, alpha=1.0, uplo="L", trans=True, leaf=256, work=None)
         Out = alpha·op(A)·B for every triangle / transposition.
 
@@ -101,6 +105,9 @@ lib.hgemm_bf16_bias_act.restype = _int
 lib.hgemm_splitk.argtypes = [_i64, _i64, _i64, _f32, _vp, _i64, _vp, _i64, _f32, _vp, _i64, _int, _int, _vp,
                              _i64, _vp]
 lib.hgemm_splitk.restype = _int
+lib.hgemm_splitk_noalloc.argtypes = [_i64, _i64, _i64, _f32, _vp, _i64, _vp, _i64, _f32, _vp, _i64, _int,
+                                     _int, _vp]
+lib.hgemm_splitk_noalloc.restype = _int
 lib.hg_hgemm_splitk_workspace_size.argtypes = [_i64, _i64, _i64, _int]
 lib.hg_hgemm_splitk_workspace_size.restype = _i64
 lib.hg_trmm_inplace.argtypes = [_int, _int, _i64, _i64, _f32, _vp, _i64, _vp, _i64, _i64, _vp, _i64,
@@ -128,7 +135,7 @@ EXPORTS = ("hgemm", "hgemm_bias_act", "hgemm_bf16", "trmm_lower_trans", "hg_trmm
            "hg_trmm_workspace_size", "hgemm_layout", "hg_hgemm_layout_workspace_size",
            "hg_trmm_inplace", "hg_trmm_inplace_workspace_size", "hgemm_splitk", "hgemm_bf16_bias_act",
            "hg_trmm_lower_trans_streams",
-           "hg_hgemm_splitk_workspace_size")
+           "hg_hgemm_splitk_workspace_size", "hgemm_splitk_noalloc")
 
 ROW_MAJOR = 0
 COL_MAJOR = 1
@@ -217,6 +224,32 @@ def hgemm_splitk(A, Bt, C, alpha: float = 1.0, beta: float = 0.0, splits: int = 
     if st != 0:
         raise HgError("hgemm_splitk", st)
     return C
+
+
+def hgemm_splitk_noalloc(A, Bt, C, alpha: float = 1.0, beta: float = 0.0, splits: int = 0):
+    """hgemm_splitk with its fp32 partials in the library's static device
+    array (HG_NOALLOC_SCRATCH_BYTES per GPU): no workspace, nothing allocated.
+    Calls that overlap on one GPU race on that array.  Returns C."""
+    import torch
+    _check_matrix(A, "A", (torch.float16,))
+    _check_matrix(Bt, "Bt", (torch.float16,))
+    _check_matrix(C, "C", (torch.float16, torch.float32))
+    M, K = A.shape
+    N = Bt.shape[0]
+    if Bt.shape[1] != K or tuple(C.shape) != (M, N):
+        raise ValueError(f"shape mismatch: A {tuple(A.shape)}, Bt {tuple(Bt.shape)}, "
+                         f"C {tuple(C.shape)}")
+    out_dtype = HG_F16 if C.dtype == torch.float16 else HG_F32
+    st = lib.hgemm_splitk_noalloc(M, N, K, float(alpha), A.data_ptr() or None, _ld(A),
+                                  Bt.data_ptr() or None, _ld(Bt), float(beta), C.data_ptr() or None,
+                                  _ld(C), out_dtype, int(splits), _stream_handle(C))
+    if st != 0:
+        raise HgError("hgemm_splitk_noalloc", st)
+    return C
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20
+ERR_SCRATCH_LIMIT = -100
 
 
 def splitk_workspace_size(M: int, N: int, K: int, splits: int = 0) -> int:

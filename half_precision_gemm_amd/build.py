@@ -15,7 +15,8 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libhgemm.so")
 SOURCES = [os.path.join(CSRC, "hg_api.cpp"), os.path.join(CSRC, "hg_kernels.hip"),
            os.path.join(CSRC, "hg_fast.hip"), os.path.join(CSRC, "hg_ring.hip"),
-           os.path.join(CSRC, "hg_trsm.hip"), os.path.join(CSRC, "hg_xform.hip")]
+           os.path.join(CSRC, "hg_trsm.hip"), os.path.join(CSRC, "hg_xform.hip"),
+           os.path.join(CSRC, "hg_noalloc.hip")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

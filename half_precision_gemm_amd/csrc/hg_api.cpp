@@ -96,6 +96,8 @@ const char *hg_strerror(int status)
     case -15: return "invalid argument 15";
     case -16: return "invalid argument 16";
     case -17: return "invalid argument 17";
+    case HG_ERR_SCRATCH_LIMIT:
+        return "problem needs more scratch than the static array holds (HG_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
     }
 }

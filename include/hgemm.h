@@ -302,6 +302,34 @@ int hgemm_splitk(int64_t M, int64_t N, int64_t K, float alpha,
  * splits outside 0..32. */
 int64_t hg_hgemm_splitk_workspace_size(int64_t M, int64_t N, int64_t K, int splits);
 
+/*
+ * hgemm_splitk_noalloc — hgemm_splitk without a workspace argument, for
+ * callers that cannot allocate device memory or pass a workspace (code under
+ * stream capture, tight serving loops, harnesses that forbid allocation).
+ *
+ *  1..13          : as hgemm_splitk (splits 0..32; 0 picks the slice count).
+ * 14 stream       : hipStream_t.
+ *
+ * The fp32 partial products go to a static device array of the library,
+ * HG_NOALLOC_SCRATCH_BYTES (32 MiB) per GPU, which each GPU the library runs
+ * on holds until the process ends; the call allocates nothing.  A problem
+ * whose partials need more (hg_hgemm_splitk_workspace_size(M, N, K, splits)
+ * > HG_NOALLOC_SCRATCH_BYTES) is rejected with HG_ERR_SCRATCH_LIMIT before
+ * anything is launched; other arguments are checked as by hgemm_splitk, with
+ * its codes.  The result is hgemm_splitk's, bit for bit.  Every call on one
+ * GPU uses the same array: calls that overlap in time on one GPU (on
+ * different streams, or from different host threads without ordering) race
+ * on it and give undefined results; calls on one stream are ordered and safe.
+ * The partials are written in full by each call before they are read, so no
+ * state carries over from the previous call.
+ */
+#define HG_NOALLOC_SCRATCH_BYTES (32 << 20)
+#define HG_ERR_SCRATCH_LIMIT (-100)
+int hgemm_splitk_noalloc(int64_t M, int64_t N, int64_t K, float alpha,
+                         const void *A, int64_t lda, const void *B, int64_t ldb,
+                         float beta, void *C, int64_t ldc, int out_dtype, int splits,
+                         void *stream);
+
 /* hg_trmm_workspace_size — bytes of workspace hg_trmm needs (host only);
  * -1/-2 for a bad uplo/trans, -3/-4 for n/m < 0. */
 int64_t hg_trmm_workspace_size(int uplo, int trans, int64_t n, int64_t m);

@@ -36,7 +36,7 @@ def test_header_declares_the_entry_points():
                                     "hg_trmm_plan",
                                     "hg_trmm_workspace_size", "hg_trsm_workspace_size", "hgemm",
                                     "hgemm_bf16", "hgemm_bf16_bias_act", "hgemm_bias_act", "hgemm_layout",
-                                    "hgemm_splitk",
+                                    "hgemm_splitk", "hgemm_splitk_noalloc",
                                     "trmm_lower_trans", "trsm_lower_trans"]
 
 
