@@ -309,36 +309,78 @@ __device__ __forceinline__ bool find_tile(const GemmParams &p, int &id, int stri
 // update, is applied once when the tile is written.  The level-by-level
 // launches keep the store between updates.
 
-// Work item of workgroup w in round r: output tile q = r·G + w (r even) or
-// r·G + G-1-w (r odd) of the tiles ordered by column, so that the columns
-// with the most K work run first and the rounds of every workgroup add up
-// to about the same work (a tile's work falls linearly with its column;
-// with tri_up it rises, and the columns are taken from the last).
-// False once q is past the end.
-__device__ __forceinline__ bool fused_item(const GemmParams &p, int w, int G, int round, int total,
-                                           int tiles_m, TileInfo &T)
+// Order of the tiles.  Tile column tn (of T = n/256) walks T - tn K blocks
+// of 256 (tri_up: tn + 1), so columns c and T-1-c together always walk T + 1:
+// a job is the pair of tiles (tm, T-1-c) then (tm, c) of one tile row, and
+// every job has the same length.  Jobs are dealt to the persistent
+// workgroups one per round, so all workgroups start each round together;
+// those of one XCD take a block of HG_TRMM_BAND tile rows × the pair columns
+// that the XCD's share of a round covers (ids regrouped per XCD, then bands
+// of rows walked pair column by pair column, as for the GEMM's tiles).
+// Counting time t in K blocks from the start of a round:
+//   lower (not tri_up): the short tile (tm, T-1-c) takes c + 1 blocks; the
+//   long tile (tm, c) then starts at t = c + 1 at K block c, so it is at K
+//   block t - 1 at time t whatever c is;
+//   tri_up: the long tile (tm, T-1-c) starts at t = 0 at K block 0 and is at
+//   K block t, whatever c is; the short tile (tm, c) follows.
+// The long tiles of co-resident jobs thus read the same K slabs of the
+// right-hand side at the same time and share them in L2, as the tiles of a
+// GEMM do; only the short tiles (a quarter of the work at n = 8192) are
+// staggered.  With T odd, the middle column's tiles pair up by rows (a
+// last odd row is a job of one tile).  Each tile still walks its own K
+// range in recursion order.
+#ifndef HG_TRMM_BAND
+#define HG_TRMM_BAND 4
+#endif
+
+// The tile of item `it` (job it/2, its first or second tile) of workgroup
+// w, or the next item that has one (it is advanced past missing second
+// tiles); false once the workgroup's jobs are done.
+__device__ __forceinline__ bool fused_item(const GemmParams &p, int w, int G, int &it, int tiles_m,
+                                           int tiles_n, TileInfo &T)
 {
-    const int q = round * G + ((round & 1) ? G - 1 - w : w);
-    if (q >= total)
-        return false;
-    const int tm = q % tiles_m;
-    const int tn = p.tri_up ? (total / tiles_m) - 1 - q / tiles_m : q / tiles_m;
-    const int N = p.e[0].N, K = p.e[0].K;
-    const int m0 = tm * BM, n0 = tn * BN;
-    T.batch = 0;
-    T.m0 = m0;
-    T.n0 = n0;
-    T.N = N;
-    T.K = K;
-    T.rows_a = min(p.M - m0, BM);
-    T.rows_b = min(N - n0, BN);
-    T.kt0 = p.tri_up ? 0 : n0 / BK;
-    T.nk = p.tri_up ? (n0 + BN) / BK : (K - n0) / BK;
-    const _Float16 *Ab = p.A + (int64_t)m0 * p.lda;
-    const _Float16 *Bb = p.B + (int64_t)n0 * p.ldb;
-    T.ra = make_rsrc(Ab, (uint32_t)(((int64_t)(T.rows_a - 1) * p.lda + K) * 2));
-    T.rb = make_rsrc(Bb, (uint32_t)(((int64_t)(T.rows_b - 1) * p.ldb + K) * 2));
-    return true;
+    const int P = tiles_n >> 1;                         // pair columns
+    const int Jp = tiles_m * P;                         // pair jobs
+    const int J = Jp + ((tiles_n & 1) ? (tiles_m + 1) >> 1 : 0);
+    constexpr int R = HG_TRMM_BAND;
+    for (;; ++it) {
+        const int id = w + (it >> 1) * G, second = it & 1;
+        if (id >= J)
+            return false;
+        const int per = J >> 3, rem = J & 7, x = id & 7;
+        const int q = x * per + min(x, rem) + (id >> 3);
+        int tm, tn;
+        if (q < Jp) {
+            const int band = q / (R * P);
+            const int first = band * R;
+            const int gsz = min(tiles_m - first, R);
+            const int r = q - band * R * P;
+            tm = first + r % gsz;
+            const int c = r / gsz;
+            tn = second ? c : tiles_n - 1 - c;
+        } else {
+            tm = 2 * (q - Jp) + second;
+            if (tm >= tiles_m)
+                continue;                               // a job of one tile
+            tn = P;                                     // the middle column
+        }
+        const int N = p.e[0].N, K = p.e[0].K;
+        const int m0 = tm * BM, n0 = tn * BN;
+        T.batch = 0;
+        T.m0 = m0;
+        T.n0 = n0;
+        T.N = N;
+        T.K = K;
+        T.rows_a = min(p.M - m0, BM);
+        T.rows_b = min(N - n0, BN);
+        T.kt0 = p.tri_up ? 0 : n0 / BK;
+        T.nk = p.tri_up ? (n0 + BN) / BK : (K - n0) / BK;
+        const _Float16 *Ab = p.A + (int64_t)m0 * p.lda;
+        const _Float16 *Bb = p.B + (int64_t)n0 * p.ldb;
+        T.ra = make_rsrc(Ab, (uint32_t)(((int64_t)(T.rows_a - 1) * p.lda + K) * 2));
+        T.rb = make_rsrc(Bb, (uint32_t)(((int64_t)(T.rows_b - 1) * p.ldb + K) * 2));
+        return true;
+    }
 }
 
 template <bool OUT_F16, bool BETA, bool TRI, bool KCHK, bool FUSED, bool EPI, bool IN_BF16>
@@ -364,18 +406,19 @@ hgemm_fast_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int c
     auto set_offsets = [&](const TileInfo &T) {
 #pragma unroll
         for (int i = 0; i < LPS; ++i) {
+            // swz() XORs the chunk index, so it is its own inverse
             const int row = wave * RPW + i * RPI + lane / KC;
-            int kc = 0;
-#pragma unroll
-            for (int c = 0; c < KC; ++c)
-                kc = swz(row, c) == lane % KC ? c : kc;
-            lkc[i] = kc;
+            lkc[i] = swz(row, lane % KC);
         }
+        // row r of the wave's share: byte offset r·ld·2, stepping by RPI rows
+        const int row0 = wave * RPW + lane / KC;
+        const uint32_t a0 = (uint32_t)(row0 * (int)p.lda * 2), sa = (uint32_t)(RPI * (int)p.lda * 2);
+        const uint32_t b0 = (uint32_t)(row0 * (int)p.ldb * 2), sb = (uint32_t)(RPI * (int)p.ldb * 2);
 #pragma unroll
         for (int i = 0; i < LPS; ++i) {
-            const int row = wave * RPW + i * RPI + lane / KC;
-            aoff[i] = row < T.rows_a ? (uint32_t)(row * (int)p.lda * 2 + lkc[i] * 16) : OOB;
-            boff[i] = row < T.rows_b ? (uint32_t)(row * (int)p.ldb * 2 + lkc[i] * 16) : OOB;
+            const int row = row0 + i * RPI;
+            aoff[i] = row < T.rows_a ? a0 + i * sa + lkc[i] * 16 : OOB;
+            boff[i] = row < T.rows_b ? b0 + i * sb + lkc[i] * 16 : OOB;
         }
     };
     // Load i of operand `isb` (A or B) of stage kt into that operand's ring
@@ -432,44 +475,54 @@ hgemm_fast_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int c
     // A fragments: one set per quarter parity (TMQ blocks each); B
     // fragments: one set per k-step of the stage (all TN blocks).
     half8 fa[2][TMQ], fb[SPS][TN];
-    // TRI: zero the B fragment elements (j, k) with k < j (tri_up: k > j).
-    // Block j of k-step s holds row jrow = n0 + wn·WTN + 16j + (lane mod 16)
-    // and the 8 k from kfirst = (kt0+kt)·BK + 32s + 8·(lane div 16); element
-    // e is zeroed when e < jrow - kfirst (tri_up: e > jrow - kfirst) by a
-    // mask (so NaN or Inf stored in the other triangle cannot reach the
-    // MFMA).
-    auto mask_tri = [&](const TileInfo &T, int kt, int s) {
-        const int frow = lane & 15;
-        const int fhi = lane >> 4;
-        const int kfirst = (T.kt0 + kt) * BK + KS * s + 8 * fhi;
+    // TRI: the B operand's elements (j, k) with k < j (tri_up: k > j) lie in
+    // the other triangle and must count as zero (NaN or Inf stored there
+    // must not reach the MFMA).  Only the BN/BK stages of the tile's
+    // diagonal block hold such elements.  Once this wave's loads of such a
+    // stage have landed, and before the barrier that publishes the stage,
+    // each lane zeroes them in its own B row of the stage in LDS (wave w
+    // loaded rows RPW·w .. RPW·w + 63): the chunks wholly in the other
+    // triangle are overwritten with zeros, the one chunk the diagonal
+    // crosses is read, masked and written back.  With jr = (the row's global
+    // index) - (the stage's first k), element k of the stage (0..63) is
+    // zeroed when k < jr (tri_up: k > jr).
+    auto zero_tri = [&](const TileInfo &T, int kt, int slot) {
+        const int jr0 = __builtin_amdgcn_readfirstlane(T.n0 + wave * RPW - (T.kt0 + kt) * BK);
+        const bool up = p.tri_up != 0;
+        if (up ? jr0 >= BK - 1 : jr0 + RPW - 1 <= 0)
+            return;                                      // nothing to zero in this wave's rows
+        const int row = wave * RPW + lane;
+        const int jr = jr0 + lane;
+        unsigned char *rp = smem + LDS_B + slot * SLOT + row * RB;
+        const int kp = jr >> 3;                          // chunk holding k = jr (floor)
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            const int t = T.n0 + wn * WTN + j * FB + frow - kfirst;   // elements to zero
-            u32x4 w = __builtin_bit_cast(u32x4, fb[s][j]);
-            if (p.tri_up) {
+        for (int kc = 0; kc < KC; ++kc) {
+            if (up ? kc > kp : kc < kp)
+                *reinterpret_cast<u32x4 *>(rp + swz(row, kc) * 16) = u32x4{0, 0, 0, 0};
+        }
+        if (kp >= 0 && kp < KC) {
+            const int e0 = jr & 7;                       // position of k = jr in its chunk
+            u32x4 *cp = reinterpret_cast<u32x4 *>(rp + swz(row, kp) * 16);
+            u32x4 w = *cp;
 #pragma unroll
-                for (int d = 0; d < 4; ++d) {
-                    const uint32_t m = (2 * d <= t ? 0x0000ffffu : 0u) | (2 * d + 1 <= t ? 0xffff0000u : 0u);
-                    w[d] &= m;
-                }
-            } else {
-#pragma unroll
-                for (int d = 0; d < 4; ++d) {
-                    const uint32_t m = (2 * d >= t ? 0x0000ffffu : 0u) | (2 * d + 1 >= t ? 0xffff0000u : 0u);
-                    w[d] &= m;
-                }
+            for (int d = 0; d < 4; ++d) {
+                const uint32_t m = up ? ((2 * d <= e0 ? 0x0000ffffu : 0u) | (2 * d + 1 <= e0 ? 0xffff0000u : 0u))
+                                      : ((2 * d >= e0 ? 0x0000ffffu : 0u) | (2 * d + 1 >= e0 ? 0xffff0000u : 0u));
+                w[d] &= m;
             }
-            fb[s][j] = __builtin_bit_cast(half8, w);
+            *cp = w;
         }
     };
+    // Whether stage kt of tile T is one of its diagonal block's stages.
+    auto tri_stage = [&](const TileInfo &T, int kt) {
+        return p.tri_up ? kt >= T.nk - BN / BK && kt < T.nk : kt < BN / BK && kt < T.nk;
+    };
 
-    int id = blockIdx.x;              // FUSED: the round
+    int id = FUSED ? 0 : blockIdx.x;  // FUSED: the work item
     TileInfo T;
-    if (FUSED ? !fused_item(p, blockIdx.x, stride, 0, total, tiles_m, T)
+    if (FUSED ? !fused_item(p, blockIdx.x, stride, id, tiles_m, tiles_n, T)
               : !find_tile<TRI>(p, id, stride, total, tiles_m, tiles_n, T))
         return;
-    if (FUSED)
-        id = 0;
     set_offsets(T);
     prologue(T);
 
@@ -500,6 +553,11 @@ hgemm_fast_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int c
             wait_vmcnt<VM_AFTER_EPI>();
         else
             wait_vmcnt<0>();
+        if constexpr (TRI) {
+            if (tri_stage(T, 0))
+                zero_tri(T, 0, 0);
+            wait_lgkmcnt<0>();
+        }
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
         // Fragments of quarter 0: A blocks 0..TMQ-1 and every B block of
@@ -525,13 +583,6 @@ hgemm_fast_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int c
             static_for<NQ>([&](auto qc) __attribute__((always_inline)) {
                 constexpr int q = decltype(qc)::value;
                 constexpr int s = q >> 1, h = q & 1;
-                // Only the BN/BK stages of the tile's diagonal block hold
-                // elements on the wrong side of its columns: the first ones
-                // of the walk, or (tri_up) the last.
-                if constexpr (TRI && h == 0) {
-                    if (p.tri_up ? kt >= T.nk - BN / BK : kt < BN / BK)
-                        mask_tri(T, kt, s);
-                }
                 // Ring loads of this quarter: operand, stage, slot, first index.
                 constexpr bool lb = q >= 2;
                 constexpr int lfirst = (q & 1) * (LPS / 2);
@@ -552,6 +603,10 @@ hgemm_fast_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int c
                         // of stage kt are complete: after the barrier every
                         // wave may read stage kt+1 and refill stage kt's B slot.
                         wait_vmcnt<LPS>();
+                        if constexpr (TRI) {
+                            if (tri_stage(T, kt + 1))
+                                zero_tri(T, kt + 1, bn);
+                        }
                         wait_lgkmcnt<0>();
                         __builtin_amdgcn_s_barrier();
                         __builtin_amdgcn_sched_barrier(0);
@@ -591,8 +646,8 @@ hgemm_fast_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int c
         TileInfo Tn;
         bool more;
         if constexpr (FUSED) {
-            nid = id + 1;                 // the next round's tile
-            more = fused_item(p, blockIdx.x, stride, nid, total, tiles_m, Tn);
+            nid = id + 1;                 // the next item
+            more = fused_item(p, blockIdx.x, stride, nid, tiles_m, tiles_n, Tn);
         } else {
             more = find_tile<TRI>(p, nid, stride, total, tiles_m, tiles_n, Tn);
         }
@@ -680,12 +735,22 @@ hgemm_fast_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int c
                         // reads see this block's writes; the fences keep the
                         // compiler from moving LDS accesses across.
                         __atomic_signal_fence(__ATOMIC_SEQ_CST);
-                        celt *c0 = crow(i) - frow * ldc - 4 * fhi;   // row 0, column 0 of the block
+                        // All reads of the block first, then the stores, so
+                        // that the reads' latencies overlap; the store address
+                        // advances by two rows at a time.
+                        const int uu = lane & 31;
+                        cvec v[TN];
 #pragma unroll
                         for (int t = 0; t < TN; ++t) {
-                            const int rr = 2 * t + (lane >> 5), uu = lane & 31;
-                            const cvec v = *reinterpret_cast<const cvec *>(stg + rr * SROW + (uu ^ (rr * SSW)) * UB);
-                            *reinterpret_cast<cvec *>(c0 + (int64_t)rr * ldc + 4 * uu) = v;
+                            const int rr = 2 * t + (lane >> 5);
+                            v[t] = *reinterpret_cast<const cvec *>(stg + rr * SROW + (uu ^ (rr * SSW)) * UB);
+                        }
+                        // row (lane div 32), column 4·(lane mod 32) of the block
+                        celt *cd = crow(i) + ((lane >> 5) - frow) * ldc + 4 * (uu - fhi);
+#pragma unroll
+                        for (int t = 0; t < TN; ++t) {
+                            *reinterpret_cast<cvec *>(cd) = v[t];
+                            cd += 2 * ldc;
                         }
                         __atomic_signal_fence(__ATOMIC_SEQ_CST);
                     }
@@ -812,10 +877,12 @@ hipError_t launch_trmm_fused(const GemmParams &p, hipStream_t stream)
     if (total64 > 0x7fffffff)
         return hipErrorInvalidConfiguration;
     const int cvec = reinterpret_cast<uintptr_t>(p.C) % 16 == 0 && p.ldc % 4 == 0;
+    // one persistent workgroup per CU, at most one per job (see fused_item)
+    const int64_t jobs = (int64_t)tiles_m * (tiles_n / 2) + ((tiles_n & 1) ? (tiles_m + 1) / 2 : 0);
     int64_t grid = cu_count();
     grid = grid / 8 * 8 > 0 ? grid / 8 * 8 : grid;
-    if (grid > total64)
-        grid = total64;
+    if (grid > jobs)
+        grid = jobs;
     hipLaunchKernelGGL((hgemm_fast_kernel<false, false, true, false, true, false, false>), dim3((unsigned)grid),
                        dim3(THREADS), 0, stream, p, tiles_m, tiles_n, (int)total64, cvec);
     return hipGetLastError();

@@ -129,10 +129,7 @@ hgemm_ring_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int c
     for (int i = 0; i < L; ++i) {
         const bool isb = i >= LA;
         const int row = ((isb ? LB : LA) * wave + (isb ? i - LA : i)) * 8 + (lane >> 3);
-        int kc = 0;
-#pragma unroll
-        for (int c = 0; c < KC; ++c)
-            kc = swz(row, c) == (lane & 7) ? c : kc;
+        const int kc = swz(row, lane & 7);   // swz() XORs the chunk index: its own inverse
         lkc[i] = kc;
         const int rows = isb ? rows_b : rows_a;
         const int64_t ld = isb ? p.ldb : p.lda;

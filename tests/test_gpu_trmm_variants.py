@@ -102,7 +102,9 @@ def test_8192_sampled(hg, uplo, trans):
 # output tiles per CU: m·n >= 2^25).  Upper/transposed and lower/non-transposed
 # walk each tile's K from 0 up to its diagonal block (the triangle on the other
 # side of the GEMM view); the other two walk down from it.
-ONE_LAUNCH = [(4096, 8192, 256), (2048, 16384, 256), (4096, 8192, 512)]
+# (768, 44288, 768): one leaf of 3 tile columns (an odd count) over 173 tile
+# rows (odd), so the job list has paired middle-column tiles and a lone one.
+ONE_LAUNCH = [(4096, 8192, 256), (2048, 16384, 256), (4096, 8192, 512), (768, 44288, 768)]
 
 
 @pytest.mark.parametrize("uplo,trans", VARIANTS)
