@@ -52,7 +52,7 @@ __device__ __forceinline__ floatx4 mfma_16x16x32(const half8 &a, const half8 &b,
 constexpr int BK = 64, RB = 128, KC = 8, THREADS = 256, NWAVES = 4;
 constexpr uint32_t OOB = 0x80000000u;
 
-__device__ __forceinline__ int swz(int r, int kc) { return kc ^ ((r >> 1) & 7); }
+__device__ __forceinline__ int swz(int r, int kc) { return kc ^ ((r >> 1) & (KC - 1)); }
 
 template <int n>
 __device__ __forceinline__ void wait_vmcnt()
@@ -101,7 +101,7 @@ hgemm_ring_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int c
     constexpr int TM = WTM / 16, TN = WTN / 16;            // 16×16 blocks per wave
     constexpr int LA = BM / (NWAVES * 8), LB = BN / (NWAVES * 8);   // load instructions per wave
     constexpr int L = LA + LB;                             // ... per stage
-    static_assert(NS >= 3 && LA >= 1 && LB >= 1 && (NS - 2) * L <= 63, "");
+    static_assert(NS >= 4 && LA >= 1 && LB >= 1 && (NS - 2) * L <= 63, "");
     __shared__ __attribute__((aligned(1024))) unsigned char smem[NS * SLOT];
 
     int batch, tm, tn;
@@ -170,34 +170,59 @@ hgemm_ring_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int c
     for (int s = 0; s < NS - 1; ++s)
         issue(s);
     const int frow = lane & 15, fhi = lane >> 4;
-    for (int kt = 0; kt < nk; ++kt) {
-        // This wave's loads of stage kt have landed (stages kt+1 .. kt+NS-2
-        // may be in flight); after the barrier everyone's have, and every
-        // wave is done with stage kt-1, whose slot takes stage kt+NS-1.
-        wait_vmcnt<(NS - 2) * L>();
-        __builtin_amdgcn_s_barrier();
-        issue(kt + NS - 1);
+    // Fragments of one stage: both k-steps of the wave's TM A and TN B blocks.
+    constexpr int SPS = BK / 32;
+    struct Frags {
+        half8 a[SPS][TM], b[SPS][TN];
+    };
+    auto read_stage = [&](int kt, Frags &f) __attribute__((always_inline)) {
         const unsigned char *As = smem + (kt % NS) * SLOT;
         const unsigned char *Bs = As + BM * RB;
 #pragma unroll
-        for (int s = 0; s < BK / 32; ++s) {
-            half8 fa[TM], fb[TN];
+        for (int s = 0; s < SPS; ++s) {
 #pragma unroll
             for (int i = 0; i < TM; ++i) {
                 const int row = wm * WTM + i * 16 + frow;
-                fa[i] = *reinterpret_cast<const half8 *>(As + row * RB + swz(row, 4 * s + fhi) * 16);
+                f.a[s][i] = *reinterpret_cast<const half8 *>(As + row * RB + swz(row, 4 * s + fhi) * 16);
             }
 #pragma unroll
             for (int j = 0; j < TN; ++j) {
                 const int row = wn * WTN + j * 16 + frow;
-                fb[j] = *reinterpret_cast<const half8 *>(Bs + row * RB + swz(row, 4 * s + fhi) * 16);
+                f.b[s][j] = *reinterpret_cast<const half8 *>(Bs + row * RB + swz(row, 4 * s + fhi) * 16);
             }
+        }
+    };
+    auto mma_stage = [&](const Frags &f) __attribute__((always_inline)) {
+#pragma unroll
+        for (int s = 0; s < SPS; ++s)
 #pragma unroll
             for (int j = 0; j < TN; ++j)
 #pragma unroll
                 for (int i = 0; i < TM; ++i)
-                    acc[i][j] = mfma_16x16x32<IN_BF16>(fb[j], fa[i], acc[i][j]);
-        }
+                    acc[i][j] = mfma_16x16x32<IN_BF16>(f.b[s][j], f.a[s][i], acc[i][j]);
+    };
+    // Stage kt's fragments are read one stage ahead, during stage kt-1's
+    // MFMAs, so the LDS latency hides behind the matrix core.  In step kt:
+    // this wave's loads of stage kt+1 have landed (stages kt+2 .. kt+NS-2 may
+    // be in flight); after the barrier everyone's have, and every wave has
+    // finished reading stage kt-1 (its MFMAs waited for those reads), whose
+    // slot then takes stage kt+NS-1.  Reads past the last stage see the
+    // zero-filled slots and are not used.
+    Frags f0, f1;
+    wait_vmcnt<(NS - 2) * L>();
+    __builtin_amdgcn_s_barrier();
+    read_stage(0, f0);
+    auto step = [&](int kt, const Frags &cur, Frags &nxt) __attribute__((always_inline)) {
+        wait_vmcnt<(NS - 3) * L>();
+        __builtin_amdgcn_s_barrier();
+        issue(kt + NS - 1);
+        read_stage(kt + 1, nxt);
+        mma_stage(cur);
+    };
+    for (int kt = 0; kt < nk; kt += 2) {
+        step(kt, f0, f1);
+        if (kt + 1 < nk)
+            step(kt + 1, f1, f0);
     }
     wait_vmcnt<0>();   // the ring's last zero-fill loads (none reach memory) drain before exit
 
@@ -238,24 +263,51 @@ hgemm_ring_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int c
             }
         }
     } else {
+        // Edge tile: rows past M are skipped; a lane's 4 columns go as one
+        // vector access when all are inside N (and C allows it), element by
+        // element otherwise.  C is read for the whole row block first.
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
             const int row = m0 + wm * WTM + i * 16 + frow;
             if (row >= M)
                 continue;
+            celt *cr = Cb + (int64_t)row * ldc;
+            float cin[TN][4];
+            if (BETA) {
+#pragma unroll
+                for (int j = 0; j < TN; ++j) {
+                    const int col = n0 + wn * WTN + j * 16 + 4 * fhi;
+                    if (cvec && col + 3 < N) {
+                        const cvec_t c4 = *reinterpret_cast<const cvec_t *>(cr + col);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            cin[j][e] = (float)c4[e];
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            cin[j][e] = col + e < N ? (float)cr[col + e] : 0.0f;
+                    }
+                }
+            }
 #pragma unroll
             for (int j = 0; j < TN; ++j) {
                 const int col = n0 + wn * WTN + j * 16 + 4 * fhi;
+                cvec_t r;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    if (col + e >= N)
-                        continue;
-                    celt *cp = Cb + (int64_t)row * ldc + col + e;
                     const float v = acc[i][j][e];
-                    float t = BETA ? __builtin_fmaf(alpha, v, beta * (float)*cp) : alpha * v;
+                    float t = BETA ? __builtin_fmaf(alpha, v, beta * cin[j][e]) : alpha * v;
                     if constexpr (EPI)
-                        t = epi_apply(t, p.bias ? p.bias[col + e] : -0.0f, p.act);
-                    *cp = (celt)t;
+                        t = epi_apply(t, p.bias && col + e < N ? p.bias[col + e] : -0.0f, p.act);
+                    r[e] = (celt)t;
+                }
+                if (cvec && col + 3 < N) {
+                    *reinterpret_cast<cvec_t *>(cr + col) = r;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (col + e < N)
+                            cr[col + e] = r[e];
                 }
             }
         }
