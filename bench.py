@@ -356,7 +356,8 @@ def config_sweep(hg, stream, main_gemm_ms=None, main_trmm_ms=None, only=None):
         del Ad, Bd, Od, TA, TB
     if want("trmm_4096x256"):
         # Skinny right-hand side (next row): the TRMM page's usage example,
-        # n = 4096, m = 256.
+        # n = 4096, m = 256, one launch of 64x64 tiles; next to it the per-level
+        # schedule on 4 streams.
         print("[bench] config trmm_4096x256 ...", file=sys.stderr, flush=True)
         w = workloads.TrmmWorkload("trmm_4096x256", 4096, 256, 1.0, 256, 6)
         TA, TB = workloads.trmm_inputs(w)
@@ -375,7 +376,8 @@ def config_sweep(hg, stream, main_gemm_ms=None, main_trmm_ms=None, only=None):
                                 "effective_tflops": round(w.flops / (ts[0] * 1e-3) / 1e12, 2),
                                 "compulsory_bytes": nb, "gbs": round(nb / (ts[0] * 1e-3) / 1e9, 1),
                                 "four_streams_ms_median": round(t4[0], 5),
-                                "note": "B 4096x256 (the TRMM page's usage example), level-by-level launches"}
+                                "note": "B 4096x256 (the TRMM page's usage example): the recursion in one launch "
+                                        "of 64x64 tiles (too few 256x256 tiles for the big one-launch kernel)"}
         del Ad, Bd, Od, TA, TB
     if want("trmm_8192_lower_notrans"):
         # The page's usage call is the lower, non-transposed product (next row):

@@ -57,6 +57,19 @@ void plan_rec(int64_t o, int64_t s, int64_t leaf, int64_t depth, std::vector<Nod
     plan_rec(o + h, s - h, leaf, depth + 1, out);
 }
 
+// Whether a TRMM of n×n A and n×m B too small for the 256×256 one-launch
+// schedule runs in one launch of 64×64 tiles rather than level by level.
+// In one launch the tiles of the first column walk all n/64 K stages, and
+// 64×64 tiles move more bytes per flop than the per-level launches' larger
+// tiles; measured (one box, HIP events): one launch wins at n = 4096, m = 256
+// (25 against 39 us), n = m = 2048 (36 / 53) and n = 4096, m = 1024
+// (68 / 72), and loses at n = 8192, m = 256 (74 / 60) and n = m = 4096
+// (191 / 139).  So: n <= 4096 and the work m·n² at most 2^34.
+bool ring_fused_wanted(int64_t m, int64_t n)
+{
+    return n <= 4096 && (double)m * (double)n * (double)n <= 17179869184.0;
+}
+
 hg::Tile choose_batched_tile(int64_t M, int64_t maxN, int64_t nbatch)
 {
     const int64_t big = ((M + 255) / 256) * ((maxN + 255) / 256) * nbatch;
@@ -302,6 +315,8 @@ int trmm_impl(int64_t n, int64_t m, float alpha, const void *A, int64_t lda, con
         p.e[0] = {0, 0, 0, (int32_t)n, (int32_t)n};
         if (hg::trmm_fused_ok(p))
             return hip_status(hg::launch_trmm_fused(p, s));
+        if (ring_fused_wanted(m, n) && hg::trmm_ring_fused_ok(p))
+            return hip_status(hg::launch_trmm_fused_ring(p, s));
     }
 
     // Several streams: events to join them between levels (every stream
@@ -811,13 +826,14 @@ int hg_trmm(int uplo, int trans, int64_t n, int64_t m, float alpha, const void *
         p.tri_up = 1;
         p.nbatch = 1;
         p.e[0] = {0, 0, 0, (int32_t)n, (int32_t)n};
-        if (hg::trmm_fused_ok(p)) {
+        const bool big = hg::trmm_fused_ok(p);
+        if (big || (ring_fused_wanted(m, n) && hg::trmm_ring_fused_ok(p))) {
             if (copy) {
                 const int st = hip_status(hg::launch_tri_xform(4, static_cast<const _Float16 *>(A), lda, L, v.ldl, n, s));
                 if (st != HG_OK)
                     return st;
             }
-            return hip_status(hg::launch_trmm_fused(p, s));
+            return hip_status(big ? hg::launch_trmm_fused(p, s) : hg::launch_trmm_fused_ring(p, s));
         }
     }
     int st = hip_status(hg::launch_tri_xform(v.mode, static_cast<const _Float16 *>(A), lda, L, v.ldl, n, s));

@@ -72,7 +72,8 @@ hipError_t launch_gemm_fast(const GemmParams &p, const LaunchOpts &o, hipStream_
 
 // 64×64 / 128×128 tiles with a deep ring of direct buffer→LDS stages
 // (hg_ring.hip), for the Small and Mid tile families when the operands
-// allow 16-byte buffer loads, K % 8 == 0 and no triangle mask is needed.
+// allow 16-byte buffer loads and K % 8 == 0 (with the triangle mask: fp32
+// output written once, fp16 operands, no epilogue extras).
 bool ring_path_ok(const GemmParams &p, const LaunchOpts &o);
 hipError_t launch_gemm_ring(const GemmParams &p, const LaunchOpts &o, hipStream_t stream);
 
@@ -89,6 +90,11 @@ hipError_t launch_gemm_ring(const GemmParams &p, const LaunchOpts &o, hipStream_
 // per CU.
 bool trmm_fused_ok(const GemmParams &p);
 hipError_t launch_trmm_fused(const GemmParams &p, hipStream_t stream);
+// The same one-launch recursion on 64×64 tiles (hg_ring.hip), one workgroup
+// per tile, for right-hand sides too narrow to give every CU two 256×256
+// tiles: every recursion boundary on a 64-column tile edge, leaf >= 64.
+bool trmm_ring_fused_ok(const GemmParams &p);
+hipError_t launch_trmm_fused_ring(const GemmParams &p, hipStream_t stream);
 
 // Recursive triangular solve X = alpha·A⁻ᵀ·B (hg_trsm.hip).  Leaves are at
 // most kTrsmLeafMax rows; their inverses V_L = A_LL⁻¹ are stored in fp16 as

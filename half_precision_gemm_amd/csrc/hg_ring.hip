@@ -37,6 +37,7 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef _Float16 halfx4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // v_mfma_f32_16x16x32 on 16-byte fragments of fp16 or bf16 values.
 template <bool BF16>
@@ -58,6 +59,11 @@ template <int n>
 __device__ __forceinline__ void wait_vmcnt()
 {
     __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+template <int n>
+__device__ __forceinline__ void wait_lgkmcnt()
+{
+    __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | ((n & 15) << 8));
 }
 
 __device__ __forceinline__ hg_r_int32x4 rsrc_of(const void *base, uint32_t bytes)
@@ -91,7 +97,16 @@ __device__ __forceinline__ void ring_map(int wg, int total, int tiles_m, int til
     tn = r / gsz;
 }
 
-template <int BM, int BN, bool OUT_F16, bool BETA, bool KCHK, bool EPI, bool IN_BF16>
+// TRI: the B operand (N×K) is triangular in the GEMM view: element (j, k)
+// counts for k >= j (p.tri_up: k <= j) and the other triangle is never
+// used.  A tile walks only the stages that can hold counted elements: from
+// its first column's stage on (tri_up: up to the stage of its last column),
+// and the elements on the other side of the diagonal in the tile's
+// diagonal-block stages are zeroed in LDS once the stage has landed.  With
+// one entry of K = N = n this is the whole recursive TRMM in one launch
+// (see trmm_ring_fused_ok); with one entry per leaf, the leaves of the
+// per-level schedule.
+template <int BM, int BN, bool OUT_F16, bool BETA, bool KCHK, bool EPI, bool IN_BF16, bool TRI = false>
 __global__ void __launch_bounds__(THREADS, 1)
 hgemm_ring_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int cvec)
 {
@@ -119,7 +134,11 @@ hgemm_ring_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int c
     const hg_r_int32x4 rb = rsrc_of(p.B + p.e[batch].b_off + (int64_t)n0 * p.ldb,
                                     (uint32_t)(((int64_t)(rows_b - 1) * p.ldb + K) * 2));
     const uint32_t lds_base = (uint32_t)reinterpret_cast<uintptr_t>(smem);
-    const int nk = (K + BK - 1) / BK;
+    // Stages kt0 .. kt0 + nk - 1 of K (TRI: only those that can hold counted
+    // elements of the tile's columns).
+    const int nkk = (K + BK - 1) / BK;
+    const int kt0 = TRI && !p.tri_up ? n0 / BK : 0;
+    const int nk = TRI ? (p.tri_up ? min(nkk, (n0 + BN + BK - 1) / BK) : nkk - kt0) : nkk;
 
     // Load i of a wave covers tile rows (wave·(LA or LB) + i)·8 .. +7; lane l
     // takes row +(l div 8) and the logical chunk that swz() puts at l mod 8.
@@ -138,14 +157,14 @@ hgemm_ring_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int c
     // Every load of stage kt into its ring slot.
     auto issue = [&](int kt) {
         const int slot = kt % NS;
-        const uint32_t kb = (uint32_t)kt * RB;
+        const uint32_t kb = (uint32_t)(kt0 + kt) * RB;
 #pragma unroll
         for (int i = 0; i < L; ++i) {
             const bool isb = i >= LA;
             hg_r_int32x4 r = isb ? rb : ra;
             uint32_t o = off[i];
             if constexpr (KCHK) {
-                o = lkc[i] * 8 < K - kt * BK ? o + kb : OOB;
+                o = lkc[i] * 8 < K - (kt0 + kt) * BK ? o + kb : OOB;
             } else {
                 const uint64_t base = ((uint64_t)(uint32_t)r[1] << 32 | (uint32_t)r[0]) + kb;
                 r[0] = (int)(uint32_t)base;
@@ -208,12 +227,60 @@ hgemm_ring_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int c
     // finished reading stage kt-1 (its MFMAs waited for those reads), whose
     // slot then takes stage kt+NS-1.  Reads past the last stage see the
     // zero-filled slots and are not used.
+    // TRI: zero the other triangle's elements of stage kt in its slot, in
+    // the B rows this wave loaded (8·LB·wave .. 8·LB·wave + 8·LB - 1), one row
+    // per lane: with jr = (the row's column index) - (the stage's first k),
+    // element k of the stage (0..63) is zeroed when k < jr (tri_up: k > jr).
+    auto zero_tri = [&](int kt) __attribute__((always_inline)) {
+        const int jr0 = __builtin_amdgcn_readfirstlane(n0 + 8 * LB * wave - (kt0 + kt) * BK);
+        const bool up = p.tri_up != 0;
+        if (up ? jr0 >= BK - 1 : jr0 + 8 * LB - 1 <= 0)
+            return;
+        if (lane < 8 * LB) {
+            const int row = 8 * LB * wave + lane;
+            const int jr = jr0 + lane;
+            unsigned char *rp = smem + (kt % NS) * SLOT + BM * RB + row * RB;
+            const int kp = jr >> 3;                         // chunk holding k = jr (floor)
+#pragma unroll
+            for (int kc = 0; kc < KC; ++kc)
+                if (up ? kc > kp : kc < kp)
+                    *reinterpret_cast<u32x4 *>(rp + swz(row, kc) * 16) = u32x4{0, 0, 0, 0};
+            if (kp >= 0 && kp < KC) {
+                const int e0 = jr & 7;
+                u32x4 *cp = reinterpret_cast<u32x4 *>(rp + swz(row, kp) * 16);
+                u32x4 w = *cp;
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    const uint32_t m = up ? ((2 * d <= e0 ? 0x0000ffffu : 0u) | (2 * d + 1 <= e0 ? 0xffff0000u : 0u))
+                                          : ((2 * d >= e0 ? 0x0000ffffu : 0u) | (2 * d + 1 >= e0 ? 0xffff0000u : 0u));
+                    w[d] &= m;
+                }
+                *cp = w;
+            }
+        }
+    };
+    // Whether stage kt is one of the tile's diagonal-block stages.
+    auto tri_stage = [&](int kt) {
+        return p.tri_up ? kt >= nk - BN / BK && kt < nk : kt < BN / BK && kt < nk;
+    };
     Frags f0, f1;
     wait_vmcnt<(NS - 2) * L>();
+    if constexpr (TRI) {
+        if (tri_stage(0)) {
+            zero_tri(0);
+            wait_lgkmcnt<0>();
+        }
+    }
     __builtin_amdgcn_s_barrier();
     read_stage(0, f0);
     auto step = [&](int kt, const Frags &cur, Frags &nxt) __attribute__((always_inline)) {
         wait_vmcnt<(NS - 3) * L>();
+        if constexpr (TRI) {
+            if (tri_stage(kt + 1)) {
+                zero_tri(kt + 1);
+                wait_lgkmcnt<0>();
+            }
+        }
         __builtin_amdgcn_s_barrier();
         issue(kt + NS - 1);
         read_stage(kt + 1, nxt);
@@ -314,7 +381,7 @@ hgemm_ring_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int c
     }
 }
 
-template <int BM, int BN, bool OUT_F16, bool BETA, bool EPI, bool IN_BF16>
+template <int BM, int BN, bool OUT_F16, bool BETA, bool EPI, bool IN_BF16, bool TRI = false>
 hipError_t launch_ring_cfg(const GemmParams &p, hipStream_t stream)
 {
     int maxN = 0;
@@ -335,10 +402,10 @@ hipError_t launch_ring_cfg(const GemmParams &p, hipStream_t stream)
     for (int b = 0; b < p.nbatch; ++b)
         cvec = cvec && (p.e[b].c_off % 4 == 0);
     if (kchk)
-        hipLaunchKernelGGL((hgemm_ring_kernel<BM, BN, OUT_F16, BETA, true, EPI, IN_BF16>), dim3((unsigned)total64),
+        hipLaunchKernelGGL((hgemm_ring_kernel<BM, BN, OUT_F16, BETA, true, EPI, IN_BF16, TRI>), dim3((unsigned)total64),
                            dim3(THREADS), 0, stream, p, tiles_m, tiles_n, (int)total64, cvec);
     else
-        hipLaunchKernelGGL((hgemm_ring_kernel<BM, BN, OUT_F16, BETA, false, EPI, IN_BF16>), dim3((unsigned)total64),
+        hipLaunchKernelGGL((hgemm_ring_kernel<BM, BN, OUT_F16, BETA, false, EPI, IN_BF16, TRI>), dim3((unsigned)total64),
                            dim3(THREADS), 0, stream, p, tiles_m, tiles_n, (int)total64, cvec);
     return hipGetLastError();
 }
@@ -366,7 +433,7 @@ hipError_t launch_ring_tile(const GemmParams &p, const LaunchOpts &o, hipStream_
 
 bool ring_path_ok(const GemmParams &p, const LaunchOpts &o)
 {
-    if (!o.vec || o.tri)
+    if (!o.vec || (o.tri && (o.out_f16 || o.beta_read || o.epi || o.in_bf16)))
         return false;
     if (p.lda > (1 << 21) || p.ldb > (1 << 21))
         return false;
@@ -376,8 +443,49 @@ bool ring_path_ok(const GemmParams &p, const LaunchOpts &o)
     return true;
 }
 
+bool trmm_ring_fused_ok(const GemmParams &p)
+{
+    constexpr int T = 64;                                  // tile edge of the Small family
+    if (p.lda > (1 << 21) || p.ldb > (1 << 21) || p.leaf < T)
+        return false;
+    if (reinterpret_cast<uintptr_t>(p.A) % 16 != 0 || reinterpret_cast<uintptr_t>(p.B) % 16 != 0 ||
+        p.lda % 8 != 0 || p.ldb % 8 != 0)
+        return false;
+    // Every recursion boundary on a 64-column tile edge.
+    const int n = p.e[0].N;
+    if (n % T != 0)
+        return false;
+    struct Frame {
+        int o, s;
+    };
+    Frame st[64];
+    int top = 0;
+    st[top++] = {0, n};
+    while (top > 0) {
+        const Frame f = st[--top];
+        if (f.o % T != 0 || f.s % T != 0)
+            return false;
+        if (f.s <= p.leaf)
+            continue;
+        const int h = f.s / 2;
+        if (top + 2 > 64)
+            return false;
+        st[top++] = {f.o, h};
+        st[top++] = {f.o + h, f.s - h};
+    }
+    return true;
+}
+
+hipError_t launch_trmm_fused_ring(const GemmParams &p, hipStream_t stream)
+{
+    return launch_ring_cfg<64, 64, false, false, false, false, true>(p, stream);
+}
+
 hipError_t launch_gemm_ring(const GemmParams &p, const LaunchOpts &o, hipStream_t stream)
 {
+    if (o.tri)   // fp32 C written once (TRMM leaves and the one-launch ring TRMM)
+        return o.tile == Tile::Mid ? launch_ring_cfg<128, 128, false, false, false, false, true>(p, stream)
+                                   : launch_ring_cfg<64, 64, false, false, false, false, true>(p, stream);
     if (o.tile == Tile::Mid)
         return launch_ring_tile<128, 128>(p, o, stream);
     return launch_ring_tile<64, 64>(p, o, stream);

@@ -152,11 +152,13 @@ def test_deterministic(hg):
 
 
 # ---- the one-launch schedule against the level-by-level one and the oracle.
-# The one-launch schedule runs when the recursion's boundaries fall on the
-# 256 grid and there are at least two 256×256 output tiles per CU (m·n >=
-# 512·256²): the shapes below with m·n of 2^25 take it; 3072 and 2560 (their
-# boundaries are off the grid) run level by level in both calls, so there
-# the two calls run the same launches and must agree bit for bit.  The
+# The one-launch schedule runs on 256×256 tiles when the recursion's
+# boundaries fall on the 256 grid and there are at least two such output
+# tiles per CU (m·n >= 512·256²: the shapes below with m·n of 2^25), and on
+# 64×64 tiles when the boundaries fall on the 64 grid (3072: pieces of 192);
+# 2560 and 2500 (boundaries off the 64 grid: pieces of 160 and 156) run level
+# by level in both calls, so there the two calls run the same launches and
+# must agree bit for bit.  The
 # one-launch schedule adds a tile's updates in its fp32 accumulators, the
 # level-by-level one rounds Out to fp32 after each update, so the two differ
 # only by fp32 rounding: each is within (K/32 + depth + 2)·6·2^-24 of
@@ -173,7 +175,8 @@ def _fp32_bound(A_cm, B_cm, ri, cj, alpha, n, leaf):
 
 @pytest.mark.parametrize("n,m,leaf,one_launch", [(4096, 8192, 256, True), (2048, 16384, 256, True),
                                                  (4096, 8192, 512, True), (8192, 4096, 256, True),
-                                                 (3072, 64, 256, False), (2560, 100, 256, False)])
+                                                 (3072, 64, 256, True), (2560, 100, 256, False),
+                                                 (2500, 64, 256, False)])
 def test_schedules_agree(hg, n, m, leaf, one_launch):
     print(f"[case] trmm schedules n={n} m={m} leaf={leaf}", flush=True)
     A_cm, B_cm = trmm_inputs(n, m, n + 3 * m + leaf)

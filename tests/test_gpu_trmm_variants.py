@@ -140,3 +140,30 @@ def test_one_launch_other_triangle_never_read(hg, uplo, trans):
     Ax, _ = _inputs(n, m, 6, uplo, np.nan)
     assert np.array_equal(run(hg, A0, B_cm, 1.0, uplo, trans).view(np.uint32),
                           run(hg, Ax, B_cm, 1.0, uplo, trans).view(np.uint32))
+
+
+# ---- The one-launch schedule on 64×64 tiles (right-hand sides too narrow for
+# the 256×256 one: n <= 4096, m·n² <= 2^34, boundaries on the 64 grid), all
+# four variants, NaN in the triangle that is never read, ragged m.
+RING_ONE_LAUNCH = [(2048, 256, 256), (1024, 100, 128), (4096, 64, 256)]
+
+
+@pytest.mark.parametrize("uplo,trans", VARIANTS)
+@pytest.mark.parametrize("n,m,leaf", RING_ONE_LAUNCH)
+def test_ring_one_launch_parity(hg, uplo, trans, n, m, leaf):
+    A_cm, B_cm = _inputs(n, m, 3 * n + m + leaf, uplo, np.nan)
+    got = run(hg, A_cm, B_cm, -0.75, uplo, trans, leaf)
+    A0, _ = _inputs(n, m, 3 * n + m + leaf, uplo)
+    check_close(got, _ref(A0, B_cm, -0.75, uplo, trans), n,
+                f"{uplo}{'T' if trans else 'N'} ring one launch n={n} m={m} leaf={leaf}")
+
+
+@pytest.mark.parametrize("uplo,trans", VARIANTS)
+def test_ring_one_launch_integer_bit_exact(hg, uplo, trans):
+    rng = np.random.default_rng(47)
+    n, m = 2048, 192
+    T = (np.tril if uplo == "L" else np.triu)(workloads.integer_f16(rng, (n, n)))
+    B = workloads.integer_f16(rng, (n, m))
+    A_cm, B_cm = np.ascontiguousarray(T.T), np.ascontiguousarray(B.T)
+    got = run(hg, A_cm, B_cm, 1.0, uplo, trans)
+    assert np.array_equal(got.astype(np.float64), _ref(A_cm, B_cm, 1.0, uplo, trans))
