@@ -155,22 +155,29 @@ def strerror(status: int) -> str:
     return lib.hg_strerror(status).decode()
 
 
+# The current stream's raw handle of a device: torch's getter of the raw
+# pointer when it has one (it skips building a Stream object, which costs
+# more than the rest of a small call's marshalling), else the public API.
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _stream_handle(t):
-    import torch
-    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+    if _raw_stream is not None:
+        return _raw_stream(t.get_device())
+    return torch.cuda.current_stream(t.device).cuda_stream
 
 
 def _check_matrix(t, name, dtypes):
-    import torch
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
-    if t.dim() != 2:
+    shape = t.shape
+    if len(shape) != 2:
         raise ValueError(f"{name} must be 2-D")
     if t.dtype not in dtypes:
         raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
     if not t.is_cuda:
         raise ValueError(f"{name} must be a device tensor")
-    if t.numel() and t.shape[1] > 1 and t.stride(1) != 1:
+    if shape[0] and shape[1] > 1 and t.stride(1) != 1:
         raise ValueError(f"{name} needs unit stride along its last axis")
 
 
