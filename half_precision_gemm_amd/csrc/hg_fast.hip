@@ -207,6 +207,19 @@ __device__ __forceinline__ void static_for(F &&f)
 {
     static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
+// Keeps one row block of accumulators in accumulation registers up to this
+// point of the epilogue.  Without it the register allocator copies all 256
+// accumulators into VGPRs as the K loop exits (about 230 moves), which
+// leaves the epilogue too few VGPRs: it spilled a few values and reloaded
+// them with a wait for every store issued before.  Pinned block by block,
+// each block is read out of its registers where it is consumed.
+template <int N>
+__device__ __forceinline__ void pin_acc(floatx4 (&blk)[N])
+{
+#pragma unroll
+    for (int j = 0; j < N; ++j)
+        __asm__ volatile("" : "+a"(blk[j]));
+}
 
 // s_waitcnt on one counter only (the others left at their maxima).
 template <int n>
@@ -712,6 +725,7 @@ hgemm_fast_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int c
                 unsigned char *stg = smem + 2 * SLOT + wave * (FB * SROW);
 #pragma unroll
                 for (int i = 0; i < TM; ++i) {
+                    pin_acc(acc[i]);
                     celt *cr = crow(i);
 #pragma unroll
                     for (int j = 0; j < TN; ++j) {
@@ -764,6 +778,7 @@ hgemm_fast_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int c
                 // Edge tile: element-wise guarded stores.
 #pragma unroll
                 for (int i = 0; i < TM; ++i) {
+                    pin_acc(acc[i]);
                     const int row = T.m0 + wm * WTM + i * FB + frow;
                     if (row >= p.M)
                         continue;
