@@ -154,13 +154,28 @@ def cpu_baseline(A, Bt, target_s=15.0):
                       f"({rows}x{Bt.shape[0]} outputs, K={K}), {dt:.1f} s"}
 
 
-def _time_calls(fn, warmup, reps, stream):
+WARM_S = 0.05
+
+
+def _last_half_avg(ts):
+    h = ts[len(ts) // 2:]
+    return sum(h) / len(h)
+
+
+def _time_calls(fn, warmup, reps, stream, warm_s=WARM_S):
     """Per-call HIP-event times (ms) of `reps` calls after `warmup` untimed
-    ones, plus the mean over the same number of back-to-back calls (which
+    ones (and at least `warm_s` seconds of them: from an idle GPU the shader
+    clock takes some milliseconds to settle, longer than 20 calls of a short
+    kernel), plus the mean over the same number of back-to-back calls (which
     includes launch cost)."""
     import torch
-    for _ in range(warmup):
+    t0 = time.perf_counter()
+    n = 0
+    while n < warmup or time.perf_counter() - t0 < warm_s:
         fn()
+        n += 1
+        if n % 16 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(reps)]
@@ -607,8 +622,14 @@ def main():
                              "A": "lower, col-major fp16", "B": "col-major fp16"}
                             if do_trmm else None)},
         "pct_of_fp16_mfma_peak": round(100.0 * tflops / PEAK_FP16_TFLOPS, 2),
+        # Per step, in order: from an idle GPU the board's power control lets
+        # the first launches run fast, then cuts the clock and takes about
+        # twenty launches of this size to settle, so the average over few
+        # warm-up steps sits above the later steps.
         "hgemm_ms": {"avg": round(gemm_avg, 4), "min": round(min(gemm_ms), 4),
-                     "max": round(max(gemm_ms), 4)},
+                     "max": round(max(gemm_ms), 4),
+                     "last_half_avg": round(_last_half_avg(gemm_ms), 4),
+                     "per_step": [round(t, 4) for t in gemm_ms]},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_FP16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_FP16_TFLOPS, 4),
                      "traffic": prof_g.get("hbm_bytes_per_launch"),
@@ -622,7 +643,9 @@ def main():
         tavg = sum(trmm_ms) / len(trmm_ms)
         ttf = wt.flops / (tavg * 1e-3) / 1e12
         out["trmm_ms"] = {"avg": round(tavg, 4), "min": round(min(trmm_ms), 4),
-                          "max": round(max(trmm_ms), 4)}
+                          "max": round(max(trmm_ms), 4),
+                          "last_half_avg": round(_last_half_avg(trmm_ms), 4),
+                          "per_step": [round(t, 4) for t in trmm_ms]}
         out["trmm_effective_tflops"] = round(ttf, 2)
         # The one-launch TRMM is MFMA-bound: n(n+1)m useful flops against
         # 0.47 GB compulsory traffic (A's lower triangle, B, Out in fp32).
