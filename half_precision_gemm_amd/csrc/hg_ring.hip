@@ -21,6 +21,7 @@
 #include "hg_internal.h"
 
 #include <type_traits>
+#include <utility>
 
 typedef int32_t hg_r_int32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) uint32_t hg_r_lds_u32;
@@ -54,6 +55,18 @@ constexpr int BK = 64, RB = 128, KC = 8, THREADS = 256, NWAVES = 4;
 constexpr uint32_t OOB = 0x80000000u;
 
 __device__ __forceinline__ int swz(int r, int kc) { return kc ^ ((r >> 1) & (KC - 1)); }
+
+// f(std::integral_constant<int, 0>{}) ... f(std::integral_constant<int, N-1>{}).
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, I...>)
+{
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F &&f)
+{
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 template <int n>
 __device__ __forceinline__ void wait_vmcnt()
@@ -154,12 +167,11 @@ hgemm_ring_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int c
         const int64_t ld = isb ? p.ldb : p.lda;
         off[i] = row < rows ? (uint32_t)(row * (int)ld * 2 + kc * 16) : OOB;
     }
-    // Every load of stage kt into its ring slot.
-    auto issue = [&](int kt) {
+    // Load i of stage kt into its ring slot.
+    auto issue_one = [&](int kt, int i) __attribute__((always_inline)) {
         const int slot = kt % NS;
         const uint32_t kb = (uint32_t)(kt0 + kt) * RB;
-#pragma unroll
-        for (int i = 0; i < L; ++i) {
+        {
             const bool isb = i >= LA;
             hg_r_int32x4 r = isb ? rb : ra;
             uint32_t o = off[i];
@@ -176,6 +188,12 @@ hgemm_ring_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int c
             hg_ring_buffer_load_lds(r, reinterpret_cast<hg_r_lds_u32 *>((uintptr_t)dst), 16, (int)o,
                                     0, 0, 0);
         }
+    };
+    // Every load of stage kt.
+    auto issue = [&](int kt) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < L; ++i)
+            issue_one(kt, i);
     };
 
     floatx4 acc[TM][TN];
@@ -194,32 +212,27 @@ hgemm_ring_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int c
     struct Frags {
         half8 a[SPS][TM], b[SPS][TN];
     };
-    auto read_stage = [&](int kt, Frags &f) __attribute__((always_inline)) {
+    // Fragment r of stage kt (r < NR: k-step r / (TM + TN), then its TM A
+    // blocks and TN B blocks).
+    constexpr int NR = SPS * (TM + TN);
+    auto read_one = [&](int kt, Frags &f, auto rc) __attribute__((always_inline)) {
+        constexpr int r = decltype(rc)::value;
+        constexpr int s = r / (TM + TN), q = r % (TM + TN);
         const unsigned char *As = smem + (kt % NS) * SLOT;
-        const unsigned char *Bs = As + BM * RB;
-#pragma unroll
-        for (int s = 0; s < SPS; ++s) {
-#pragma unroll
-            for (int i = 0; i < TM; ++i) {
-                const int row = wm * WTM + i * 16 + frow;
-                f.a[s][i] = *reinterpret_cast<const half8 *>(As + row * RB + swz(row, 4 * s + fhi) * 16);
-            }
-#pragma unroll
-            for (int j = 0; j < TN; ++j) {
-                const int row = wn * WTN + j * 16 + frow;
-                f.b[s][j] = *reinterpret_cast<const half8 *>(Bs + row * RB + swz(row, 4 * s + fhi) * 16);
-            }
+        if constexpr (q < TM) {
+            const int row = wm * WTM + q * 16 + frow;
+            f.a[s][q] = *reinterpret_cast<const half8 *>(As + row * RB + swz(row, 4 * s + fhi) * 16);
+        } else {
+            const int row = wn * WTN + (q - TM) * 16 + frow;
+            f.b[s][q - TM] = *reinterpret_cast<const half8 *>(As + BM * RB + row * RB +
+                                                             swz(row, 4 * s + fhi) * 16);
         }
     };
-    auto mma_stage = [&](const Frags &f) __attribute__((always_inline)) {
-#pragma unroll
-        for (int s = 0; s < SPS; ++s)
-#pragma unroll
-            for (int j = 0; j < TN; ++j)
-#pragma unroll
-                for (int i = 0; i < TM; ++i)
-                    acc[i][j] = mfma_16x16x32<IN_BF16>(f.b[s][j], f.a[s][i], acc[i][j]);
+    auto read_stage = [&](int kt, Frags &f) __attribute__((always_inline)) {
+        static_for<NR>([&](auto rc) __attribute__((always_inline)) { read_one(kt, f, rc); });
     };
+    constexpr int NM = SPS * TN * TM;                      // MFMAs per stage and wave
+    constexpr bool SPREAD = BM >= 128;
     // Stage kt's fragments are read one stage ahead, during stage kt-1's
     // MFMAs, so the LDS latency hides behind the matrix core.  In step kt:
     // this wave's loads of stage kt+1 have landed (stages kt+2 .. kt+NS-2 may
@@ -282,9 +295,42 @@ hgemm_ring_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int c
             }
         }
         __builtin_amdgcn_s_barrier();
-        issue(kt + NS - 1);
-        read_stage(kt + 1, nxt);
-        mma_stage(cur);
+        if constexpr (!SPREAD) {
+            issue(kt + NS - 1);
+            read_stage(kt + 1, nxt);
+#pragma unroll
+            for (int s = 0; s < SPS; ++s)
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+#pragma unroll
+                    for (int i = 0; i < TM; ++i)
+                        acc[i][j] = mfma_16x16x32<IN_BF16>(cur.b[s][j], cur.a[s][i], acc[i][j]);
+            return;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // 128×128 tiles: the stage's 32 MFMAs per wave with the ring loads of
+        // stage kt+NS-1 and the reads of stage kt+1 at fixed positions
+        // between them (load l after MFMA l·NM/L, read r after MFMA r·NM/NR).
+        // Issued in a burst, the loads wait for the CU's memory path one
+        // after another and hold back the wave's MFMAs behind them (2048³:
+        // 23.1 -> 20.5 us).  With 64×64 tiles (8 MFMAs per wave) the stage is
+        // bound by that path either way and the burst order is kept.
+        static_for<NM>([&](auto mc) __attribute__((always_inline)) {
+            constexpr int m = decltype(mc)::value;
+            constexpr int s = m / (TN * TM), j = m / TM % TN, i = m % TM;
+            acc[i][j] = mfma_16x16x32<IN_BF16>(cur.b[s][j], cur.a[s][i], acc[i][j]);
+            static_for<L>([&](auto lc) __attribute__((always_inline)) {
+                constexpr int l = decltype(lc)::value;
+                if constexpr (l * NM / L == m)
+                    issue_one(kt + NS - 1, l);
+            });
+            static_for<NR>([&](auto rc) __attribute__((always_inline)) {
+                constexpr int r = decltype(rc)::value;
+                if constexpr (r * NM / NR == m)
+                    read_one(kt + 1, nxt, rc);
+            });
+            __builtin_amdgcn_sched_barrier(0);
+        });
     };
     for (int kt = 0; kt < nk; kt += 2) {
         step(kt, f0, f1);
