@@ -61,13 +61,16 @@ void plan_rec(int64_t o, int64_t s, int64_t leaf, int64_t depth, std::vector<Nod
 // schedule runs in one launch of 64×64 tiles rather than level by level.
 // In one launch the tiles of the first column walk all n/64 K stages, and
 // 64×64 tiles move more bytes per flop than the per-level launches' larger
-// tiles; measured (one box, HIP events): one launch wins at n = 4096, m = 256
-// (25 against 39 us), n = m = 2048 (36 / 53) and n = 4096, m = 1024
-// (68 / 72), and loses at n = 8192, m = 256 (74 / 60) and n = m = 4096
-// (191 / 139).  So: n <= 4096 and the work m·n² at most 2^34.
+// tiles, but with two or more tiles per CU two workgroups share each CU.
+// Measured back to back (one box, HIP events), one launch against level by
+// level: n = 4096, m = 2048 67 / 84 us, n = m = 4096 129 / 150, n = m = 3072
+// 68 / 118, n = 2048, m = 8192 79 / 104, n = 8192, m = 256 50 / 59, but
+// n = 8192, m = 1024 150 / 122 and n = 8192, m = 2048 225 / 230 (n = m =
+// 2048 and n = 4096, m = 1024 were one launch before: 23 and 43 us).  So:
+// n <= 4096, or the work m·n² at most 2^34.
 bool ring_fused_wanted(int64_t m, int64_t n)
 {
-    return n <= 4096 && (double)m * (double)n * (double)n <= 17179869184.0;
+    return n <= 4096 || (double)m * (double)n * (double)n <= 17179869184.0;
 }
 
 hg::Tile choose_batched_tile(int64_t M, int64_t maxN, int64_t nbatch)

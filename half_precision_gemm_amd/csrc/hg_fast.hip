@@ -818,6 +818,8 @@ hgemm_fast_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int c
     }
 }
 
+}  // namespace
+
 // Persistent grid size: one workgroup per CU (the 160 KiB ring allows one).
 // The count is cached per device; concurrent first calls may both query it
 // and store the same value (relaxed atomics: no data race).
@@ -836,6 +838,8 @@ int cu_count()
     }
     return n;
 }
+
+namespace {
 
 template <bool OUT_F16, bool BETA, bool TRI, bool EPI, bool IN_BF16 = false>
 hipError_t launch(const GemmParams &p, hipStream_t stream)

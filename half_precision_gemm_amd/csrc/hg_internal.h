@@ -48,6 +48,9 @@ __device__ __forceinline__ float epi_apply(float t, float bias, int act)
     return (act == 1 && t < 0.0f) ? 0.0f : t;
 }
 
+// Compute units of the current device (queried once per device).
+int cu_count();
+
 // Kernel families the launcher can pick.
 enum class Tile { Big, Mid, Small };
 

@@ -119,12 +119,15 @@ __device__ __forceinline__ void ring_map(int wg, int total, int tiles_m, int til
 // one entry of K = N = n this is the whole recursive TRMM in one launch
 // (see trmm_ring_fused_ok); with one entry per leaf, the leaves of the
 // per-level schedule.
-template <int BM, int BN, bool OUT_F16, bool BETA, bool KCHK, bool EPI, bool IN_BF16, bool TRI = false>
+// NSQ: the ring depth, 0 for the default (128 KiB of stages, at most 8);
+// NSQ = 5 with 64×64 tiles (80 KiB) lets two workgroups share a CU.
+template <int BM, int BN, bool OUT_F16, bool BETA, bool KCHK, bool EPI, bool IN_BF16, bool TRI = false,
+          int NSQ = 0>
 __global__ void __launch_bounds__(THREADS, 1)
 hgemm_ring_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int cvec)
 {
     constexpr int SLOT = (BM + BN) * RB;                   // one stage: A rows then B rows
-    constexpr int NS = (128 * 1024) / SLOT < 8 ? (128 * 1024) / SLOT : 8;   // ring depth
+    constexpr int NS = NSQ > 0 ? NSQ : (128 * 1024) / SLOT < 8 ? (128 * 1024) / SLOT : 8;   // ring depth
     constexpr int WTM = BM / 2, WTN = BN / 2;              // wave sub-tile
     constexpr int TM = WTM / 16, TN = WTN / 16;            // 16×16 blocks per wave
     constexpr int LA = BM / (NWAVES * 8), LB = BN / (NWAVES * 8);   // load instructions per wave
@@ -427,7 +430,7 @@ hgemm_ring_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int c
     }
 }
 
-template <int BM, int BN, bool OUT_F16, bool BETA, bool EPI, bool IN_BF16, bool TRI = false>
+template <int BM, int BN, bool OUT_F16, bool BETA, bool EPI, bool IN_BF16, bool TRI = false, int NSQ = 0>
 hipError_t launch_ring_cfg(const GemmParams &p, hipStream_t stream)
 {
     int maxN = 0;
@@ -448,10 +451,10 @@ hipError_t launch_ring_cfg(const GemmParams &p, hipStream_t stream)
     for (int b = 0; b < p.nbatch; ++b)
         cvec = cvec && (p.e[b].c_off % 4 == 0);
     if (kchk)
-        hipLaunchKernelGGL((hgemm_ring_kernel<BM, BN, OUT_F16, BETA, true, EPI, IN_BF16, TRI>), dim3((unsigned)total64),
+        hipLaunchKernelGGL((hgemm_ring_kernel<BM, BN, OUT_F16, BETA, true, EPI, IN_BF16, TRI, NSQ>), dim3((unsigned)total64),
                            dim3(THREADS), 0, stream, p, tiles_m, tiles_n, (int)total64, cvec);
     else
-        hipLaunchKernelGGL((hgemm_ring_kernel<BM, BN, OUT_F16, BETA, false, EPI, IN_BF16, TRI>), dim3((unsigned)total64),
+        hipLaunchKernelGGL((hgemm_ring_kernel<BM, BN, OUT_F16, BETA, false, EPI, IN_BF16, TRI, NSQ>), dim3((unsigned)total64),
                            dim3(THREADS), 0, stream, p, tiles_m, tiles_n, (int)total64, cvec);
     return hipGetLastError();
 }
@@ -524,6 +527,12 @@ bool trmm_ring_fused_ok(const GemmParams &p)
 
 hipError_t launch_trmm_fused_ring(const GemmParams &p, hipStream_t stream)
 {
+    // With at least two tiles per CU, a 5-stage ring (80 KiB) lets two
+    // workgroups share each CU: n = m = 2048 (1024 tiles) 33.0 -> 21.9 us.
+    // With fewer tiles one workgroup per CU gets the deeper default ring.
+    const int64_t tiles = (int64_t)((p.M + 63) / 64) * ((p.e[0].N + 63) / 64);
+    if (tiles >= 2 * (int64_t)cu_count())
+        return launch_ring_cfg<64, 64, false, false, false, false, true, 5>(p, stream);
     return launch_ring_cfg<64, 64, false, false, false, false, true>(p, stream);
 }
 
