@@ -145,8 +145,10 @@ def test_one_launch_other_triangle_never_read(hg, uplo, trans):
 # ---- The one-launch schedule on 64×64 tiles (problems with too few 256×256
 # tiles for that one: n <= 4096 or m·n² <= 2^34, boundaries on the 64 grid),
 # all four variants, NaN in the triangle that is never read, ragged m.
-# The last has at least two 64×64 tiles per CU (the 5-stage ring).
-RING_ONE_LAUNCH = [(2048, 256, 256), (1024, 100, 128), (4096, 64, 256), (2048, 1024, 256)]
+# The last two have at least two 64×64 tiles per CU (the 5-stage ring), the
+# very last with a ragged m.
+RING_ONE_LAUNCH = [(2048, 256, 256), (1024, 100, 128), (4096, 64, 256), (2048, 1024, 256),
+                   (2048, 1000, 128)]
 
 
 @pytest.mark.parametrize("uplo,trans", VARIANTS)
