@@ -64,13 +64,18 @@ void plan_rec(int64_t o, int64_t s, int64_t leaf, int64_t depth, std::vector<Nod
 // tiles, but with two or more tiles per CU two workgroups share each CU.
 // Measured back to back (one box, HIP events), one launch against level by
 // level: n = 4096, m = 2048 67 / 84 us, n = m = 4096 129 / 150, n = m = 3072
-// 68 / 118, n = 2048, m = 8192 79 / 104, n = 8192, m = 256 50 / 59, but
-// n = 8192, m = 1024 150 / 122 and n = 8192, m = 2048 225 / 230 (n = m =
-// 2048 and n = 4096, m = 1024 were one launch before: 23 and 43 us).  So:
-// n <= 4096, or the work m·n² at most 2^34.
+// 68 / 118, n = 2048, m = 8192 79 / 104, n = 8192, m = 256 50 / 59, n = 8192,
+// m = 512 87 / 93, n = 6144, m = 512 60 / 85, n = 16384, m = 64 77 / 118;
+// but n = 8192, m = 1024 150 / 122, n = 8192, m = 2048 225 / 230 and
+// n = 12288, m = 128 100 / 77 (there the tiles of the first column, which
+// walk all n/64 stages, set the time); n = 6144, m = 256 55 / 52 and
+// n = 16384, m = 128 111 / 119 are close either way (n = m = 2048 and
+// n = 4096, m = 1024 were one launch before: 23 and 43 us).  So: n <= 4096,
+// or n <= 8192 with m <= 512, or the work m·n² at most 2^34.
 bool ring_fused_wanted(int64_t m, int64_t n)
 {
-    return n <= 4096 || (double)m * (double)n * (double)n <= 17179869184.0;
+    return n <= 4096 || (n <= 8192 && m <= 512) ||
+           (double)m * (double)n * (double)n <= 17179869184.0;
 }
 
 hg::Tile choose_batched_tile(int64_t M, int64_t maxN, int64_t nbatch)

@@ -178,7 +178,8 @@ def _fp32_bound(A_cm, B_cm, ri, cj, alpha, n, leaf):
                                                  (3072, 64, 256, True), (2560, 100, 256, False),
                                                  (2500, 64, 256, False),
                                                  # 64×64 one launch, two workgroups per CU
-                                                 (3072, 3072, 256, True), (2048, 1024, 128, True)])
+                                                 (3072, 3072, 256, True), (2048, 1024, 128, True),
+                                                 (8192, 300, 256, True)])
 def test_schedules_agree(hg, n, m, leaf, one_launch):
     print(f"[case] trmm schedules n={n} m={m} leaf={leaf}", flush=True)
     A_cm, B_cm = trmm_inputs(n, m, n + 3 * m + leaf)

@@ -143,7 +143,8 @@ def test_one_launch_other_triangle_never_read(hg, uplo, trans):
 
 
 # ---- The one-launch schedule on 64×64 tiles (problems with too few 256×256
-# tiles for that one: n <= 4096 or m·n² <= 2^34, boundaries on the 64 grid),
+# tiles for that one: n <= 4096, n <= 8192 with m <= 512, or m·n² <= 2^34;
+# boundaries on the 64 grid),
 # all four variants, NaN in the triangle that is never read, ragged m.
 # The last two have at least two 64×64 tiles per CU (the 5-stage ring), the
 # very last with a ragged m.
