@@ -223,10 +223,13 @@ int hgemm_bf16_bias_act(int64_t M, int64_t N, int64_t K, float alpha,
  * output tiles per compute unit, all terms run in one launch in which each
  * output tile walks its own terms in that order and adds each update to
  * the leaf in its fp32 accumulators (alpha applied once, when the tile is
- * written); otherwise one batched launch runs all leaves and one each
- * update level, rounding Out to fp32 after every update.  The two
- * schedules differ only by those fp32 roundings (integer-valued inputs:
- * the same bits; see hg_trmm_lower_trans_by_level).
+ * written).  With fewer such tiles, the same one-launch schedule runs on
+ * 64×64 output tiles when every boundary falls on a multiple of 64 (leaf
+ * >= 64, the same alignment) and n <= 4096, or n <= 8192 with m <= 512, or
+ * m·n² <= 2^34.  Otherwise one batched launch runs all leaves and one each
+ * update level, rounding Out to fp32 after every update.  The schedules
+ * differ only by those fp32 roundings (integer-valued inputs: the same
+ * bits; see hg_trmm_lower_trans_by_level).
  */
 int trmm_lower_trans(int64_t n, int64_t m, float alpha,
                      const void *A, int64_t lda,
