@@ -36,10 +36,13 @@
  * are asynchronous on `stream` (a hipStream_t; NULL = the default stream);
  * results are valid once the stream has been synchronised.  The library
  * allocates no memory, never copies between host and device and keeps no
- * state beyond a per-device cache of the compute-unit count (atomic), so
- * calls from several host threads are safe; hg_trmm_lower_trans_streams
- * creates and destroys HIP events within each call.  The caller owns every
- * buffer, including the device workspaces some entry points take.
+ * host state beyond per-device caches (the compute-unit count and the
+ * address of hgemm_splitk_noalloc's static device array; atomics), so calls
+ * from several host threads are safe (hgemm_splitk_noalloc's calls that
+ * overlap on one GPU share that array: see there);
+ * hg_trmm_lower_trans_streams creates and destroys HIP events within each
+ * call.  The caller owns every buffer, including the device workspaces some
+ * entry points take.
  *
  * Return value: 0 on success.  A negative value -i means argument i (1-based,
  * in the order of the prototype) is invalid, following the BLAS xerbla
