@@ -266,7 +266,10 @@ __device__ __forceinline__ void map_tile(int id, int total, int tiles_m, int til
 
 // Everything a workgroup needs to know about one tile.
 struct TileInfo {
-    int batch, m0, n0, N, K, rows_a, rows_b, kt0, nk;
+    int batch, m0, n0, N, K, rows_a, rows_b, nk;
+    // K stage (BK columns) of loop step kt: kbase + kdir·kt.  The one-launch
+    // TRMM's short tiles walk their stages downward (kdir = -1).
+    int kbase, kdir;
     hg_int32x4 ra, rb;
 };
 
@@ -293,8 +296,9 @@ __device__ __forceinline__ bool find_tile(const GemmParams &p, int &id, int stri
         T.rows_b = min(N - n0, BN);
         // TRI: B element (j, k) counts only for k >= j, so slices wholly
         // left of the tile's first column are skipped.
-        T.kt0 = TRI ? n0 / BK : 0;
-        T.nk = (T.K + BK - 1) / BK - T.kt0;
+        T.kbase = TRI ? n0 / BK : 0;
+        T.nk = (T.K + BK - 1) / BK - T.kbase;
+        T.kdir = 1;
         const _Float16 *Ab = p.A + p.e[batch].a_off + (int64_t)m0 * p.lda;
         const _Float16 *Bb = p.B + p.e[batch].b_off + (int64_t)n0 * p.ldb;
         T.ra = make_rsrc(Ab, (uint32_t)(((int64_t)(T.rows_a - 1) * p.lda + T.K) * 2));
@@ -315,8 +319,9 @@ __device__ __forceinline__ bool find_tile(const GemmParams &p, int &id, int stri
 // contiguous K ranges in increasing order -- the leaf's end, then the ends
 // of the ancestors whose upper half holds the tile, deepest first, the last
 // one n -- which is the order in which the depth-first recursion
-// accumulates into that tile.  One workgroup therefore walks K from the
-// tile's first column to n in that order, and each update's β = 1
+// accumulates into that tile.  One workgroup therefore walks K over the
+// tile's first column to n (in that order, or -- the short tiles below -- in
+// the reverse one), and each update's β = 1
 // accumulation into the tile happens in the fp32 accumulators rather than
 // through a store and a reload of Out; α, common to the leaf and every
 // update, is applied once when the tile is written.  The level-by-level
@@ -331,17 +336,22 @@ __device__ __forceinline__ bool find_tile(const GemmParams &p, int &id, int stri
 // that the XCD's share of a round covers (ids regrouped per XCD, then bands
 // of rows walked pair column by pair column, as for the GEMM's tiles).
 // Counting time t in K blocks from the start of a round:
-//   lower (not tri_up): the short tile (tm, T-1-c) takes c + 1 blocks; the
-//   long tile (tm, c) then starts at t = c + 1 at K block c, so it is at K
-//   block t - 1 at time t whatever c is;
+//   lower (not tri_up): the short tile (tm, T-1-c) takes c + 1 blocks,
+//   walking down from K block T-1, so it is at K block T-1-t; the long tile
+//   (tm, c) then starts at t = c + 1 at K block c and walks up, so it is at K
+//   block t - 1 at time t; both whatever c is;
 //   tri_up: the long tile (tm, T-1-c) starts at t = 0 at K block 0 and is at
-//   K block t, whatever c is; the short tile (tm, c) follows.
-// The long tiles of co-resident jobs thus read the same K slabs of the
+//   K block t; the short tile (tm, c) follows at t = T - c, walking down from
+//   its diagonal block c, so it is at K block T - t.
+// The tiles of co-resident jobs thus read the same K slabs of the
 // right-hand side at the same time and share them in L2, as the tiles of a
-// GEMM do; only the short tiles (a quarter of the work at n = 8192) are
-// staggered.  With T odd, the middle column's tiles pair up by rows (a
-// last odd row is a job of one tile).  Each tile still walks its own K
-// range in recursion order.
+// GEMM do.  The long tiles walk K in the recursion's order of accumulation
+// (the updates' K ranges after the leaf's; tri_up: the outermost update
+// first, the leaf last), the short tiles in the reverse one; the order
+// changes only fp32 rounding.  (Walking upward too, the short tiles, a
+// quarter of the work at n = 8192, read staggered slabs: 1.5-2 % slower.)
+// With T odd, the middle column's tiles pair up by rows (a last odd row is a
+// job of one tile) and walk upward.
 #ifndef HG_TRMM_BAND
 #define HG_TRMM_BAND 4
 #endif
@@ -386,8 +396,12 @@ __device__ __forceinline__ bool fused_item(const GemmParams &p, int w, int G, in
         T.K = K;
         T.rows_a = min(p.M - m0, BM);
         T.rows_b = min(N - n0, BN);
-        T.kt0 = p.tri_up ? 0 : n0 / BK;
+        const int kt0 = p.tri_up ? 0 : n0 / BK;
         T.nk = p.tri_up ? (n0 + BN) / BK : (K - n0) / BK;
+        // The short tile of a pair job walks its stages downward.
+        const bool down = q < Jp && second == (p.tri_up ? 1 : 0);
+        T.kbase = down ? kt0 + T.nk - 1 : kt0;
+        T.kdir = down ? -1 : 1;
         const _Float16 *Ab = p.A + (int64_t)m0 * p.lda;
         const _Float16 *Bb = p.B + (int64_t)n0 * p.ldb;
         T.ra = make_rsrc(Ab, (uint32_t)(((int64_t)(T.rows_a - 1) * p.lda + K) * 2));
@@ -443,12 +457,12 @@ hgemm_fast_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int c
     // multiple of BK) the last stage is partial: each lane's chunk is checked
     // against K and chunks past it get the out-of-range offset.
     auto issue = [&](const TileInfo &T, bool isb, int kt, int slot, int i) {
-        const uint32_t kb = (uint32_t)(T.kt0 + kt) * RB;
+        const uint32_t kb = (uint32_t)(T.kbase + T.kdir * kt) * RB;
         const uint32_t sbase = lds_base + (isb ? LDS_B : 0) + slot * SLOT + wave * RPW * RB;
         hg_int32x4 r = isb ? T.rb : T.ra;
         uint32_t off = isb ? boff[i] : aoff[i];
         if constexpr (KCHK) {
-            const int kval = T.K - (T.kt0 + kt) * BK;  // K % 8 == 0: chunks are all in or all out
+            const int kval = T.K - (T.kbase + T.kdir * kt) * BK;  // K % 8 == 0: chunks are all in or all out
             off = lkc[i] * 8 < kval ? off + kb : OOB;
         } else {
             const uint64_t base = ((uint64_t)(uint32_t)r[1] << 32 | (uint32_t)r[0]) + kb;
@@ -500,7 +514,7 @@ hgemm_fast_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int c
     // index) - (the stage's first k), element k of the stage (0..63) is
     // zeroed when k < jr (tri_up: k > jr).
     auto zero_tri = [&](const TileInfo &T, int kt, int slot) {
-        const int jr0 = __builtin_amdgcn_readfirstlane(T.n0 + wave * RPW - (T.kt0 + kt) * BK);
+        const int jr0 = __builtin_amdgcn_readfirstlane(T.n0 + wave * RPW - (T.kbase + T.kdir * kt) * BK);
         const bool up = p.tri_up != 0;
         if (up ? jr0 >= BK - 1 : jr0 + RPW - 1 <= 0)
             return;                                      // nothing to zero in this wave's rows
@@ -526,9 +540,12 @@ hgemm_fast_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int c
             *cp = w;
         }
     };
-    // Whether stage kt of tile T is one of its diagonal block's stages.
+    // Whether loop step kt of tile T is one of its diagonal block's stages:
+    // the first BN/BK of its walk, or the last when it walks toward the
+    // diagonal (tri_up upward, or lower downward).
     auto tri_stage = [&](const TileInfo &T, int kt) {
-        return p.tri_up ? kt >= T.nk - BN / BK && kt < T.nk : kt < BN / BK && kt < T.nk;
+        return (p.tri_up != 0) != (T.kdir < 0) ? kt >= T.nk - BN / BK && kt < T.nk
+                                               : kt < BN / BK && kt < T.nk;
     };
 
     int id = FUSED ? 0 : blockIdx.x;  // FUSED: the work item

@@ -206,17 +206,22 @@ def test_one_launch_odd_tile_columns(hg):
     """n = 768 with leaf >= n is a single leaf of 3 tile columns (the only way
     an odd count of 256-wide columns reaches the one-launch schedule), and
     m = 44288 gives 173 tile rows: the middle column's tiles pair up by rows
-    and the last forms a job of its own.  A single leaf is the same K loop in
-    both schedules, so the two agree bit for bit; sampled entries against the
-    oracle."""
+    and the last forms a job of its own.  A single leaf is one K loop per tile
+    in both schedules; the one-launch schedule walks it upward in tile
+    columns 0 (the long tile of each pair) and 1 (the middle column), as the
+    level-by-level one does, so there the two agree bit for bit, and
+    downward in column 2 (the short tile), where they differ by fp32
+    rounding only.  Sampled entries against the oracle and its fp32 bound."""
     n, m = 768, 44288
     A_cm, B_cm = trmm_inputs(n, m, 29)
     one = run(hg, A_cm, B_cm, 1.5, 768)
     lev = run(hg, A_cm, B_cm, 1.5, 768, by_level=True)
-    assert np.array_equal(one.view(np.uint32), lev.view(np.uint32))
+    assert np.array_equal(one[:, :512].view(np.uint32), lev[:, :512].view(np.uint32))
     ri, cj = workloads.sample_indices(31, n, m, 4096)
     ref = oracle.trmm_lower_trans_sampled(A_cm, B_cm, ri, cj, 1.5)
     check_close(one[cj, ri], ref, n, "n=768 m=44288 one launch")
+    lim = _fp32_bound(A_cm, B_cm, ri, cj, 1.5, n, 768)
+    assert (np.abs(one[cj, ri] - ref) <= lim).all()
 
 
 def test_one_launch_integer_bit_exact(hg):
