@@ -655,7 +655,7 @@ def main():
             "bound_ms": round(wt.flops / (PEAK_FP16_TFLOPS * 1e12) * 1e3, 4),
             "traffic": prof_t.get("hbm_bytes_per_launch"),
             "kernel": "hgemm_fast_kernel, one-launch recursive TRMM (each 256x256 output tile walks its "
-                      "leaf and its updates in recursion order), n = m = 8192, leaf 256, fp32 out",
+                      "leaf and its updates in its fp32 accumulators), n = m = 8192, leaf 256, fp32 out",
             "algorithmic_flops_per_launch": wt.flops,
             "algorithmic_bytes_per_launch": wt.n * (wt.n + 1) + 2 * wt.n * wt.m + 4 * wt.n * wt.m,
             **clock_fields(prof_t, ttf)}

@@ -252,8 +252,8 @@ int64_t hg_trmm_plan(int64_t n, int64_t leaf, int64_t *nodes, int64_t cap)
 namespace {
 
 // Both TRMM entry points: `fused` allows the one-launch schedule (each
-// output tile walks its own leaf and updates in recursion order, adding the
-// updates in its accumulators); without
+// output tile walks its own leaf and updates, adding the updates in its
+// accumulators); without
 // it, or when the recursion's boundaries do not fall on tile edges, one
 // batched launch per recursion level.
 // With `streams` (nstreams > 1, fused off) the per-level schedule puts each

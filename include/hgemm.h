@@ -19,8 +19,10 @@
  *                     updates by hgemm's GEMM kernel.  By default (aligned
  *                     operands, recursion boundaries on 256-column tile edges)
  *                     the whole recursion is one launch: each output tile
- *                     walks its leaf and then its updates in recursion order
- *                     and adds the updates in its fp32 accumulators.
+ *                     walks its leaf and its updates (in recursion order, or
+ *                     the reverse one for the shorter tile of each pair of
+ *                     tiles a workgroup takes) and adds the updates in its
+ *                     fp32 accumulators.
  *                     hg_trmm_lower_trans_by_level runs the page's schedule
  *                     literally: one launch for the leaves, then one GEMM
  *                     launch with beta = 1 per recursion level.
@@ -224,9 +226,11 @@ int hgemm_bf16_bias_act(int64_t M, int64_t N, int64_t K, float alpha,
  * 256 split down to leaves of at least 256), the operands are 16-byte
  * aligned with lda, ldb multiples of 8 and there are at least two 256×256
  * output tiles per compute unit, all terms run in one launch in which each
- * output tile walks its own terms in that order and adds each update to
- * the leaf in its fp32 accumulators (alpha applied once, when the tile is
- * written).  With fewer such tiles, the same one-launch schedule runs on
+ * output tile walks its own terms and adds each update to the leaf in its
+ * fp32 accumulators (alpha applied once, when the tile is written); a
+ * workgroup takes output tile columns c and T-1-c of one tile row (T tile
+ * columns) in turn, the longer walk in that order, the shorter one in the
+ * reverse order, so that concurrent tiles read the same slices of B.  With fewer such tiles, the same one-launch schedule runs on
  * 64×64 output tiles when every boundary falls on a multiple of 64 (leaf
  * >= 64, the same alignment) and n <= 4096, or n <= 8192 with m <= 512, or
  * m·n² <= 2^34.  Otherwise one batched launch runs all leaves and one each
@@ -262,7 +266,7 @@ int trmm_lower_trans(int64_t n, int64_t m, float alpha,
  * one-launch schedule applies (see trmm_lower_trans), run it with the
  * triangle on the other side of the GEMM view: each output tile walks K from
  * 0 up to its diagonal block (the recursion's outermost update first, the
- * leaf last), on A itself (upper/trans) or on an upper triangular copy of Aᵀ
+ * leaf last; the shorter tile of each pair the other way), on A itself (upper/trans) or on an upper triangular copy of Aᵀ
  * (lower/notrans).  Otherwise they run on a lower triangular L with the row
  * order reversed by P: upper/trans: P·Out = (P·A·P)ᵀ·(P·B); lower/notrans:
  * P·Out = (P·Aᵀ·P)ᵀ·(P·B), B's rows reversed into the workspace and Out's
