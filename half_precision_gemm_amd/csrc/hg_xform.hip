@@ -74,6 +74,71 @@ __global__ void __launch_bounds__(256) tri_xform_kernel(const _Float16 *__restri
 }
 
 typedef _Float16 half8v __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+
+// The same maps with 16-byte accesses, for n a multiple of 64, A and L
+// 16-byte aligned and lda, ldl multiples of 8: each wave moves one 64×64
+// tile of the triangle (the tile set of tri_xform_kernel).  Lane (rb, cb) =
+// (lane / 8, lane % 8):
+//   MODE 2 copies columns 8rb..8rb+7 of the L tile, rows 8cb..8cb+7 of each:
+//          one 16-byte chunk of A's mirrored column, its 8 elements reversed;
+//   MODES 1, 3, 4 load the 8×8 block of L rows 8rb.., columns 8cb.. as 8
+//          chunks (L row y, columns x..x+7: A column y, rows x..x+7 for the
+//          plain transposes; A column n-1-y, rows n-8-x..n-1-x reversed for
+//          MODE 3), transpose it in registers and store 8 L column chunks.
+// The 8 lanes of one rb (loads) or one cb (stores) cover a whole 128-byte
+// line of one column.
+template <int MODE>
+__global__ void __launch_bounds__(256) tri_xform64_kernel(const _Float16 *__restrict__ A, int64_t lda,
+                                                          _Float16 *__restrict__ L, int64_t ldl, int n,
+                                                          int ntiles)
+{
+    const int b = blockIdx.x * 4 + (int)(threadIdx.x >> 6);
+    if (b >= ntiles)
+        return;
+    int tr = (int)((__builtin_sqrtf(8.0f * (float)b + 1.0f) - 1.0f) * 0.5f);
+    while ((tr + 1) * (tr + 2) / 2 <= b)
+        ++tr;
+    while (tr * (tr + 1) / 2 > b)
+        --tr;
+    const int tc = b - tr * (tr + 1) / 2;
+    const int64_t R0 = (int64_t)(MODE == 4 ? tc : tr) * XT, C0 = (int64_t)(MODE == 4 ? tr : tc) * XT;
+    const int lane = threadIdx.x & 63, rb = lane >> 3, cb = lane & 7;
+    if constexpr (MODE == 2) {
+        const int64_t r = R0 + 8 * cb;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int64_t c = C0 + 8 * rb + k;
+            const half8v v = *reinterpret_cast<const half8v *>(A + (n - 1 - c) * lda + (n - 8 - r));
+            *reinterpret_cast<half8v *>(L + c * ldl + r) = __builtin_shufflevector(v, v, 7, 6, 5, 4, 3, 2, 1, 0);
+        }
+    } else {
+        const int64_t y0 = R0 + 8 * rb, x = C0 + 8 * cb;
+        u32x4v in[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int64_t y = y0 + k;
+            if constexpr (MODE == 3) {
+                const half8v v = *reinterpret_cast<const half8v *>(A + (n - 1 - y) * lda + (n - 8 - x));
+                in[k] = __builtin_bit_cast(u32x4v, __builtin_shufflevector(v, v, 7, 6, 5, 4, 3, 2, 1, 0));
+            } else {
+                in[k] = *reinterpret_cast<const u32x4v *>(A + y * lda + x);
+            }
+        }
+        // in[e] half k2 = L(y0 + e, x + k2); L column x + k2, rows y0..y0+7:
+        // dword d packs rows 2d (low half) and 2d + 1.
+#pragma unroll
+        for (int k2 = 0; k2 < 8; ++k2) {
+            u32x4v o;
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                const uint32_t lo = in[2 * d][k2 >> 1], hi = in[2 * d + 1][k2 >> 1];
+                o[d] = (k2 & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
+            }
+            *reinterpret_cast<u32x4v *>(L + (x + k2) * ldl + y0) = o;
+        }
+    }
+}
 
 // D = Sᵀ for row-major fp16 matrices: S is rows×cols (S[r·lds + c]), D is
 // cols×rows (D[c·ldd + r]).  64×64 tiles through LDS so that both the reads
@@ -264,6 +329,28 @@ hipError_t launch_tri_xform(int mode, const _Float16 *A, int64_t lda, _Float16 *
     const int64_t tiles = nt * (nt + 1) / 2;
     if (tiles > 0x7fffffff || n > 0x7fffffff)
         return hipErrorInvalidValue;
+    const bool vec = n % XT == 0 && lda % 8 == 0 && ldl % 8 == 0 && reinterpret_cast<uintptr_t>(A) % 16 == 0 &&
+                     reinterpret_cast<uintptr_t>(L) % 16 == 0;
+    if (vec) {
+        const dim3 grid((unsigned)((tiles + 3) / 4));
+        switch (mode) {
+        case 1:
+            hipLaunchKernelGGL(tri_xform64_kernel<1>, grid, dim3(256), 0, stream, A, lda, L, ldl, (int)n, (int)tiles);
+            break;
+        case 2:
+            hipLaunchKernelGGL(tri_xform64_kernel<2>, grid, dim3(256), 0, stream, A, lda, L, ldl, (int)n, (int)tiles);
+            break;
+        case 3:
+            hipLaunchKernelGGL(tri_xform64_kernel<3>, grid, dim3(256), 0, stream, A, lda, L, ldl, (int)n, (int)tiles);
+            break;
+        case 4:
+            hipLaunchKernelGGL(tri_xform64_kernel<4>, grid, dim3(256), 0, stream, A, lda, L, ldl, (int)n, (int)tiles);
+            break;
+        default:
+            return hipErrorInvalidValue;
+        }
+        return hipGetLastError();
+    }
     switch (mode) {
     case 1:
         hipLaunchKernelGGL(tri_xform_kernel<1>, dim3((unsigned)tiles), dim3(256), 0, stream, A, lda, L, ldl, (int)n);
@@ -282,8 +369,6 @@ hipError_t launch_tri_xform(int mode, const _Float16 *A, int64_t lda, _Float16 *
     }
     return hipGetLastError();
 }
-
-typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
 
 // D = Sᵀ when rows and cols are multiples of 64 and rows are 16-byte
 // aligned, without LDS: each wave moves one 64×64 tile.  Lane (rb, cb) =

@@ -46,7 +46,10 @@ def _ref(A_cm, B_cm, alpha, uplo, trans):
 
 @pytest.mark.parametrize("uplo,trans", VARIANTS)
 @pytest.mark.parametrize("n,m,leaf", [(1, 1, 256), (2, 5, 256), (300, 77, 256), (1000, 50, 100),
-                                      (2048, 300, 256), (4096, 256, 256), (777, 64, 64)])
+                                      (2048, 300, 256), (4096, 256, 256), (777, 64, 64),
+                                      # n a multiple of 64 with boundaries off the 64 grid (pieces
+                                      # of 160): the per-level schedule on the 16-byte copies of A
+                                      (2560, 100, 256)])
 def test_parity(hg, uplo, trans, n, m, leaf):
     A_cm, B_cm = _inputs(n, m, n + m, uplo)
     got = run(hg, A_cm, B_cm, -0.75, uplo, trans, leaf)
