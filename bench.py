@@ -456,8 +456,9 @@ def config_sweep(hg, stream, main_gemm_ms=None, main_trmm_ms=None, only=None):
         res["trmm_8192_inplace"] = {
             "gpu_ms_median": round(ts[len(ts) // 2], 5), "gpu_ms_min": round(ts[0], 5),
             "effective_tflops": round(w.flops / (ts[len(ts) // 2] * 1e-3) / 1e12, 2),
-            "note": "B <- A*B in fp16, A lower: the lower, non-transposed product into an fp32 "
-                    "workspace, then one rounding pass into B"}
+            "note": "B <- A*B in fp16, A lower: the lower, non-transposed product in one launch "
+                    "whose tiles round alpha*acc (fp32) to fp16 into the workspace, then one "
+                    "device-to-device copy into B"}
         del Ad, B0, Bd, TA, TB, work
     for name, w in workloads.TRSM_WORKLOADS.items():
         if not want(name):

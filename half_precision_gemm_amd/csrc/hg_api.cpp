@@ -78,6 +78,46 @@ bool ring_fused_wanted(int64_t m, int64_t n)
            (double)m * (double)n * (double)n <= 17179869184.0;
 }
 
+// The one-launch TRMM in the row-major view of the column-major operands
+// (C = Outᵀ, M = m; its A is Bᵀ; its B is the triangle T, N = K = n): T
+// lower walked down from each tile's diagonal block, or (tri_up) T upper
+// walked from K = 0 up to it.
+hg::GemmParams one_launch_params(const void *T, int64_t ldt, const void *B, int64_t ldb, void *Out,
+                                 int64_t ldo, int64_t m, int64_t n, float alpha, int64_t leaf, bool tri_up)
+{
+    hg::GemmParams p{};
+    p.A = static_cast<const _Float16 *>(B);
+    p.B = static_cast<const _Float16 *>(T);
+    p.C = Out;
+    p.lda = ldb;
+    p.ldb = ldt;
+    p.ldc = ldo;
+    p.M = (int32_t)m;
+    p.alpha = alpha;
+    p.beta = 1.0f;
+    p.leaf = (int32_t)std::min<int64_t>(leaf <= 0 ? 256 : leaf, kI32Max);
+    p.tri_up = tri_up ? 1 : 0;
+    p.nbatch = 1;
+    p.e[0] = {0, 0, 0, (int32_t)n, (int32_t)n};
+    return p;
+}
+
+// Which one-launch kernel runs p: 1 the 256×256 tiles, 2 the 64×64 tiles,
+// 0 none (the per-level launches run instead).
+int one_launch_kind(const hg::GemmParams &p, int64_t m, int64_t n)
+{
+    if (hg::trmm_fused_ok(p))
+        return 1;
+    if (ring_fused_wanted(m, n) && hg::trmm_ring_fused_ok(p))
+        return 2;
+    return 0;
+}
+
+hipError_t launch_one_launch(const hg::GemmParams &p, int kind, bool out_f16, hipStream_t s)
+{
+    return kind == 1 ? hg::launch_trmm_fused(p, s, out_f16) : hg::launch_trmm_fused_ring(p, s, out_f16);
+}
+
 hg::Tile choose_batched_tile(int64_t M, int64_t maxN, int64_t nbatch)
 {
     const int64_t big = ((M + 255) / 256) * ((maxN + 255) / 256) * nbatch;
@@ -316,15 +356,10 @@ int trmm_impl(int64_t n, int64_t m, float alpha, const void *A, int64_t lda, con
     const bool base_vec = aligned16(A) && aligned16(B) && lda % 8 == 0 && ldb % 8 == 0;
 
     if (fused) {
-        hg::GemmParams p = base;
-        p.beta = 1.0f;
-        p.leaf = (int32_t)std::min<int64_t>(leaf, kI32Max);
-        p.nbatch = 1;
-        p.e[0] = {0, 0, 0, (int32_t)n, (int32_t)n};
-        if (hg::trmm_fused_ok(p))
-            return hip_status(hg::launch_trmm_fused(p, s));
-        if (ring_fused_wanted(m, n) && hg::trmm_ring_fused_ok(p))
-            return hip_status(hg::launch_trmm_fused_ring(p, s));
+        const hg::GemmParams p = one_launch_params(A, lda, B, ldb, Out, ldo, m, n, alpha, leaf, false);
+        const int kind = one_launch_kind(p, m, n);
+        if (kind != 0)
+            return hip_status(launch_one_launch(p, kind, false, s));
     }
 
     // Several streams: events to join them between levels (every stream
@@ -821,27 +856,16 @@ int hg_trmm(int uplo, int trans, int64_t n, int64_t m, float alpha, const void *
     // diagonal block (tri_up), with no row reversal of B or Out.
     if ((uplo == HG_UPPER && trans == HG_TRANS) || (uplo == HG_LOWER && trans == HG_NOTRANS)) {
         const bool copy = uplo == HG_LOWER;
-        hg::GemmParams p{};
-        p.A = static_cast<const _Float16 *>(B);
-        p.B = copy ? L : static_cast<const _Float16 *>(A);
-        p.C = Out;
-        p.lda = ldb;
-        p.ldb = copy ? v.ldl : lda;
-        p.ldc = ldo;
-        p.M = (int32_t)m;
-        p.alpha = alpha;
-        p.leaf = (int32_t)std::min<int64_t>(leaf <= 0 ? 256 : leaf, kI32Max);
-        p.tri_up = 1;
-        p.nbatch = 1;
-        p.e[0] = {0, 0, 0, (int32_t)n, (int32_t)n};
-        const bool big = hg::trmm_fused_ok(p);
-        if (big || (ring_fused_wanted(m, n) && hg::trmm_ring_fused_ok(p))) {
+        const hg::GemmParams p = one_launch_params(copy ? static_cast<const void *>(L) : A, copy ? v.ldl : lda,
+                                                   B, ldb, Out, ldo, m, n, alpha, leaf, true);
+        const int kind = one_launch_kind(p, m, n);
+        if (kind != 0) {
             if (copy) {
                 const int st = hip_status(hg::launch_tri_xform(4, static_cast<const _Float16 *>(A), lda, L, v.ldl, n, s));
                 if (st != HG_OK)
                     return st;
             }
-            return hip_status(big ? hg::launch_trmm_fused(p, s) : hg::launch_trmm_fused_ring(p, s));
+            return hip_status(launch_one_launch(p, kind, false, s));
         }
     }
     int st = hip_status(hg::launch_tri_xform(v.mode, static_cast<const _Float16 *>(A), lda, L, v.ldl, n, s));
@@ -1032,12 +1056,41 @@ int hg_trmm_inplace(int uplo, int trans, int64_t n, int64_t m, float alpha, cons
         return -8;
     float *X = static_cast<float *>(work);
     unsigned char *vwork = static_cast<unsigned char *>(work) + x_bytes;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    // When the variant runs in one launch, its tiles round alpha·acc to fp16
+    // themselves (the rounding the fp32 route below applies to the same fp32
+    // value) into the workspace's first ldx·m·2 bytes, and one copy moves the
+    // product into B: at n = m = 8192, 384 MiB less traffic than writing the
+    // fp32 product and rounding it in a second pass.  The variants map onto
+    // the one-launch kernel as hg_trmm's do: lower/trans on A, upper/trans
+    // with tri_up on A, lower/notrans with tri_up on an upper copy of Aᵀ,
+    // upper/notrans on the lower copy L = Aᵀ.
+    if (alpha != 0.0f) {
+        const TrmmVariant v = trmm_variant(uplo, trans, n, m);
+        _Float16 *L = reinterpret_cast<_Float16 *>(vwork);
+        const bool up = (uplo == HG_UPPER) == (trans == HG_TRANS);
+        const int copy_mode = trans == HG_TRANS ? 0 : (uplo == HG_LOWER ? 4 : 1);
+        _Float16 *Y = static_cast<_Float16 *>(work);
+        const hg::GemmParams p = one_launch_params(copy_mode ? static_cast<const void *>(L) : A,
+                                                   copy_mode ? v.ldl : lda, B, ldb, Y, ldx, m, n, alpha, leaf, up);
+        const int kind = one_launch_kind(p, m, n);
+        if (kind != 0) {
+            int st = HG_OK;
+            if (copy_mode)
+                st = hip_status(hg::launch_tri_xform(copy_mode, static_cast<const _Float16 *>(A), lda, L, v.ldl, n, s));
+            if (st == HG_OK)
+                st = hip_status(launch_one_launch(p, kind, true, s));
+            if (st == HG_OK)
+                st = hip_status(hipMemcpy2DAsync(B, (size_t)ldb * 2, Y, (size_t)ldx * 2, (size_t)n * 2, (size_t)m,
+                                                 hipMemcpyDeviceToDevice, s));
+            return st;
+        }
+    }
     int st = hg_trmm(uplo, trans, n, m, alpha, A, lda, B, ldb, X, ldx, HG_F32, leaf, vwork,
                      work_bytes - x_bytes, stream);
     if (st != HG_OK)
         return st;   // a HIP error: the arguments were checked above
-    return hip_status(hg::launch_f32_to_f16(X, ldx, static_cast<_Float16 *>(B), ldb, n, m,
-                                            static_cast<hipStream_t>(stream)));
+    return hip_status(hg::launch_f32_to_f16(X, ldx, static_cast<_Float16 *>(B), ldb, n, m, s));
 }
 
 }  // extern "C"

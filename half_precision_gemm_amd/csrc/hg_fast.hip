@@ -754,6 +754,8 @@ hgemm_fast_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int c
                                          : alpha * v;
                             if constexpr (EPI)
                                 t = epi_apply(t, bv[j][e], p.act);
+                            if constexpr (OUT_F16 && TRI)
+                                t = opaque_f32(t);   // the in-place TRMM: the fp32 result, rounded
                             r[e] = (celt)t;
                         }
                         if constexpr (STAGE)
@@ -814,6 +816,8 @@ hgemm_fast_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int c
                                 float t = RD ? __builtin_fmaf(alpha, v, beta * (float)*cp) : alpha * v;
                                 if constexpr (EPI)
                                     t = epi_apply(t, b, p.act);
+                                if constexpr (TRI)
+                                    t = opaque_f32(t);
                                 *cp = (e16)t;
                             } else {
                                 float *cp = static_cast<float *>(p.C) + off + e;
@@ -903,7 +907,7 @@ hipError_t launch(const GemmParams &p, hipStream_t stream)
 
 }  // namespace
 
-hipError_t launch_trmm_fused(const GemmParams &p, hipStream_t stream)
+hipError_t launch_trmm_fused(const GemmParams &p, hipStream_t stream, bool out_f16)
 {
     const int tiles_m = (p.M + BM - 1) / BM;
     const int tiles_n = p.e[0].N / BN;
@@ -912,15 +916,19 @@ hipError_t launch_trmm_fused(const GemmParams &p, hipStream_t stream)
         return hipSuccess;
     if (total64 > 0x7fffffff)
         return hipErrorInvalidConfiguration;
-    const int cvec = reinterpret_cast<uintptr_t>(p.C) % 16 == 0 && p.ldc % 4 == 0;
+    const int cvec = reinterpret_cast<uintptr_t>(p.C) % (out_f16 ? 8 : 16) == 0 && p.ldc % 4 == 0;
     // one persistent workgroup per CU, at most one per job (see fused_item)
     const int64_t jobs = (int64_t)tiles_m * (tiles_n / 2) + ((tiles_n & 1) ? (tiles_m + 1) / 2 : 0);
     int64_t grid = cu_count();
     grid = grid / 8 * 8 > 0 ? grid / 8 * 8 : grid;
     if (grid > jobs)
         grid = jobs;
-    hipLaunchKernelGGL((hgemm_fast_kernel<false, false, true, false, true, false, false>), dim3((unsigned)grid),
-                       dim3(THREADS), 0, stream, p, tiles_m, tiles_n, (int)total64, cvec);
+    if (out_f16)
+        hipLaunchKernelGGL((hgemm_fast_kernel<true, false, true, false, true, false, false>), dim3((unsigned)grid),
+                           dim3(THREADS), 0, stream, p, tiles_m, tiles_n, (int)total64, cvec);
+    else
+        hipLaunchKernelGGL((hgemm_fast_kernel<false, false, true, false, true, false, false>), dim3((unsigned)grid),
+                           dim3(THREADS), 0, stream, p, tiles_m, tiles_n, (int)total64, cvec);
     return hipGetLastError();
 }
 

@@ -48,6 +48,16 @@ __device__ __forceinline__ float epi_apply(float t, float bias, int act)
     return (act == 1 && t < 0.0f) ? 0.0f : t;
 }
 
+// v as an fp32 value the compiler cannot see through: a product rounded to
+// fp32 here and then converted to a 16-bit type is rounded twice, as when an
+// fp32 result is stored and converted later, instead of being fused with the
+// conversion into one rounding (v_fma_mix).
+__device__ __forceinline__ float opaque_f32(float v)
+{
+    __asm__("" : "+v"(v));
+    return v;
+}
+
 // Compute units of the current device (queried once per device).
 int cu_count();
 
@@ -91,13 +101,15 @@ hipError_t launch_gemm_ring(const GemmParams &p, const LaunchOpts &o, hipStream_
 // trmm_fused_ok: the operands suit the fast path, every recursion boundary
 // falls on a 256-column tile edge, and there are at least two output tiles
 // per CU.
+// With out_f16 the tiles are written as fp16 (alpha·acc rounded once to
+// nearest even) instead of fp32; p.C points to fp16 elements then.
 bool trmm_fused_ok(const GemmParams &p);
-hipError_t launch_trmm_fused(const GemmParams &p, hipStream_t stream);
+hipError_t launch_trmm_fused(const GemmParams &p, hipStream_t stream, bool out_f16 = false);
 // The same one-launch recursion on 64×64 tiles (hg_ring.hip), one workgroup
 // per tile, for right-hand sides too narrow to give every CU two 256×256
 // tiles: every recursion boundary on a 64-column tile edge, leaf >= 64.
 bool trmm_ring_fused_ok(const GemmParams &p);
-hipError_t launch_trmm_fused_ring(const GemmParams &p, hipStream_t stream);
+hipError_t launch_trmm_fused_ring(const GemmParams &p, hipStream_t stream, bool out_f16 = false);
 
 // Recursive triangular solve X = alpha·A⁻ᵀ·B (hg_trsm.hip).  Leaves are at
 // most kTrsmLeafMax rows; their inverses V_L = A_LL⁻¹ are stored in fp16 as

@@ -373,6 +373,8 @@ hgemm_ring_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int c
                     if constexpr (EPI)
                         t = epi_apply(t, p.bias ? p.bias[n0 + wn * WTN + j * 16 + 4 * fhi + e] : -0.0f,
                                       p.act);
+                    if constexpr (OUT_F16 && TRI)
+                        t = opaque_f32(t);   // the in-place TRMM: the fp32 result, rounded
                     r[e] = (celt)t;
                 }
                 *reinterpret_cast<cvec_t *>(cr + j * 16) = r;
@@ -415,6 +417,8 @@ hgemm_ring_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int c
                     float t = BETA ? __builtin_fmaf(alpha, v, beta * cin[j][e]) : alpha * v;
                     if constexpr (EPI)
                         t = epi_apply(t, p.bias && col + e < N ? p.bias[col + e] : -0.0f, p.act);
+                    if constexpr (OUT_F16 && TRI)
+                        t = opaque_f32(t);
                     r[e] = (celt)t;
                 }
                 if (cvec && col + 3 < N) {
@@ -525,15 +529,18 @@ bool trmm_ring_fused_ok(const GemmParams &p)
     return true;
 }
 
-hipError_t launch_trmm_fused_ring(const GemmParams &p, hipStream_t stream)
+hipError_t launch_trmm_fused_ring(const GemmParams &p, hipStream_t stream, bool out_f16)
 {
     // With at least two tiles per CU, a 5-stage ring (80 KiB) lets two
     // workgroups share each CU: n = m = 2048 (1024 tiles) 33.0 -> 21.9 us.
     // With fewer tiles one workgroup per CU gets the deeper default ring.
     const int64_t tiles = (int64_t)((p.M + 63) / 64) * ((p.e[0].N + 63) / 64);
-    if (tiles >= 2 * (int64_t)cu_count())
-        return launch_ring_cfg<64, 64, false, false, false, false, true, 5>(p, stream);
-    return launch_ring_cfg<64, 64, false, false, false, false, true>(p, stream);
+    const bool two = tiles >= 2 * (int64_t)cu_count();
+    if (out_f16)
+        return two ? launch_ring_cfg<64, 64, true, false, false, false, true, 5>(p, stream)
+                   : launch_ring_cfg<64, 64, true, false, false, false, true>(p, stream);
+    return two ? launch_ring_cfg<64, 64, false, false, false, false, true, 5>(p, stream)
+               : launch_ring_cfg<64, 64, false, false, false, false, true>(p, stream);
 }
 
 hipError_t launch_gemm_ring(const GemmParams &p, const LaunchOpts &o, hipStream_t stream)

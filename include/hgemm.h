@@ -355,13 +355,16 @@ int64_t hg_trmm_workspace_size(int uplo, int trans, int64_t n, int64_t m);
  * 10 leaf        : as hg_trmm.
  * 11 work        : device workspace, 16-byte aligned, of at least
  * 12 work_bytes    hg_trmm_inplace_workspace_size(uplo, trans, n, m) bytes:
- *                  the fp32 product and hg_trmm's own workspace; must not
- *                  overlap A or B (-11; too small: -12).
+ *                  the product (fp32 room) and hg_trmm's own workspace; must
+ *                  not overlap A or B (-11; too small: -12).
  * 13 stream      : hipStream_t.
  *
- * The product is formed in fp32 (hg_trmm into the workspace) and rounded to
- * fp16 once, so B receives hg_trmm's result rounded to nearest even; no
- * intermediate of the recursion is rounded to fp16.
+ * B receives hg_trmm's fp32 result rounded to nearest even, bit for bit; no
+ * intermediate of the recursion is rounded to fp16.  When hg_trmm would run
+ * the one-launch schedule (see trmm_lower_trans), that kernel rounds each
+ * finished tile to fp16 into the workspace and one device-to-device copy
+ * moves the product into B; otherwise hg_trmm writes the fp32 product into
+ * the workspace and one pass rounds it into B.
  */
 int hg_trmm_inplace(int uplo, int trans, int64_t n, int64_t m, float alpha,
                     const void *A, int64_t lda, void *B, int64_t ldb,

@@ -2,8 +2,9 @@
 ("异构计算中高性能TRMM与TRSM的递归算法实现" §2.2), against the fp64 oracle,
 through the C ABI.
 
-The product is formed in fp32 and rounded to fp16 once, so the fp16 rule of
-the GEMM holds: |gpu − ref| <= 1e-3·sqrt(n) + 2^-10·|ref|.  Integer inputs give
+The product is accumulated in fp32 and rounded to fp16 once (in the
+one-launch kernel's epilogue, or by a pass over the fp32 product), so the
+fp16 rule of the GEMM holds: |gpu − ref| <= 1e-3·sqrt(n) + 2^-10·|ref|.  Integer inputs give
 an exact fp32 product, so B must equal the oracle's product rounded to fp16
 (nearest even) bit for bit.
 """
@@ -75,23 +76,26 @@ def test_integer_bit_exact(hg, uplo, trans):
     assert np.array_equal(got.view(np.uint16), ref.astype(np.float16).view(np.uint16))
 
 
-@pytest.mark.parametrize("pad", [5, 0])
-def test_equals_out_of_place_rounded(hg, pad):
+@pytest.mark.parametrize("uplo,trans", VARIANTS)
+@pytest.mark.parametrize("n,m,pad", [(1536, 200, 5), (1536, 200, 0), (2048, 16384, 0)])
+def test_equals_out_of_place_rounded(hg, uplo, trans, n, m, pad):
     """The in-place result is hg_trmm's fp32 result rounded to nearest even,
     bit for bit, with a workspace of NaN patterns.  The out-of-place call
     gets B with the same leading dimension, so both take the same schedule:
-    per level when it is padded to an odd value, in one launch otherwise."""
+    per level when it is padded to an odd value, in one launch otherwise
+    (n = 1536, m = 200: 64×64 tiles; n = 2048, m = 16384: 256×256 tiles),
+    where the in-place form rounds each tile to fp16 in the kernel instead
+    of rounding the fp32 product in a second pass."""
     import torch
-    n, m = 1536, 200
-    rng = np.random.default_rng(5)
-    A_cm = _tri(rng, n, "L")
+    rng = np.random.default_rng(5 + n + m + pad)
+    A_cm = _tri(rng, n, uplo)
     B_cm = workloads.uniform_f16(rng, (m, n))
-    got = run(hg, A_cm, B_cm, -1.25, "L", False, pad=pad, work_fill=0xFF)
+    got = run(hg, A_cm, B_cm, -1.25, uplo, trans, pad=pad, work_fill=0xFF)
     dev = torch.device("cuda:0")
     Out = torch.empty((m, n), dtype=torch.float32, device=dev)
     Bd = torch.zeros((m, n + pad), dtype=torch.float16, device=dev)[:, :n]
     Bd.copy_(torch.from_numpy(B_cm))
-    hg.trmm(torch.from_numpy(A_cm).to(dev), Bd, Out, -1.25, "L", False)
+    hg.trmm(torch.from_numpy(A_cm).to(dev), Bd, Out, -1.25, uplo, trans)
     torch.cuda.synchronize()
     want = Out.cpu().numpy().astype(np.float16)
     assert np.array_equal(got.view(np.uint16), want.view(np.uint16))
