@@ -671,6 +671,22 @@ hgemm_fast_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int c
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
 
+        // EPI: this lane's 4 columns of each column block of an interior
+        // tile.  Loaded before the next tile's prologue: the counter retires
+        // in issue order, so loads issued after the prologue would also
+        // wait for its two stages.
+        float bv[EPI ? TN : 1][4];
+        if constexpr (EPI) {
+            if (T.rows_a == BM && T.rows_b == BN && cvec) {
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        bv[j][e] = p.bias ? p.bias[T.n0 + wn * WTN + j * FB + 4 * (lane >> 4) + e] : -0.0f;
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+
         // ---- Next tile's first stages, in flight during this epilogue.
         int nid = id + stride;
         TileInfo Tn;
@@ -719,15 +735,6 @@ hgemm_fast_kernel(const GemmParams p, int tiles_m, int tiles_n, int total, int c
 #pragma unroll
                         for (int j = 0; j < TN; ++j)
                             cin[i][j] = *reinterpret_cast<const cvec *>(crow(i) + j * FB);
-                }
-                // EPI: this lane's 4 columns of each column block, once per tile.
-                float bv[EPI ? TN : 1][4];
-                if constexpr (EPI) {
-#pragma unroll
-                    for (int j = 0; j < TN; ++j)
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            bv[j][e] = p.bias ? p.bias[T.n0 + wn * WTN + j * FB + 4 * fhi + e] : -0.0f;
                 }
                 // With 128-column wave sub-tiles each 16-row block goes
                 // through LDS (A ring slot 2, which the next tile's prologue
