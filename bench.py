@@ -304,6 +304,32 @@ def config_sweep(hg, stream, main_gemm_ms=None, main_trmm_ms=None, only=None):
             "note": "C = relu(A*B + bias), 8192^3, fp16 out, one launch; the unfused sequence adds "
                     "two passes over C (torch elementwise ops)"}
         del Ad, Btd, Cd, biasd
+    if only is not None and "torch_matmul_8192" in only:
+        # Same-box reference, only when asked for by name: the vendor GEMM
+        # behind torch.matmul (fp16 C) on the 8192³ inputs, alternated with
+        # this library's fp16-C GEMM, three rounds of 30 timed calls each.
+        print("[bench] config torch_matmul_8192 ...", file=sys.stderr, flush=True)
+        w = workloads.WORKLOADS["hgemm_8192"]
+        A, Bt, _ = workloads.gemm_inputs(w)
+        Ad, Btd = torch.from_numpy(A).to(dev), torch.from_numpy(Bt).to(dev)
+        Bcm = Btd.t()                      # K×N column-major view: B of C = A·B
+        Cv = torch.empty((w.M, w.N), dtype=torch.float16, device=dev)
+        Co = torch.empty((w.M, w.N), dtype=torch.float16, device=dev)
+        vendor = lambda: torch.matmul(Ad, Bcm, out=Cv)
+        ours = lambda: hg.hgemm(Ad, Btd, Co)
+        tv, to = [], []
+        for _ in range(3):
+            tv.append(_time_calls(vendor, 20, 30, stream)[0])
+            to.append(_time_calls(ours, 20, 30, stream)[0])
+        torch.cuda.synchronize()
+        diff = (Cv.float() - Co.float()).abs().max().item()
+        res["torch_matmul_8192"] = {
+            "torch_matmul_fp16_out_ms_median": [round(x, 5) for x in tv],
+            "hgemm_fp16_out_ms_median": [round(x, 5) for x in to],
+            "max_abs_diff_fp16_outputs": diff,
+            "note": "same-box reference: torch.matmul (fp16 in, fp16 out) against hgemm with fp16 C "
+                    "on the same inputs, alternated, one median per round"}
+        del Ad, Btd, Cv, Co
     if want("hgemm_bf16_8192"):
         # bf16 operands (next row): the 8192³ shape, values drawn as the HGEMM
         # workload's and rounded to bf16, fp32 C.
