@@ -174,3 +174,25 @@ def test_ring_one_launch_integer_bit_exact(hg, uplo, trans):
     A_cm, B_cm = np.ascontiguousarray(T.T), np.ascontiguousarray(B.T)
     got = run(hg, A_cm, B_cm, 1.0, uplo, trans)
     assert np.array_equal(got.astype(np.float64), _ref(A_cm, B_cm, 1.0, uplo, trans))
+
+
+# ---- A with a padded leading dimension.  n a multiple of 64: the variants
+# that copy A (all but lower/transposed) take the 16-byte copy kernel when
+# lda is a multiple of 8 (pad 8) and the element-wise one otherwise (pad 3);
+# n = 2560 runs the per-level schedule (reversing copies for two variants),
+# n = 2048 with m = 300 the one-launch schedule on 64×64 tiles.
+@pytest.mark.parametrize("uplo,trans", VARIANTS)
+@pytest.mark.parametrize("n,m,pad", [(2560, 100, 3), (2560, 100, 8), (2048, 300, 8)])
+def test_padded_lda(hg, uplo, trans, n, m, pad):
+    import torch
+    dev = torch.device("cuda:0")
+    A_cm, B_cm = _inputs(n, m, n + m + pad, uplo, other_fill=np.nan)
+    Ap = torch.full((n, n + pad), float("nan"), dtype=torch.float16, device=dev)
+    Ap[:, :n] = torch.from_numpy(A_cm).to(dev)
+    print(f"[trmm-variant] padded lda n={n} m={m} pad={pad} uplo={uplo} trans={trans}", flush=True)
+    Out = torch.full((m, n), float("nan"), dtype=torch.float32, device=dev)
+    hg.trmm(Ap[:, :n], torch.from_numpy(B_cm).to(dev), Out, 0.75, uplo, trans)
+    torch.cuda.synchronize()
+    got = Out.cpu().numpy()
+    ref = _ref(np.where(np.isnan(A_cm), np.float16(0), A_cm), B_cm, 0.75, uplo, trans)
+    check_close(got, ref, n, f"padded lda {uplo}{'T' if trans else 'N'} n={n} pad={pad}")
