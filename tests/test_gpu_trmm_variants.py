@@ -196,3 +196,25 @@ def test_padded_lda(hg, uplo, trans, n, m, pad):
     got = Out.cpu().numpy()
     ref = _ref(np.where(np.isnan(A_cm), np.float16(0), A_cm), B_cm, 0.75, uplo, trans)
     check_close(got, ref, n, f"padded lda {uplo}{'T' if trans else 'N'} n={n} pad={pad}")
+
+
+@pytest.mark.parametrize("uplo,trans", VARIANTS)
+def test_one_launch_ragged_tile_rows(hg, uplo, trans):
+    """m = 16484 gives 65 tile rows of 256, the last holding 100 rows of Out's
+    transpose (columns of B), with 8 tile columns at n = 2048: the 256×256
+    one-launch schedule, whose last row of tiles takes the edge epilogue.
+    Every entry of B's last 100 columns against the oracle, plus the usual
+    1024 samples."""
+    n, m = 2048, 16484
+    A_cm, B_cm = _inputs(n, m, 61, uplo)
+    got = run(hg, A_cm, B_cm, 0.5, uplo, trans)
+    assert np.isfinite(got).all()
+    u = oracle.LOWER if uplo == "L" else oracle.UPPER
+    t = oracle.TRANS if trans else oracle.NOTRANS
+    jj, ii = np.meshgrid(np.arange(m - 100, m), np.arange(n), indexing="ij")
+    ri, cj = ii.ravel(), jj.ravel()
+    ref = oracle.trmm_sampled(A_cm, B_cm, ri, cj, 0.5, u, t)
+    check_close(got[cj, ri], ref, n, f"{uplo}{'T' if trans else 'N'} ragged tile row")
+    ri, cj = workloads.sample_indices(n + m, n, m)
+    ref = oracle.trmm_sampled(A_cm, B_cm, ri, cj, 0.5, u, t)
+    check_close(got[cj, ri], ref, n, f"{uplo}{'T' if trans else 'N'} n={n} m={m} sampled")
