@@ -77,13 +77,15 @@ def test_integer_bit_exact(hg, uplo, trans):
 
 
 @pytest.mark.parametrize("uplo,trans", VARIANTS)
-@pytest.mark.parametrize("n,m,pad", [(1536, 200, 5), (1536, 200, 0), (2048, 16384, 0), (2048, 16484, 0)])
+@pytest.mark.parametrize("n,m,pad", [(1536, 200, 5), (1536, 200, 0), (2048, 1024, 0), (2048, 16384, 0),
+                                     (2048, 16484, 0)])
 def test_equals_out_of_place_rounded(hg, uplo, trans, n, m, pad):
     """The in-place result is hg_trmm's fp32 result rounded to nearest even,
     bit for bit, with a workspace of NaN patterns.  The out-of-place call
     gets B with the same leading dimension, so both take the same schedule:
     per level when it is padded to an odd value, in one launch otherwise
-    (n = 1536, m = 200: 64×64 tiles; n = 2048, m = 16384: 256×256 tiles;
+    (n = 1536, m = 200: 64×64 tiles, one workgroup per CU; n = 2048, m = 1024:
+    64×64 tiles, two per CU; n = 2048, m = 16384: 256×256 tiles;
     m = 16484: the last row of 256×256 tiles holds 100 rows, edge epilogue),
     where the in-place form rounds each tile to fp16 in the kernel instead
     of rounding the fp32 product in a second pass."""
